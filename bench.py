@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark on one MI355X: FP8 (e4m3) vs BF16 paged KV cache.
+
+A step is one pass of the whole hot path for one attention layer over one
+batch: the batched page-tag check, the append of every request's new token
+(quantised to e4m3 for the FP8 cache) and paged decode attention (split
+kernel + log-sum-exp merge when the context is split).  Inputs are resident
+in HBM before timing starts.  Default workload: 64 requests x 8192 tokens,
+64 query / 8 KV heads, head_dim 128, page size 16, 40,000-page pool, one
+stale expected tag (1% of requests, that request aborted and its bytes
+excluded).
+
+Prints one JSON line (rank 0).  Metric: KV-read GB/s of the whole step
+(algorithmic bytes: sum over non-aborted requests of L * Hkv * D * 2 * bytes
+per element) and steps/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8.0 TB/s
+METRIC = "decode-attn KV-read GB/s (% of HBM peak) + steps/s, FP8 vs BF16 KV cache"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="sweep_b64")
+    p.add_argument("--splits", type=int, default=0, help="0 = library choice")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-bf16", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=4, help="requests in the CPU oracle sample")
+    p.add_argument("--fp8-only-steps", action="store_true", help="time only the FP8 step (profiling runs)")
+    return p.parse_args()
+
+
+class DeviceCache:
+    """One workload's cache on the device (FP8 or BF16), filled through the library's append."""
+
+    def __init__(self, w, kv_dtype, host, torch, kv):
+        self.w, self.kv_dtype, self.torch, self.kv = w, kv_dtype, torch, kv
+        dev = host["dev"]
+        elt = 1 if kv_dtype == "fp8" else 2
+        nk = w.num_pages * w.num_kv_heads * w.page_size * w.head_dim
+        tdt = torch.uint8 if kv_dtype == "fp8" else torch.int16
+        # pool contents before the fill do not matter for timing: zero them on the device
+        self.kp = torch.zeros(nk, dtype=tdt, device="cuda")
+        self.vp = torch.zeros(nk, dtype=tdt, device="cuda")
+        self.desc = kv.pool_desc(w.num_pages, w.page_size, w.num_kv_heads, w.head_dim, w.v_dim)
+        self.pt, self.lens, self.q = host["dpt"], host["dlens"], host["dq"]
+        self.tags, self.exp = host["dtags"], host["dexp"]
+        self.max_ctx = host["max_ctx"]
+        if kv_dtype == "fp8":
+            self.k_scale = kv.calibrate_scale(host["dk"])
+            self.v_scale = kv.calibrate_scale(host["dv"])
+            kv.kv_append_fp8(self.desc, self.kp, self.vp, host["dk"], host["dv"], host["dreq"], host["dpos"],
+                             self.pt, k_scale=self.k_scale, v_scale=self.v_scale)
+        else:
+            self.k_scale = self.v_scale = 1.0
+            kv.kv_append_bf16(self.desc, self.kp, self.vp, host["dk"], host["dv"], host["dreq"], host["dpos"],
+                              self.pt)
+        self.k_new, self.v_new = host["dk_new"], host["dv_new"]
+        self.s_req, self.s_pos = host["ds_req"], host["ds_pos"]
+        self.out = torch.empty((w.batch, w.num_q_heads, w.v_dim), dtype=torch.int16, device="cuda")
+        self.flags = torch.zeros(w.batch, dtype=torch.int32, device="cuda")
+        self.splits = host["splits"] or kv.paged_decode_attn_auto_splits(w.batch, w.num_kv_heads, self.max_ctx)
+        n = kv.paged_decode_attn_workspace_bytes(w.batch, w.num_q_heads, w.v_dim, self.splits)
+        self.ws = torch.empty(max(n // 4, 4), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+
+    def check(self):
+        self.kv.kv_tag_check(self.tags, self.pt, self.exp, self.lens, self.w.page_size, self.flags)
+
+    def append(self, tracker=True):
+        f = self.flags if tracker else None
+        if self.kv_dtype == "fp8":
+            self.kv.kv_append_fp8(self.desc, self.kp, self.vp, self.k_new, self.v_new, self.s_req, self.s_pos,
+                                  self.pt, f, k_scale=self.k_scale, v_scale=self.v_scale)
+        else:
+            self.kv.kv_append_bf16(self.desc, self.kp, self.vp, self.k_new, self.v_new, self.s_req, self.s_pos,
+                                   self.pt, f)
+
+    def attend(self, tracker=True):
+        f = self.flags if tracker else None
+        if self.kv_dtype == "fp8":
+            self.kv.paged_decode_attn_fp8(self.desc, self.q, self.kp, self.vp, self.pt, self.lens, self.max_ctx,
+                                          self.out, f, k_scale=self.k_scale, v_scale=self.v_scale,
+                                          num_splits=self.splits, workspace=self.ws)
+        else:
+            self.kv.paged_decode_attn_bf16(self.desc, self.q, self.kp, self.vp, self.pt, self.lens, self.max_ctx,
+                                           self.out, f, num_splits=self.splits, workspace=self.ws)
+
+    def run(self, steps, warmup, tracker=True):
+        """Time `steps` steps; per-kernel HIP events on the launch stream (torch's current stream)."""
+        torch = self.torch
+        for _ in range(warmup):
+            if tracker:
+                self.check()
+            self.append(tracker)
+            self.attend(tracker)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t0.record()
+        for e in evs:
+            e[0].record()
+            if tracker:
+                self.check()
+            e[1].record()
+            self.append(tracker)
+            e[2].record()
+            self.attend(tracker)
+            e[3].record()
+        t1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
+        total_ms = t0.elapsed_time(t1)
+        return dict(ms_per_step=total_ms / steps, wall_ms_per_step=1e3 * wall / steps,
+                    check_ms=float(np.median(per[:, 0])), append_ms=float(np.median(per[:, 1])),
+                    attn_ms=float(np.median(per[:, 2])), attn_ms_mean=float(per[:, 2].mean()),
+                    attn_ms_p95=float(np.percentile(per[:, 2], 95)),
+                    step_ms_p95=float(np.percentile(per.sum(axis=1), 95)))
+
+
+def cpu_baseline(w, n_req):
+    """The oracle's step (tag check, e4m3 append of one token per request, fp64 attention) on a sample."""
+    from concurrent.futures import ThreadPoolExecutor  # noqa: F401
+    from threadpoolctl import threadpool_limits
+
+    from kvsynth import workloads as wl
+    from oracle import codec, paged, step
+
+    ws = w.with_(batch=n_req, num_pages=int(wl.pages_needed(wl.ctx_lens(w.with_(batch=n_req)), w.page_size).sum()),
+                 stale=False)
+    lens = wl.ctx_lens(ws)
+    pt, _ = wl.page_table(ws, lens)
+    k, v = wl.all_kv(ws, lens)
+    req, pos = wl.token_index(lens)
+    ks, vs = codec.calibrate_scale(k), codec.calibrate_scale(v)
+    kp, vp = wl.pool_bytes(ws, "k", 1), wl.pool_bytes(ws, "v", 1)
+    paged.append_fp8(kp, vp, k, v, req, pos, pt, ws.num_kv_heads, ws.page_size, ks, vs)
+    tags = wl.page_tags(ws)
+    st = dict(dtype="fp8", k_pool=kp, v_pool=vp, page_table=pt, ctx_lens=lens, page_tags=tags,
+              expected_tags=wl.expected_tags(ws, pt, lens, tags), num_kv_heads=ws.num_kv_heads,
+              page_size=ws.page_size, head_dim=ws.head_dim, v_dim=ws.v_dim, k_scale=ks, v_scale=vs,
+              sm_scale=1 / math.sqrt(ws.head_dim), latent=False)
+    last = np.cumsum(lens) - 1
+    workers = min(16, os.cpu_count() or 1, n_req)
+    with threadpool_limits(1):
+        t = time.perf_counter()
+        step.decode_step(st, wl.queries(ws), k[last], v[last], np.arange(n_req, dtype=np.int32),
+                         (lens - 1).astype(np.int32), workers=workers)
+        dt = time.perf_counter() - t
+    kv_bytes = int(lens.astype(np.int64).sum()) * ws.num_kv_heads * ws.head_dim * 2
+    return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": f"{n_req} of {w.batch} requests of {w.name} (same shapes, FP8 cache), one decode step "
+                      f"(tag check + e4m3 append + fp64 attention) in {dt:.2f} s",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the decode path is single-GPU "
+                                   "(requests or KV heads would shard across GPUs with no exchange)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import fp8_paged_kv_append_amd as kv
+    from kvsynth import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    log(f"workload {w}")
+    t = time.perf_counter()
+    lens = wl.ctx_lens(w)
+    pt, _ = wl.page_table(w, lens)
+    tags = wl.page_tags(w)
+    stale = wl.stale_requests(w)
+    exp = wl.expected_tags(w, pt, lens, tags, stale)
+    k, v = wl.all_kv(w, lens)
+    req, pos = wl.token_index(lens)
+    q = wl.queries(w)
+    log(f"generated inputs in {time.perf_counter() - t:.1f} s")
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        elif a.dtype == np.uint32:
+            a = a.view(np.int32)
+        return torch.from_numpy(a).cuda()
+
+    last = np.cumsum(lens.astype(np.int64)) - 1
+    host = dict(dev=dev, dpt=dev(pt), dlens=dev(lens), dq=dev(q), dtags=dev(tags), dexp=dev(exp),
+                dk=dev(k), dv=dev(v), dreq=dev(req), dpos=dev(pos), dk_new=dev(k[last]), dv_new=dev(v[last]),
+                ds_req=dev(np.arange(w.batch, dtype=np.int32)), ds_pos=dev((lens - 1).astype(np.int32)),
+                max_ctx=int(lens.max()), splits=args.splits)
+    del k, v
+    live = np.ones(w.batch, dtype=bool)
+    live[stale] = False
+    kv_elems = int(lens[live].astype(np.int64).sum()) * w.num_kv_heads * (w.head_dim + w.v_dim)
+
+    results = {}
+    for kvd in (["fp8"] if (args.no_bf16 or args.fp8_only_steps) else ["fp8", "bf16"]):
+        t = time.perf_counter()
+        c = DeviceCache(w, kvd, host, torch, kv)
+        log(f"{kvd}: cache filled in {time.perf_counter() - t:.1f} s, splits={c.splits}")
+        r = c.run(args.steps, args.warmup, tracker=True)
+        flags = c.flags.cpu().numpy().view(np.uint32)
+        assert np.flatnonzero(flags).tolist() == stale.tolist(), "abort flags differ from the planted stale set"
+        if not args.fp8_only_steps:
+            r["no_tracker"] = c.run(args.steps, args.warmup, tracker=False)
+        elt = 1 if kvd == "fp8" else 2
+        r["kv_bytes"] = kv_elems * elt
+        r["gbs_step"] = r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
+        r["gbs_attn"] = r["kv_bytes"] / (r["attn_ms_mean"] * 1e-3) / 1e9
+        r["splits"] = c.splits
+        results[kvd] = r
+        log(f"{kvd}: {json.dumps({k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in r.items() if k_ != 'no_tracker'})}")
+        del c
+        torch.cuda.empty_cache()
+
+    f8 = results["fp8"]
+    line = {
+        "metric": METRIC,
+        "value": round(f8["gbs_step"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(f8["ms_per_step"], 5),
+        "steps_per_s": round(1e3 / f8["ms_per_step"], 1),
+        "pct_hbm_peak": round(100 * f8["gbs_step"] / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "kv_cache": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.batch} requests x {w.ctx_hi} tokens, {w.num_q_heads} query / "
+                               f"{w.num_kv_heads} KV heads, head_dim {w.head_dim}, page {w.page_size}, "
+                               f"{w.num_pages}-page pool, FP8 e4m3 cache, 1% stale tags",
+                   "batch": w.batch, "ctx": int(w.ctx_hi), "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
+                   "splits": f8["splits"], "step": "tag check + append(1 token/request) + attention + merge"},
+        "roofline": {"bound": "hbm", "achieved": round(f8["gbs_attn"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(f8["gbs_attn"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_decode_attn_fp8 (split kernel + merge)",
+                     "attn_ms_mean": round(f8["attn_ms_mean"], 5), "attn_ms_p95": round(f8["attn_ms_p95"], 5)},
+        "step_breakdown_ms": {"tag_check": round(f8["check_ms"], 5), "append": round(f8["append_ms"], 5),
+                              "attention": round(f8["attn_ms"], 5), "step_p95": round(f8["step_ms_p95"], 5)},
+    }
+    if "no_tracker" in f8:
+        nt = f8["no_tracker"]
+        line["tracker_off"] = {"ms_per_step": round(nt["ms_per_step"], 5),
+                               "check_overhead_pct": round(100 * (f8["ms_per_step"] / nt["ms_per_step"] - 1), 2)}
+    if "bf16" in results:
+        b = results["bf16"]
+        line["bf16_twin"] = {"value": round(b["gbs_step"], 1), "unit": "GB/s", "ms_per_step": round(b["ms_per_step"], 5),
+                             "attn_gbs": round(b["gbs_attn"], 1), "attn_ms_mean": round(b["attn_ms_mean"], 5),
+                             "fp8_speedup_step": round(b["ms_per_step"] / f8["ms_per_step"], 3)}
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_sample} requests")
+        cb = cpu_baseline(w, args.cpu_sample)
+        line["cpu_baseline"] = {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in cb.items()
+                                if k_ != "seconds"}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,219 @@
+"""MI355X (gfx950) paged decode attention over an FP8 e4m3 or BF16 KV cache.
+
+Thin Python binding over libkvfp8.so (C ABI in include/kvfp8.h).  Every
+function here only checks and marshals torch tensors (device, dtype,
+contiguity) and passes raw pointers plus the current HIP stream; all work
+runs in the library's HIP kernels.  There is no CPU fallback: if the library
+is missing, calls raise.
+
+bf16 tensors may be passed as torch.bfloat16 or as 16-bit integer views;
+e4m3 pools as torch.uint8 (or torch.float8_e4m3fn).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import FLAG_BAD_PAGE, FLAG_TAG_MISMATCH, PoolDesc  # noqa: F401
+
+__all__ = ["KvFp8Error", "PoolDesc", "pool_desc", "kv_absmax_bf16", "kv_scale_from_absmax", "calibrate_scale",
+           "kv_append_fp8", "kv_append_bf16", "kv_tag_check", "paged_decode_attn_workspace_bytes",
+           "paged_decode_attn_auto_splits", "paged_decode_attn_fp8", "paged_decode_attn_bf16",
+           "kv_gather_fp8", "kv_gather_bf16", "decode_step", "lib"]
+
+
+class KvFp8Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.STATUS.get(status, status)} ({lib().kvfp8_status_string(status).decode()})")
+
+
+def lib():
+    return _lib.load()
+
+
+def _check(status: int, where: str):
+    if status != _lib.KVFP8_OK:
+        raise KvFp8Error(status, where)
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16) if hasattr(torch, "uint16") else (torch.bfloat16, torch.int16)
+_U8 = (torch.uint8, torch.float8_e4m3fn)
+_I32 = (torch.int32,)
+_U32 = (torch.int32, torch.uint32) if hasattr(torch, "uint32") else (torch.int32,)
+
+
+def _ptr(t: Optional[torch.Tensor], dtypes, name: str, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def pool_desc(num_pages, page_size, num_kv_heads, head_dim, v_dim=None) -> PoolDesc:
+    return PoolDesc(int(num_pages), int(page_size), int(num_kv_heads), int(head_dim),
+                    int(head_dim if v_dim is None else v_dim))
+
+
+# ----------------------------------------------------------------------------- scale
+
+def kv_absmax_bf16(x: torch.Tensor, absmax_bits: torch.Tensor, stream=None):
+    """Max-accumulate max|x| (float32 bits) into absmax_bits[0] (a device int32/uint32 tensor)."""
+    _check(lib().kv_absmax_bf16(_ptr(x, _BF16, "x"), x.numel(), _ptr(absmax_bits, _U32, "absmax_bits"),
+                                _stream(stream)), "kv_absmax_bf16")
+
+
+def kv_scale_from_absmax(absmax_bits: int) -> float:
+    return float(lib().kv_scale_from_absmax(int(absmax_bits) & 0xFFFFFFFF))
+
+
+def calibrate_scale(*tensors: torch.Tensor) -> float:
+    """Per-tensor scale fl32(max|x| / 448) over one or more bf16 device tensors (synchronises once)."""
+    acc = torch.zeros(1, dtype=torch.int32, device=tensors[0].device)
+    for t in tensors:
+        kv_absmax_bf16(t, acc)
+    return kv_scale_from_absmax(int(acc.item()))
+
+
+# ----------------------------------------------------------------------------- write path
+
+def kv_append_fp8(desc: PoolDesc, k_pool, v_pool, k_new, v_new, tok_req, tok_pos, page_table,
+                  abort_flags=None, *, k_scale: float, v_scale: float = 1.0, stream=None):
+    B, stride = page_table.shape
+    _check(lib().kv_append_fp8(
+        desc, _ptr(k_pool, _U8, "k_pool"), _ptr(v_pool, _U8, "v_pool", True), _ptr(k_new, _BF16, "k_new"),
+        _ptr(v_new, _BF16, "v_new", True), _ptr(tok_req, _I32, "tok_req"), _ptr(tok_pos, _I32, "tok_pos"),
+        tok_req.numel(), _ptr(page_table, _I32, "page_table"), B, stride,
+        _ptr(abort_flags, _U32, "abort_flags", True), float(k_scale), float(v_scale), _stream(stream)),
+        "kv_append_fp8")
+
+
+def kv_append_bf16(desc: PoolDesc, k_pool, v_pool, k_new, v_new, tok_req, tok_pos, page_table,
+                   abort_flags=None, *, stream=None):
+    B, stride = page_table.shape
+    _check(lib().kv_append_bf16(
+        desc, _ptr(k_pool, _BF16, "k_pool"), _ptr(v_pool, _BF16, "v_pool", True), _ptr(k_new, _BF16, "k_new"),
+        _ptr(v_new, _BF16, "v_new", True), _ptr(tok_req, _I32, "tok_req"), _ptr(tok_pos, _I32, "tok_pos"),
+        tok_req.numel(), _ptr(page_table, _I32, "page_table"), B, stride,
+        _ptr(abort_flags, _U32, "abort_flags", True), _stream(stream)), "kv_append_bf16")
+
+
+# ----------------------------------------------------------------------------- integrity check
+
+def kv_tag_check(page_tags, page_table, expected_tags, ctx_lens, page_size: int, abort_flags, stream=None):
+    B, stride = page_table.shape
+    _check(lib().kv_tag_check(
+        _ptr(page_tags, _U32, "page_tags"), page_tags.numel(), _ptr(page_table, _I32, "page_table"),
+        _ptr(expected_tags, _U32, "expected_tags"), stride, _ptr(ctx_lens, _I32, "ctx_lens"), B, int(page_size),
+        _ptr(abort_flags, _U32, "abort_flags"), _stream(stream)), "kv_tag_check")
+
+
+# ----------------------------------------------------------------------------- attention
+
+def paged_decode_attn_workspace_bytes(batch, num_q_heads, v_dim, num_splits) -> int:
+    return int(lib().paged_decode_attn_workspace_bytes(int(batch), int(num_q_heads), int(v_dim), int(num_splits)))
+
+
+def paged_decode_attn_auto_splits(batch, num_kv_heads, max_ctx_len) -> int:
+    return int(lib().paged_decode_attn_auto_splits(int(batch), int(num_kv_heads), int(max_ctx_len)))
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def paged_decode_attn_fp8(desc: PoolDesc, q, k_pool, v_pool, page_table, ctx_lens, max_ctx_len: int, out,
+                          abort_flags=None, *, k_scale: float, v_scale: float, sm_scale: Optional[float] = None,
+                          num_splits: int = 0, workspace=None, stream=None):
+    B, Hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    ws, wsb = _ws(workspace)
+    _check(lib().paged_decode_attn_fp8(
+        desc, _ptr(q, _BF16, "q"), Hq, _ptr(k_pool, _U8, "k_pool"), _ptr(v_pool, _U8, "v_pool"),
+        _ptr(page_table, _I32, "page_table"), page_table.shape[1], _ptr(ctx_lens, _I32, "ctx_lens"), B,
+        int(max_ctx_len), _ptr(abort_flags, _U32, "abort_flags", True), float(k_scale), float(v_scale),
+        float(sm_scale), int(num_splits), ws, wsb, _ptr(out, _BF16, "out"), _stream(stream)),
+        "paged_decode_attn_fp8")
+
+
+def paged_decode_attn_bf16(desc: PoolDesc, q, k_pool, v_pool, page_table, ctx_lens, max_ctx_len: int, out,
+                           abort_flags=None, *, sm_scale: Optional[float] = None, num_splits: int = 0,
+                           workspace=None, stream=None):
+    B, Hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    ws, wsb = _ws(workspace)
+    _check(lib().paged_decode_attn_bf16(
+        desc, _ptr(q, _BF16, "q"), Hq, _ptr(k_pool, _BF16, "k_pool"), _ptr(v_pool, _BF16, "v_pool"),
+        _ptr(page_table, _I32, "page_table"), page_table.shape[1], _ptr(ctx_lens, _I32, "ctx_lens"), B,
+        int(max_ctx_len), _ptr(abort_flags, _U32, "abort_flags", True), float(sm_scale), int(num_splits), ws, wsb,
+        _ptr(out, _BF16, "out"), _stream(stream)), "paged_decode_attn_bf16")
+
+
+# ----------------------------------------------------------------------------- read back (tests)
+
+def kv_gather_fp8(desc: PoolDesc, k_pool, v_pool, tok_req, tok_pos, page_table, k_out, v_out=None, stream=None):
+    B, stride = page_table.shape
+    _check(lib().kv_gather_fp8(
+        desc, _ptr(k_pool, _U8, "k_pool"), _ptr(v_pool, _U8, "v_pool", True), _ptr(tok_req, _I32, "tok_req"),
+        _ptr(tok_pos, _I32, "tok_pos"), tok_req.numel(), _ptr(page_table, _I32, "page_table"), B, stride,
+        _ptr(k_out, _U8, "k_out"), _ptr(v_out, _U8, "v_out", True), _stream(stream)), "kv_gather_fp8")
+
+
+def kv_gather_bf16(desc: PoolDesc, k_pool, v_pool, tok_req, tok_pos, page_table, k_out, v_out=None, stream=None):
+    B, stride = page_table.shape
+    _check(lib().kv_gather_bf16(
+        desc, _ptr(k_pool, _BF16, "k_pool"), _ptr(v_pool, _BF16, "v_pool", True), _ptr(tok_req, _I32, "tok_req"),
+        _ptr(tok_pos, _I32, "tok_pos"), tok_req.numel(), _ptr(page_table, _I32, "page_table"), B, stride,
+        _ptr(k_out, _BF16, "k_out"), _ptr(v_out, _BF16, "v_out", True), _stream(stream)), "kv_gather_bf16")
+
+
+# ----------------------------------------------------------------------------- one decode step
+
+def decode_step(desc: PoolDesc, kv_dtype: str, k_pool, v_pool, page_table, ctx_lens, max_ctx_len: int, q,
+                k_new, v_new, tok_req, tok_pos, out, *, page_tags=None, expected_tags=None, abort_flags=None,
+                k_scale: float = 1.0, v_scale: float = 1.0, sm_scale: Optional[float] = None, num_splits: int = 0,
+                workspace=None, stream=None):
+    """One attention layer's decode step, in stream order: tag check -> append -> attention.
+
+    With page_tags/expected_tags given, the batched check writes abort_flags
+    first and both later launches honour them; with page_tags None (the
+    no-op tracker) no check runs and abort_flags is passed through (None =
+    no flags).
+    """
+    if page_tags is not None:
+        if expected_tags is None or abort_flags is None:
+            raise ValueError("the tag check needs expected_tags and an abort_flags buffer")
+        kv_tag_check(page_tags, page_table, expected_tags, ctx_lens, desc.page_size, abort_flags, stream=stream)
+    if kv_dtype == "fp8":
+        kv_append_fp8(desc, k_pool, v_pool, k_new, v_new, tok_req, tok_pos, page_table, abort_flags,
+                      k_scale=k_scale, v_scale=v_scale, stream=stream)
+        paged_decode_attn_fp8(desc, q, k_pool, v_pool, page_table, ctx_lens, max_ctx_len, out, abort_flags,
+                              k_scale=k_scale, v_scale=v_scale, sm_scale=sm_scale, num_splits=num_splits,
+                              workspace=workspace, stream=stream)
+    elif kv_dtype == "bf16":
+        kv_append_bf16(desc, k_pool, v_pool, k_new, v_new, tok_req, tok_pos, page_table, abort_flags, stream=stream)
+        paged_decode_attn_bf16(desc, q, k_pool, v_pool, page_table, ctx_lens, max_ctx_len, out, abort_flags,
+                               sm_scale=sm_scale, num_splits=num_splits, workspace=workspace, stream=stream)
+    else:
+        raise ValueError(f"kv_dtype {kv_dtype!r}")

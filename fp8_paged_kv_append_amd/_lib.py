@@ -1,0 +1,65 @@
+"""ctypes loader for libkvfp8.so and the C prototypes of include/kvfp8.h."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvfp8.so")
+
+KVFP8_OK = 0
+STATUS = {0: "KVFP8_OK", -1: "KVFP8_ERR_NULL", -2: "KVFP8_ERR_SHAPE", -3: "KVFP8_ERR_UNSUPPORTED",
+          -4: "KVFP8_ERR_WORKSPACE", -5: "KVFP8_ERR_ALIGN", -6: "KVFP8_ERR_HIP", -7: "KVFP8_ERR_VALUE"}
+FLAG_TAG_MISMATCH = 1
+FLAG_BAD_PAGE = 2
+
+
+class PoolDesc(C.Structure):
+    _fields_ = [("num_pages", C.c_int32), ("page_size", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("v_dim", C.c_int32)]
+
+
+_p = C.c_void_p
+_i32 = C.c_int32
+_i64 = C.c_int64
+_f32 = C.c_float
+_u32 = C.c_uint32
+_sz = C.c_size_t
+_desc = C.POINTER(PoolDesc)
+
+PROTOTYPES = {
+    "kvfp8_abi_version": (C.c_int, []),
+    "kvfp8_status_string": (C.c_char_p, [C.c_int]),
+    "kv_absmax_bf16": (C.c_int, [_p, _i64, _p, _p]),
+    "kv_scale_from_absmax": (_f32, [_u32]),
+    "kv_append_fp8": (C.c_int, [_desc, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _p, _f32, _f32, _p]),
+    "kv_append_bf16": (C.c_int, [_desc, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _p, _p]),
+    "kv_tag_check": (C.c_int, [_p, _i32, _p, _p, _i32, _p, _i32, _i32, _p, _p]),
+    "paged_decode_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "paged_decode_attn_auto_splits": (_i32, [_i32, _i32, _i32]),
+    "paged_decode_attn_fp8": (C.c_int, [_desc, _p, _i32, _p, _p, _p, _i32, _p, _i32, _i32, _p, _f32, _f32,
+                                        _f32, _i32, _p, _sz, _p, _p]),
+    "paged_decode_attn_bf16": (C.c_int, [_desc, _p, _i32, _p, _p, _p, _i32, _p, _i32, _i32, _p, _f32, _i32,
+                                         _p, _sz, _p, _p]),
+    "kv_gather_fp8": (C.c_int, [_desc, _p, _p, _p, _p, _i32, _p, _i32, _i32, _p, _p, _p]),
+    "kv_gather_bf16": (C.c_int, [_desc, _p, _p, _p, _p, _i32, _p, _i32, _i32, _p, _p, _p]),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> C.CDLL:
+    """Load the HIP library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m fp8_paged_kv_append_amd.build` "
+                           "(the decode path has no fallback)")
+    lib = C.CDLL(path)
+    for name, (res, args) in PROTOTYPES.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib

@@ -1,0 +1,280 @@
+// Host side of the C ABI declared in include/kvfp8.h: argument checks, the
+// split heuristic, scalar pre-computation, launches.  No allocation, no
+// synchronisation, no printing.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/kvfp8.h"
+#include "kvfp8_internal.h"
+
+using namespace kvfp8;
+
+namespace {
+
+constexpr int kHeadDim = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool good_scale(float s) { return isfinite(s) && s > 0.f; }
+
+int check_pool(const kvfp8_pool_desc* d, bool need_v_dim_eq) {
+  if (d == nullptr) return KVFP8_ERR_NULL;
+  if (d->num_pages < 1 || d->page_size < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->v_dim < 0)
+    return KVFP8_ERR_SHAPE;
+  if (d->page_size % 16 != 0 || d->page_size > 256) return KVFP8_ERR_UNSUPPORTED;
+  if (d->head_dim % 16 != 0 || d->v_dim % 16 != 0) return KVFP8_ERR_UNSUPPORTED;
+  if (need_v_dim_eq && (d->head_dim != kHeadDim || d->v_dim != kHeadDim)) return KVFP8_ERR_UNSUPPORTED;
+  return KVFP8_OK;
+}
+
+int32_t n_tiles_of(int32_t max_ctx) { return (int32_t)(((int64_t)max_ctx + kAttnTileTokens - 1) / kAttnTileTokens); }
+
+// Blocks (4 waves each) the launch aims for: 4 per CU on 256 CUs.
+constexpr int64_t kTargetBlocks = 1024;
+
+int32_t auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_ctx) {
+  const int64_t items = (int64_t)batch * num_kv_heads;
+  const int32_t tiles = n_tiles_of(max_ctx);
+  if (items <= 0 || tiles <= 0) return 1;
+  int64_t s = (kTargetBlocks + items - 1) / items;
+  int64_t cap = tiles / 4;  // at least one tile per wave
+  if (cap < 1) cap = 1;
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  return (int32_t)s;
+}
+
+int append_common(const kvfp8_pool_desc* desc, void* k_pool, void* v_pool, const uint16_t* k_new,
+                  const uint16_t* v_new, const int32_t* tok_req, const int32_t* tok_pos, int32_t n_tokens,
+                  const int32_t* page_table, int32_t batch, int32_t pt_stride, const uint32_t* flags,
+                  bool fp8, float k_scale, float v_scale, hipStream_t stream) {
+  int st = check_pool(desc, false);
+  if (st) return st;
+  if (n_tokens < 0 || batch < 0 || pt_stride < 1) return KVFP8_ERR_SHAPE;
+  if (n_tokens == 0) return KVFP8_OK;
+  if (!k_pool || !k_new || !tok_req || !tok_pos || !page_table) return KVFP8_ERR_NULL;
+  if ((v_pool == nullptr) != (v_new == nullptr)) return KVFP8_ERR_NULL;
+  if (!aligned16(k_pool) || !aligned16(k_new) || (v_pool && (!aligned16(v_pool) || !aligned16(v_new))))
+    return KVFP8_ERR_ALIGN;
+  if (fp8 && (!good_scale(k_scale) || (v_pool && !good_scale(v_scale)))) return KVFP8_ERR_VALUE;
+  if ((int64_t)n_tokens * desc->num_kv_heads > ((int64_t)1 << 33)) return KVFP8_ERR_SHAPE;
+  AppendArgs a;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.tok_req = tok_req;
+  a.tok_pos = tok_pos;
+  a.page_table = page_table;
+  a.flags = flags;
+  a.n_tokens = n_tokens;
+  a.batch = batch;
+  a.pt_stride = pt_stride;
+  a.num_pages = desc->num_pages;
+  a.page_size = desc->page_size;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.head_dim = desc->head_dim;
+  a.v_dim = desc->v_dim;
+  a.k_inv = fp8 ? 1.0f / k_scale : 1.0f;  // fl32(1/scale): one IEEE fp32 division
+  a.v_inv = fp8 && v_pool ? 1.0f / v_scale : 1.0f;
+  return launch_append(a, fp8, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
+}
+
+int gather_common(const kvfp8_pool_desc* desc, const void* k_pool, const void* v_pool, const int32_t* tok_req,
+                  const int32_t* tok_pos, int32_t n_tokens, const int32_t* page_table, int32_t batch,
+                  int32_t pt_stride, void* k_out, void* v_out, bool fp8, hipStream_t stream) {
+  int st = check_pool(desc, false);
+  if (st) return st;
+  if (n_tokens < 0 || batch < 0 || pt_stride < 1) return KVFP8_ERR_SHAPE;
+  if (n_tokens == 0) return KVFP8_OK;
+  if (!k_pool || !tok_req || !tok_pos || !page_table || !k_out) return KVFP8_ERR_NULL;
+  if ((v_out != nullptr) && v_pool == nullptr) return KVFP8_ERR_NULL;
+  GatherArgs a;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.tok_req = tok_req;
+  a.tok_pos = tok_pos;
+  a.page_table = page_table;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.n_tokens = n_tokens;
+  a.batch = batch;
+  a.pt_stride = pt_stride;
+  a.num_pages = desc->num_pages;
+  a.page_size = desc->page_size;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.head_dim = desc->head_dim;
+  a.v_dim = desc->v_dim;
+  return launch_gather(a, fp8, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
+}
+
+int attn_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads, const void* k_pool,
+                const void* v_pool, const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens,
+                int32_t batch, int32_t max_ctx_len, const uint32_t* flags, bool fp8, float k_scale,
+                float v_scale, float sm_scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                uint16_t* out, hipStream_t stream) {
+  int st = check_pool(desc, true);
+  if (st) return st;
+  if (batch < 0 || num_q_heads < 1 || pt_stride < 1 || num_splits < 0) return KVFP8_ERR_SHAPE;
+  if (batch == 0) return KVFP8_OK;
+  if (!q || !k_pool || !v_pool || !page_table || !ctx_lens || !out) return KVFP8_ERR_NULL;
+  if (num_q_heads % desc->num_kv_heads != 0) return KVFP8_ERR_SHAPE;
+  const int32_t group = num_q_heads / desc->num_kv_heads;
+  if (group > 16) return KVFP8_ERR_UNSUPPORTED;
+  if (max_ctx_len < 1) return KVFP8_ERR_SHAPE;
+  if ((int64_t)pt_stride * desc->page_size < max_ctx_len) return KVFP8_ERR_SHAPE;
+  if (batch > 65535 || desc->num_kv_heads > 65535) return KVFP8_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return KVFP8_ERR_ALIGN;
+  if (!good_scale(k_scale) || !good_scale(v_scale) || !good_scale(sm_scale)) return KVFP8_ERR_VALUE;
+  const int32_t tiles = n_tiles_of(max_ctx_len);
+  int32_t splits = num_splits == 0 ? auto_splits(batch, desc->num_kv_heads, max_ctx_len) : num_splits;
+  if (splits > tiles) return KVFP8_ERR_SHAPE;
+  const int32_t chunk_tiles = (tiles + splits - 1) / splits;
+  splits = (tiles + chunk_tiles - 1) / chunk_tiles;  // drop splits that would start past max_ctx_len
+  AttnArgs a;
+  a.o_part = nullptr;
+  a.lse_part = nullptr;
+  if (splits > 1) {
+    const size_t need = paged_decode_attn_workspace_bytes(batch, num_q_heads, kHeadDim, splits);
+    if (workspace == nullptr) return KVFP8_ERR_NULL;
+    if (workspace_bytes < need) return KVFP8_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KVFP8_ERR_ALIGN;
+    a.o_part = reinterpret_cast<float*>(workspace);
+    a.lse_part = a.o_part + (size_t)batch * num_q_heads * splits * kHeadDim;
+  }
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.page_table = page_table;
+  a.ctx_lens = ctx_lens;
+  a.flags = flags;
+  a.out = out;
+  a.num_pages = desc->num_pages;
+  a.page_size = desc->page_size;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.group = group;
+  a.num_q_heads = num_q_heads;
+  a.pt_stride = pt_stride;
+  a.chunk_tiles = chunk_tiles;
+  a.num_splits = splits;
+  a.max_ctx = max_ctx_len;
+  a.qk_scale_log2 = fp8 ? sm_scale * k_scale * kLog2e : sm_scale * kLog2e;
+  a.v_scale = fp8 ? v_scale : 1.0f;
+  return launch_attn_gqa(a, fp8, batch, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvfp8_abi_version(void) { return KVFP8_ABI_VERSION; }
+
+const char* kvfp8_status_string(int s) {
+  switch (s) {
+    case KVFP8_OK: return "ok";
+    case KVFP8_ERR_NULL: return "null pointer";
+    case KVFP8_ERR_SHAPE: return "bad shape";
+    case KVFP8_ERR_UNSUPPORTED: return "unsupported size";
+    case KVFP8_ERR_WORKSPACE: return "workspace too small";
+    case KVFP8_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case KVFP8_ERR_HIP: return "HIP launch error";
+    case KVFP8_ERR_VALUE: return "invalid scalar argument";
+    default: return "unknown status";
+  }
+}
+
+int kv_absmax_bf16(const uint16_t* x, int64_t n, uint32_t* absmax_bits, hipStream_t stream) {
+  if (n < 0) return KVFP8_ERR_SHAPE;
+  if (n == 0) return KVFP8_OK;
+  if (!x || !absmax_bits) return KVFP8_ERR_NULL;
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(absmax_bits) & 3u)) return KVFP8_ERR_ALIGN;
+  return launch_absmax(x, n, absmax_bits, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
+}
+
+float kv_scale_from_absmax(uint32_t absmax_bits) {
+  float a;
+  memcpy(&a, &absmax_bits, sizeof a);
+  return a / 448.0f;
+}
+
+int kv_append_fp8(const kvfp8_pool_desc* desc, uint8_t* k_pool, uint8_t* v_pool, const uint16_t* k_new,
+                  const uint16_t* v_new, const int32_t* tok_req, const int32_t* tok_pos, int32_t n_tokens,
+                  const int32_t* page_table, int32_t batch, int32_t pt_stride, const uint32_t* abort_flags,
+                  float k_scale, float v_scale, hipStream_t stream) {
+  return append_common(desc, k_pool, v_pool, k_new, v_new, tok_req, tok_pos, n_tokens, page_table, batch,
+                       pt_stride, abort_flags, true, k_scale, v_scale, stream);
+}
+
+int kv_append_bf16(const kvfp8_pool_desc* desc, uint16_t* k_pool, uint16_t* v_pool, const uint16_t* k_new,
+                   const uint16_t* v_new, const int32_t* tok_req, const int32_t* tok_pos, int32_t n_tokens,
+                   const int32_t* page_table, int32_t batch, int32_t pt_stride, const uint32_t* abort_flags,
+                   hipStream_t stream) {
+  return append_common(desc, k_pool, v_pool, k_new, v_new, tok_req, tok_pos, n_tokens, page_table, batch,
+                       pt_stride, abort_flags, false, 1.f, 1.f, stream);
+}
+
+int kv_tag_check(const uint32_t* page_tags, int32_t num_pages, const int32_t* page_table,
+                 const uint32_t* expected_tags, int32_t pt_stride, const int32_t* ctx_lens, int32_t batch,
+                 int32_t page_size, uint32_t* abort_flags, hipStream_t stream) {
+  if (batch < 0 || num_pages < 0 || pt_stride < 1 || page_size < 1) return KVFP8_ERR_SHAPE;
+  if (batch == 0) return KVFP8_OK;
+  if (!page_table || !expected_tags || !ctx_lens || !abort_flags || (num_pages > 0 && !page_tags))
+    return KVFP8_ERR_NULL;
+  TagArgs a;
+  a.page_tags = page_tags;
+  a.page_table = page_table;
+  a.expected = expected_tags;
+  a.ctx_lens = ctx_lens;
+  a.flags = abort_flags;
+  a.num_pages = num_pages;
+  a.pt_stride = pt_stride;
+  a.batch = batch;
+  a.page_size = page_size;
+  return launch_tag_check(a, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
+}
+
+size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t v_dim, int32_t num_splits) {
+  if (batch <= 0 || num_q_heads <= 0 || v_dim <= 0 || num_splits <= 1) return 0;
+  const size_t rows = (size_t)batch * num_q_heads * num_splits;
+  return rows * (size_t)v_dim * sizeof(float) + rows * sizeof(float);
+}
+
+int32_t paged_decode_attn_auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_ctx_len) {
+  return auto_splits(batch, num_kv_heads, max_ctx_len);
+}
+
+int paged_decode_attn_fp8(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads,
+                          const uint8_t* k_pool, const uint8_t* v_pool, const int32_t* page_table,
+                          int32_t pt_stride, const int32_t* ctx_lens, int32_t batch, int32_t max_ctx_len,
+                          const uint32_t* abort_flags, float k_scale, float v_scale, float sm_scale,
+                          int32_t num_splits, void* workspace, size_t workspace_bytes, uint16_t* out,
+                          hipStream_t stream) {
+  return attn_common(desc, q, num_q_heads, k_pool, v_pool, page_table, pt_stride, ctx_lens, batch, max_ctx_len,
+                     abort_flags, true, k_scale, v_scale, sm_scale, num_splits, workspace, workspace_bytes, out,
+                     stream);
+}
+
+int paged_decode_attn_bf16(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads,
+                           const uint16_t* k_pool, const uint16_t* v_pool, const int32_t* page_table,
+                           int32_t pt_stride, const int32_t* ctx_lens, int32_t batch, int32_t max_ctx_len,
+                           const uint32_t* abort_flags, float sm_scale, int32_t num_splits, void* workspace,
+                           size_t workspace_bytes, uint16_t* out, hipStream_t stream) {
+  return attn_common(desc, q, num_q_heads, k_pool, v_pool, page_table, pt_stride, ctx_lens, batch, max_ctx_len,
+                     abort_flags, false, 1.f, 1.f, sm_scale, num_splits, workspace, workspace_bytes, out, stream);
+}
+
+int kv_gather_fp8(const kvfp8_pool_desc* desc, const uint8_t* k_pool, const uint8_t* v_pool, const int32_t* tok_req,
+                  const int32_t* tok_pos, int32_t n_tokens, const int32_t* page_table, int32_t batch,
+                  int32_t pt_stride, uint8_t* k_out, uint8_t* v_out, hipStream_t stream) {
+  return gather_common(desc, k_pool, v_pool, tok_req, tok_pos, n_tokens, page_table, batch, pt_stride, k_out,
+                       v_out, true, stream);
+}
+
+int kv_gather_bf16(const kvfp8_pool_desc* desc, const uint16_t* k_pool, const uint16_t* v_pool,
+                   const int32_t* tok_req, const int32_t* tok_pos, int32_t n_tokens, const int32_t* page_table,
+                   int32_t batch, int32_t pt_stride, uint16_t* k_out, uint16_t* v_out, hipStream_t stream) {
+  return gather_common(desc, k_pool, v_pool, tok_req, tok_pos, n_tokens, page_table, batch, pt_stride, k_out,
+                       v_out, false, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, e4m3 and
+// bf16 conversions, wave reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvfp8 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kE4M3Max = 448.0f;
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2_t v;
+  v[0] = (_Float16)lo;
+  v[1] = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// e4m3 encode of two fp32 values into the low 16 bits (byte 0 = a, byte 1 = b).
+// OCP E4M3, round to nearest even; magnitudes above 448 saturate (the
+// conversion is fed values clamped to +-448, which under round-to-nearest
+// gives the same code as saturating after rounding); NaN -> 0x7F | sign.
+__device__ __forceinline__ uint32_t e4m3_clamp_nan_fix(float x, uint32_t code) {
+  // code: the hardware code for the clamped value; NaN gets the input's sign.
+  uint32_t s = (__float_as_uint(x) >> 24) & 0x80u;
+  return (x != x) ? (0x7Fu | s) : code;
+}
+
+__device__ __forceinline__ float clamp448(float x) {
+  // NaN passes through unchanged (both compares are false).
+  return fabsf(x) > kE4M3Max ? copysignf(kE4M3Max, x) : x;
+}
+
+__device__ __forceinline__ uint32_t encode_e4m3x2(float a, float b) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+  uint32_t c0 = e4m3_clamp_nan_fix(a, w & 0xFFu);
+  uint32_t c1 = e4m3_clamp_nan_fix(b, (w >> 8) & 0xFFu);
+  return c0 | (c1 << 8);
+}
+
+// Four e4m3 codes (one dword, byte 0 first) -> four exact bf16 / f16 values.
+__device__ __forceinline__ u32x2_t e4m3x4_to_bf16x4(uint32_t w) {
+  bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  u32x2_t r;
+  r[0] = __builtin_bit_cast(uint32_t, lo);
+  r[1] = __builtin_bit_cast(uint32_t, hi);
+  return r;
+}
+
+__device__ __forceinline__ u32x2_t e4m3x4_to_f16x4(uint32_t w) {
+  f16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  f16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  u32x2_t r;
+  r[0] = __builtin_bit_cast(uint32_t, lo);
+  r[1] = __builtin_bit_cast(uint32_t, hi);
+  return r;
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  // element 0 of the packed conversion of byte 0
+  return __builtin_amdgcn_cvt_pk_f32_fp8(code & 0xFFu, false)[0];
+}
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int mask) {
+  return __shfl_xor(v, mask, kWave);
+}
+
+}  // namespace kvfp8

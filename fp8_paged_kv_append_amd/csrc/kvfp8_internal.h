@@ -1,0 +1,79 @@
+// Kernel argument blocks and launchers shared between the kernels and the
+// host-side C ABI (api.hip).  Not part of the public interface.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvfp8 {
+
+struct AttnArgs {
+  const uint16_t* q;          // bf16 [B][Hq][D]
+  const void* k_pool;         // [P][Hkv][S][D]
+  const void* v_pool;         // [P][Hkv][Dv][S]
+  const int32_t* page_table;  // [B][pt_stride]
+  const int32_t* ctx_lens;    // [B]
+  const uint32_t* flags;      // [B] or null
+  float* o_part;              // [B][Hq][num_splits][Dv] (num_splits > 1)
+  float* lse_part;            // [B][Hq][num_splits]
+  uint16_t* out;              // bf16 [B][Hq][Dv]
+  int32_t num_pages, page_size, num_kv_heads, group, num_q_heads, pt_stride;
+  int32_t chunk_tiles;        // 64-token tiles per split
+  int32_t num_splits;
+  int32_t max_ctx;
+  float qk_scale_log2;        // sm_scale * k_scale * log2(e)
+  float v_scale;
+};
+
+struct MergeArgs {
+  const float* o_part;
+  const float* lse_part;
+  uint16_t* out;
+  const int32_t* ctx_lens;
+  const uint32_t* flags;
+  int32_t num_q_heads, v_dim, num_splits, chunk_tokens, max_ctx, pt_stride, page_size;
+};
+
+struct AppendArgs {
+  void* k_pool;
+  void* v_pool;               // null for the latent cache
+  const uint16_t* k_new;      // bf16 [N][Hkv][D]
+  const uint16_t* v_new;      // bf16 [N][Hkv][Dv]
+  const int32_t* tok_req;
+  const int32_t* tok_pos;
+  const int32_t* page_table;
+  const uint32_t* flags;
+  int32_t n_tokens, batch, pt_stride;
+  int32_t num_pages, page_size, num_kv_heads, head_dim, v_dim;
+  float k_inv, v_inv;         // fl32(1/scale)
+};
+
+struct GatherArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* tok_req;
+  const int32_t* tok_pos;
+  const int32_t* page_table;
+  void* k_out;
+  void* v_out;
+  int32_t n_tokens, batch, pt_stride;
+  int32_t num_pages, page_size, num_kv_heads, head_dim, v_dim;
+};
+
+struct TagArgs {
+  const uint32_t* page_tags;
+  const int32_t* page_table;
+  const uint32_t* expected;
+  const int32_t* ctx_lens;
+  uint32_t* flags;
+  int32_t num_pages, pt_stride, batch, page_size;
+};
+
+constexpr int kAttnTileTokens = 64;
+
+hipError_t launch_attn_gqa(const AttnArgs& a, bool fp8, int batch, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_gather(const GatherArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_tag_check(const TagArgs& a, hipStream_t stream);
+hipError_t launch_absmax(const uint16_t* x, int64_t n, uint32_t* out, hipStream_t stream);
+
+}  // namespace kvfp8

@@ -1,0 +1,185 @@
+/*
+ * kvfp8.h -- C ABI of the MI355X (gfx950) library for decode attention over a
+ * paged KV cache stored as FP8 e4m3 (or BF16), its write path and its batched
+ * page-tag integrity check.
+ *
+ * What the operations compute comes from these pages:
+ *  [Q] Cloudflare blog, "Smaller, faster, safer: running Kimi and GLM at
+ *      scale", section "Quantized KV cache": K and V are cached as FP8 e4m3
+ *      instead of BF16 (half the bytes); the attention kernel converts the
+ *      stored values as it reads them; BF16 and FP8 caches are compared.
+ *  [T] agentlenshq summary "Cloudflare Workers AI: 大规模优化 Kimi 和 GLM 推理",
+ *      section "KV Cache 完整性检查", and the xujun.org note on the same post,
+ *      section "一个不能出错的共享缓存": every physical cache page carries a
+ *      tag that changes on reallocation; each request's expected (page, tag)
+ *      list is validated before decode reads the cache; a mismatch aborts the
+ *      request; the check runs as a separate batched pass, not inside the
+ *      attention kernel; deployments that do not want it use a no-op tracker.
+ * Readings where the pages are silent (OCP E4M3, round-to-nearest-even,
+ * saturation, per-tensor scale, layouts, flag bits) are stated per call.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless marked (host).  The library never
+ *    allocates, frees, synchronises or prints; the caller owns all memory,
+ *    including the attention workspace.
+ *  - Every call is asynchronous on `stream` (0 = the null stream) and returns
+ *    a status: KVFP8_OK or a negative KVFP8_ERR_*.  A call that returns an
+ *    error has enqueued nothing.  KVFP8_ERR_HIP means a launch failed.
+ *  - Data faults that live in device memory (stale tags, bad page ids, bad
+ *    context lengths) never become status codes: they surface through the
+ *    abort flags and, in attention, as all-zero output rows.
+ *  - bf16 values travel as uint16_t bit patterns; e4m3 codes as uint8_t.
+ *  - Pools and q/out/new-row buffers must be 16-byte aligned.
+ *
+ * Page pool layout (element = 1 byte e4m3 or 2 bytes bf16):
+ *    K pool  [P][Hkv][S][D]    element (page, kv head, slot, d)
+ *    V pool  [P][Hkv][Dv][S]   element (page, kv head, d, slot): each
+ *                              (page, head) block of V is stored transposed
+ *    latent  [P][1][S][Dl]     the K-pool layout with one head, no V pool
+ * Page table: int32 [B][pt_stride]; entry i of request r is the physical page
+ * of its tokens [i*S, (i+1)*S).  Entries at or past ceil(L_r/S) are never read.
+ * Context length L_r counts the token appended in the current step.
+ */
+#ifndef KVFP8_H
+#define KVFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+#define KVFP8_ABI_VERSION 1
+
+#define KVFP8_OK 0
+#define KVFP8_ERR_NULL (-1)        /* a required pointer is NULL                       */
+#define KVFP8_ERR_SHAPE (-2)       /* sizes inconsistent or out of range               */
+#define KVFP8_ERR_UNSUPPORTED (-3) /* a size outside the compiled set                  */
+#define KVFP8_ERR_WORKSPACE (-4)   /* workspace smaller than the query says            */
+#define KVFP8_ERR_ALIGN (-5)       /* a pointer is not 16-byte aligned                 */
+#define KVFP8_ERR_HIP (-6)         /* the HIP runtime reported a launch error          */
+#define KVFP8_ERR_VALUE (-7)       /* a scalar argument is invalid (scale <= 0, NaN)   */
+
+/* Abort-flag bits written by kv_tag_check (uint32 per request). */
+#define KVFP8_FLAG_TAG_MISMATCH 1u /* a used entry's page tag != the expected tag      */
+#define KVFP8_FLAG_BAD_PAGE 2u     /* a used page id outside [0,P), or ceil(L/S) > pt_stride */
+
+/* Shape of a page pool (host struct). */
+typedef struct kvfp8_pool_desc {
+  int32_t num_pages;    /* P                                                   */
+  int32_t page_size;    /* S tokens per page; a multiple of 16, at most 256    */
+  int32_t num_kv_heads; /* Hkv (1 for the latent cache)                        */
+  int32_t head_dim;     /* D: K width (the latent width Dl for the latent cache) */
+  int32_t v_dim;        /* Dv: V width (for the latent cache: the value part)  */
+} kvfp8_pool_desc;
+
+int kvfp8_abi_version(void);
+/* Static string naming a status code. */
+const char* kvfp8_status_string(int status);
+
+/* ---------------------------------------------------------------- scale calibration
+ * Per-tensor scale = fl32(max|x| / 448) (448 = largest finite e4m3).  The
+ * pages give no scale rule; this per-tensor max-abs reading is recorded with
+ * the tests.  kv_absmax_bf16 max-accumulates max|x| over n bf16 values into
+ * *absmax_bits (device, float32 bit pattern, NaN inputs ignored, +inf
+ * counts): zero it first, or call repeatedly to calibrate over chunks.
+ * kv_scale_from_absmax is a host function: fl32(absmax / 448). */
+int kv_absmax_bf16(const uint16_t* x, int64_t n, uint32_t* absmax_bits, hipStream_t stream);
+float kv_scale_from_absmax(uint32_t absmax_bits);
+
+/* ---------------------------------------------------------------- write path  [Q]
+ * For each new token n (request tok_req[n], position tok_pos[n]) and KV head
+ * h: store its K row and V row at page page_table[r][pos / S], slot pos % S.
+ * kv_append_fp8 first quantises: code = E4M3(fl32(x * fl32(1/scale))), with
+ * OCP E4M3 round-to-nearest-even, |value| > 448 saturating to +-448, NaN ->
+ * 0x7F with the input's sign.  kv_append_bf16 copies the bf16 bits.
+ *   k_new [N][Hkv][D], v_new [N][Hkv][Dv] (bf16).  v_pool/v_new may both be
+ *   NULL (latent cache: only the K-layout pool is written).
+ *   abort_flags [B] or NULL (NULL = no-op tracker): tokens of a request whose
+ *   flag is non-zero are skipped [T].  Tokens whose request is outside [0,B),
+ *   whose position is outside [0, pt_stride*S) or whose page id is outside
+ *   [0,P) are skipped (memory safety; the tag check reports such pages).
+ *   Two tokens aimed at the same slot: which one lands is unspecified.
+ *   Scales must be finite and > 0 (KVFP8_ERR_VALUE otherwise). */
+int kv_append_fp8(const kvfp8_pool_desc* desc, uint8_t* k_pool, uint8_t* v_pool,
+                  const uint16_t* k_new, const uint16_t* v_new, const int32_t* tok_req,
+                  const int32_t* tok_pos, int32_t n_tokens, const int32_t* page_table,
+                  int32_t batch, int32_t pt_stride, const uint32_t* abort_flags, float k_scale,
+                  float v_scale, hipStream_t stream);
+int kv_append_bf16(const kvfp8_pool_desc* desc, uint16_t* k_pool, uint16_t* v_pool,
+                   const uint16_t* k_new, const uint16_t* v_new, const int32_t* tok_req,
+                   const int32_t* tok_pos, int32_t n_tokens, const int32_t* page_table,
+                   int32_t batch, int32_t pt_stride, const uint32_t* abort_flags,
+                   hipStream_t stream);
+
+/* ---------------------------------------------------------------- integrity check  [T]
+ * abort_flags[r] = OR over the used entries i < ceil(L_r/S) of request r of
+ *   KVFP8_FLAG_BAD_PAGE      if page_table[r][i] is outside [0, num_pages),
+ *   KVFP8_FLAG_TAG_MISMATCH  else if page_tags[page] != expected_tags[r][i];
+ * plus KVFP8_FLAG_BAD_PAGE when ceil(L_r/S) > pt_stride.  L_r <= 0 gives 0.
+ * Rewritten on every call (flags are not sticky).  One batched launch;
+ * attention and append read the flags it leaves, in stream order.
+ *   page_tags uint32 [P]; page_table int32 [B][pt_stride];
+ *   expected_tags uint32 [B][pt_stride]; ctx_lens int32 [B]; abort_flags out [B]. */
+int kv_tag_check(const uint32_t* page_tags, int32_t num_pages, const int32_t* page_table,
+                 const uint32_t* expected_tags, int32_t pt_stride, const int32_t* ctx_lens,
+                 int32_t batch, int32_t page_size, uint32_t* abort_flags, hipStream_t stream);
+
+/* ---------------------------------------------------------------- decode attention  [Q]
+ * For request r, query head h (KV head g = h / (Hq/Hkv)), over positions t < L_r:
+ *   s_t = sm_scale * <q_h, K^_t>,  o_h = sum_t softmax(s)_t V^_t,
+ * with K^ = dec(K)*k_scale, V^ = dec(V)*v_scale for the FP8 cache (e4m3
+ * decoded in registers as pages are read) and K^ = K, V^ = V for BF16.  The
+ * fp32 result is rounded to bf16 (RNE).  Long contexts are cut into
+ * num_splits chunks whose partial softmax states are merged by log-sum-exp.
+ *   q bf16 [B][Hq][D]; out bf16 [B][Hq][Dv].  D = Dv = 128; Hq/Hkv <= 16.
+ *   ctx_lens int32 [B]; max_ctx_len (host) bounds every L_r and sizes the
+ *   grid: a request with L_r > max_ctx_len, L_r > pt_stride*S or L_r <= 0
+ *   gets zero rows.
+ *   abort_flags [B] or NULL (no-op tracker).  A flagged request reads no
+ *   pages and gets zero rows [T].  A page id outside [0,P) met while reading
+ *   also zeroes the request's rows (memory safety when the tracker is off).
+ *   num_splits: 0 = chosen by the library; otherwise at most
+ *   ceil(max_ctx_len/64).  workspace: fp32 partials, at least
+ *   paged_decode_attn_workspace_bytes(...) bytes for the split count used
+ *   (0 when it is 1; then workspace may be NULL).
+ *   sm_scale: usually 1/sqrt(D).  Scales must be finite and > 0. */
+size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t v_dim,
+                                         int32_t num_splits);
+/* The split count that num_splits = 0 selects for this shape (host only). */
+int32_t paged_decode_attn_auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_ctx_len);
+
+int paged_decode_attn_fp8(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads,
+                          const uint8_t* k_pool, const uint8_t* v_pool, const int32_t* page_table,
+                          int32_t pt_stride, const int32_t* ctx_lens, int32_t batch,
+                          int32_t max_ctx_len, const uint32_t* abort_flags, float k_scale,
+                          float v_scale, float sm_scale, int32_t num_splits, void* workspace,
+                          size_t workspace_bytes, uint16_t* out, hipStream_t stream);
+int paged_decode_attn_bf16(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads,
+                           const uint16_t* k_pool, const uint16_t* v_pool,
+                           const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens,
+                           int32_t batch, int32_t max_ctx_len, const uint32_t* abort_flags,
+                           float sm_scale, int32_t num_splits, void* workspace,
+                           size_t workspace_bytes, uint16_t* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------- test export
+ * Read back tokens through the page table: k_out [N][Hkv][D], v_out
+ * [N][Hkv][Dv] (v_out NULL for the latent cache) receive the stored
+ * elements of token (tok_req[n], tok_pos[n]); a token whose request,
+ * position or page is out of range gets zero elements. */
+int kv_gather_fp8(const kvfp8_pool_desc* desc, const uint8_t* k_pool, const uint8_t* v_pool,
+                  const int32_t* tok_req, const int32_t* tok_pos, int32_t n_tokens,
+                  const int32_t* page_table, int32_t batch, int32_t pt_stride, uint8_t* k_out,
+                  uint8_t* v_out, hipStream_t stream);
+int kv_gather_bf16(const kvfp8_pool_desc* desc, const uint16_t* k_pool, const uint16_t* v_pool,
+                   const int32_t* tok_req, const int32_t* tok_pos, int32_t n_tokens,
+                   const int32_t* page_table, int32_t batch, int32_t pt_stride, uint16_t* k_out,
+                   uint16_t* v_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVFP8_H */

@@ -1,0 +1,96 @@
+"""The C ABI on the CPU: the header is plain C, the library loads and exports every declared entry
+point, and host-side argument checks return their status codes before touching any device."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvfp8.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ["kv_append_fp8", "kv_append_bf16", "kv_tag_check", "paged_decode_attn_fp8", "paged_decode_attn_bf16",
+              "paged_decode_attn_workspace_bytes", "kv_gather_fp8", "kv_gather_bf16", "kv_absmax_bf16",
+              "kv_scale_from_absmax", "kvfp8_abi_version", "kvfp8_status_string"]:
+        assert n in names, n
+
+
+def test_header_compiles_as_c_and_cxx():
+    for lang, std in (("c", "-std=c11"), ("c++", "-std=c++17")):
+        r = subprocess.run(["gcc", "-x", lang, std, "-Wall", "-Werror", "-fsyntax-only", HEADER],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from fp8_paged_kv_append_amd import _lib
+    return _lib.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from fp8_paged_kv_append_amd import _lib
+    for n in _declared():
+        assert hasattr(lib, n), n
+        assert n in _lib.PROTOTYPES, n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kvfp8_abi_version() == 1
+    for s in range(-7, 1):
+        assert lib.kvfp8_status_string(s).decode() not in ("", "unknown status")
+    assert lib.kvfp8_status_string(5) == b"unknown status"
+
+
+def test_scale_from_absmax_is_fp32_division(lib):
+    import numpy as np
+    for a in [3.0, 4.5, 1e-3, 17.25, 3.3e38]:
+        bits = int(np.float32(a).view(np.uint32))
+        assert lib.kv_scale_from_absmax(bits) == float(np.float32(a) / np.float32(448))
+
+
+def test_host_validation_codes(lib):
+    from fp8_paged_kv_append_amd import _lib
+    d = _lib.PoolDesc(16, 16, 1, 128, 128)
+    A = 4096                      # a fake, 16-byte aligned "device" address; never dereferenced
+    # null descriptor / pointers
+    assert lib.kv_append_fp8(None, A, A, A, A, A, A, 1, A, 1, 1, None, 1.0, 1.0, None) == -1
+    assert lib.kv_append_fp8(d, None, A, A, A, A, A, 1, A, 1, 1, None, 1.0, 1.0, None) == -1
+    assert lib.kv_append_fp8(d, A, None, A, A, A, A, 1, A, 1, 1, None, 1.0, 1.0, None) == -1   # v_pool w/o v_new
+    # shapes and values
+    assert lib.kv_append_fp8(d, A, A, A, A, A, A, -1, A, 1, 1, None, 1.0, 1.0, None) == -2
+    assert lib.kv_append_fp8(d, A, A, A, A, A, A, 0, A, 1, 1, None, 1.0, 1.0, None) == 0      # nothing to do
+    assert lib.kv_append_fp8(d, A, A, A, A, A, A, 1, A, 1, 1, None, 0.0, 1.0, None) == -7
+    assert lib.kv_append_fp8(d, A, A, A, A, A, A, 1, A, 1, 1, None, float("nan"), 1.0, None) == -7
+    assert lib.kv_append_fp8(d, A + 2, A, A, A, A, A, 1, A, 1, 1, None, 1.0, 1.0, None) == -5
+    bad = _lib.PoolDesc(16, 24, 1, 128, 128)                        # page size not a multiple of 16
+    assert lib.kv_append_bf16(bad, A, A, A, A, A, A, 1, A, 1, 1, None, None) == -3
+    # tag check
+    assert lib.kv_tag_check(A, 4, A, A, 0, A, 1, 16, A, None) == -2
+    assert lib.kv_tag_check(A, 4, A, None, 1, A, 1, 16, A, None) == -1
+    assert lib.kv_tag_check(A, 4, A, A, 1, A, 0, 16, A, None) == 0
+    # attention
+    f = lib.paged_decode_attn_fp8
+    assert f(d, A, 8, A, A, A, 16, A, 0, 256, None, 1., 1., 1., 0, None, 0, A, None) == 0     # empty batch
+    assert f(d, A, 8, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 0, None, 0, None, None) == -1
+    assert f(d, A, 8, A, A, A, 15, A, 1, 256, None, 1., 1., 1., 0, None, 0, A, None) == -2     # 15*16 < 256
+    assert f(d, A, 32, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 0, None, 0, A, None) == -3    # group 32 > 16
+    assert f(d, A, 8, A, A, A, 16, A, 1, 256, None, 1., -1., 1., 0, None, 0, A, None) == -7
+    assert f(d, A, 8, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 5, None, 0, A, None) == -2     # 5 splits > 4 tiles
+    assert f(d, A, 8, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 2, None, 0, A, None) == -1     # no workspace
+    assert f(d, A, 8, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 2, A, 64, A, None) == -4       # too small
+    d64 = _lib.PoolDesc(16, 16, 1, 64, 64)
+    assert f(d64, A, 8, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 0, None, 0, A, None) == -3
+    assert lib.paged_decode_attn_workspace_bytes(64, 64, 128, 1) == 0
+    assert lib.paged_decode_attn_workspace_bytes(64, 64, 128, 2) == 64 * 64 * 2 * 129 * 4

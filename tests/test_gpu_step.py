@@ -1,0 +1,93 @@
+"""GPU parity of a whole decode step (tag check -> append -> attention), small and at full size."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_paged_kv_append_amd as kv
+from kvsynth import workloads as wl
+from oracle import attention, codec, paged, step
+from tests.gpu_util import ATTN_TOL, Case, attn_error, dev, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+def _device_step(c, k_new, v_new, req, pos, tracker=True, num_splits=0):
+    w = c.w
+    out = c.out_tensor()
+    flags = torch.full((w.batch,), -1, dtype=torch.int32, device="cuda") if tracker else None
+    splits = num_splits or kv.paged_decode_attn_auto_splits(w.batch, w.num_kv_heads, c.max_ctx)
+    kv.decode_step(c.desc, c.kv_dtype, c.dkp, c.dvp, c.dpt, c.dlens, c.max_ctx, c.dq, dev(k_new),
+                   None if v_new is None else dev(v_new), dev(req), dev(pos), out,
+                   page_tags=c.dtags if tracker else None, expected_tags=c.dexp if tracker else None,
+                   abort_flags=flags, k_scale=c.d_k_scale, v_scale=c.d_v_scale, sm_scale=c.sm_scale,
+                   num_splits=num_splits, workspace=c.workspace(splits))
+    torch.cuda.synchronize()
+    return (None if flags is None else host(flags, np.uint32)), host(out, np.uint16)
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_step_with_stale_request(kv_dtype):
+    """16 requests, one with a stale expected tag: its flag is set, its page is not written, its rows are 0."""
+    w = wl.WORKLOADS["sweep_b16"].with_(num_pages=3000, ctx_lo=700, ctx_hi=700)
+    note(f"step stale {kv_dtype}")
+    c = Case(w, kv_dtype)
+    c.fill_device()
+    k_new, v_new, req, pos = c.step_inputs()
+    # the new rows differ from what is stored, so a skipped write is visible
+    k_new = k_new ^ np.uint16(0x0040)
+    st = dict(dtype=kv_dtype, k_pool=c.okp, v_pool=c.ovp, page_table=c.pt, ctx_lens=c.lens, page_tags=c.tags,
+              expected_tags=c.exp, num_kv_heads=w.num_kv_heads, page_size=w.page_size, head_dim=w.head_dim,
+              v_dim=w.v_dim, k_scale=c.o_k_scale, v_scale=c.o_v_scale, sm_scale=c.sm_scale, latent=False)
+    o_flags, o_out = step.decode_step(st, c.q, k_new, v_new, req, pos)
+    g_flags, g_out = _device_step(c, k_new, v_new, req, pos)
+    assert np.array_equal(g_flags, o_flags)
+    assert np.flatnonzero(g_flags).tolist() == c.stale.tolist()
+    et = np.uint8 if kv_dtype == "fp8" else np.uint16
+    assert np.array_equal(host(c.dkp, et), c.okp) and np.array_equal(host(c.dvp, et), c.ovp)
+    err = attn_error(g_out, o_out)
+    note(f"  step error {err:.3e}")
+    assert err <= ATTN_TOL
+    for r in c.stale:
+        assert not g_out[r].any()
+    # the no-op tracker: no check, every request attended
+    g2_flags, g2_out = _device_step(c, k_new, v_new, req, pos, tracker=False)
+    assert g2_flags is None and all(g2_out[r].any() for r in range(w.batch))
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_full_size_64x8192_sampled(kv_dtype):
+    """The 64 x 8192 workload (64/8 heads, page 16, 40k-page pool) at full size, in the bench's launch
+    configuration: all flags bit-exact, scales bit-exact, sampled requests' pages byte-exact and their
+    attention rows within tolerance of the oracle."""
+    w = wl.WORKLOADS["sweep_b64"]
+    note(f"full 64x8192 {kv_dtype}: generating")
+    c = Case(w, kv_dtype, oracle_fill=False)
+    assert c.d_k_scale == float(c.o_k_scale) and c.d_v_scale == float(c.o_v_scale)
+    note("  filling")
+    c.fill_device()
+    k_new, v_new, req, pos = c.step_inputs()
+    g_flags, g_out = _device_step(c, k_new, v_new, req, pos)
+    o_flags = paged.tag_check(c.tags, c.pt, c.exp, c.lens, w.page_size)
+    assert np.array_equal(g_flags, o_flags) and o_flags.sum() > 0
+    sample = sorted(set([0, 17, 63] + c.stale.tolist()))
+    et = np.uint8 if kv_dtype == "fp8" else np.uint16
+    for r in sample:
+        note(f"  request {r}")
+        if g_flags[r]:
+            assert not g_out[r].any()
+            continue
+        a, b = int(c.off[r]), int(c.off[r + 1])
+        ko = torch.empty((b - a, w.num_kv_heads, w.head_dim), dtype=c.dkp.dtype, device="cuda")
+        vo = torch.empty((b - a, w.num_kv_heads, w.v_dim), dtype=c.dkp.dtype, device="cuda")
+        g = kv.kv_gather_fp8 if kv_dtype == "fp8" else kv.kv_gather_bf16
+        g(c.desc, c.dkp, c.dvp, c.dreq[a:b].contiguous(), c.dpos[a:b].contiguous(), c.dpt, ko, vo)
+        torch.cuda.synchronize()
+        if kv_dtype == "fp8":
+            assert np.array_equal(host(ko, et), codec.quantize_e4m3(c.k[a:b], c.o_k_scale))
+            assert np.array_equal(host(vo, et), codec.quantize_e4m3(c.v[a:b], c.o_v_scale))
+        else:
+            assert np.array_equal(host(ko, et), c.k[a:b]) and np.array_equal(host(vo, et), c.v[a:b])
+        ref = c.oracle_request(r)
+        err = float(np.max(attention.row_rel_error(codec.f64_from_bf16(g_out[r]), ref)))
+        note(f"    row error {err:.3e}")
+        assert err <= ATTN_TOL
