@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--no-bf16", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=4, help="requests in the CPU oracle sample")
     p.add_argument("--fp8-only-steps", action="store_true", help="time only the FP8 step (profiling runs)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="after timing, copy a MIB-MiB buffer 3 times (a known-size kernel for HBM counters)")
     return p.parse_args()
 
 
@@ -280,6 +282,14 @@ def main():
         line["bf16_twin"] = {"value": round(b["gbs_step"], 1), "unit": "GB/s", "ms_per_step": round(b["ms_per_step"], 5),
                              "attn_gbs": round(b["gbs_attn"], 1), "attn_ms_mean": round(b["attn_ms_mean"], 5),
                              "fp8_speedup_step": round(b["ms_per_step"] / f8["ms_per_step"], 3)}
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = n
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_sample} requests")
         cb = cpu_baseline(w, args.cpu_sample)
