@@ -17,12 +17,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool good_scale(float s) { return isfinite(s) && s > 0.f; }
 
-int check_pool(const kvfp8_pool_desc* d, bool need_v_dim_eq) {
+int check_pool(const kvfp8_pool_desc* d, bool need_v_dim_eq, int elt_bytes) {
   if (d == nullptr) return KVFP8_ERR_NULL;
   if (d->num_pages < 1 || d->page_size < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->v_dim < 0)
     return KVFP8_ERR_SHAPE;
   if (d->page_size % 16 != 0 || d->page_size > 256) return KVFP8_ERR_UNSUPPORTED;
-  if (d->head_dim % 16 != 0 || d->v_dim % 16 != 0) return KVFP8_ERR_UNSUPPORTED;
+  // K rows are cut into 64-byte slices (the chunk-reordered K layout)
+  if ((d->head_dim * elt_bytes) % 64 != 0 || d->v_dim % 16 != 0) return KVFP8_ERR_UNSUPPORTED;
   if (need_v_dim_eq && (d->head_dim != kHeadDim || d->v_dim != kHeadDim)) return KVFP8_ERR_UNSUPPORTED;
   return KVFP8_OK;
 }
@@ -48,7 +49,7 @@ int append_common(const kvfp8_pool_desc* desc, void* k_pool, void* v_pool, const
                   const uint16_t* v_new, const int32_t* tok_req, const int32_t* tok_pos, int32_t n_tokens,
                   const int32_t* page_table, int32_t batch, int32_t pt_stride, const uint32_t* flags,
                   bool fp8, float k_scale, float v_scale, hipStream_t stream) {
-  int st = check_pool(desc, false);
+  int st = check_pool(desc, false, fp8 ? 1 : 2);
   if (st) return st;
   if (n_tokens < 0 || batch < 0 || pt_stride < 1) return KVFP8_ERR_SHAPE;
   if (n_tokens == 0) return KVFP8_OK;
@@ -83,7 +84,7 @@ int append_common(const kvfp8_pool_desc* desc, void* k_pool, void* v_pool, const
 int gather_common(const kvfp8_pool_desc* desc, const void* k_pool, const void* v_pool, const int32_t* tok_req,
                   const int32_t* tok_pos, int32_t n_tokens, const int32_t* page_table, int32_t batch,
                   int32_t pt_stride, void* k_out, void* v_out, bool fp8, hipStream_t stream) {
-  int st = check_pool(desc, false);
+  int st = check_pool(desc, false, fp8 ? 1 : 2);
   if (st) return st;
   if (n_tokens < 0 || batch < 0 || pt_stride < 1) return KVFP8_ERR_SHAPE;
   if (n_tokens == 0) return KVFP8_OK;
@@ -113,7 +114,7 @@ int attn_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_he
                 int32_t batch, int32_t max_ctx_len, const uint32_t* flags, bool fp8, float k_scale,
                 float v_scale, float sm_scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
                 uint16_t* out, hipStream_t stream) {
-  int st = check_pool(desc, true);
+  int st = check_pool(desc, true, fp8 ? 1 : 2);
   if (st) return st;
   if (batch < 0 || num_q_heads < 1 || pt_stride < 1 || num_splits < 0) return KVFP8_ERR_SHAPE;
   if (batch == 0) return KVFP8_OK;

@@ -19,8 +19,10 @@
 //    B = q^T.  Row m of chain s is token (sub-page m/4, position 4s + m%4);
 //    the contraction index of lane group q, k-step kk, slot j is dimension
 //    32q + 8kk + j (any permutation of the head dimension is valid as long as
-//    both operands use it).  Lane (q, n) loads 32 contiguous bytes (64 for
-//    bf16) of each of its 4 K rows.
+//    both operands use it).  Lane (q, n) loads 32 bytes (64 for bf16) of
+//    each of its 4 K rows; the K pool keeps those bytes as 16-byte chunks
+//    256 bytes apart, so that each load instruction of the wave reads four
+//    runs of 256 contiguous bytes (one per page) instead of 64 half lines.
 //  * C layout of a 16x16 MFMA: lane (q, n) holds rows 4q..4q+3 of column n,
 //    so it ends up with head n's scores for sub-page q, positions 4s+i: the
 //    sixteen tokens of sub-page q.
@@ -49,13 +51,19 @@ constexpr int kThreads = kWaves * kWave;
 
 template <bool FP8>
 struct KRow;  // one lane's slice of one K row
+// Streaming loads: every KV byte is read once per step, so they bypass cache retention.
+__device__ __forceinline__ u32x4_t ld_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+// K rows live in chunk-reordered sub-page blocks: a lane's k-th 16-byte chunk of its row is
+// 256*k bytes after its first one (see k_elem_offset).
 template <>
 struct KRow<true> {
   u32x4_t w[2];  // 32 bytes: dims 32q .. 32q+31
   __device__ __forceinline__ void load(const uint8_t* p) {
-    const u32x4_t* v = reinterpret_cast<const u32x4_t*>(p);
-    w[0] = v[0];
-    w[1] = v[1];
+    w[0] = ld_stream(p);
+    w[1] = ld_stream(p + 256);
   }
   __device__ __forceinline__ void zero() { w[0] = w[1] = u32x4_t{0, 0, 0, 0}; }
   __device__ __forceinline__ bf16x8_t op(int kk) const {
@@ -70,11 +78,10 @@ template <>
 struct KRow<false> {
   u32x4_t w[4];  // 64 bytes: dims 32q .. 32q+31 as bf16
   __device__ __forceinline__ void load(const uint8_t* p) {
-    const u32x4_t* v = reinterpret_cast<const u32x4_t*>(p);
-    w[0] = v[0];
-    w[1] = v[1];
-    w[2] = v[2];
-    w[3] = v[3];
+    w[0] = ld_stream(p);
+    w[1] = ld_stream(p + 256);
+    w[2] = ld_stream(p + 512);
+    w[3] = ld_stream(p + 768);
   }
   __device__ __forceinline__ void zero() { w[0] = w[1] = w[2] = w[3] = u32x4_t{0, 0, 0, 0}; }
   __device__ __forceinline__ bf16x8_t op(int kk) const { return __builtin_bit_cast(bf16x8_t, w[kk]); }
@@ -85,7 +92,7 @@ struct VRow;  // one lane's slice of one V^T row: 16 consecutive slots
 template <>
 struct VRow<true> {
   u32x4_t w;  // 16 e4m3 codes
-  __device__ __forceinline__ void load(const uint8_t* p) { w = *reinterpret_cast<const u32x4_t*>(p); }
+  __device__ __forceinline__ void load(const uint8_t* p) { w = ld_stream(p); }
   __device__ __forceinline__ void zero() { w = u32x4_t{0, 0, 0, 0}; }
   // keep slots < nv, zero the rest (nv in [0, 16])
   __device__ __forceinline__ void mask(int nv) {
@@ -106,9 +113,8 @@ template <>
 struct VRow<false> {
   u32x4_t w[2];  // 16 bf16
   __device__ __forceinline__ void load(const uint8_t* p) {
-    const u32x4_t* v = reinterpret_cast<const u32x4_t*>(p);
-    w[0] = v[0];
-    w[1] = v[1];
+    w[0] = ld_stream(p);
+    w[1] = ld_stream(p + 16);
   }
   __device__ __forceinline__ void zero() { w[0] = w[1] = u32x4_t{0, 0, 0, 0}; }
   __device__ __forceinline__ void mask(int nv) {
@@ -140,15 +146,114 @@ __device__ __forceinline__ f32x4_t mfma_pv<false>(const VRow<false>& v, int kb, 
 
 // --- the split kernel ---------------------------------------------------------------------------
 
+// Page ids of the block's token range are staged in LDS, at most kPidWin entries at a time.
+constexpr int kPidWin = 2048;
+
+// One tile's loads for one lane, plus what the softmax needs to mask it.
+template <bool FP8>
+struct TileRegs {
+  KRow<FP8> k[4];
+  VRow<FP8> v[8];
+  int nv;  // valid slots of this lane's V sub-page (0 when the tile or page is absent)
+};
+
+template <bool FP8>
+__device__ __forceinline__ void issue_tile(TileRegs<FP8>& T, int tb, int w1, int e0, int ne, const int* s_pid,
+                                           const uint8_t* kpool, const uint8_t* vpool, int64_t blk, int S,
+                                           int Hkv, int g, int q4, int n) {
+  constexpr int ELT = FP8 ? 1 : 2;
+  const int tok_k = tb + 16 * (n >> 2);
+  const int tok_v = tb + 16 * q4;
+  // LDS index clamped into the staged range, the result discarded past w1: no branch
+  const int ik = min(tok_k / S - e0, ne - 1), iv = min(tok_v / S - e0, ne - 1);
+  const int sk = s_pid[ik], sv = s_pid[iv];
+  const int pid_k = tok_k < w1 ? sk : -1;
+  const int pid_v = tok_v < w1 ? sv : -1;
+  // Absent or invalid pages read the pool's first bytes (one cached line per wave) and are
+  // masked afterwards, so every tile issues the same loads with no branch around them.
+  // offsets computed for max(pid, 0) and zeroed by a mask: arithmetic, not a branch
+  // K: sub-page block base + lane (q4, i = n&3)'s first chunk of token 4s+i (byte offsets)
+  const int64_t ko = ((((int64_t)max(pid_k, 0) * Hkv + g) * blk + (int64_t)(tok_k % S) * kD) * ELT + 64 * q4 +
+                      16 * (n & 3)) & -(int64_t)(pid_k >= 0);
+  const int64_t vo = ((((int64_t)max(pid_v, 0) * Hkv + g) * blk + (int64_t)n * S + tok_v % S) * ELT) &
+                     -(int64_t)(pid_v >= 0);
+  const uint8_t* kb = kpool + ko;
+  const uint8_t* vb = vpool + vo;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) T.k[s].load(kb + 4 * s * kD * ELT);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) T.v[j].load(vb + (int64_t)(16 * j) * S * ELT);
+  T.nv = pid_v >= 0 ? max(0, min(16, w1 - tok_v)) : 0;
+}
+
+struct SoftmaxState {
+  float m, l;
+  f32x4_t acc[8];
+};
+
+template <bool FP8>
+__device__ __forceinline__ void compute_tile(TileRegs<FP8>& T, const u32x4_t (&qv)[4], float c_log2,
+                                             SoftmaxState& st) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) T.v[j].mask(T.nv);
+  // S^T = K q^T, four chains of 16 tokens
+  f32x4_t sc[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    sc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      sc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T.k[s].op(kk), __builtin_bit_cast(bf16x8_t, qv[kk]), sc[s],
+                                                      0, 0, 0);
+  }
+  // online softmax for head n over the 16 tokens of sub-page q4 this lane holds
+  float x[16];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pos = 4 * s + i;
+      const float v = pos < T.nv ? sc[s][i] * c_log2 : -INFINITY;
+      x[pos] = v;
+      tmax = fmaxf(tmax, v);
+    }
+  tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+  const float m_new = fmaxf(st.m, tmax);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = exp2f(st.m - m_use);  // st.m = -inf -> 0
+  float psum = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    x[k] = exp2f(x[k] - m_use);
+    psum += x[k];
+  }
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+  u32x4_t pp[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pp[kb][e] = pack_p<FP8>(x[8 * kb + 2 * e], x[8 * kb + 2 * e + 1]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    st.acc[j] *= alpha;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) st.acc[j] = mfma_pv<FP8>(T.v[j], kb, pp[kb], st.acc[j]);
+  }
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(kThreads) void attn_gqa_split_kernel(AttnArgs a) {
-  constexpr int ELT = FP8 ? 1 : 2;
   const int split = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave index in an SGPR: the tile loop is then a scalar loop, not an exec-masked one
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int q4 = lane >> 4, n = lane & 15;
   const int G = a.group;
   const int S = a.page_size;
 
+  __shared__ int s_pid[kPidWin];
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
   __shared__ float s_acc[kWaves][16][kD];
@@ -168,9 +273,6 @@ __global__ __launch_bounds__(kThreads) void attn_gqa_split_kernel(AttnArgs a) {
   }
   if (c0 >= L) return;  // past this request's context: the merge does not read this split
   const int c1 = min(L, c0 + chunk);
-  const int ntile = (c1 - c0 + kTile - 1) / kTile;
-
-  if (threadIdx.x == 0) s_bad = 0;
 
   // q^T operand: lane (q4, n) holds head g*G+n, dims 32*q4 .. 32*q4+31 (zero for padding heads)
   u32x4_t qv[4];
@@ -187,121 +289,80 @@ __global__ __launch_bounds__(kThreads) void attn_gqa_split_kernel(AttnArgs a) {
   const int32_t* pt = a.page_table + (int64_t)r * a.pt_stride;
   const uint8_t* kpool = reinterpret_cast<const uint8_t*>(a.k_pool);
   const uint8_t* vpool = reinterpret_cast<const uint8_t*>(a.v_pool);
-  const int64_t head_blk_k = (int64_t)S * kD;  // elements per (page, head) block
+  const int64_t blk = (int64_t)S * kD;  // elements per (page, head) block
   const float c_log2 = a.qk_scale_log2;
 
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x4_t acc[8];
+  SoftmaxState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 8; ++j) st.acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   bool bad = false;
 
-  for (int t = wave; t < ntile; t += kWaves) {
-    const int tb = c0 + t * kTile;
-    // page of the sub-page this lane reads K rows from (n/4) and V^T rows from (q4)
-    const int tok_k = tb + 16 * (n >> 2);
-    const int tok_v = tb + 16 * q4;
-    int pid_k = -1, pid_v = -1;
-    if (tok_k < c1) {
-      pid_k = pt[tok_k / S];
-      if (pid_k < 0 || pid_k >= a.num_pages) pid_k = -1;
-    }
-    if (tok_v < c1) {
-      pid_v = pt[tok_v / S];
-      if (pid_v < 0 || pid_v >= a.num_pages) {
-        pid_v = -1;
+  // tokens per page-id window: a multiple of the tile and of the page size
+  const int win = (kPidWin * S / kTile) * kTile;
+  for (int w0 = c0; w0 < c1; w0 += win) {
+    const int w1 = min(c1, w0 + win);
+    const int e0 = w0 / S;
+    const int ne = (w1 - 1) / S - e0 + 1;  // entries of the pages holding [w0, w1)
+    __syncthreads();                       // the previous window's ids are no longer read
+    for (int i = threadIdx.x; i < ne; i += kThreads) {
+      int p = pt[e0 + i];
+      if (p < 0 || p >= a.num_pages) {
         bad = true;
+        p = -1;
       }
+      s_pid[i] = p;
     }
-    const int off_k = tok_k % S, off_v = tok_v % S;
-
-    KRow<FP8> kr[4];
-    if (pid_k >= 0) {
-      const uint8_t* kb = kpool + (((int64_t)pid_k * a.num_kv_heads + g) * head_blk_k +
-                                   (int64_t)(off_k + (n & 3)) * kD + 32 * q4) * ELT;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kr[s].load(kb + (int64_t)(4 * s) * kD * ELT);
+    __syncthreads();
+    const int ntile = (w1 - w0 + kTile - 1) / kTile;
+    int t = wave;
+#define KVFP8_ISSUE(T_, t_) \
+  issue_tile<FP8>(T_, w0 + (t_) * kTile, w1, e0, ne, s_pid, kpool, vpool, blk, S, a.num_kv_heads, g, q4, n)
+    if (FP8) {
+      // Two tiles in flight per wave.  Tiles past the end issue loads of the pool's first
+      // line (masked), so the body is straight-line and both loop edges leave the same
+      // 2 x 16 loads outstanding (A older than B).
+      const int nt = wave < ntile ? (ntile - wave + kWaves - 1) / kWaves : 0;  // this wave's tiles
+      TileRegs<FP8> A, B;
+      KVFP8_ISSUE(A, t);
+      __builtin_amdgcn_sched_barrier(0);
+      KVFP8_ISSUE(B, t + kWaves);
+      __builtin_amdgcn_sched_barrier(0);
+      int i = 0;
+      for (; i + 2 <= nt; i += 2) {
+        compute_tile<FP8>(A, qv, c_log2, st);
+        KVFP8_ISSUE(A, t + (i + 2) * kWaves);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_tile<FP8>(B, qv, c_log2, st);
+        KVFP8_ISSUE(B, t + (i + 3) * kWaves);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i < nt) compute_tile<FP8>(A, qv, c_log2, st);
     } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kr[s].zero();
-    }
-    VRow<FP8> vr[8];
-    const int nv = max(0, min(16, c1 - tok_v));
-    if (pid_v >= 0) {
-      const uint8_t* vb = vpool + (((int64_t)pid_v * a.num_kv_heads + g) * kD * S +
-                                   (int64_t)n * S + off_v) * ELT;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) vr[j].load(vb + (int64_t)(16 * j) * S * ELT);
-      if (nv < 16) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) vr[j].mask(nv);
+      // bf16 tiles are twice as large: one tile in flight per wave
+      for (; t < ntile; t += kWaves) {
+        TileRegs<FP8> A;
+        KVFP8_ISSUE(A, t);
+        compute_tile<FP8>(A, qv, c_log2, st);
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) vr[j].zero();
     }
-
-    // S^T = K q^T, four chains of 16 tokens
-    f32x4_t sc[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      sc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        sc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[s].op(kk), __builtin_bit_cast(bf16x8_t, qv[kk]),
-                                                        sc[s], 0, 0, 0);
-    }
-    // online softmax for head n over the 16 tokens of sub-page q4 this lane holds
-    float x[16];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pos = 4 * s + i;
-        const bool valid = pid_v >= 0 && pos < nv;
-        const float v = valid ? sc[s][i] * c_log2 : -INFINITY;
-        x[pos] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);  // m_run = -inf -> 0
-    float psum = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      x[k] = exp2f(x[k] - m_use);
-      psum += x[k];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    u32x4_t pp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pp[kb][e] = pack_p<FP8>(x[8 * kb + 2 * e], x[8 * kb + 2 * e + 1]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      acc[j] *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) acc[j] = mfma_pv<FP8>(vr[j], kb, pp[kb], acc[j]);
-    }
+#undef KVFP8_ISSUE
   }
 
   // ---- merge the four waves
+  float l_run = st.l;
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
+  if (threadIdx.x == 0) s_bad = 0;
+  __syncthreads();
   if (q4 == 0) {
-    s_m[wave][n] = m_run;
+    s_m[wave][n] = st.m;
     s_l[wave][n] = l_run;
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    *reinterpret_cast<f32x4_t*>(&s_acc[wave][n][16 * j + 4 * q4]) = acc[j];
-  __syncthreads();
+    *reinterpret_cast<f32x4_t*>(&s_acc[wave][n][16 * j + 4 * q4]) = st.acc[j];
   if (bad) s_bad = 1;
   __syncthreads();
   const bool any_bad = s_bad != 0;

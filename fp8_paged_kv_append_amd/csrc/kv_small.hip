@@ -48,7 +48,7 @@ hipError_t launch_tag_check(const TagArgs& a, hipStream_t stream) {
 
 // ------------------------------------------------------------------ write path
 // Cloudflare post, section "Quantized KV cache": the cache holds e4m3 instead of bf16.
-// One wave per (token, KV head).  K rows are written as contiguous bytes; V goes to
+// One wave per (token, KV head).  K rows go to the chunk-reordered sub-page block; V goes to
 // the transposed page block, one element per d row.
 struct AppendTarget {
   int page, slot;
@@ -76,15 +76,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int H = a.num_kv_heads, S = a.page_size, D = a.head_dim, Dv = a.v_dim;
 
   const uint32_t* ksrc = reinterpret_cast<const uint32_t*>(a.k_new + ((int64_t)tok * H + h) * D);
-  const int64_t kbase = (((int64_t)t.page * H + h) * S + t.slot) * D;
   for (int d2 = lane; d2 < D / 2; d2 += kWave) {
     const uint32_t w = ksrc[d2];
+    // elements 2*d2 and 2*d2+1 share a 16-byte chunk: one 2-element store
+    const int64_t o = k_elem_offset<FP8 ? 1 : 2>(t.page, h, t.slot, 2 * d2, H, S, D);
     if (FP8) {
       const float x0 = bf16_bits_to_f32(w & 0xFFFFu) * a.k_inv;
       const float x1 = bf16_bits_to_f32(w >> 16) * a.k_inv;
-      reinterpret_cast<uint16_t*>(a.k_pool)[(kbase >> 1) + d2] = (uint16_t)encode_e4m3x2(x0, x1);
+      reinterpret_cast<uint16_t*>(a.k_pool)[o >> 1] = (uint16_t)encode_e4m3x2(x0, x1);
     } else {
-      reinterpret_cast<uint32_t*>(a.k_pool)[(kbase >> 1) + d2] = w;
+      reinterpret_cast<uint32_t*>(a.k_pool)[o >> 1] = w;
     }
   }
   if (a.v_pool == nullptr) return;
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   T* ko = reinterpret_cast<T*>(a.k_out) + ((int64_t)tok * H + h) * D;
   const T* kp = reinterpret_cast<const T*>(a.k_pool);
   for (int d = lane; d < D; d += kWave)
-    ko[d] = page < 0 ? T(0) : kp[(((int64_t)page * H + h) * S + slot) * D + d];
+    ko[d] = page < 0 ? T(0) : kp[k_elem_offset<sizeof(T)>(page, h, slot, d, H, S, D)];
   if (a.v_out == nullptr) return;
   T* vo = reinterpret_cast<T*>(a.v_out) + ((int64_t)tok * H + h) * Dv;
   const T* vp = reinterpret_cast<const T*>(a.v_pool);

@@ -80,6 +80,22 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
   return __builtin_amdgcn_cvt_pk_f32_fp8(code & 0xFFu, false)[0];
 }
 
+// Element offset of K element (page, head, slot, d) in a K-layout pool of ELT-byte elements.
+// Each (page, head) block is [S/16] sub-page blocks of 16 tokens x D; inside a sub-page block
+// the rows are cut into 16-byte chunks c = q*NI + k (NI = D*ELT/64, q = 0..3) and token
+// t = 4s + i of the sub-page keeps chunk c at chunk position ((s*NI + k)*4 + q)*4 + i.  A wave
+// that reads lane (q, i)'s k-th chunk of four tokens from four pages then touches four runs of
+// 256 contiguous bytes per instruction.
+template <int ELT>
+__device__ __forceinline__ int64_t k_elem_offset(int page, int head, int slot, int d, int H, int S, int D) {
+  constexpr int E = 16 / ELT;
+  const int NI = D * ELT / 64;
+  const int u = slot >> 4, t = slot & 15, s = t >> 2, i = t & 3;
+  const int c = d / E, q = c / NI, k = c - q * NI;
+  const int chunk = ((s * NI + k) * 4 + q) * 4 + i;
+  return ((int64_t)page * H + head) * S * D + (int64_t)u * 16 * D + (int64_t)chunk * E + (d % E);
+}
+
 template <typename T>
 __device__ __forceinline__ T shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, kWave);

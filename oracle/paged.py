@@ -13,12 +13,19 @@ Readings where the pages are silent:
 * Page table: int32 [B][stride]; entry i of request r is the physical page
   of its tokens [i*S, (i+1)*S).  Entries at or past ceil(L_r / S) are never
   read or checked.
-* Pool layout (element = one e4m3 byte or one bf16).  GQA cache:
-    K: [P][Hkv][S][D]   element (page, head, slot, d)
+* Pool layout (element = one e4m3 byte or one bf16; E = 16 bytes of elements).
+  Every (page, head) block is contiguous.
     V: [P][Hkv][Dv][S]  element (page, head, d, slot) -- each (page, head)
-                        block of V is stored transposed (slot fastest)
+                        block of V is stored transposed (slot fastest).
+    K: [P][Hkv][S/16][16][D] with the 16-token sub-page block reordered in
+       16-byte chunks: token t = 4s + i of the sub-page (s, i in 0..3) and
+       byte chunk c of its row (c = q*NI + k, NI = D*bytes/64, q in 0..3)
+       sit at chunk position ((s*NI + k)*4 + q)*4 + i.  Each group of four
+       tokens thus holds, for each k, four 64-byte runs (one per q) of four
+       16-byte chunks (one per token).  S must be a multiple of 16 and a
+       K row a multiple of 64 bytes.
   Latent cache (one vector per token shared by all query heads):
-    C: [P][1][S][Dl]    same as K with one head; no V pool.
+    C: the K layout with one head and D = Dl; no V pool.
 * Flags, rewritten on every check (not sticky), uint32 per request:
     bit0 (1) a used entry's page tag differs from the expected tag;
     bit1 (2) a used entry's page id is outside [0, P), or the context needs
@@ -37,9 +44,19 @@ FLAG_TAG_MISMATCH = 1
 FLAG_BAD_PAGE = 2
 
 
-def k_offset(page, head, slot, d, num_kv_heads, page_size, head_dim):
-    """Flat element offset of K (or latent) element (page, head, slot, d)."""
-    return ((np.int64(page) * num_kv_heads + head) * page_size + slot) * head_dim + d
+def k_offset(page, head, slot, d, num_kv_heads, page_size, head_dim, elt_bytes):
+    """Flat element offset of K (or latent) element (page, head, slot, d) in the chunk-reordered block."""
+    E = 16 // elt_bytes                      # elements per 16-byte chunk
+    NI = head_dim * elt_bytes // 64          # chunks per 64-byte slice of a row
+    slot = np.asarray(slot, dtype=np.int64)
+    d = np.asarray(d, dtype=np.int64)
+    u, t = slot // 16, slot % 16
+    s, i = t // 4, t % 4
+    c = d // E
+    q, k = c // NI, c % NI
+    chunk = ((s * NI + k) * 4 + q) * 4 + i
+    block = (np.int64(page) * num_kv_heads + head) * page_size * head_dim
+    return block + u * 16 * head_dim + chunk * E + d % E
 
 
 def v_offset(page, head, slot, d, num_kv_heads, page_size, v_dim):
@@ -102,13 +119,14 @@ def append(k_pool, v_pool, k_new, v_new, tok_req, tok_pos, page_table, num_kv_he
     """
     N, H, D = k_new.shape
     assert H == num_kv_heads
+    elt = k_pool.dtype.itemsize
     num_pages = k_pool.size // (H * page_size * D)
     idx, page, slot = _token_targets(tok_req, tok_pos, page_table, num_pages, page_size, flags)
     h = np.arange(H, dtype=np.int64)[None, :, None]
     d = np.arange(D, dtype=np.int64)[None, None, :]
     for a in range(0, idx.size, chunk):
         i, p, s = idx[a:a + chunk], page[a:a + chunk, None, None], slot[a:a + chunk, None, None]
-        k_pool[k_offset(p, h, s, d, H, page_size, D)] = k_new[i]
+        k_pool[k_offset(p, h, s, d, H, page_size, D, elt)] = k_new[i]
         if v_pool is not None:
             Dv = v_new.shape[2]
             dv = np.arange(Dv, dtype=np.int64)[None, None, :]
@@ -135,7 +153,7 @@ def gather(k_pool, v_pool, page_table, r, length, num_kv_heads, page_size, head_
     h = np.arange(num_kv_heads, dtype=np.int64)
     d = np.arange(head_dim, dtype=np.int64)
     ko = k_offset(page[:, None, None], h[None, :, None], slot[:, None, None], d[None, None, :],
-                  num_kv_heads, page_size, head_dim)
+                  num_kv_heads, page_size, head_dim, k_pool.dtype.itemsize)
     k = k_pool[ko]
     v = None
     if v_pool is not None:

@@ -80,8 +80,19 @@ def test_equal_keys_give_mean_of_values(dtype):
         np.testing.assert_allclose(o[h], ref, rtol=0, atol=1e-13)
 
 
+def _k_index(page, h, slot, d, H, S, D, elt):
+    """K element position, written out from the layout rule (16-token sub-pages, 16-byte chunks)."""
+    per_chunk = 16 // elt
+    ni = D * elt // 64
+    sub, tok = divmod(slot, 16)
+    grp, i = divmod(tok, 4)
+    q, k = divmod(d // per_chunk, ni)
+    return (page * H + h) * S * D + sub * 16 * D + (((grp * ni + k) * 4 + q) * 4 + i) * per_chunk + d % per_chunk
+
+
 def _brute_force(q_bits, k_pool, v_pool, pt, lens, H, S, D, Dv, Hq, dtype, ks, vs, sm):
     """Pure-Python loops straight from the definition, reading the pools element by element."""
+    elt = 1 if dtype == "fp8" else 2
     dec = (lambda c: float(codec.e4m3_decode([c])[0])) if dtype == "fp8" else \
           (lambda b: float(codec.f32_from_bf16([b])[0]))
     out = []
@@ -94,7 +105,7 @@ def _brute_force(q_bits, k_pool, v_pool, pt, lens, H, S, D, Dv, Hq, dtype, ks, v
             scores = []
             for t in range(lens[r]):
                 page, slot = int(pt[r, t // S]), t % S
-                kk = [dec(k_pool[((page * H + g) * S + slot) * D + d]) * ks for d in range(D)]
+                kk = [dec(k_pool[_k_index(page, g, slot, d, H, S, D, elt)]) * ks for d in range(D)]
                 scores.append(sm * sum(a * b for a, b in zip(q, kk)))
             mx = max(scores)
             e = [math.exp(s - mx) for s in scores]
@@ -111,13 +122,13 @@ def _brute_force(q_bits, k_pool, v_pool, pt, lens, H, S, D, Dv, Hq, dtype, ks, v
 
 @pytest.mark.parametrize("dtype", ["fp8", "bf16"])
 def test_brute_force_tiny_shapes(dtype):
-    w = wl.Workload("bf", batch=3, num_q_heads=4, num_kv_heads=2, head_dim=16, v_dim=16, page_size=16,
+    w = wl.Workload("bf", batch=3, num_q_heads=4, num_kv_heads=2, head_dim=64, v_dim=16, page_size=16,
                     num_pages=12, ctx_lo=1, ctx_hi=40, seed=99)
     lens = np.array([40, 17, 1], dtype=np.int32)
     st, k, v, _ = _cache(w, dtype, lens=lens)
     q = wl.queries(w)
     got = _attn(st, q)
-    ref = _brute_force(q, st["k_pool"], st["v_pool"], st["page_table"], lens, 2, 16, 16, 16, 4, dtype,
+    ref = _brute_force(q, st["k_pool"], st["v_pool"], st["page_table"], lens, 2, 16, 64, 16, 4, dtype,
                        float(st["k_scale"]), float(st["v_scale"]), st["sm_scale"])
     for r in range(3):
         np.testing.assert_allclose(got[r], ref[r], rtol=1e-12, atol=1e-13)
@@ -167,7 +178,7 @@ def test_physical_page_permutation_invariance():
 
 def test_gqa_group_mapping_against_single_head_runs():
     """Head h of a 4-head/2-group cache equals a 1-KV-head run over group h // 2."""
-    w = wl.Workload("g", batch=1, num_q_heads=4, num_kv_heads=2, head_dim=16, v_dim=16, page_size=16,
+    w = wl.Workload("g", batch=1, num_q_heads=4, num_kv_heads=2, head_dim=64, v_dim=16, page_size=16,
                     num_pages=4, ctx_lo=20, ctx_hi=20, seed=11)
     st, k, v, lens = _cache(w, "bf16")
     q = wl.queries(w)
@@ -194,7 +205,7 @@ def test_aborted_and_empty_requests_give_zero_rows():
 
 def test_latent_matches_gqa_formula():
     """The latent cache is one shared K of width 576 whose first 512 dims are V."""
-    w = wl.Workload("lat", batch=2, num_q_heads=4, num_kv_heads=1, head_dim=24, v_dim=16, page_size=16,
+    w = wl.Workload("lat", batch=2, num_q_heads=4, num_kv_heads=1, head_dim=64, v_dim=16, page_size=16,
                     num_pages=8, ctx_lo=30, ctx_hi=30, seed=12, latent=True)
     st, k, _, lens = _cache(w, "fp8")
     q = wl.queries(w)
@@ -202,7 +213,7 @@ def test_latent_matches_gqa_formula():
     off = np.concatenate([[0], np.cumsum(lens)])
     for r in range(2):
         c = codec.e4m3_decode(codec.quantize_e4m3(k[off[r]:off[r + 1], 0], st["k_scale"])) * np.float64(st["k_scale"])
-        ref = attention.softmax_attention(codec.f64_from_bf16(q[r]), c, c[:, :16], 1 / math.sqrt(24))
+        ref = attention.softmax_attention(codec.f64_from_bf16(q[r]), c, c[:, :16], 1 / math.sqrt(64))
         np.testing.assert_allclose(o[r], ref, rtol=1e-13, atol=1e-14)
 
 

@@ -80,29 +80,51 @@ def test_tag_check_bad_page_ids_and_lengths():
 # ----------------------------------------------------------------------------- layout / append / gather
 
 def test_layout_offsets_by_hand():
-    """Hand-worked offsets of the pool layout (P=3, Hkv=2, S=4, D=Dv=5)."""
-    # K element (page 2, head 1, slot 3, d 4): ((2*2+1)*4+3)*5+4 = 119
-    assert paged.k_offset(2, 1, 3, 4, 2, 4, 5) == 119
-    # V element (page 2, head 1, slot 3, d 4): ((2*2+1)*5+4)*4+3 = 119
+    """Hand-worked offsets of the pool layout."""
+    # e4m3 K, Hkv=2, S=16, D=64 (one 64-byte slice per row, NI=1): element (page 2, head 1, slot 13, d 37)
+    #   block (2*2+1)*16*64 = 5120; token 13 = 4*3+1 (s=3, i=1); chunk 37//16 = 2 (q=2, k=0)
+    #   chunk position ((3*1+0)*4+2)*4+1 = 57 -> 5120 + 57*16 + 37%16 = 6037
+    assert paged.k_offset(2, 1, 13, 37, 2, 16, 64, 1) == 6037
+    # e4m3 K, Hkv=1, S=32, D=64: (page 1, head 0, slot 17, d 0) -> 2048 + sub-page 1 (1024) + chunk 1 (16)
+    assert paged.k_offset(1, 0, 17, 0, 1, 32, 64, 1) == 3088
+    # bf16 K, Hkv=1, S=16, D=128 (8 elements a chunk, NI=4): (page 0, head 0, slot 5, d 100)
+    #   token 5 (s=1, i=1); chunk 100//8 = 12 (q=3, k=0); position ((1*4+0)*4+3)*4+1 = 77 -> 77*8 + 4
+    assert paged.k_offset(0, 0, 5, 100, 1, 16, 128, 2) == 620
+    # e4m3 K, D=128 (NI=2): the 32 bytes lane group q reads of token 4s+i start at 512s + 64q + 16i
+    # (first half, k=0) and 256 bytes later (second half, k=1)
+    for s_ in range(4):
+        for q in range(4):
+            for i in range(4):
+                assert paged.k_offset(0, 0, 4 * s_ + i, 32 * q, 1, 16, 128, 1) == 512 * s_ + 64 * q + 16 * i
+                assert paged.k_offset(0, 0, 4 * s_ + i, 32 * q + 16, 1, 16, 128, 1) == 512 * s_ + 256 + 64 * q + 16 * i
+    # V element (page 2, head 1, slot 3, d 4), Hkv=2, S=4, Dv=5: ((2*2+1)*5+4)*4+3 = 119
     assert paged.v_offset(2, 1, 3, 4, 2, 4, 5) == 119
-    # V element (page 0, head 0, slot 1, d 0) is the 2nd byte; K's is the 6th
     assert paged.v_offset(0, 0, 1, 0, 2, 4, 5) == 1
-    assert paged.k_offset(0, 0, 1, 0, 2, 4, 5) == 5
+
+
+@pytest.mark.parametrize("S,D,elt", [(16, 128, 1), (16, 128, 2), (64, 128, 1), (32, 576, 1), (16, 576, 2), (16, 64, 1)])
+def test_k_layout_is_a_bijection_per_block(S, D, elt):
+    slot, d = np.meshgrid(np.arange(S), np.arange(D), indexing="ij")
+    off = paged.k_offset(1, 1, slot, d, 2, S, D, elt)
+    base = (1 * 2 + 1) * S * D
+    assert np.array_equal(np.sort(off.ravel()), base + np.arange(S * D))
 
 
 def test_append_writes_exactly_the_addressed_elements():
-    H, S, D, P = 2, 4, 5, 3
+    H, S, D, P = 2, 16, 64, 3
     kp = np.zeros(P * H * S * D, dtype=np.uint8)
     vp = np.zeros(P * H * S * D, dtype=np.uint8)
     pt = np.array([[2, 0]], dtype=np.int32)
     k_new = np.arange(1, 1 + H * D, dtype=np.uint8).reshape(1, H, D)
-    v_new = (100 + np.arange(H * D, dtype=np.uint8)).reshape(1, H, D)
-    paged.append(kp, vp, k_new, v_new, [0], [7], pt, H, S)        # token 7 -> page pt[0][1] = 0, slot 3
-    kk = kp.reshape(P, H, S, D)
+    v_new = (100 + np.arange(H * D) % 100).astype(np.uint8).reshape(1, H, D)
+    paged.append(kp, vp, k_new, v_new, [0], [19], pt, H, S)       # token 19 -> page pt[0][1] = 0, slot 3
+    for h in range(H):
+        for d in range(D):
+            assert kp[paged.k_offset(0, h, 3, d, H, S, D, 1)] == k_new[0, h, d]
     vv = vp.reshape(P, H, D, S)
-    assert np.array_equal(kk[0, :, 3, :], k_new[0])
     assert np.array_equal(vv[0, :, :, 3], v_new[0])
-    assert kp.sum() == k_new.astype(np.int64).sum() and vp.sum() == v_new.astype(np.int64).sum()
+    assert kp.astype(np.int64).sum() == k_new.astype(np.int64).sum()
+    assert vp.astype(np.int64).sum() == v_new.astype(np.int64).sum()
 
 
 def test_append_gather_roundtrip_and_untouched_bytes():
@@ -131,22 +153,23 @@ def test_append_gather_roundtrip_and_untouched_bytes():
 
 
 def test_append_skips_flagged_and_out_of_range():
-    H, S, D, P = 1, 4, 3, 4
+    H, S, D, P = 1, 16, 32, 4
     kp = np.zeros(P * H * S * D, dtype=np.uint16)
     vp = np.zeros(P * H * S * D, dtype=np.uint16)
     pt = np.array([[0, 1], [2, -1], [3, 9]], dtype=np.int32)
     k_new = np.full((5, H, D), 7, dtype=np.uint16)
     req = [0, 1, 1, 2, 2]
-    pos = [1, 0, 5, 2, 6]        # r1 pos5 -> entry -1 (skip); r2 pos6 -> page 9 (skip)
+    pos = [1, 0, 17, 2, 18]      # r1 pos17 -> entry -1 (skip); r2 pos18 -> page 9 (skip)
     flags = np.array([1, 0, 0], dtype=np.uint32)                 # r0 aborted
     paged.append(kp, vp, k_new, k_new, req, pos, pt, H, S, flags=flags)
-    kk = kp.reshape(P, H, S, D)
-    assert kk[0].sum() == 0 and kk[1].sum() == 0
-    assert (kk[2, 0, 0] == 7).all() and (kk[3, 0, 2] == 7).all()
+    blk = H * S * D
+    assert kp[:2 * blk].sum() == 0
+    got = lambda page, slot: kp[paged.k_offset(page, 0, slot, np.arange(D), H, S, D, 2)]
+    assert (got(2, 0) == 7).all() and (got(3, 2) == 7).all()
     assert kp.astype(np.int64).sum() == 7 * D * 2
     # positions beyond the page-table row are skipped too
     kp2 = np.zeros_like(kp)
-    paged.append(kp2, None, k_new[:1], None, [2], [8], pt, H, S)
+    paged.append(kp2, None, k_new[:1], None, [2], [32], pt, H, S)
     assert kp2.sum() == 0
 
 
