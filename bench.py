@@ -45,8 +45,10 @@ def parse():
     p.add_argument("--splits", type=int, default=0, help="0 = library choice")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bf16", action="store_true")
-    p.add_argument("--cpu-sample", type=int, default=4, help="requests in the CPU oracle sample")
+    p.add_argument("--cpu-sample", type=int, default=8, help="requests in the CPU oracle sample")
     p.add_argument("--fp8-only-steps", action="store_true", help="time only the FP8 step (profiling runs)")
+    p.add_argument("--graph", action="store_true",
+                   help="time replays of a captured HIP graph of one step (default: eager launches)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after timing, copy a MIB-MiB buffer 3 times (a known-size kernel for HBM counters)")
     return p.parse_args()
@@ -108,21 +110,52 @@ class DeviceCache:
             self.kv.paged_decode_attn_bf16(self.desc, self.q, self.kp, self.vp, self.pt, self.lens, self.max_ctx,
                                            self.out, f, num_splits=self.splits, workspace=self.ws)
 
-    def run(self, steps, warmup, tracker=True):
-        """Time `steps` steps; per-kernel HIP events on the launch stream (torch's current stream)."""
+    def step(self, tracker=True):
+        if tracker:
+            self.check()
+        self.append(tracker)
+        self.attend(tracker)
+
+    def run(self, steps, warmup, tracker=True, graph=False):
+        """Time `steps` back-to-back steps between two events on the launch stream (torch's current
+        stream), eagerly or as replays of a captured graph of one step."""
         torch = self.torch
         for _ in range(warmup):
-            if tracker:
-                self.check()
-            self.append(tracker)
-            self.attend(tracker)
+            self.step(tracker)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                self.step(tracker)
+            torch.cuda.current_stream().wait_stream(side)
+            with torch.cuda.graph(g):
+                self.step(tracker)
+            for _ in range(warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            fn = g.replay
+        else:
+            fn = lambda: self.step(tracker)  # noqa: E731
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
         t0.record()
+        for _ in range(steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        total_ms = t0.elapsed_time(t1)
+        return dict(ms_per_step=total_ms / steps, wall_ms_per_step=1e3 * wall / steps)
+
+    def breakdown(self, steps, tracker=True):
+        """Per-kernel durations: an event before and after each launch of every step."""
+        torch = self.torch
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        torch.cuda.synchronize()
         for e in evs:
             e[0].record()
             if tracker:
@@ -132,19 +165,31 @@ class DeviceCache:
             e[2].record()
             self.attend(tracker)
             e[3].record()
-        t1.record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
         per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
-        total_ms = t0.elapsed_time(t1)
-        return dict(ms_per_step=total_ms / steps, wall_ms_per_step=1e3 * wall / steps,
-                    check_ms=float(np.median(per[:, 0])), append_ms=float(np.median(per[:, 1])),
+        return dict(check_ms=float(np.median(per[:, 0])), append_ms=float(np.median(per[:, 1])),
                     attn_ms=float(np.median(per[:, 2])), attn_ms_mean=float(per[:, 2].mean()),
                     attn_ms_p95=float(np.percentile(per[:, 2], 95)),
                     step_ms_p95=float(np.percentile(per.sum(axis=1), 95)))
 
 
-def cpu_baseline(w, n_req):
+def measured_traffic(workload, splits):
+    """HBM bytes per launch of the FP8 attention kernel from the committed counter runs, or None when the
+    kernel's sources changed since those counters were taken (or they cover another launch shape)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_fp8_64x8192_traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    h = hashlib.sha256()
+    for src in d["kernel_sources"]:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    if h.hexdigest() != d["kernel_sources_sha256"] or d["workload"] != workload or d["splits"] != splits:
+        return None
+    return d["traffic_bytes"]
+
+
+def cpu_baseline(w, n_req, min_seconds=10.0):
     """The oracle's step (tag check, e4m3 append of one token per request, fp64 attention) on a sample."""
     from concurrent.futures import ThreadPoolExecutor  # noqa: F401
     from threadpoolctl import threadpool_limits
@@ -168,15 +213,19 @@ def cpu_baseline(w, n_req):
               sm_scale=1 / math.sqrt(ws.head_dim), latent=False)
     last = np.cumsum(lens) - 1
     workers = min(16, os.cpu_count() or 1, n_req)
+    times = []
     with threadpool_limits(1):
-        t = time.perf_counter()
-        step.decode_step(st, wl.queries(ws), k[last], v[last], np.arange(n_req, dtype=np.int32),
-                         (lens - 1).astype(np.int32), workers=workers)
-        dt = time.perf_counter() - t
+        while len(times) < 3 or sum(times) < min_seconds:
+            t = time.perf_counter()
+            step.decode_step(st, wl.queries(ws), k[last], v[last], np.arange(n_req, dtype=np.int32),
+                             (lens - 1).astype(np.int32), workers=workers)
+            times.append(time.perf_counter() - t)
+    dt = float(np.median(times))
     kv_bytes = int(lens.astype(np.int64).sum()) * ws.num_kv_heads * ws.head_dim * 2
     return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
             "sample": f"{n_req} of {w.batch} requests of {w.name} (same shapes, FP8 cache), one decode step "
-                      f"(tag check + e4m3 append + fp64 attention) in {dt:.2f} s",
+                      f"(tag check + e4m3 append + fp64 attention), median of {len(times)} runs "
+                      f"({sum(times):.1f} s of CPU time in all): {dt:.2f} s per step",
             "seconds": dt}
 
 
@@ -228,18 +277,21 @@ def main():
         t = time.perf_counter()
         c = DeviceCache(w, kvd, host, torch, kv)
         log(f"{kvd}: cache filled in {time.perf_counter() - t:.1f} s, splits={c.splits}")
-        r = c.run(args.steps, args.warmup, tracker=True)
+        r = c.run(args.steps, args.warmup, tracker=True, graph=args.graph)
+        r["other"] = c.run(args.steps, args.warmup, tracker=True, graph=not args.graph)
+        r.update(c.breakdown(args.steps, tracker=True))
         flags = c.flags.cpu().numpy().view(np.uint32)
         assert np.flatnonzero(flags).tolist() == stale.tolist(), "abort flags differ from the planted stale set"
         if not args.fp8_only_steps:
-            r["no_tracker"] = c.run(args.steps, args.warmup, tracker=False)
+            r["no_tracker"] = c.run(args.steps, args.warmup, tracker=False, graph=args.graph)
         elt = 1 if kvd == "fp8" else 2
         r["kv_bytes"] = kv_elems * elt
         r["gbs_step"] = r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
         r["gbs_attn"] = r["kv_bytes"] / (r["attn_ms_mean"] * 1e-3) / 1e9
         r["splits"] = c.splits
         results[kvd] = r
-        log(f"{kvd}: {json.dumps({k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in r.items() if k_ != 'no_tracker'})}")
+        log(f"{kvd}: {json.dumps({k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in r.items() if k_ not in ('no_tracker', 'other')})}")
+        log(f"{kvd}: {'eager' if args.graph else 'graph'} {r['other']}; tracker off {r.get('no_tracker')}")
         del c
         torch.cuda.empty_cache()
 
@@ -267,11 +319,17 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
                    "splits": f8["splits"], "step": "tag check + append(1 token/request) + attention + merge"},
         "roofline": {"bound": "hbm", "achieved": round(f8["gbs_attn"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(f8["gbs_attn"] / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_decode_attn_fp8 (split kernel + merge)",
+                     "frac": round(f8["gbs_attn"] / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name, f8["splits"]),
+                     "algorithmic_bytes": f8["kv_bytes"],
+                     "kernel": "paged_decode_attn_fp8 (split kernel, plus the merge kernel when splits > 1)",
                      "attn_ms_mean": round(f8["attn_ms_mean"], 5), "attn_ms_p95": round(f8["attn_ms_p95"], 5)},
         "step_breakdown_ms": {"tag_check": round(f8["check_ms"], 5), "append": round(f8["append_ms"], 5),
-                              "attention": round(f8["attn_ms"], 5), "step_p95": round(f8["step_ms_p95"], 5)},
+                              "attention": round(f8["attn_ms"], 5), "step_p95": round(f8["step_ms_p95"], 5),
+                              "note": "events around each launch of eager steps"},
+        "timing": ("steps replayed from a captured HIP graph of one step" if args.graph else
+                   "eager back-to-back steps") + ", between two events on the launch stream",
+        ("eager_ms_per_step" if args.graph else "graph_ms_per_step"): round(f8["other"]["ms_per_step"], 5),
     }
     if "no_tracker" in f8:
         nt = f8["no_tracker"]

@@ -30,8 +30,9 @@ int check_pool(const kvfp8_pool_desc* d, bool need_v_dim_eq, int elt_bytes) {
 
 int32_t n_tiles_of(int32_t max_ctx) { return (int32_t)(((int64_t)max_ctx + kAttnTileTokens - 1) / kAttnTileTokens); }
 
-// Blocks (4 waves each) the launch aims for: 4 per CU on 256 CUs.
-constexpr int64_t kTargetBlocks = 1024;
+// Blocks (4 waves each) the launch aims for: the attention kernel holds two blocks per CU
+// (two waves per SIMD), so 512 blocks fill the 256 CUs once.
+constexpr int64_t kTargetBlocks = 512;
 
 int32_t auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_ctx) {
   const int64_t items = (int64_t)batch * num_kv_heads;
