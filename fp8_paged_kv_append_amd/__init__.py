@@ -22,7 +22,8 @@ from ._lib import FLAG_BAD_PAGE, FLAG_TAG_MISMATCH, PoolDesc  # noqa: F401
 __all__ = ["KvFp8Error", "PoolDesc", "pool_desc", "kv_absmax_bf16", "kv_scale_from_absmax", "calibrate_scale",
            "kv_append_fp8", "kv_append_bf16", "kv_tag_check", "paged_decode_attn_workspace_bytes",
            "paged_decode_attn_auto_splits", "paged_decode_attn_fp8", "paged_decode_attn_bf16",
-           "kv_gather_fp8", "kv_gather_bf16", "decode_step", "lib"]
+           "paged_decode_attn_latent_auto_splits", "paged_decode_attn_latent_fp8",
+           "paged_decode_attn_latent_bf16", "kv_gather_fp8", "kv_gather_bf16", "decode_step", "lib"]
 
 
 class KvFp8Error(RuntimeError):
@@ -168,6 +169,38 @@ def paged_decode_attn_bf16(desc: PoolDesc, q, k_pool, v_pool, page_table, ctx_le
         _ptr(page_table, _I32, "page_table"), page_table.shape[1], _ptr(ctx_lens, _I32, "ctx_lens"), B,
         int(max_ctx_len), _ptr(abort_flags, _U32, "abort_flags", True), float(sm_scale), int(num_splits), ws, wsb,
         _ptr(out, _BF16, "out"), _stream(stream)), "paged_decode_attn_bf16")
+
+
+def paged_decode_attn_latent_auto_splits(batch, num_q_heads, max_ctx_len) -> int:
+    return int(lib().paged_decode_attn_latent_auto_splits(int(batch), int(num_q_heads), int(max_ctx_len)))
+
+
+def paged_decode_attn_latent_fp8(desc: PoolDesc, q, pool, page_table, ctx_lens, max_ctx_len: int, out,
+                                 abort_flags=None, *, scale: float, sm_scale: Optional[float] = None,
+                                 num_splits: int = 0, workspace=None, stream=None):
+    B, Hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    ws, wsb = _ws(workspace)
+    _check(lib().paged_decode_attn_latent_fp8(
+        desc, _ptr(q, _BF16, "q"), Hq, _ptr(pool, _U8, "pool"), _ptr(page_table, _I32, "page_table"),
+        page_table.shape[1], _ptr(ctx_lens, _I32, "ctx_lens"), B, int(max_ctx_len),
+        _ptr(abort_flags, _U32, "abort_flags", True), float(scale), float(sm_scale), int(num_splits), ws, wsb,
+        _ptr(out, _BF16, "out"), _stream(stream)), "paged_decode_attn_latent_fp8")
+
+
+def paged_decode_attn_latent_bf16(desc: PoolDesc, q, pool, page_table, ctx_lens, max_ctx_len: int, out,
+                                  abort_flags=None, *, sm_scale: Optional[float] = None, num_splits: int = 0,
+                                  workspace=None, stream=None):
+    B, Hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    ws, wsb = _ws(workspace)
+    _check(lib().paged_decode_attn_latent_bf16(
+        desc, _ptr(q, _BF16, "q"), Hq, _ptr(pool, _BF16, "pool"), _ptr(page_table, _I32, "page_table"),
+        page_table.shape[1], _ptr(ctx_lens, _I32, "ctx_lens"), B, int(max_ctx_len),
+        _ptr(abort_flags, _U32, "abort_flags", True), float(sm_scale), int(num_splits), ws, wsb,
+        _ptr(out, _BF16, "out"), _stream(stream)), "paged_decode_attn_latent_bf16")
 
 
 # ----------------------------------------------------------------------------- read back (tests)

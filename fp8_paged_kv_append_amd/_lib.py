@@ -41,6 +41,11 @@ PROTOTYPES = {
                                         _f32, _i32, _p, _sz, _p, _p]),
     "paged_decode_attn_bf16": (C.c_int, [_desc, _p, _i32, _p, _p, _p, _i32, _p, _i32, _i32, _p, _f32, _i32,
                                          _p, _sz, _p, _p]),
+    "paged_decode_attn_latent_auto_splits": (_i32, [_i32, _i32, _i32]),
+    "paged_decode_attn_latent_fp8": (C.c_int, [_desc, _p, _i32, _p, _p, _i32, _p, _i32, _i32, _p, _f32, _f32, _i32,
+                                               _p, _sz, _p, _p]),
+    "paged_decode_attn_latent_bf16": (C.c_int, [_desc, _p, _i32, _p, _p, _i32, _p, _i32, _i32, _p, _f32, _i32, _p,
+                                                _sz, _p, _p]),
     "kv_gather_fp8": (C.c_int, [_desc, _p, _p, _p, _p, _i32, _p, _i32, _i32, _p, _p, _p]),
     "kv_gather_bf16": (C.c_int, [_desc, _p, _p, _p, _p, _i32, _p, _i32, _i32, _p, _p, _p]),
 }

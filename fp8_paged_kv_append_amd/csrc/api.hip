@@ -165,6 +165,76 @@ int attn_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_he
   return launch_attn_gqa(a, fp8, batch, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
 }
 
+int32_t latent_head_groups(int32_t num_q_heads) {
+  return (num_q_heads + kLatentHeadsPerBlock - 1) / kLatentHeadsPerBlock;
+}
+
+int32_t latent_auto_splits(int32_t batch, int32_t num_q_heads, int32_t max_ctx) {
+  const int64_t items = (int64_t)batch * latent_head_groups(num_q_heads);
+  const int32_t tiles = (int32_t)(((int64_t)max_ctx + kLatentTileTokens - 1) / kLatentTileTokens);
+  if (items <= 0 || tiles <= 0) return 1;
+  int64_t s = (kTargetBlocks + items - 1) / items;
+  int64_t cap = tiles / 2;
+  if (cap < 1) cap = 1;
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  return (int32_t)s;
+}
+
+int latent_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads, const void* pool,
+                  const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens, int32_t batch,
+                  int32_t max_ctx_len, const uint32_t* flags, bool fp8, float scale, float sm_scale,
+                  int32_t num_splits, void* workspace, size_t workspace_bytes, uint16_t* out, hipStream_t stream) {
+  int st = check_pool(desc, false, fp8 ? 1 : 2);
+  if (st) return st;
+  if (desc->num_kv_heads != 1 || desc->head_dim != kLatentDim || desc->v_dim != kLatentVDim)
+    return KVFP8_ERR_UNSUPPORTED;
+  if (batch < 0 || num_q_heads < 1 || pt_stride < 1 || num_splits < 0) return KVFP8_ERR_SHAPE;
+  if (batch == 0) return KVFP8_OK;
+  if (!q || !pool || !page_table || !ctx_lens || !out) return KVFP8_ERR_NULL;
+  if (num_q_heads % 16 != 0) return KVFP8_ERR_UNSUPPORTED;
+  if (max_ctx_len < 1) return KVFP8_ERR_SHAPE;
+  if ((int64_t)pt_stride * desc->page_size < max_ctx_len) return KVFP8_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(pool) || !aligned16(out)) return KVFP8_ERR_ALIGN;
+  if (!good_scale(scale) || !good_scale(sm_scale)) return KVFP8_ERR_VALUE;
+  const int32_t tiles = (int32_t)(((int64_t)max_ctx_len + kLatentTileTokens - 1) / kLatentTileTokens);
+  int32_t splits = num_splits == 0 ? latent_auto_splits(batch, num_q_heads, max_ctx_len) : num_splits;
+  if (splits > tiles) return KVFP8_ERR_SHAPE;
+  const int32_t chunk_tiles = (tiles + splits - 1) / splits;
+  splits = (tiles + chunk_tiles - 1) / chunk_tiles;
+  const int32_t n_hg = latent_head_groups(num_q_heads);
+  if ((((int64_t)batch * splits + 7) / 8) * 8 * n_hg > 2147483647LL) return KVFP8_ERR_SHAPE;
+  LatentArgs a;
+  a.o_part = nullptr;
+  a.lse_part = nullptr;
+  if (splits > 1) {
+    const size_t need = paged_decode_attn_workspace_bytes(batch, num_q_heads, kLatentVDim, splits);
+    if (workspace == nullptr) return KVFP8_ERR_NULL;
+    if (workspace_bytes < need) return KVFP8_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KVFP8_ERR_ALIGN;
+    a.o_part = reinterpret_cast<float*>(workspace);
+    a.lse_part = a.o_part + (size_t)batch * num_q_heads * splits * kLatentVDim;
+  }
+  a.q = q;
+  a.pool = pool;
+  a.page_table = page_table;
+  a.ctx_lens = ctx_lens;
+  a.flags = flags;
+  a.out = out;
+  a.num_pages = desc->num_pages;
+  a.page_size = desc->page_size;
+  a.num_q_heads = num_q_heads;
+  a.pt_stride = pt_stride;
+  a.chunk_tiles = chunk_tiles;
+  a.num_splits = splits;
+  a.max_ctx = max_ctx_len;
+  a.batch = batch;
+  a.n_hg = n_hg;
+  a.qk_scale_log2 = (fp8 ? sm_scale * scale : sm_scale) * kLog2e;
+  a.v_scale = fp8 ? scale : 1.0f;
+  return launch_attn_latent(a, fp8, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -263,6 +333,28 @@ int paged_decode_attn_bf16(const kvfp8_pool_desc* desc, const uint16_t* q, int32
                            size_t workspace_bytes, uint16_t* out, hipStream_t stream) {
   return attn_common(desc, q, num_q_heads, k_pool, v_pool, page_table, pt_stride, ctx_lens, batch, max_ctx_len,
                      abort_flags, false, 1.f, 1.f, sm_scale, num_splits, workspace, workspace_bytes, out, stream);
+}
+
+int32_t paged_decode_attn_latent_auto_splits(int32_t batch, int32_t num_q_heads, int32_t max_ctx_len) {
+  return latent_auto_splits(batch, num_q_heads, max_ctx_len);
+}
+
+int paged_decode_attn_latent_fp8(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads,
+                                 const uint8_t* pool, const int32_t* page_table, int32_t pt_stride,
+                                 const int32_t* ctx_lens, int32_t batch, int32_t max_ctx_len,
+                                 const uint32_t* abort_flags, float scale, float sm_scale, int32_t num_splits,
+                                 void* workspace, size_t workspace_bytes, uint16_t* out, hipStream_t stream) {
+  return latent_common(desc, q, num_q_heads, pool, page_table, pt_stride, ctx_lens, batch, max_ctx_len, abort_flags,
+                       true, scale, sm_scale, num_splits, workspace, workspace_bytes, out, stream);
+}
+
+int paged_decode_attn_latent_bf16(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads,
+                                  const uint16_t* pool, const int32_t* page_table, int32_t pt_stride,
+                                  const int32_t* ctx_lens, int32_t batch, int32_t max_ctx_len,
+                                  const uint32_t* abort_flags, float sm_scale, int32_t num_splits, void* workspace,
+                                  size_t workspace_bytes, uint16_t* out, hipStream_t stream) {
+  return latent_common(desc, q, num_q_heads, pool, page_table, pt_stride, ctx_lens, batch, max_ctx_len, abort_flags,
+                       false, 1.f, sm_scale, num_splits, workspace, workspace_bytes, out, stream);
 }
 
 int kv_gather_fp8(const kvfp8_pool_desc* desc, const uint8_t* k_pool, const uint8_t* v_pool, const int32_t* tok_req,

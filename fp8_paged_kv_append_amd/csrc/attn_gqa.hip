@@ -299,8 +299,9 @@ __global__ __launch_bounds__(kThreads) void attn_gqa_split_kernel(AttnArgs a) {
   for (int j = 0; j < 8; ++j) st.acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   bool bad = false;
 
-  // tokens per page-id window: a multiple of the tile and of the page size
-  const int win = (kPidWin * S / kTile) * kTile;
+  // tokens per page-id window: a multiple of the tile, at most kPidWin - 1 pages long, so that even
+  // a window that does not start on a page boundary touches at most kPidWin pages
+  const int win = ((kPidWin - 1) * S / kTile) * kTile;
   for (int w0 = c0; w0 < c1; w0 += win) {
     const int w1 = min(c1, w0 + win);
     const int e0 = w0 / S;
@@ -450,7 +451,11 @@ hipError_t launch_attn_gqa(const AttnArgs& a, bool fp8, int batch, hipStream_t s
   m.max_ctx = a.max_ctx;
   m.pt_stride = a.pt_stride;
   m.page_size = a.page_size;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(batch * a.num_q_heads), dim3(kD), 0, stream, m);
+  return launch_merge(m, batch, stream);
+}
+
+hipError_t launch_merge(const MergeArgs& m, int batch, hipStream_t stream) {
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(batch * m.num_q_heads), dim3(kD), 0, stream, m);
   return hipGetLastError();
 }
 

@@ -1,0 +1,283 @@
+// Split-K paged decode attention over a latent (MLA-style) cache: one vector of
+// width 576 per token, shared by every query head; scores use all 576 dims, the
+// values are its first 512.  FP8 (e4m3) or BF16 cache, gfx950.
+//
+// What it computes is the same softmax attention as the GQA kernel (Cloudflare
+// blog "Smaller, faster, safer: running Kimi and GLM at scale", section
+// "Quantized KV cache": the FP8 cache is converted as it is read), with one
+// cached vector serving as both key and value.  Unlike GQA this shape is bound
+// by the matrix units, not by HBM: 128 heads x (576 + 512) MACs per cached byte.
+//
+// Block = (request r, 64-head group hg, split c), 4 waves of 16 heads each.
+// The two head groups of one (r, c) are 8 block ids apart, so round-robin
+// dispatch puts them on the same XCD and the second read of a tile hits L2.
+// Per 32-token tile the block stages the tile once into LDS as bf16, in two
+// shapes: token rows (for S^T = C q^T) and a transposed [dv][token] copy (for
+// O^T += V^T P^T).  With lane = 16*q + n:
+//  * S^T: two 16-token blocks, A = C rows (lane (q, m) reads 8 dims of token
+//    m), B = q^T (lane (q, n) holds 8 dims of head n); the contraction slot
+//    (q, kk, j) is dim 144q + 8kk + j for both operands.
+//  * C layout: lane (q, n) holds head n's scores for tokens 16mb + 4q + i;
+//    the PV contraction slot (q, j) is token 16(j/4) + 4q + j%4, so the P it
+//    holds is already the B operand and V^T is read as two 4-token runs.
+//  * O^T accumulators: 32 d-blocks x 4 fp32 per lane, column = head n, so the
+//    online-softmax rescale is lane-local.
+#include "kvfp8_device.h"
+#include "kvfp8_internal.h"
+
+namespace kvfp8 {
+
+constexpr int kLD = 576;            // latent width (score dim)
+constexpr int kLV = 512;            // value dim
+constexpr int kLT = 32;             // tokens per tile
+constexpr int kLWaves = 4;
+constexpr int kLThreads = kLWaves * kWave;
+constexpr int kLHeadsPerBlock = 64;
+constexpr int kKtStride = kLD + 8;  // bf16 per staged token row (16 bytes of padding)
+constexpr int kVtStride = kLT + 4;  // bf16 per staged value row (8 bytes of padding)
+constexpr int kLPidWin = 1024;
+
+template <bool FP8>
+__global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs a) {
+  constexpr int ELT = FP8 ? 1 : 2;
+  constexpr int E = 16 / ELT;                  // elements per 16-byte chunk
+  constexpr int NI = kLD * ELT / 64;           // chunks per 64-byte slice of a row
+  constexpr int SUBCH = 16 * kLD * ELT / 16;   // chunks per 16-token sub-page block
+  constexpr int NCH = 2 * SUBCH;               // chunks per 32-token tile
+  constexpr int NLD = (NCH + kLThreads - 1) / kLThreads;
+
+  __shared__ __align__(16) uint16_t s_kt[kLT * kKtStride];
+  __shared__ __align__(16) uint16_t s_vt[kLV * kVtStride];
+  __shared__ int s_pid[kLPidWin];
+
+  // XCD-aware block decode: head groups of one (request, split) unit are 8 ids apart
+  const int b = blockIdx.x;
+  const int grp = b / (8 * a.n_hg), rem = b % (8 * a.n_hg);
+  const int hg = rem / 8;
+  const int unit = grp * 8 + rem % 8;
+  if (unit >= a.batch * a.num_splits) return;
+  const int r = unit / a.num_splits, split = unit % a.num_splits;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int q4 = lane >> 4, n = lane & 15;
+  const int S = a.page_size;
+  const int Hq = a.num_q_heads;
+  const int h0 = hg * kLHeadsPerBlock + wave * 16;     // this wave's first head
+  const bool active = h0 < Hq;                          // wave-uniform
+  const int hb0 = hg * kLHeadsPerBlock, hb1 = min(Hq, hb0 + kLHeadsPerBlock);
+
+  const int L = a.ctx_lens[r];
+  const bool aborted = a.flags != nullptr && a.flags[r] != 0u;
+  const bool bad_len = L <= 0 || L > a.max_ctx || L > a.pt_stride * S;
+  const int chunk = a.chunk_tiles * kLT;
+  const int c0 = split * chunk;
+  if (aborted || bad_len) {
+    if (a.num_splits == 1) {
+      for (int e = threadIdx.x; e < (hb1 - hb0) * kLV; e += kLThreads)
+        a.out[((int64_t)r * Hq + hb0) * kLV + e] = 0;
+    }
+    return;
+  }
+  if (c0 >= L) return;
+  const int c1 = min(L, c0 + chunk);
+
+  // q^T operand: lane (q4, n) holds head h0+n, dims 144*q4 + 8*kk .. +8 for kk = 0..17
+  u32x4_t qv[18];
+  if (active) {
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.q + ((int64_t)r * Hq + h0 + n) * kLD + 144 * q4);
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) qv[kk] = *reinterpret_cast<const u32x4_t*>(qp + 16 * kk);
+  }
+
+  const int32_t* pt = a.page_table + (int64_t)r * a.pt_stride;
+  const uint8_t* pool = reinterpret_cast<const uint8_t*>(a.pool);
+  const float c_log2 = a.qk_scale_log2;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4_t acc[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  bool bad = false;
+
+  // at most kLPidWin - 1 pages of tokens per window: a window starting mid-page still fits kLPidWin ids
+  const int win = ((kLPidWin - 1) * S / kLT) * kLT;
+  for (int w0 = c0; w0 < c1; w0 += win) {
+    const int w1 = min(c1, w0 + win);
+    const int e0 = w0 / S;
+    const int ne = (w1 - 1) / S - e0 + 1;
+    __syncthreads();
+    for (int i = threadIdx.x; i < ne; i += kLThreads) {
+      int p = pt[e0 + i];
+      if (p < 0 || p >= a.num_pages) {
+        bad = true;
+        p = -1;
+      }
+      s_pid[i] = p;
+    }
+    __syncthreads();
+    const int ntile = (w1 - w0 + kLT - 1) / kLT;
+    for (int t = 0; t < ntile; ++t) {
+      const int tb = w0 + t * kLT;
+      // ---- load this thread's chunks of the tile (chunk positions in storage order)
+      u32x4_t raw[NLD];
+      int tokc[NLD], cc[NLD];
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const int pa = threadIdx.x + kLThreads * j;
+        const int sub = pa / SUBCH, p = pa % SUBCH;
+        const int i = p & 3, qq = (p >> 2) & 3, rest = p >> 4;
+        const int kq = rest % NI, s = rest / NI;
+        tokc[j] = 16 * sub + 4 * s + i;
+        cc[j] = qq * NI + kq;
+        const int tok_sub = tb + 16 * sub;
+        int pid = -1;
+        if (pa < NCH && tok_sub < w1) pid = s_pid[min(tok_sub / S - e0, ne - 1)];
+        const bool ok = pid >= 0 && tb + tokc[j] < w1;
+        if (ok) {
+          const uint8_t* src = pool + ((int64_t)pid * S * kLD + (int64_t)(tok_sub % S) * kLD) * ELT + 16 * (int64_t)p;
+          raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
+        } else {
+          raw[j] = u32x4_t{0, 0, 0, 0};
+        }
+      }
+      __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const int pa = threadIdx.x + kLThreads * j;
+        if (pa >= NCH) continue;
+        const int tok = tokc[j], d0 = cc[j] * E;
+        uint32_t w[8];
+        if (FP8) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const u32x2_t h2 = e4m3x4_to_bf16x4(raw[j][k]);
+            w[2 * k] = h2[0];
+            w[2 * k + 1] = h2[1];
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) w[k] = raw[j][k];
+        }
+        u32x4_t* kt = reinterpret_cast<u32x4_t*>(&s_kt[tok * kKtStride + d0]);
+        kt[0] = u32x4_t{w[0], w[1], w[2], w[3]};
+        if (FP8) kt[1] = u32x4_t{w[4], w[5], w[6], w[7]};
+        if (d0 < kLV) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const uint32_t word = w[e >> 1];
+            s_vt[(d0 + e) * kVtStride + tok] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xFFFFu));
+          }
+        }
+      }
+      __syncthreads();
+      if (!active) continue;
+
+      // ---- S^T = C q^T for two 16-token blocks
+      f32x4_t sc[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        sc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const uint16_t* row = &s_kt[(16 * mb + n) * kKtStride + 144 * q4];
+#pragma unroll
+        for (int kk = 0; kk < 18; ++kk) {
+          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(row + 8 * kk);
+          sc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                           __builtin_bit_cast(bf16x8_t, qv[kk]), sc[mb], 0, 0, 0);
+        }
+      }
+      // ---- online softmax for head n over tokens 16mb + 4q4 + i
+      float x[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool valid = tb + 16 * mb + 4 * q4 + i < w1;
+          const float v = valid ? sc[mb][i] * c_log2 : -INFINITY;
+          x[4 * mb + i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(m_run - m_use);
+      float psum = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        x[k] = exp2f(x[k] - m_use);
+        psum += x[k];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      const u32x4_t pp = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                          pack_bf16x2(x[6], x[7])};
+      // ---- O^T += V^T P^T, 32 blocks of 16 value dims
+#pragma unroll
+      for (int db = 0; db < 32; ++db) {
+        const uint16_t* vrow = &s_vt[(16 * db + n) * kVtStride + 4 * q4];
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 16);
+        const u32x4_t vv = {lo[0], lo[1], hi[0], hi[1]};
+        acc[db] *= alpha;
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vv),
+                                                          __builtin_bit_cast(bf16x8_t, pp), acc[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- write this wave's heads (a page id outside the pool zeroes the request)
+  __syncthreads();
+  if (threadIdx.x == 0) s_pid[0] = 0;
+  __syncthreads();
+  if (bad) s_pid[0] = 1;
+  __syncthreads();
+  const bool any_bad = s_pid[0] != 0;
+  if (!active) return;
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+  const int h = h0 + n;
+  const int64_t row = (int64_t)r * Hq + h;
+  const float inv = l_run > 0.f ? a.v_scale / l_run : 0.f;
+  if (a.num_splits == 1) {
+#pragma unroll
+    for (int db = 0; db < 32; ++db) {
+      const float o0 = any_bad ? 0.f : acc[db][0] * inv, o1 = any_bad ? 0.f : acc[db][1] * inv;
+      const float o2 = any_bad ? 0.f : acc[db][2] * inv, o3 = any_bad ? 0.f : acc[db][3] * inv;
+      const u32x2_t v2 = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+      *reinterpret_cast<u32x2_t*>(&a.out[row * kLV + 16 * db + 4 * q4]) = v2;
+    }
+  } else {
+    const int64_t slot = row * a.num_splits + split;
+#pragma unroll
+    for (int db = 0; db < 32; ++db)
+      *reinterpret_cast<f32x4_t*>(&a.o_part[slot * kLV + 16 * db + 4 * q4]) = acc[db] * inv;
+    if (q4 == 0) a.lse_part[slot] = any_bad ? NAN : (l_run == 0.f ? -INFINITY : m_run + __log2f(l_run));
+  }
+}
+
+hipError_t launch_attn_latent(const LatentArgs& a, bool fp8, hipStream_t stream) {
+  const int units = a.batch * a.num_splits;
+  const int blocks = ((units + 7) / 8) * 8 * a.n_hg;
+  if (fp8)
+    hipLaunchKernelGGL(attn_latent_split_kernel<true>, dim3(blocks), dim3(kLThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_latent_split_kernel<false>, dim3(blocks), dim3(kLThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_splits == 1) return e;
+  MergeArgs m;
+  m.o_part = a.o_part;
+  m.lse_part = a.lse_part;
+  m.out = a.out;
+  m.ctx_lens = a.ctx_lens;
+  m.flags = a.flags;
+  m.num_q_heads = a.num_q_heads;
+  m.v_dim = kLV;
+  m.num_splits = a.num_splits;
+  m.chunk_tokens = a.chunk_tiles * kLT;
+  m.max_ctx = a.max_ctx;
+  m.pt_stride = a.pt_stride;
+  m.page_size = a.page_size;
+  return launch_merge(m, a.batch, stream);
+}
+
+}  // namespace kvfp8

@@ -68,9 +68,31 @@ struct TagArgs {
   int32_t num_pages, pt_stride, batch, page_size;
 };
 
+struct LatentArgs {
+  const uint16_t* q;          // bf16 [B][Hq][576]
+  const void* pool;           // K-layout pool, one head, 576 wide
+  const int32_t* page_table;
+  const int32_t* ctx_lens;
+  const uint32_t* flags;
+  float* o_part;              // [B][Hq][num_splits][512]
+  float* lse_part;            // [B][Hq][num_splits]
+  uint16_t* out;              // bf16 [B][Hq][512]
+  int32_t num_pages, page_size, num_q_heads, pt_stride;
+  int32_t chunk_tiles;        // 32-token tiles per split
+  int32_t num_splits, max_ctx, batch, n_hg;
+  float qk_scale_log2;        // sm_scale * scale * log2(e)
+  float v_scale;
+};
+
 constexpr int kAttnTileTokens = 64;
+constexpr int kLatentTileTokens = 32;
+constexpr int kLatentDim = 576;
+constexpr int kLatentVDim = 512;
+constexpr int kLatentHeadsPerBlock = 64;
 
 hipError_t launch_attn_gqa(const AttnArgs& a, bool fp8, int batch, hipStream_t stream);
+hipError_t launch_attn_latent(const LatentArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& m, int batch, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_tag_check(const TagArgs& a, hipStream_t stream);

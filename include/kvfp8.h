@@ -31,11 +31,18 @@
  *  - bf16 values travel as uint16_t bit patterns; e4m3 codes as uint8_t.
  *  - Pools and q/out/new-row buffers must be 16-byte aligned.
  *
- * Page pool layout (element = 1 byte e4m3 or 2 bytes bf16):
- *    K pool  [P][Hkv][S][D]    element (page, kv head, slot, d)
+ * Page pool layout (element = 1 byte e4m3 or 2 bytes bf16).  Every (page,
+ * head) block is contiguous.
  *    V pool  [P][Hkv][Dv][S]   element (page, kv head, d, slot): each
- *                              (page, head) block of V is stored transposed
- *    latent  [P][1][S][Dl]     the K-pool layout with one head, no V pool
+ *                              (page, head) block of V is stored transposed.
+ *    K pool  [P][Hkv][S/16][16 tokens x D]: each 16-token sub-page block is
+ *            kept as 16-byte chunks in a fixed order: token t = 4s + i of the
+ *            sub-page (s, i in 0..3) and chunk c of its row (c = q*NI + k,
+ *            NI = D*bytes/64, q in 0..3) sit at chunk position
+ *            ((s*NI + k)*4 + q)*4 + i.  (A wave reading one chunk of four
+ *            tokens from each of four pages then reads four contiguous
+ *            256-byte runs per instruction.)  D*bytes must be a multiple of 64.
+ *    latent  the K-pool layout with one head and D = Dl; no V pool.
  * Page table: int32 [B][pt_stride]; entry i of request r is the physical page
  * of its tokens [i*S, (i+1)*S).  Entries at or past ceil(L_r/S) are never read.
  * Context length L_r counts the token appended in the current step.
@@ -164,6 +171,30 @@ int paged_decode_attn_bf16(const kvfp8_pool_desc* desc, const uint16_t* q, int32
                            int32_t batch, int32_t max_ctx_len, const uint32_t* abort_flags,
                            float sm_scale, int32_t num_splits, void* workspace,
                            size_t workspace_bytes, uint16_t* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------- latent (MLA-style) cache  [Q]
+ * One cached vector c_t of width Dl = 576 per token, shared by every query
+ * head (the pool: K layout, num_kv_heads = 1, head_dim = 576, v_dim = 512,
+ * written by kv_append_* with v_pool = v_new = NULL).  For request r, head h:
+ *   s_t = sm_scale * <q_h, c^_t>,  o_h = sum_t softmax(s)_t c^_t[0:512],
+ * with c^ = dec(c) * scale for the FP8 cache (one per-tensor scale) and
+ * c^ = c for BF16; fp32 result rounded to bf16.
+ *   q bf16 [B][Hq][576]; out bf16 [B][Hq][512]; Hq a multiple of 16.
+ *   Page ids, lengths, abort flags, splits and workspace behave as for
+ *   paged_decode_attn_fp8 (with 32-token tiles: num_splits at most
+ *   ceil(max_ctx_len/32); workspace from
+ *   paged_decode_attn_workspace_bytes(B, Hq, 512, splits)). */
+int32_t paged_decode_attn_latent_auto_splits(int32_t batch, int32_t num_q_heads, int32_t max_ctx_len);
+int paged_decode_attn_latent_fp8(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads,
+                                 const uint8_t* pool, const int32_t* page_table, int32_t pt_stride,
+                                 const int32_t* ctx_lens, int32_t batch, int32_t max_ctx_len,
+                                 const uint32_t* abort_flags, float scale, float sm_scale, int32_t num_splits,
+                                 void* workspace, size_t workspace_bytes, uint16_t* out, hipStream_t stream);
+int paged_decode_attn_latent_bf16(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads,
+                                  const uint16_t* pool, const int32_t* page_table, int32_t pt_stride,
+                                  const int32_t* ctx_lens, int32_t batch, int32_t max_ctx_len,
+                                  const uint32_t* abort_flags, float sm_scale, int32_t num_splits, void* workspace,
+                                  size_t workspace_bytes, uint16_t* out, hipStream_t stream);
 
 /* ---------------------------------------------------------------- test export
  * Read back tokens through the page table: k_out [N][Hkv][D], v_out

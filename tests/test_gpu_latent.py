@@ -1,0 +1,95 @@
+"""GPU parity of the latent (MLA-style) cache: 576-wide shared vector per token, values = first 512 dims.
+
+Bar as for GQA: every (request, head) row within max|o - ref| / max|ref| <= 1e-2 of the fp64 oracle;
+aborted or invalid requests give zero rows; the pool bytes written by the append equal the oracle's.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_paged_kv_append_amd as kv
+from kvsynth import workloads as wl
+from oracle import attention, codec
+from tests.gpu_util import ATTN_TOL, Case, attn_error, dev, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+def _latent_attend(c, flags=None, num_splits=0, max_ctx=None):
+    w = c.w
+    mc = c.max_ctx if max_ctx is None else max_ctx
+    out = c.out_tensor()
+    splits = num_splits or kv.paged_decode_attn_latent_auto_splits(w.batch, w.num_q_heads, mc)
+    ws = c.workspace(splits)
+    if c.kv_dtype == "fp8":
+        kv.paged_decode_attn_latent_fp8(c.desc, c.dq, c.dkp, c.dpt, c.dlens, mc, out, flags, scale=c.d_k_scale,
+                                        sm_scale=c.sm_scale, num_splits=num_splits, workspace=ws)
+    else:
+        kv.paged_decode_attn_latent_bf16(c.desc, c.dq, c.dkp, c.dpt, c.dlens, mc, out, flags,
+                                         sm_scale=c.sm_scale, num_splits=num_splits, workspace=ws)
+    torch.cuda.synchronize()
+    return host(out, np.uint16)
+
+
+def _check(c, got, flags=None):
+    ref = c.oracle_attend(flags=flags)
+    err = attn_error(got, ref)
+    note(f"  latent {c.kv_dtype} Hq={c.w.num_q_heads}: max row error {err:.3e}")
+    assert err <= ATTN_TOL
+    return err
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+@pytest.mark.parametrize("hq", [128, 16, 80])
+def test_latent_ragged(kv_dtype, hq):
+    w = wl.WORKLOADS["latent"].with_(batch=5, num_q_heads=hq, num_pages=120, ctx_lo=1, ctx_hi=700)
+    lens = np.array([1, 31, 33, 64, 700], dtype=np.int32)
+    note(f"latent ragged {kv_dtype} Hq={hq}")
+    c = Case(w, kv_dtype, lens=lens)
+    c.fill_device()
+    torch.cuda.synchronize()
+    et = np.uint8 if kv_dtype == "fp8" else np.uint16
+    assert np.array_equal(host(c.dkp, et), c.okp)
+    outs = []
+    for splits in (0, 1, 2, 5):
+        got = _latent_attend(c, num_splits=splits)
+        _check(c, got)
+        outs.append(codec.f64_from_bf16(got))
+    for o in outs[1:]:
+        assert np.max(attention.row_rel_error(o, outs[0])) <= 2.0 ** -7
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_latent_page16_and_abort(kv_dtype):
+    w = wl.WORKLOADS["latent"].with_(batch=4, num_q_heads=64, page_size=16, num_pages=200, ctx_lo=100, ctx_hi=800)
+    note(f"latent page16/abort {kv_dtype}")
+    c = Case(w, kv_dtype)
+    c.fill_device()
+    base = _latent_attend(c)
+    _check(c, base)
+    fl = np.array([0, 2, 0, 1], dtype=np.uint32)
+    got = _latent_attend(c, flags=dev(fl), num_splits=3)
+    assert not got[1].any() and not got[3].any()
+    _check(c, got, flags=fl)
+    # a bad page id with the tracker off zeroes that request only
+    pt = c.pt.copy()
+    pt[2, 1] = w.num_pages + 3
+    c.dpt = dev(pt)
+    got = _latent_attend(c, num_splits=2)
+    assert not got[2].any() and got[0].any()
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_latent_full_size_sampled(kv_dtype):
+    """64 requests x 4096 tokens, 128 heads, page 64, 8192-page pool, in the library's default split."""
+    w = wl.WORKLOADS["latent"]
+    note(f"latent full size {kv_dtype}")
+    c = Case(w, kv_dtype, oracle_fill=False)
+    assert c.d_k_scale == float(c.o_k_scale)
+    c.fill_device()
+    got = _latent_attend(c)
+    for r in (0, 31, 63):
+        ref = c.oracle_request(r)
+        err = float(np.max(attention.row_rel_error(codec.f64_from_bf16(got[r]), ref)))
+        note(f"  request {r}: row error {err:.3e}")
+        assert err <= ATTN_TOL
