@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8.0 TB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix peak
 METRIC = "decode-attn KV-read GB/s (% of HBM peak) + steps/s, FP8 vs BF16 KV cache"
 
 
@@ -45,6 +46,7 @@ def parse():
     p.add_argument("--splits", type=int, default=0, help="0 = library choice")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bf16", action="store_true")
+    p.add_argument("--no-extra", action="store_true", help="skip the other workloads (GQA batch, long, latent)")
     p.add_argument("--cpu-sample", type=int, default=8, help="requests in the CPU oracle sample")
     p.add_argument("--fp8-only-steps", action="store_true", help="time only the FP8 step (profiling runs)")
     p.add_argument("--graph", action="store_true",
@@ -59,31 +61,35 @@ class DeviceCache:
 
     def __init__(self, w, kv_dtype, host, torch, kv):
         self.w, self.kv_dtype, self.torch, self.kv = w, kv_dtype, torch, kv
-        dev = host["dev"]
-        elt = 1 if kv_dtype == "fp8" else 2
         nk = w.num_pages * w.num_kv_heads * w.page_size * w.head_dim
+        nv = w.num_pages * w.num_kv_heads * w.page_size * w.v_dim
         tdt = torch.uint8 if kv_dtype == "fp8" else torch.int16
         # pool contents before the fill do not matter for timing: zero them on the device
         self.kp = torch.zeros(nk, dtype=tdt, device="cuda")
-        self.vp = torch.zeros(nk, dtype=tdt, device="cuda")
+        self.vp = None if w.latent else torch.zeros(nv, dtype=tdt, device="cuda")
         self.desc = kv.pool_desc(w.num_pages, w.page_size, w.num_kv_heads, w.head_dim, w.v_dim)
         self.pt, self.lens, self.q = host["dpt"], host["dlens"], host["dq"]
         self.tags, self.exp = host["dtags"], host["dexp"]
         self.max_ctx = host["max_ctx"]
+        dv = None if w.latent else host["dv"]
         if kv_dtype == "fp8":
-            self.k_scale = kv.calibrate_scale(host["dk"])
-            self.v_scale = kv.calibrate_scale(host["dv"])
-            kv.kv_append_fp8(self.desc, self.kp, self.vp, host["dk"], host["dv"], host["dreq"], host["dpos"],
+            self.k_scale = kv.calibrate_scale(host["dk_calib"])
+            self.v_scale = self.k_scale if w.latent else kv.calibrate_scale(dv)
+            kv.kv_append_fp8(self.desc, self.kp, self.vp, host["dk"], dv, host["dreq"], host["dpos"],
                              self.pt, k_scale=self.k_scale, v_scale=self.v_scale)
         else:
             self.k_scale = self.v_scale = 1.0
-            kv.kv_append_bf16(self.desc, self.kp, self.vp, host["dk"], host["dv"], host["dreq"], host["dpos"],
-                              self.pt)
+            kv.kv_append_bf16(self.desc, self.kp, self.vp, host["dk"], dv, host["dreq"], host["dpos"], self.pt)
         self.k_new, self.v_new = host["dk_new"], host["dv_new"]
         self.s_req, self.s_pos = host["ds_req"], host["ds_pos"]
         self.out = torch.empty((w.batch, w.num_q_heads, w.v_dim), dtype=torch.int16, device="cuda")
         self.flags = torch.zeros(w.batch, dtype=torch.int32, device="cuda")
-        self.splits = host["splits"] or kv.paged_decode_attn_auto_splits(w.batch, w.num_kv_heads, self.max_ctx)
+        if host["splits"]:
+            self.splits = host["splits"]
+        elif w.latent:
+            self.splits = kv.paged_decode_attn_latent_auto_splits(w.batch, w.num_q_heads, self.max_ctx)
+        else:
+            self.splits = kv.paged_decode_attn_auto_splits(w.batch, w.num_kv_heads, self.max_ctx)
         n = kv.paged_decode_attn_workspace_bytes(w.batch, w.num_q_heads, w.v_dim, self.splits)
         self.ws = torch.empty(max(n // 4, 4), dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
@@ -102,13 +108,20 @@ class DeviceCache:
 
     def attend(self, tracker=True):
         f = self.flags if tracker else None
-        if self.kv_dtype == "fp8":
-            self.kv.paged_decode_attn_fp8(self.desc, self.q, self.kp, self.vp, self.pt, self.lens, self.max_ctx,
-                                          self.out, f, k_scale=self.k_scale, v_scale=self.v_scale,
-                                          num_splits=self.splits, workspace=self.ws)
+        kv, w = self.kv, self.w
+        if w.latent and self.kv_dtype == "fp8":
+            kv.paged_decode_attn_latent_fp8(self.desc, self.q, self.kp, self.pt, self.lens, self.max_ctx, self.out, f,
+                                            scale=self.k_scale, num_splits=self.splits, workspace=self.ws)
+        elif w.latent:
+            kv.paged_decode_attn_latent_bf16(self.desc, self.q, self.kp, self.pt, self.lens, self.max_ctx, self.out,
+                                             f, num_splits=self.splits, workspace=self.ws)
+        elif self.kv_dtype == "fp8":
+            kv.paged_decode_attn_fp8(self.desc, self.q, self.kp, self.vp, self.pt, self.lens, self.max_ctx,
+                                     self.out, f, k_scale=self.k_scale, v_scale=self.v_scale,
+                                     num_splits=self.splits, workspace=self.ws)
         else:
-            self.kv.paged_decode_attn_bf16(self.desc, self.q, self.kp, self.vp, self.pt, self.lens, self.max_ctx,
-                                           self.out, f, num_splits=self.splits, workspace=self.ws)
+            kv.paged_decode_attn_bf16(self.desc, self.q, self.kp, self.vp, self.pt, self.lens, self.max_ctx,
+                                      self.out, f, num_splits=self.splits, workspace=self.ws)
 
     def step(self, tracker=True):
         if tracker:
@@ -241,19 +254,6 @@ def main():
     import fp8_paged_kv_append_amd as kv
     from kvsynth import workloads as wl
 
-    w = wl.WORKLOADS[args.workload]
-    log(f"workload {w}")
-    t = time.perf_counter()
-    lens = wl.ctx_lens(w)
-    pt, _ = wl.page_table(w, lens)
-    tags = wl.page_tags(w)
-    stale = wl.stale_requests(w)
-    exp = wl.expected_tags(w, pt, lens, tags, stale)
-    k, v = wl.all_kv(w, lens)
-    req, pos = wl.token_index(lens)
-    q = wl.queries(w)
-    log(f"generated inputs in {time.perf_counter() - t:.1f} s")
-
     def dev(a):
         a = np.ascontiguousarray(a)
         if a.dtype == np.uint16:
@@ -262,38 +262,91 @@ def main():
             a = a.view(np.int32)
         return torch.from_numpy(a).cuda()
 
-    last = np.cumsum(lens.astype(np.int64)) - 1
-    host = dict(dev=dev, dpt=dev(pt), dlens=dev(lens), dq=dev(q), dtags=dev(tags), dexp=dev(exp),
-                dk=dev(k), dv=dev(v), dreq=dev(req), dpos=dev(pos), dk_new=dev(k[last]), dv_new=dev(v[last]),
-                ds_req=dev(np.arange(w.batch, dtype=np.int32)), ds_pos=dev((lens - 1).astype(np.int32)),
-                max_ctx=int(lens.max()), splits=args.splits)
-    del k, v
-    live = np.ones(w.batch, dtype=bool)
-    live[stale] = False
-    kv_elems = int(lens[live].astype(np.int64).sum()) * w.num_kv_heads * (w.head_dim + w.v_dim)
+    def prepare(w, splits):
+        """Generate one workload's inputs on the host and move them to the device."""
+        t = time.perf_counter()
+        lens = wl.ctx_lens(w)
+        pt, _ = wl.page_table(w, lens)
+        tags = wl.page_tags(w)
+        stale = wl.stale_requests(w)
+        exp = wl.expected_tags(w, pt, lens, tags, stale)
+        k, v = wl.all_kv(w, lens)
+        req, pos = wl.token_index(lens)
+        q = wl.queries(w)
+        last = np.cumsum(lens.astype(np.int64)) - 1
+        host = dict(dpt=dev(pt), dlens=dev(lens), dq=dev(q), dtags=dev(tags), dexp=dev(exp), dk=dev(k),
+                    dv=None if v is None else dev(v), dreq=dev(req), dpos=dev(pos), dk_new=dev(k[last]),
+                    dv_new=None if v is None else dev(v[last]), ds_req=dev(np.arange(w.batch, dtype=np.int32)),
+                    ds_pos=dev((lens - 1).astype(np.int32)), max_ctx=int(lens.max()), splits=splits)
+        host["dk_calib"] = host["dk"]
+        if w.outlier_frac > 0:               # the K scale comes from the outlier-free draw
+            kc, _ = wl.all_kv(w, lens, outliers=False)
+            host["dk_calib"] = dev(kc)
+            del kc
+        del k, v
+        live = np.ones(w.batch, dtype=bool)
+        live[stale] = False
+        row = w.head_dim if w.latent else w.num_kv_heads * (w.head_dim + w.v_dim)
+        elems = int(lens[live].astype(np.int64).sum()) * row
+        flops = int(lens[live].astype(np.int64).sum()) * w.num_q_heads * (w.head_dim + w.v_dim) * 2
+        log(f"{w.name}: inputs ready in {time.perf_counter() - t:.1f} s")
+        return host, stale, elems, flops
 
-    results = {}
-    for kvd in (["fp8"] if (args.no_bf16 or args.fp8_only_steps) else ["fp8", "bf16"]):
+    def measure(w, kvd, host, stale, elems, steps, warmup, full=True):
         t = time.perf_counter()
         c = DeviceCache(w, kvd, host, torch, kv)
-        log(f"{kvd}: cache filled in {time.perf_counter() - t:.1f} s, splits={c.splits}")
-        r = c.run(args.steps, args.warmup, tracker=True, graph=args.graph)
-        r["other"] = c.run(args.steps, args.warmup, tracker=True, graph=not args.graph)
-        r.update(c.breakdown(args.steps, tracker=True))
+        log(f"{w.name} {kvd}: cache filled in {time.perf_counter() - t:.1f} s, splits={c.splits}")
+        r = c.run(steps, warmup, tracker=True, graph=args.graph)
+        if full:
+            r["other"] = c.run(steps, warmup, tracker=True, graph=not args.graph)
+        r.update(c.breakdown(steps, tracker=True))
         flags = c.flags.cpu().numpy().view(np.uint32)
         assert np.flatnonzero(flags).tolist() == stale.tolist(), "abort flags differ from the planted stale set"
-        if not args.fp8_only_steps:
-            r["no_tracker"] = c.run(args.steps, args.warmup, tracker=False, graph=args.graph)
+        if full and not args.fp8_only_steps:
+            r["no_tracker"] = c.run(steps, warmup, tracker=False, graph=args.graph)
         elt = 1 if kvd == "fp8" else 2
-        r["kv_bytes"] = kv_elems * elt
+        r["kv_bytes"] = elems * elt
         r["gbs_step"] = r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
         r["gbs_attn"] = r["kv_bytes"] / (r["attn_ms_mean"] * 1e-3) / 1e9
         r["splits"] = c.splits
-        results[kvd] = r
-        log(f"{kvd}: {json.dumps({k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in r.items() if k_ not in ('no_tracker', 'other')})}")
-        log(f"{kvd}: {'eager' if args.graph else 'graph'} {r['other']}; tracker off {r.get('no_tracker')}")
+        log(f"{w.name} {kvd}: " + json.dumps({k_: (round(v_, 4) if isinstance(v_, float) else v_)
+                                              for k_, v_ in r.items() if k_ not in ("no_tracker", "other")}))
         del c
         torch.cuda.empty_cache()
+        return r
+
+    w = wl.WORKLOADS[args.workload]
+    log(f"workload {w}")
+    host, stale, kv_elems, flops = prepare(w, args.splits)
+    results = {}
+    for kvd in (["fp8"] if (args.no_bf16 or args.fp8_only_steps) else ["fp8", "bf16"]):
+        results[kvd] = measure(w, kvd, host, stale, kv_elems, args.steps, args.warmup)
+    del host
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not args.no_extra and not args.fp8_only_steps:
+        for name in ("gqa_batch", "long", "latent"):
+            we = wl.WORKLOADS[name]
+            he, st_e, el_e, fl_e = prepare(we, we.num_splits)
+            ex = {"workload": f"{we.batch} requests, context {we.ctx_lo}-{we.ctx_hi}, {we.num_q_heads} query / "
+                              f"{we.num_kv_heads} KV heads, score dim {we.head_dim}, value dim {we.v_dim}, "
+                              f"page {we.page_size}" + (", K outliers x20" if we.outlier_frac else "")}
+            for kvd in ("fp8", "bf16"):
+                r = measure(we, kvd, he, st_e, el_e, max(10, args.steps // 2), 3, full=False)
+                e = {"ms_per_step": round(r["ms_per_step"], 5), "step_gbs": round(r["gbs_step"], 1),
+                     "attn_ms": round(r["attn_ms_mean"], 5), "attn_gbs": round(r["gbs_attn"], 1),
+                     "attn_pct_hbm_peak": round(100 * r["gbs_attn"] / HBM_PEAK_GBS, 2), "splits": r["splits"]}
+                if we.latent:
+                    tf = fl_e / (r["attn_ms_mean"] * 1e-3) / 1e12
+                    e["attn_tflops"] = round(tf, 1)
+                    e["mfma_roofline"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                                          "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                          "flops_per_launch": fl_e}
+                ex[kvd] = e
+            extra[name] = ex
+            del he
+            torch.cuda.empty_cache()
 
     f8 = results["fp8"]
     line = {
@@ -340,6 +393,8 @@ def main():
         line["bf16_twin"] = {"value": round(b["gbs_step"], 1), "unit": "GB/s", "ms_per_step": round(b["ms_per_step"], 5),
                              "attn_gbs": round(b["gbs_attn"], 1), "attn_ms_mean": round(b["attn_ms_mean"], 5),
                              "fp8_speedup_step": round(b["ms_per_step"] / f8["ms_per_step"], 3)}
+    if extra:
+        line["other_workloads"] = extra
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.ones(n // 4, dtype=torch.int32, device="cuda")

@@ -11,15 +11,22 @@
 // Block = (request r, 64-head group hg, split c), 4 waves of 16 heads each.
 // The two head groups of one (r, c) are 8 block ids apart, so round-robin
 // dispatch puts them on the same XCD and the second read of a tile hits L2.
-// Per 32-token tile the block stages the tile once into LDS as bf16, in two
-// shapes: token rows (for S^T = C q^T) and a transposed [dv][token] copy (for
-// O^T += V^T P^T).  With lane = 16*q + n:
-//  * S^T: two 16-token blocks, A = C rows (lane (q, m) reads 8 dims of token
-//    m), B = q^T (lane (q, n) holds 8 dims of head n); the contraction slot
-//    (q, kk, j) is dim 144q + 8kk + j for both operands.
+// Each 32-token tile is copied once into LDS as stored (e4m3 bytes or bf16),
+// one padded row per token, into one of two buffers: the copy of tile t+1
+// (whose global loads were issued during tile t-1) and the math of tile t
+// share one barrier.  With lane = 16*q + n:
+//  * S^T = C q^T: two 16-token blocks, A = C rows (lane (q, m) reads 16
+//    bytes of token m, converted to bf16 in registers), B = q^T (lane (q, n)
+//    holds head n); the contraction slot (q, kk, j) is dim 144q + 8kk + j for
+//    both operands.
 //  * C layout: lane (q, n) holds head n's scores for tokens 16mb + 4q + i;
 //    the PV contraction slot (q, j) is token 16(j/4) + 4q + j%4, so the P it
-//    holds is already the B operand and V^T is read as two 4-token runs.
+//    holds is already the B operand.
+//  * O^T += V^T P^T: the A operand (8 tokens at one value dim per lane) is
+//    read straight from the token rows with the gfx950 LDS transpose reads:
+//    ds_read_b64_tr_b8 gives lane 8h+e byte e of the 8-byte blocks named by
+//    lanes h, h+2, .., h+14 of its 16-lane group, ds_read_b64_tr_b16 gives
+//    lane 4a+e element e of the blocks named by lanes a, a+4, a+8, a+12.
 //  * O^T accumulators: 32 d-blocks x 4 fp32 per lane, column = head n, so the
 //    online-softmax rescale is lane-local.
 #include "kvfp8_device.h"
@@ -33,21 +40,24 @@ constexpr int kLT = 32;             // tokens per tile
 constexpr int kLWaves = 4;
 constexpr int kLThreads = kLWaves * kWave;
 constexpr int kLHeadsPerBlock = 64;
-constexpr int kKtStride = kLD + 8;  // bf16 per staged token row (16 bytes of padding)
-constexpr int kVtStride = kLT + 4;  // bf16 per staged value row (8 bytes of padding)
 constexpr int kLPidWin = 1024;
+constexpr float kLazy = 8.f;        // log2-domain slack before the accumulators are rescaled
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+#define KVFP8_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 template <bool FP8>
 __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs a) {
   constexpr int ELT = FP8 ? 1 : 2;
-  constexpr int E = 16 / ELT;                  // elements per 16-byte chunk
   constexpr int NI = kLD * ELT / 64;           // chunks per 64-byte slice of a row
-  constexpr int SUBCH = 16 * kLD * ELT / 16;   // chunks per 16-token sub-page block
+  constexpr int SUBCH = 16 * kLD * ELT / 16;   // 16-byte chunks per 16-token sub-page block
   constexpr int NCH = 2 * SUBCH;               // chunks per 32-token tile
   constexpr int NLD = (NCH + kLThreads - 1) / kLThreads;
+  constexpr int RS = kLD * ELT + 16;           // LDS bytes per token row (16 bytes of padding)
+  constexpr int BUF = kLT * RS;                // LDS bytes per tile buffer
 
-  __shared__ __align__(16) uint16_t s_kt[kLT * kKtStride];
-  __shared__ __align__(16) uint16_t s_vt[kLV * kVtStride];
+  __shared__ __align__(16) uint8_t s_tile[2 * BUF];
   __shared__ int s_pid[kLPidWin];
 
   // XCD-aware block decode: head groups of one (request, split) unit are 8 ids apart
@@ -89,6 +99,18 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
     for (int kk = 0; kk < 18; ++kk) qv[kk] = *reinterpret_cast<const u32x4_t*>(qp + 16 * kk);
   }
 
+  // LDS byte offsets this lane reads, relative to a tile buffer
+  const int qk_off = n * RS + 144 * q4 * ELT;  // + 16*mb rows, + 16 bytes per k-step pair (fp8) or k-step (bf16)
+  int pv_off0, pv_off1 = 0;                   // PV source addresses for d-block 0 (+16*ELT bytes per d-block)
+  if (FP8) {
+    const int j = (lane & 15) >> 1, h = lane & 1;
+    pv_off0 = (16 * (j >> 2) + 4 * q4 + (j & 3)) * RS + 8 * h;
+  } else {
+    const int jj = (lane & 15) >> 2, aa = lane & 3;
+    pv_off0 = (4 * q4 + jj) * RS + 8 * aa;
+    pv_off1 = (16 + 4 * q4 + jj) * RS + 8 * aa;
+  }
+
   const int32_t* pt = a.page_table + (int64_t)r * a.pt_stride;
   const uint8_t* pool = reinterpret_cast<const uint8_t*>(a.pool);
   const float c_log2 = a.qk_scale_log2;
@@ -115,76 +137,85 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
     }
     __syncthreads();
     const int ntile = (w1 - w0 + kLT - 1) / kLT;
-    for (int t = 0; t < ntile; ++t) {
+
+    // This thread's chunks of one tile, in storage order; each goes to LDS row tok, bytes 16c.
+    u32x4_t raw[NLD];
+    int dst[NLD];
+    auto issue = [&](int t) {
       const int tb = w0 + t * kLT;
-      // ---- load this thread's chunks of the tile (chunk positions in storage order)
-      u32x4_t raw[NLD];
-      int tokc[NLD], cc[NLD];
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
         const int pa = threadIdx.x + kLThreads * j;
         const int sub = pa / SUBCH, p = pa % SUBCH;
         const int i = p & 3, qq = (p >> 2) & 3, rest = p >> 4;
         const int kq = rest % NI, s = rest / NI;
-        tokc[j] = 16 * sub + 4 * s + i;
-        cc[j] = qq * NI + kq;
+        const int tok = 16 * sub + 4 * s + i;
+        dst[j] = pa < NCH ? tok * RS + 16 * (qq * NI + kq) : -1;
         const int tok_sub = tb + 16 * sub;
         int pid = -1;
-        if (pa < NCH && tok_sub < w1) pid = s_pid[min(tok_sub / S - e0, ne - 1)];
-        const bool ok = pid >= 0 && tb + tokc[j] < w1;
-        if (ok) {
+        if (t < ntile && pa < NCH && tok_sub < w1) pid = s_pid[min(tok_sub / S - e0, ne - 1)];
+        if (pid >= 0 && tb + tok < w1) {
           const uint8_t* src = pool + ((int64_t)pid * S * kLD + (int64_t)(tok_sub % S) * kLD) * ELT + 16 * (int64_t)p;
           raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
         } else {
-          raw[j] = u32x4_t{0, 0, 0, 0};
+          raw[j] = u32x4_t{0, 0, 0, 0};     // absent token: zeros (masked below)
         }
       }
-      __syncthreads();  // the previous tile's LDS reads are done
+    };
+    auto stage = [&](int buf) {
 #pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        const int pa = threadIdx.x + kLThreads * j;
-        if (pa >= NCH) continue;
-        const int tok = tokc[j], d0 = cc[j] * E;
-        uint32_t w[8];
-        if (FP8) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const u32x2_t h2 = e4m3x4_to_bf16x4(raw[j][k]);
-            w[2 * k] = h2[0];
-            w[2 * k + 1] = h2[1];
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) w[k] = raw[j][k];
-        }
-        u32x4_t* kt = reinterpret_cast<u32x4_t*>(&s_kt[tok * kKtStride + d0]);
-        kt[0] = u32x4_t{w[0], w[1], w[2], w[3]};
-        if (FP8) kt[1] = u32x4_t{w[4], w[5], w[6], w[7]};
-        if (d0 < kLV) {
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const uint32_t word = w[e >> 1];
-            s_vt[(d0 + e) * kVtStride + tok] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xFFFFu));
-          }
-        }
-      }
-      __syncthreads();
-      if (!active) continue;
+      for (int j = 0; j < NLD; ++j)
+        if (dst[j] >= 0) *reinterpret_cast<u32x4_t*>(&s_tile[buf * BUF + dst[j]]) = raw[j];
+    };
 
-      // ---- S^T = C q^T for two 16-token blocks
+    issue(0);
+    __syncthreads();  // the previous window's last tile is no longer read
+    stage(0);
+    issue(1);
+    for (int t = 0; t < ntile; ++t) {
+      const int tb = w0 + t * kLT;
+      const int cur = t & 1;
+      __syncthreads();  // tile t is in LDS; buffer cur^1 is no longer read
+      if (t + 1 < ntile) {
+        stage(cur ^ 1);
+        issue(t + 2);
+      }
+      if (!active) continue;
+      const uint8_t* tile = &s_tile[cur * BUF];
+
+      // ---- S^T = C q^T for two 16-token blocks (even and odd k-steps in separate chains)
       f32x4_t sc[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        sc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const uint16_t* row = &s_kt[(16 * mb + n) * kKtStride + 144 * q4];
+        f32x4_t ch[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+        const uint8_t* row = tile + qk_off + 16 * mb * RS;
+        if (FP8) {
 #pragma unroll
-        for (int kk = 0; kk < 18; ++kk) {
-          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(row + 8 * kk);
-          sc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                           __builtin_bit_cast(bf16x8_t, qv[kk]), sc[mb], 0, 0, 0);
+          for (int k2 = 0; k2 < 9; ++k2) {
+            const u32x4_t c16 = *reinterpret_cast<const u32x4_t*>(row + 16 * k2);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const u32x2_t lo = e4m3x4_to_bf16x4(c16[2 * hh]), hi = e4m3x4_to_bf16x4(c16[2 * hh + 1]);
+              const u32x4_t av = {lo[0], lo[1], hi[0], hi[1]};
+              ch[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                               __builtin_bit_cast(bf16x8_t, qv[2 * k2 + hh]), ch[hh],
+                                                               0, 0, 0);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < 18; ++kk) {
+            const u32x4_t av = *reinterpret_cast<const u32x4_t*>(row + 16 * kk);
+            ch[kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                                 __builtin_bit_cast(bf16x8_t, qv[kk]), ch[kk & 1], 0,
+                                                                 0, 0);
+          }
         }
+        sc[mb] = ch[0] + ch[1];
       }
-      // ---- online softmax for head n over tokens 16mb + 4q4 + i
+      // ---- online softmax for head n over tokens 16mb + 4q4 + i.  The accumulators stay
+      // referenced to m_run until a tile's max exceeds it by more than kLazy (log2 units):
+      // p <= 2^kLazy meanwhile, exact up to rounding, and the 128-value rescale is rare.
       float x[8];
       float tmax = -INFINITY;
 #pragma unroll
@@ -198,27 +229,41 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
         }
       tmax = fmaxf(tmax, shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
+      const bool grow = tmax > m_run + kLazy;  // m_run = -inf: any finite tile max grows it
+      if (__any(grow)) {
+        const float m_new = grow ? tmax : m_run;
+        const float alpha = grow ? exp2f(m_run - m_new) : 1.f;  // m_run = -inf -> 0
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 32; ++db) acc[db] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
       float psum = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         x[k] = exp2f(x[k] - m_use);
         psum += x[k];
       }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+      l_run += psum;
       const u32x4_t pp = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
                           pack_bf16x2(x[6], x[7])};
-      // ---- O^T += V^T P^T, 32 blocks of 16 value dims
+      // ---- O^T += V^T P^T, 32 blocks of 16 value dims, A operand by LDS transpose reads
+      __attribute__((address_space(3))) uint8_t* lt =
+          (__attribute__((address_space(3))) uint8_t*)(tile);
 #pragma unroll
       for (int db = 0; db < 32; ++db) {
-        const uint16_t* vrow = &s_vt[(16 * db + n) * kVtStride + 4 * q4];
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 16);
-        const u32x4_t vv = {lo[0], lo[1], hi[0], hi[1]};
-        acc[db] *= alpha;
+        u32x4_t vv;
+        if (FP8) {
+          const i32x2_t t8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(KVFP8_LDS(i32x2_t, lt + pv_off0 + 16 * db));
+          const u32x2_t lo = e4m3x4_to_bf16x4((uint32_t)t8[0]), hi = e4m3x4_to_bf16x4((uint32_t)t8[1]);
+          vv = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+          const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(KVFP8_LDS(i16x4_t, lt + pv_off0 + 32 * db));
+          const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(KVFP8_LDS(i16x4_t, lt + pv_off1 + 32 * db));
+          const u32x2_t a0 = __builtin_bit_cast(u32x2_t, t0), a1 = __builtin_bit_cast(u32x2_t, t1);
+          vv = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+        }
         acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vv),
                                                           __builtin_bit_cast(bf16x8_t, pp), acc[db], 0, 0, 0);
       }
