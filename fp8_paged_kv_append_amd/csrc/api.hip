@@ -30,16 +30,18 @@ int check_pool(const kvfp8_pool_desc* d, bool need_v_dim_eq, int elt_bytes) {
 
 int32_t n_tiles_of(int32_t max_ctx) { return (int32_t)(((int64_t)max_ctx + kAttnTileTokens - 1) / kAttnTileTokens); }
 
-// Blocks (4 waves each) the launch aims for: the attention kernel holds two blocks per CU
-// (two waves per SIMD), so 512 blocks fill the 256 CUs once.
-constexpr int64_t kTargetBlocks = 512;
+// Blocks (4 waves each) the split heuristic aims for: one per CU.  Measured on MI355X, a block
+// over a whole 8192-token context is cheaper than splitting it further once every CU has a
+// block (each extra split costs its block set-up, partial writes and the merge launch); below
+// that, splits add the parallelism that short batches lack.
+constexpr int64_t kTargetBlocks = 256;
 
 int32_t auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_ctx) {
   const int64_t items = (int64_t)batch * num_kv_heads;
   const int32_t tiles = n_tiles_of(max_ctx);
   if (items <= 0 || tiles <= 0) return 1;
   int64_t s = (kTargetBlocks + items - 1) / items;
-  int64_t cap = tiles / 4;  // at least one tile per wave
+  int64_t cap = tiles / 8;  // at least two tiles per wave
   if (cap < 1) cap = 1;
   if (s > cap) s = cap;
   if (s < 1) s = 1;
