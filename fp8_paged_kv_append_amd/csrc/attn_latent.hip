@@ -8,27 +8,31 @@
 // cached vector serving as both key and value.  Unlike GQA this shape is bound
 // by the matrix units, not by HBM: 128 heads x (576 + 512) MACs per cached byte.
 //
-// Block = (request r, 64-head group hg, split c), 4 waves of 16 heads each.
-// The two head groups of one (r, c) are 8 block ids apart, so round-robin
-// dispatch puts them on the same XCD and the second read of a tile hits L2.
-// Each 32-token tile is copied once into LDS as stored (e4m3 bytes or bf16),
-// one padded row per token, into one of two buffers: the copy of tile t+1
-// (whose global loads were issued during tile t-1) and the math of tile t
+// Block = (request r, 64-head group hg, split c), 8 waves: wave (hb, kh) works
+// on heads 16hb..16hb+15 of the group, half kh of the contraction and half kh
+// of the value dims.  The head groups of one (r, c) are 8 block ids apart, so
+// round-robin dispatch puts them on the same XCD and later reads of a tile hit
+// L2.  Each 32-token tile is copied once into LDS as stored (e4m3 bytes or
+// bf16), one padded row per token, into one of two buffers: the copy of tile
+// t+1 (whose global loads were issued during tile t-1) and the math of tile t
 // share one barrier.  With lane = 16*q + n:
-//  * S^T = C q^T: two 16-token blocks, A = C rows (lane (q, m) reads 16
-//    bytes of token m, converted to bf16 in registers), B = q^T (lane (q, n)
-//    holds head n); the contraction slot (q, kk, j) is dim 144q + 8kk + j for
-//    both operands.
+//  * S^T = C q^T: two 16-token blocks; wave (hb, kh) contracts dims
+//    288kh + 72q + 8kk + j (kk = 0..8) with A = C rows (lane (q, m) reads 8
+//    elements of token m, e4m3 converted to bf16 in registers) and B = q^T
+//    (lane (q, n) holds head n).  The two partial sums of a pair meet in LDS;
+//    fp32 addition commutes, so both waves hold the same scores and the same
+//    softmax state, bit for bit.
 //  * C layout: lane (q, n) holds head n's scores for tokens 16mb + 4q + i;
 //    the PV contraction slot (q, j) is token 16(j/4) + 4q + j%4, so the P it
 //    holds is already the B operand.
-//  * O^T += V^T P^T: the A operand (8 tokens at one value dim per lane) is
-//    read straight from the token rows with the gfx950 LDS transpose reads:
-//    ds_read_b64_tr_b8 gives lane 8h+e byte e of the 8-byte blocks named by
-//    lanes h, h+2, .., h+14 of its 16-lane group, ds_read_b64_tr_b16 gives
-//    lane 4a+e element e of the blocks named by lanes a, a+4, a+8, a+12.
-//  * O^T accumulators: 32 d-blocks x 4 fp32 per lane, column = head n, so the
-//    online-softmax rescale is lane-local.
+//  * O^T += V^T P^T over value dims 256kh .. 256kh+255: the A operand (8 tokens
+//    at one value dim per lane) is read straight from the token rows with the
+//    gfx950 LDS transpose loads: ds_read_b64_tr_b8 gives lane 8h+e byte e of
+//    the 8-byte blocks named by lanes h, h+2, .., h+14 of its 16-lane group,
+//    ds_read_b64_tr_b16 gives lane 4a+e element e of the blocks named by
+//    lanes a, a+4, a+8, a+12.
+//  * 16 accumulator blocks per lane, column = head n: the online-softmax
+//    rescale is lane-local, and lazy (see below).
 #include "kvfp8_device.h"
 #include "kvfp8_internal.h"
 
@@ -37,7 +41,7 @@ namespace kvfp8 {
 constexpr int kLD = 576;            // latent width (score dim)
 constexpr int kLV = 512;            // value dim
 constexpr int kLT = 32;             // tokens per tile
-constexpr int kLWaves = 4;
+constexpr int kLWaves = 8;
 constexpr int kLThreads = kLWaves * kWave;
 constexpr int kLHeadsPerBlock = 64;
 constexpr int kLPidWin = 1024;
@@ -58,6 +62,7 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   constexpr int BUF = kLT * RS;                // LDS bytes per tile buffer
 
   __shared__ __align__(16) uint8_t s_tile[2 * BUF];
+  __shared__ __align__(16) f32x4_t s_part[kLWaves][2][kWave];  // partial scores of each wave
   __shared__ int s_pid[kLPidWin];
 
   // XCD-aware block decode: head groups of one (request, split) unit are 8 ids apart
@@ -69,11 +74,12 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   const int r = unit / a.num_splits, split = unit % a.num_splits;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int hb = wave >> 1, kh = wave & 1;
   const int q4 = lane >> 4, n = lane & 15;
   const int S = a.page_size;
   const int Hq = a.num_q_heads;
-  const int h0 = hg * kLHeadsPerBlock + wave * 16;     // this wave's first head
-  const bool active = h0 < Hq;                          // wave-uniform
+  const int h0 = hg * kLHeadsPerBlock + hb * 16;       // this wave's first head
+  const bool active = h0 < Hq;                          // wave-uniform, equal within a pair
   const int hb0 = hg * kLHeadsPerBlock, hb1 = min(Hq, hb0 + kLHeadsPerBlock);
 
   const int L = a.ctx_lens[r];
@@ -91,33 +97,34 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   if (c0 >= L) return;
   const int c1 = min(L, c0 + chunk);
 
-  // q^T operand: lane (q4, n) holds head h0+n, dims 144*q4 + 8*kk .. +8 for kk = 0..17
-  u32x4_t qv[18];
+  // q^T operand: lane (q4, n) holds head h0+n, dims 288*kh + 72*q4 + 8*kk .. +8 for kk = 0..8
+  const int dim0 = 288 * kh + 72 * q4;
+  u32x4_t qv[9];
   if (active) {
-    const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.q + ((int64_t)r * Hq + h0 + n) * kLD + 144 * q4);
+    const uint16_t* qp = a.q + ((int64_t)r * Hq + h0 + n) * kLD + dim0;
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) qv[kk] = *reinterpret_cast<const u32x4_t*>(qp + 16 * kk);
+    for (int kk = 0; kk < 9; ++kk) qv[kk] = *reinterpret_cast<const u32x4_t*>(qp + 8 * kk);
   }
 
   // LDS byte offsets this lane reads, relative to a tile buffer
-  const int qk_off = n * RS + 144 * q4 * ELT;  // + 16*mb rows, + 16 bytes per k-step pair (fp8) or k-step (bf16)
-  int pv_off0, pv_off1 = 0;                   // PV source addresses for d-block 0 (+16*ELT bytes per d-block)
+  const int qk_off = n * RS + dim0 * ELT;  // + 16*RS per token block, + 8*ELT bytes per k-step
+  int pv_off0, pv_off1 = 0;               // PV source addresses for this wave's first d-block
   if (FP8) {
     const int j = (lane & 15) >> 1, h = lane & 1;
-    pv_off0 = (16 * (j >> 2) + 4 * q4 + (j & 3)) * RS + 8 * h;
+    pv_off0 = (16 * (j >> 2) + 4 * q4 + (j & 3)) * RS + 8 * h + 256 * kh;
   } else {
     const int jj = (lane & 15) >> 2, aa = lane & 3;
-    pv_off0 = (4 * q4 + jj) * RS + 8 * aa;
-    pv_off1 = (16 + 4 * q4 + jj) * RS + 8 * aa;
+    pv_off0 = (4 * q4 + jj) * RS + 8 * aa + 512 * kh;
+    pv_off1 = (16 + 4 * q4 + jj) * RS + 8 * aa + 512 * kh;
   }
 
   const int32_t* pt = a.page_table + (int64_t)r * a.pt_stride;
   const uint8_t* pool = reinterpret_cast<const uint8_t*>(a.pool);
   const float c_log2 = a.qk_scale_log2;
   float m_run = -INFINITY, l_run = 0.f;
-  f32x4_t acc[32];
+  f32x4_t acc[16];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 16; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   bool bad = false;
 
   // at most kLPidWin - 1 pages of tokens per window: a window starting mid-page still fits kLPidWin ids
@@ -175,47 +182,49 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
     for (int t = 0; t < ntile; ++t) {
       const int tb = w0 + t * kLT;
       const int cur = t & 1;
-      __syncthreads();  // tile t is in LDS; buffer cur^1 is no longer read
+      __syncthreads();  // tile t is in LDS; buffer cur^1 and the score exchange are free
       if (t + 1 < ntile) {
         stage(cur ^ 1);
         issue(t + 2);
       }
-      if (!active) continue;
       const uint8_t* tile = &s_tile[cur * BUF];
 
-      // ---- S^T = C q^T for two 16-token blocks (even and odd k-steps in separate chains)
+      // ---- partial S^T = C q^T over this wave's half of the dims, two 16-token blocks
       f32x4_t sc[2];
+      if (active) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        f32x4_t ch[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-        const uint8_t* row = tile + qk_off + 16 * mb * RS;
-        if (FP8) {
+        for (int mb = 0; mb < 2; ++mb) {
+          f32x4_t ch[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+          const uint8_t* row = tile + qk_off + 16 * mb * RS;
 #pragma unroll
-          for (int k2 = 0; k2 < 9; ++k2) {
-            const u32x4_t c16 = *reinterpret_cast<const u32x4_t*>(row + 16 * k2);
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const u32x2_t lo = e4m3x4_to_bf16x4(c16[2 * hh]), hi = e4m3x4_to_bf16x4(c16[2 * hh + 1]);
-              const u32x4_t av = {lo[0], lo[1], hi[0], hi[1]};
-              ch[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                               __builtin_bit_cast(bf16x8_t, qv[2 * k2 + hh]), ch[hh],
-                                                               0, 0, 0);
+          for (int kk = 0; kk < 9; ++kk) {
+            u32x4_t av;
+            if (FP8) {
+              const u32x2_t c8 = *reinterpret_cast<const u32x2_t*>(row + 8 * kk);
+              const u32x2_t lo = e4m3x4_to_bf16x4(c8[0]), hi = e4m3x4_to_bf16x4(c8[1]);
+              av = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+            } else {
+              av = *reinterpret_cast<const u32x4_t*>(row + 16 * kk);
             }
-          }
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < 18; ++kk) {
-            const u32x4_t av = *reinterpret_cast<const u32x4_t*>(row + 16 * kk);
             ch[kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
                                                                  __builtin_bit_cast(bf16x8_t, qv[kk]), ch[kk & 1], 0,
                                                                  0, 0);
           }
+          sc[mb] = ch[0] + ch[1];
+          s_part[wave][mb][lane] = sc[mb];
         }
-        sc[mb] = ch[0] + ch[1];
+      }
+      __syncthreads();  // both halves of every pair's scores are in LDS
+      if (!active) continue;
+      {
+        const f32x4_t o0 = s_part[wave ^ 1][0][lane], o1 = s_part[wave ^ 1][1][lane];
+        // same operands in the same order in both waves of the pair
+        sc[0] = kh == 0 ? sc[0] + o0 : o0 + sc[0];
+        sc[1] = kh == 0 ? sc[1] + o1 : o1 + sc[1];
       }
       // ---- online softmax for head n over tokens 16mb + 4q4 + i.  The accumulators stay
       // referenced to m_run until a tile's max exceeds it by more than kLazy (log2 units):
-      // p <= 2^kLazy meanwhile, exact up to rounding, and the 128-value rescale is rare.
+      // p <= 2^kLazy meanwhile, exact up to rounding, and the rescale is rare.
       float x[8];
       float tmax = -INFINITY;
 #pragma unroll
@@ -235,7 +244,7 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
         const float alpha = grow ? exp2f(m_run - m_new) : 1.f;  // m_run = -inf -> 0
         l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < 32; ++db) acc[db] *= alpha;
+        for (int db = 0; db < 16; ++db) acc[db] *= alpha;
         m_run = m_new;
       }
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
@@ -248,11 +257,10 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
       l_run += psum;
       const u32x4_t pp = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
                           pack_bf16x2(x[6], x[7])};
-      // ---- O^T += V^T P^T, 32 blocks of 16 value dims, A operand by LDS transpose reads
-      __attribute__((address_space(3))) uint8_t* lt =
-          (__attribute__((address_space(3))) uint8_t*)(tile);
+      // ---- O^T += V^T P^T, 16 blocks of 16 value dims, A operand by LDS transpose reads
+      __attribute__((address_space(3))) uint8_t* lt = (__attribute__((address_space(3))) uint8_t*)(tile);
 #pragma unroll
-      for (int db = 0; db < 32; ++db) {
+      for (int db = 0; db < 16; ++db) {
         u32x4_t vv;
         if (FP8) {
           const i32x2_t t8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(KVFP8_LDS(i32x2_t, lt + pv_off0 + 16 * db));
@@ -270,7 +278,7 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
     }
   }
 
-  // ---- write this wave's heads (a page id outside the pool zeroes the request)
+  // ---- write this wave's heads and value half (a page id outside the pool zeroes the request)
   __syncthreads();
   if (threadIdx.x == 0) s_pid[0] = 0;
   __syncthreads();
@@ -283,20 +291,21 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   const int h = h0 + n;
   const int64_t row = (int64_t)r * Hq + h;
   const float inv = l_run > 0.f ? a.v_scale / l_run : 0.f;
+  const int dv0 = 256 * kh + 4 * q4;
   if (a.num_splits == 1) {
 #pragma unroll
-    for (int db = 0; db < 32; ++db) {
+    for (int db = 0; db < 16; ++db) {
       const float o0 = any_bad ? 0.f : acc[db][0] * inv, o1 = any_bad ? 0.f : acc[db][1] * inv;
       const float o2 = any_bad ? 0.f : acc[db][2] * inv, o3 = any_bad ? 0.f : acc[db][3] * inv;
       const u32x2_t v2 = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-      *reinterpret_cast<u32x2_t*>(&a.out[row * kLV + 16 * db + 4 * q4]) = v2;
+      *reinterpret_cast<u32x2_t*>(&a.out[row * kLV + dv0 + 16 * db]) = v2;
     }
   } else {
     const int64_t slot = row * a.num_splits + split;
 #pragma unroll
-    for (int db = 0; db < 32; ++db)
-      *reinterpret_cast<f32x4_t*>(&a.o_part[slot * kLV + 16 * db + 4 * q4]) = acc[db] * inv;
-    if (q4 == 0) a.lse_part[slot] = any_bad ? NAN : (l_run == 0.f ? -INFINITY : m_run + __log2f(l_run));
+    for (int db = 0; db < 16; ++db)
+      *reinterpret_cast<f32x4_t*>(&a.o_part[slot * kLV + dv0 + 16 * db]) = acc[db] * inv;
+    if (q4 == 0 && kh == 0) a.lse_part[slot] = any_bad ? NAN : (l_run == 0.f ? -INFINITY : m_run + __log2f(l_run));
   }
 }
 
