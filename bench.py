@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads (GQA batch, long, latent)")
     p.add_argument("--cpu-sample", type=int, default=8, help="requests in the CPU oracle sample")
     p.add_argument("--fp8-only-steps", action="store_true", help="time only the FP8 step (profiling runs)")
+    p.add_argument("--unfused", action="store_true",
+                   help="tag check and append as two launches instead of kv_tag_check_append_*")
     p.add_argument("--graph", action="store_true",
                    help="time replays of a captured HIP graph of one step (default: eager launches)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -59,8 +61,9 @@ def parse():
 class DeviceCache:
     """One workload's cache on the device (FP8 or BF16), filled through the library's append."""
 
-    def __init__(self, w, kv_dtype, host, torch, kv):
+    def __init__(self, w, kv_dtype, host, torch, kv, fused=True):
         self.w, self.kv_dtype, self.torch, self.kv = w, kv_dtype, torch, kv
+        self.fused = fused
         nk = w.num_pages * w.num_kv_heads * w.page_size * w.head_dim
         nv = w.num_pages * w.num_kv_heads * w.page_size * w.v_dim
         tdt = torch.uint8 if kv_dtype == "fp8" else torch.int16
@@ -97,6 +100,16 @@ class DeviceCache:
     def check(self):
         self.kv.kv_tag_check(self.tags, self.pt, self.exp, self.lens, self.w.page_size, self.flags)
 
+    def check_append(self):
+        """The tag check and the write of one token per request as one launch."""
+        if self.kv_dtype == "fp8":
+            self.kv.kv_tag_check_append_fp8(self.desc, self.kp, self.vp, self.k_new, self.v_new, self.pt, self.lens,
+                                            self.tags, self.exp, self.flags, k_scale=self.k_scale,
+                                            v_scale=self.v_scale)
+        else:
+            self.kv.kv_tag_check_append_bf16(self.desc, self.kp, self.vp, self.k_new, self.v_new, self.pt,
+                                             self.lens, self.tags, self.exp, self.flags)
+
     def append(self, tracker=True):
         f = self.flags if tracker else None
         if self.kv_dtype == "fp8":
@@ -124,9 +137,12 @@ class DeviceCache:
                                       self.out, f, num_splits=self.splits, workspace=self.ws)
 
     def step(self, tracker=True):
-        if tracker:
-            self.check()
-        self.append(tracker)
+        if tracker and self.fused:
+            self.check_append()
+        else:
+            if tracker:
+                self.check()
+            self.append(tracker)
         self.attend(tracker)
 
     def run(self, steps, warmup, tracker=True, graph=False):
@@ -171,10 +187,13 @@ class DeviceCache:
         torch.cuda.synchronize()
         for e in evs:
             e[0].record()
-            if tracker:
+            if tracker and self.fused:
+                self.check_append()
+            elif tracker:
                 self.check()
             e[1].record()
-            self.append(tracker)
+            if not (tracker and self.fused):
+                self.append(tracker)
             e[2].record()
             self.attend(tracker)
             e[3].record()
@@ -294,7 +313,7 @@ def main():
 
     def measure(w, kvd, host, stale, elems, steps, warmup, full=True):
         t = time.perf_counter()
-        c = DeviceCache(w, kvd, host, torch, kv)
+        c = DeviceCache(w, kvd, host, torch, kv, fused=not args.unfused)
         log(f"{w.name} {kvd}: cache filled in {time.perf_counter() - t:.1f} s, splits={c.splits}")
         r = c.run(steps, warmup, tracker=True, graph=args.graph)
         if full:
@@ -370,15 +389,18 @@ def main():
                                f"{w.num_pages}-page pool, FP8 e4m3 cache, 1% stale tags",
                    "batch": w.batch, "ctx": int(w.ctx_hi), "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
-                   "splits": f8["splits"], "step": "tag check + append(1 token/request) + attention + merge"},
+                   "splits": f8["splits"],
+                   "step": ("tag check + append(1 token/request)" if args.unfused else
+                            "fused tag check + append(1 token/request)") + " + attention (+ merge when split)"},
         "roofline": {"bound": "hbm", "achieved": round(f8["gbs_attn"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(f8["gbs_attn"] / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name, f8["splits"]),
                      "algorithmic_bytes": f8["kv_bytes"],
                      "kernel": "paged_decode_attn_fp8 (split kernel, plus the merge kernel when splits > 1)",
                      "attn_ms_mean": round(f8["attn_ms_mean"], 5), "attn_ms_p95": round(f8["attn_ms_p95"], 5)},
-        "step_breakdown_ms": {"tag_check": round(f8["check_ms"], 5), "append": round(f8["append_ms"], 5),
-                              "attention": round(f8["attn_ms"], 5), "step_p95": round(f8["step_ms_p95"], 5),
+        "step_breakdown_ms": ({"tag_check": round(f8["check_ms"], 5), "append": round(f8["append_ms"], 5)}
+                              if args.unfused else {"tag_check_append": round(f8["check_ms"], 5)}) |
+                             {"attention": round(f8["attn_ms"], 5), "step_p95": round(f8["step_ms_p95"], 5),
                               "note": "events around each launch of eager steps"},
         "timing": ("steps replayed from a captured HIP graph of one step" if args.graph else
                    "eager back-to-back steps") + ", between two events on the launch stream",

@@ -20,7 +20,8 @@ from . import _lib
 from ._lib import FLAG_BAD_PAGE, FLAG_TAG_MISMATCH, PoolDesc  # noqa: F401
 
 __all__ = ["KvFp8Error", "PoolDesc", "pool_desc", "kv_absmax_bf16", "kv_scale_from_absmax", "calibrate_scale",
-           "kv_append_fp8", "kv_append_bf16", "kv_tag_check", "paged_decode_attn_workspace_bytes",
+           "kv_append_fp8", "kv_append_bf16", "kv_tag_check", "kv_tag_check_append_fp8",
+           "kv_tag_check_append_bf16", "paged_decode_attn_workspace_bytes",
            "paged_decode_attn_auto_splits", "paged_decode_attn_fp8", "paged_decode_attn_bf16",
            "paged_decode_attn_latent_auto_splits", "paged_decode_attn_latent_fp8",
            "paged_decode_attn_latent_bf16", "kv_gather_fp8", "kv_gather_bf16", "decode_step", "lib"]
@@ -122,6 +123,29 @@ def kv_tag_check(page_tags, page_table, expected_tags, ctx_lens, page_size: int,
         _ptr(page_tags, _U32, "page_tags"), page_tags.numel(), _ptr(page_table, _I32, "page_table"),
         _ptr(expected_tags, _U32, "expected_tags"), stride, _ptr(ctx_lens, _I32, "ctx_lens"), B, int(page_size),
         _ptr(abort_flags, _U32, "abort_flags"), _stream(stream)), "kv_tag_check")
+
+
+def kv_tag_check_append_fp8(desc: PoolDesc, k_pool, v_pool, k_new, v_new, page_table, ctx_lens, page_tags,
+                            expected_tags, abort_flags, *, k_scale: float, v_scale: float = 1.0, stream=None):
+    """One launch: tag check, then each clean request's token r written at position ctx_lens[r] - 1."""
+    B, stride = page_table.shape
+    _check(lib().kv_tag_check_append_fp8(
+        desc, _ptr(k_pool, _U8, "k_pool"), _ptr(v_pool, _U8, "v_pool", True), _ptr(k_new, _BF16, "k_new"),
+        _ptr(v_new, _BF16, "v_new", True), _ptr(page_table, _I32, "page_table"), stride,
+        _ptr(ctx_lens, _I32, "ctx_lens"), B, _ptr(page_tags, _U32, "page_tags"),
+        _ptr(expected_tags, _U32, "expected_tags"), _ptr(abort_flags, _U32, "abort_flags"), float(k_scale),
+        float(v_scale), _stream(stream)), "kv_tag_check_append_fp8")
+
+
+def kv_tag_check_append_bf16(desc: PoolDesc, k_pool, v_pool, k_new, v_new, page_table, ctx_lens, page_tags,
+                             expected_tags, abort_flags, *, stream=None):
+    B, stride = page_table.shape
+    _check(lib().kv_tag_check_append_bf16(
+        desc, _ptr(k_pool, _BF16, "k_pool"), _ptr(v_pool, _BF16, "v_pool", True), _ptr(k_new, _BF16, "k_new"),
+        _ptr(v_new, _BF16, "v_new", True), _ptr(page_table, _I32, "page_table"), stride,
+        _ptr(ctx_lens, _I32, "ctx_lens"), B, _ptr(page_tags, _U32, "page_tags"),
+        _ptr(expected_tags, _U32, "expected_tags"), _ptr(abort_flags, _U32, "abort_flags"), _stream(stream)),
+        "kv_tag_check_append_bf16")
 
 
 # ----------------------------------------------------------------------------- attention
@@ -232,21 +256,35 @@ def decode_step(desc: PoolDesc, kv_dtype: str, k_pool, v_pool, page_table, ctx_l
     With page_tags/expected_tags given, the batched check writes abort_flags
     first and both later launches honour them; with page_tags None (the
     no-op tracker) no check runs and abort_flags is passed through (None =
-    no flags).
+    no flags).  tok_req/tok_pos None means one new token per request, at
+    position ctx_lens[r] - 1: the check and the write then run as one launch
+    (kv_tag_check_append_*), which needs the tracker.
     """
-    if page_tags is not None:
-        if expected_tags is None or abort_flags is None:
-            raise ValueError("the tag check needs expected_tags and an abort_flags buffer")
+    if kv_dtype not in ("fp8", "bf16"):
+        raise ValueError(f"kv_dtype {kv_dtype!r}")
+    if page_tags is not None and (expected_tags is None or abort_flags is None):
+        raise ValueError("the tag check needs expected_tags and an abort_flags buffer")
+    fused = tok_req is None and tok_pos is None
+    if fused and page_tags is None:
+        raise ValueError("tok_req/tok_pos None (fused check + write) needs page_tags")
+    if fused and kv_dtype == "fp8":
+        kv_tag_check_append_fp8(desc, k_pool, v_pool, k_new, v_new, page_table, ctx_lens, page_tags, expected_tags,
+                                abort_flags, k_scale=k_scale, v_scale=v_scale, stream=stream)
+    elif fused:
+        kv_tag_check_append_bf16(desc, k_pool, v_pool, k_new, v_new, page_table, ctx_lens, page_tags, expected_tags,
+                                 abort_flags, stream=stream)
+    elif page_tags is not None:
         kv_tag_check(page_tags, page_table, expected_tags, ctx_lens, desc.page_size, abort_flags, stream=stream)
     if kv_dtype == "fp8":
-        kv_append_fp8(desc, k_pool, v_pool, k_new, v_new, tok_req, tok_pos, page_table, abort_flags,
-                      k_scale=k_scale, v_scale=v_scale, stream=stream)
+        if not fused:
+            kv_append_fp8(desc, k_pool, v_pool, k_new, v_new, tok_req, tok_pos, page_table, abort_flags,
+                          k_scale=k_scale, v_scale=v_scale, stream=stream)
         paged_decode_attn_fp8(desc, q, k_pool, v_pool, page_table, ctx_lens, max_ctx_len, out, abort_flags,
                               k_scale=k_scale, v_scale=v_scale, sm_scale=sm_scale, num_splits=num_splits,
                               workspace=workspace, stream=stream)
-    elif kv_dtype == "bf16":
-        kv_append_bf16(desc, k_pool, v_pool, k_new, v_new, tok_req, tok_pos, page_table, abort_flags, stream=stream)
+    else:
+        if not fused:
+            kv_append_bf16(desc, k_pool, v_pool, k_new, v_new, tok_req, tok_pos, page_table, abort_flags,
+                           stream=stream)
         paged_decode_attn_bf16(desc, q, k_pool, v_pool, page_table, ctx_lens, max_ctx_len, out, abort_flags,
                                sm_scale=sm_scale, num_splits=num_splits, workspace=workspace, stream=stream)
-    else:
-        raise ValueError(f"kv_dtype {kv_dtype!r}")

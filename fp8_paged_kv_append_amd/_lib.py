@@ -35,6 +35,8 @@ PROTOTYPES = {
     "kv_append_fp8": (C.c_int, [_desc, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _p, _f32, _f32, _p]),
     "kv_append_bf16": (C.c_int, [_desc, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _p, _p]),
     "kv_tag_check": (C.c_int, [_p, _i32, _p, _p, _i32, _p, _i32, _i32, _p, _p]),
+    "kv_tag_check_append_fp8": (C.c_int, [_desc, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _p, _f32, _f32, _p]),
+    "kv_tag_check_append_bf16": (C.c_int, [_desc, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _p, _p]),
     "paged_decode_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "paged_decode_attn_auto_splits": (_i32, [_i32, _i32, _i32]),
     "paged_decode_attn_fp8": (C.c_int, [_desc, _p, _i32, _p, _p, _p, _i32, _p, _i32, _i32, _p, _f32, _f32,

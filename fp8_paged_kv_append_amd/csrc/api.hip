@@ -167,6 +167,56 @@ int attn_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_he
   return launch_attn_gqa(a, fp8, batch, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
 }
 
+int check_append_common(const kvfp8_pool_desc* desc, void* k_pool, void* v_pool, const uint16_t* k_new,
+                        const uint16_t* v_new, const int32_t* page_table, int32_t pt_stride,
+                        const int32_t* ctx_lens, int32_t batch, const uint32_t* page_tags,
+                        const uint32_t* expected_tags, uint32_t* abort_flags, bool fp8, float k_scale,
+                        float v_scale, hipStream_t stream) {
+  int st = check_pool(desc, false, fp8 ? 1 : 2);
+  if (st) return st;
+  if (batch < 0 || pt_stride < 1) return KVFP8_ERR_SHAPE;
+  if (batch == 0) return KVFP8_OK;
+  if (!k_pool || !k_new || !page_table || !ctx_lens || !page_tags || !expected_tags || !abort_flags)
+    return KVFP8_ERR_NULL;
+  if ((v_pool == nullptr) != (v_new == nullptr)) return KVFP8_ERR_NULL;
+  if (!aligned16(k_pool) || !aligned16(k_new) || (v_pool && (!aligned16(v_pool) || !aligned16(v_new))))
+    return KVFP8_ERR_ALIGN;
+  if (fp8 && (!good_scale(k_scale) || (v_pool && !good_scale(v_scale)))) return KVFP8_ERR_VALUE;
+  if ((int64_t)desc->num_kv_heads * desc->head_dim / 2 > kCheckAppendMaxPairs ||
+      (int64_t)desc->num_kv_heads * desc->v_dim / 2 > kCheckAppendMaxPairs)
+    return KVFP8_ERR_UNSUPPORTED;
+  TagArgs c;
+  c.page_tags = page_tags;
+  c.page_table = page_table;
+  c.expected = expected_tags;
+  c.ctx_lens = ctx_lens;
+  c.flags = abort_flags;
+  c.num_pages = desc->num_pages;
+  c.pt_stride = pt_stride;
+  c.batch = batch;
+  c.page_size = desc->page_size;
+  AppendArgs a;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.tok_req = nullptr;
+  a.tok_pos = nullptr;
+  a.page_table = page_table;
+  a.flags = nullptr;
+  a.n_tokens = batch;
+  a.batch = batch;
+  a.pt_stride = pt_stride;
+  a.num_pages = desc->num_pages;
+  a.page_size = desc->page_size;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.head_dim = desc->head_dim;
+  a.v_dim = desc->v_dim;
+  a.k_inv = fp8 ? 1.0f / k_scale : 1.0f;
+  a.v_inv = fp8 && v_pool ? 1.0f / v_scale : 1.0f;
+  return launch_check_append(c, a, fp8, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
+}
+
 int32_t latent_head_groups(int32_t num_q_heads) {
   return (num_q_heads + kLatentHeadsPerBlock - 1) / kLatentHeadsPerBlock;
 }
@@ -305,6 +355,23 @@ int kv_tag_check(const uint32_t* page_tags, int32_t num_pages, const int32_t* pa
   a.batch = batch;
   a.page_size = page_size;
   return launch_tag_check(a, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
+}
+
+int kv_tag_check_append_fp8(const kvfp8_pool_desc* desc, uint8_t* k_pool, uint8_t* v_pool, const uint16_t* k_new,
+                            const uint16_t* v_new, const int32_t* page_table, int32_t pt_stride,
+                            const int32_t* ctx_lens, int32_t batch, const uint32_t* page_tags,
+                            const uint32_t* expected_tags, uint32_t* abort_flags, float k_scale, float v_scale,
+                            hipStream_t stream) {
+  return check_append_common(desc, k_pool, v_pool, k_new, v_new, page_table, pt_stride, ctx_lens, batch, page_tags,
+                             expected_tags, abort_flags, true, k_scale, v_scale, stream);
+}
+
+int kv_tag_check_append_bf16(const kvfp8_pool_desc* desc, uint16_t* k_pool, uint16_t* v_pool, const uint16_t* k_new,
+                             const uint16_t* v_new, const int32_t* page_table, int32_t pt_stride,
+                             const int32_t* ctx_lens, int32_t batch, const uint32_t* page_tags,
+                             const uint32_t* expected_tags, uint32_t* abort_flags, hipStream_t stream) {
+  return check_append_common(desc, k_pool, v_pool, k_new, v_new, page_table, pt_stride, ctx_lens, batch, page_tags,
+                             expected_tags, abort_flags, false, 1.f, 1.f, stream);
 }
 
 size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t v_dim, int32_t num_splits) {

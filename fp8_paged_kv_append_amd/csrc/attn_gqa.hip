@@ -33,7 +33,8 @@
 //    ([d][slot] per page and head): the load is one 16-byte read per d row.
 //  * Online softmax per head n in the log2 domain; only the tile max needs
 //    cross-lane traffic (two xor shuffles).  The accumulator layout (column =
-//    head n) keeps the rescale lane-local.
+//    head n) keeps the rescale lane-local, and it is lazy: it runs only when
+//    a head's running max grows by more than 2^8.
 // The four waves merge their (m, l, O) through LDS; with one split the block
 // writes bf16 output, otherwise normalised fp32 partials and lse for the merge
 // kernel.
@@ -46,6 +47,7 @@ constexpr int kTile = 64;
 constexpr int kD = 128;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
+constexpr float kLazy = 8.f;  // log2-domain slack before the accumulators are rescaled
 
 // --- per-dtype loads and operand conversions -------------------------------------------------
 
@@ -220,28 +222,35 @@ __device__ __forceinline__ void compute_tile(TileRegs<FP8>& T, const u32x4_t (&q
     }
   tmax = fmaxf(tmax, shfl_xor(tmax, 16));
   tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-  const float m_new = fmaxf(st.m, tmax);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = exp2f(st.m - m_use);  // st.m = -inf -> 0
+  // The accumulators stay referenced to st.m until a tile's max exceeds it by more than kLazy
+  // (log2 units): p <= 2^kLazy meanwhile (exact up to rounding) and the rescale of the
+  // AGPR-resident accumulators runs only when some head's max really grows.
+  const bool grow = tmax > st.m + kLazy;  // st.m = -inf: any finite tile max grows it
+  if (__any(grow)) {
+    const float m_new = grow ? tmax : st.m;
+    const float alpha = grow ? exp2f(st.m - m_new) : 1.f;  // st.m = -inf -> 0
+    st.l *= alpha;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.acc[j] *= alpha;
+    st.m = m_new;
+  }
+  const float m_use = st.m == -INFINITY ? 0.f : st.m;
   float psum = 0.f;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     x[k] = exp2f(x[k] - m_use);
     psum += x[k];
   }
-  st.l = st.l * alpha + psum;
-  st.m = m_new;
+  st.l += psum;
   u32x4_t pp[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int e = 0; e < 4; ++e) pp[kb][e] = pack_p<FP8>(x[8 * kb + 2 * e], x[8 * kb + 2 * e + 1]);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    st.acc[j] *= alpha;
+  for (int j = 0; j < 8; ++j)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) st.acc[j] = mfma_pv<FP8>(T.v[j], kb, pp[kb], st.acc[j]);
-  }
 }
 
 template <bool FP8>

@@ -120,6 +120,99 @@ hipError_t launch_append(const AppendArgs& a, bool fp8, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ check + write in one launch
+// The decode step's first two passes fused per request: block r ORs the flags of request r's used
+// pages exactly as tag_check_kernel does, and only when they are clear writes r's new token
+// (position ctx_lens[r] - 1) exactly as append_kernel would.  The new rows are loaded before the
+// check so their latency overlaps it.  Check before write is preserved inside the block.
+template <bool FP8>
+__global__ __launch_bounds__(256) void check_append_kernel(TagArgs c, AppendArgs a) {
+  __shared__ uint32_t s_or[4];
+  const int r = blockIdx.x;
+  const int H = a.num_kv_heads, S = a.page_size, D = a.head_dim, Dv = a.v_dim;
+  constexpr int kMaxPairs = 8;  // new-row element pairs per thread held across the check
+  const int nk = H * D / 2, nv = a.v_pool ? H * Dv / 2 : 0;
+  uint32_t kw[kMaxPairs], vw[kMaxPairs];
+  const uint32_t* ksrc = reinterpret_cast<const uint32_t*>(a.k_new + (int64_t)r * H * D);
+  const uint32_t* vsrc = reinterpret_cast<const uint32_t*>(a.v_new + (int64_t)r * H * Dv);
+#pragma unroll
+  for (int i = 0; i < kMaxPairs; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    kw[i] = e < nk ? ksrc[e] : 0u;
+    vw[i] = e < nv ? vsrc[e] : 0u;
+  }
+  // ---- the check
+  const int64_t L = c.ctx_lens[r];
+  uint32_t f = 0;
+  if (L > 0) {
+    const int64_t need = (L + c.page_size - 1) / c.page_size;
+    int64_t n = need;
+    if (need > c.pt_stride) {
+      f |= 2u;
+      n = c.pt_stride;
+    }
+    const int32_t* pt = c.page_table + (int64_t)r * c.pt_stride;
+    const uint32_t* ex = c.expected + (int64_t)r * c.pt_stride;
+    for (int64_t i = threadIdx.x; i < n; i += 256) {
+      const int32_t p = pt[i];
+      if (p < 0 || p >= c.num_pages)
+        f |= 2u;
+      else if (c.page_tags[p] != ex[i])
+        f |= 1u;
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) f |= shfl_xor(f, m);
+  if ((threadIdx.x & 63) == 0) s_or[threadIdx.x >> 6] = f;
+  __syncthreads();
+  const uint32_t flag = s_or[0] | s_or[1] | s_or[2] | s_or[3];
+  if (threadIdx.x == 0) c.flags[r] = flag;
+  // ---- the write, for a request whose pages all check out
+  if (flag != 0u || L <= 0) return;
+  const int pos = (int)(L - 1);
+  const int page = a.page_table[(int64_t)r * a.pt_stride + pos / S];  // validated above
+  const int slot = pos % S;
+#pragma unroll
+  for (int i = 0; i < kMaxPairs; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    if (e < nk) {
+      const int h = e / (D / 2), d2 = e % (D / 2);
+      const int64_t o = k_elem_offset<FP8 ? 1 : 2>(page, h, slot, 2 * d2, H, S, D);
+      if (FP8) {
+        const float x0 = bf16_bits_to_f32(kw[i] & 0xFFFFu) * a.k_inv;
+        const float x1 = bf16_bits_to_f32(kw[i] >> 16) * a.k_inv;
+        reinterpret_cast<uint16_t*>(a.k_pool)[o >> 1] = (uint16_t)encode_e4m3x2(x0, x1);
+      } else {
+        reinterpret_cast<uint32_t*>(a.k_pool)[o >> 1] = kw[i];
+      }
+    }
+    if (e < nv) {
+      const int h = e / (Dv / 2), d2 = e % (Dv / 2);
+      const int64_t o = ((int64_t)page * H + h) * Dv * S + (int64_t)(2 * d2) * S + slot;
+      if (FP8) {
+        const float x0 = bf16_bits_to_f32(vw[i] & 0xFFFFu) * a.v_inv;
+        const float x1 = bf16_bits_to_f32(vw[i] >> 16) * a.v_inv;
+        const uint32_t cc = encode_e4m3x2(x0, x1);
+        uint8_t* vp = reinterpret_cast<uint8_t*>(a.v_pool);
+        vp[o] = (uint8_t)(cc & 0xFFu);
+        vp[o + S] = (uint8_t)(cc >> 8);
+      } else {
+        uint16_t* vp = reinterpret_cast<uint16_t*>(a.v_pool);
+        vp[o] = (uint16_t)(vw[i] & 0xFFFFu);
+        vp[o + S] = (uint16_t)(vw[i] >> 16);
+      }
+    }
+  }
+}
+
+hipError_t launch_check_append(const TagArgs& c, const AppendArgs& a, bool fp8, hipStream_t stream) {
+  if (fp8)
+    hipLaunchKernelGGL(check_append_kernel<true>, dim3(c.batch), dim3(256), 0, stream, c, a);
+  else
+    hipLaunchKernelGGL(check_append_kernel<false>, dim3(c.batch), dim3(256), 0, stream, c, a);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ gather (read back)
 template <typename T>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {

@@ -96,6 +96,8 @@ hipError_t launch_merge(const MergeArgs& m, int batch, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_tag_check(const TagArgs& a, hipStream_t stream);
+hipError_t launch_check_append(const TagArgs& c, const AppendArgs& a, bool fp8, hipStream_t stream);
+constexpr int kCheckAppendMaxPairs = 8 * 256;  // (Hkv*D)/2 and (Hkv*Dv)/2 limit of the fused kernel
 hipError_t launch_absmax(const uint16_t* x, int64_t n, uint32_t* out, hipStream_t stream);
 
 }  // namespace kvfp8

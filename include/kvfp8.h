@@ -135,6 +135,26 @@ int kv_tag_check(const uint32_t* page_tags, int32_t num_pages, const int32_t* pa
                  const uint32_t* expected_tags, int32_t pt_stride, const int32_t* ctx_lens,
                  int32_t batch, int32_t page_size, uint32_t* abort_flags, hipStream_t stream);
 
+/* ---------------------------------------------------------------- check + write, one launch  [T][Q]
+ * The decode step's first two passes for the usual case of one new token per
+ * request: token r of k_new/v_new [B][Hkv][D|Dv] belongs to request r at
+ * position ctx_lens[r] - 1.  Writes abort_flags exactly as kv_tag_check does
+ * (page tags uint32 [desc->num_pages]) and then writes each request's token
+ * exactly as kv_append_* would with those flags; the check of a request
+ * still completes before its write.  Same result as kv_tag_check followed by
+ * kv_append_* with tok_req[n] = n, tok_pos[n] = ctx_lens[n] - 1, in one
+ * launch.  Hkv*D and Hkv*Dv at most 4096 (KVFP8_ERR_UNSUPPORTED otherwise). */
+int kv_tag_check_append_fp8(const kvfp8_pool_desc* desc, uint8_t* k_pool, uint8_t* v_pool,
+                            const uint16_t* k_new, const uint16_t* v_new, const int32_t* page_table,
+                            int32_t pt_stride, const int32_t* ctx_lens, int32_t batch,
+                            const uint32_t* page_tags, const uint32_t* expected_tags,
+                            uint32_t* abort_flags, float k_scale, float v_scale, hipStream_t stream);
+int kv_tag_check_append_bf16(const kvfp8_pool_desc* desc, uint16_t* k_pool, uint16_t* v_pool,
+                             const uint16_t* k_new, const uint16_t* v_new, const int32_t* page_table,
+                             int32_t pt_stride, const int32_t* ctx_lens, int32_t batch,
+                             const uint32_t* page_tags, const uint32_t* expected_tags,
+                             uint32_t* abort_flags, hipStream_t stream);
+
 /* ---------------------------------------------------------------- decode attention  [Q]
  * For request r, query head h (KV head g = h / (Hq/Hkv)), over positions t < L_r:
  *   s_t = sm_scale * <q_h, K^_t>,  o_h = sum_t softmax(s)_t V^_t,

@@ -80,6 +80,15 @@ def test_host_validation_codes(lib):
     assert lib.kv_tag_check(A, 4, A, A, 0, A, 1, 16, A, None) == -2
     assert lib.kv_tag_check(A, 4, A, None, 1, A, 1, 16, A, None) == -1
     assert lib.kv_tag_check(A, 4, A, A, 1, A, 0, 16, A, None) == 0
+    # fused check + write
+    g = lib.kv_tag_check_append_fp8
+    assert g(d, A, A, A, A, A, 16, A, 0, A, A, A, 1., 1., None) == 0                           # empty batch
+    assert g(d, A, A, A, A, A, 0, A, 1, A, A, A, 1., 1., None) == -2
+    assert g(d, A, A, A, A, A, 16, A, 1, A, None, A, 1., 1., None) == -1                       # no expected tags
+    assert g(d, A, None, A, A, A, 16, A, 1, A, A, A, 1., 1., None) == -1                       # v_new w/o v_pool
+    assert g(d, A, A, A, A, A, 16, A, 1, A, A, A, 1., 0., None) == -7
+    wide = _lib.PoolDesc(16, 16, 64, 128, 128)                      # 64 x 128 > 4096 elements per row
+    assert lib.kv_tag_check_append_bf16(wide, A, A, A, A, A, 16, A, 1, A, A, A, None) == -3
     # attention
     f = lib.paged_decode_attn_fp8
     assert f(d, A, 8, A, A, A, 16, A, 0, 256, None, 1., 1., 1., 0, None, 0, A, None) == 0     # empty batch

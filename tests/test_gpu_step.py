@@ -91,3 +91,93 @@ def test_full_size_64x8192_sampled(kv_dtype):
         err = float(np.max(attention.row_rel_error(codec.f64_from_bf16(g_out[r]), ref)))
         note(f"    row error {err:.3e}")
         assert err <= ATTN_TOL
+
+
+def _fused_case(kv_dtype, latent):
+    """A batch with planted faults for the fused check + write: stale tags, a page-table hole inside a used
+    range, an empty request; the new rows differ from what is stored so a skipped write is visible."""
+    if latent:
+        w = wl.WORKLOADS["latent"].with_(batch=9, num_q_heads=16, num_pages=400, ctx_lo=1, ctx_hi=600)
+    else:
+        w = wl.WORKLOADS["sweep_b16"].with_(num_pages=3000, ctx_lo=1, ctx_hi=700)
+    lens = wl.ctx_lens(w)
+    lens[3] = 0
+    c = Case(w, kv_dtype, lens=lens, stale=[1, 6])
+    c.fill_device()
+    hole = 5                                             # its middle used entry becomes -1 after the fill
+    c.pt[hole, (int(c.lens[hole]) - 1) // w.page_size // 2] = -1
+    c.dpt = dev(c.pt)
+    k_new, v_new, req, pos = c.step_inputs()
+    k_new = k_new ^ np.uint16(0x0040)
+    return c, k_new, v_new, req, pos, hole
+
+
+@pytest.mark.parametrize("latent", [False, True])
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_fused_check_append_step(kv_dtype, latent):
+    """decode_step with implicit tokens (kv_tag_check_append_* then attention): flags and both pools
+    bit-exact to the oracle's check -> append, attention rows within tolerance, faulty requests zero."""
+    note(f"fused check+append {kv_dtype} latent={latent}")
+    c, k_new, v_new, req, pos, hole = _fused_case(kv_dtype, latent)
+    w = c.w
+    st = dict(dtype=kv_dtype, k_pool=c.okp, v_pool=c.ovp, page_table=c.pt, ctx_lens=c.lens, page_tags=c.tags,
+              expected_tags=c.exp, num_kv_heads=w.num_kv_heads, page_size=w.page_size, head_dim=w.head_dim,
+              v_dim=w.v_dim, k_scale=c.o_k_scale, v_scale=c.o_v_scale, sm_scale=c.sm_scale, latent=latent)
+    o_flags, o_out = step.decode_step(st, c.q, k_new, v_new, req, pos)
+    assert o_flags[hole] == paged.FLAG_BAD_PAGE and o_flags[1] and o_flags[6] and not o_flags[3]
+    flags = torch.full((w.batch,), -1, dtype=torch.int32, device="cuda")
+    out = c.out_tensor()
+    if latent:
+        # the step's write through the fused launch, then the latent attention
+        f = kv.kv_tag_check_append_fp8 if kv_dtype == "fp8" else kv.kv_tag_check_append_bf16
+        kw = dict(k_scale=c.d_k_scale, v_scale=c.d_v_scale) if kv_dtype == "fp8" else {}
+        f(c.desc, c.dkp, None, dev(k_new), None, c.dpt, c.dlens, c.dtags, c.dexp, flags, **kw)
+        splits = kv.paged_decode_attn_latent_auto_splits(w.batch, w.num_q_heads, c.max_ctx)
+        ws = c.workspace(splits)
+        if kv_dtype == "fp8":
+            kv.paged_decode_attn_latent_fp8(c.desc, c.dq, c.dkp, c.dpt, c.dlens, c.max_ctx, out, flags,
+                                            scale=c.d_k_scale, sm_scale=c.sm_scale, workspace=ws)
+        else:
+            kv.paged_decode_attn_latent_bf16(c.desc, c.dq, c.dkp, c.dpt, c.dlens, c.max_ctx, out, flags,
+                                             sm_scale=c.sm_scale, workspace=ws)
+    else:
+        splits = kv.paged_decode_attn_auto_splits(w.batch, w.num_kv_heads, c.max_ctx)
+        kv.decode_step(c.desc, kv_dtype, c.dkp, c.dvp, c.dpt, c.dlens, c.max_ctx, c.dq, dev(k_new), dev(v_new),
+                       None, None, out, page_tags=c.dtags, expected_tags=c.dexp, abort_flags=flags,
+                       k_scale=c.d_k_scale, v_scale=c.d_v_scale, sm_scale=c.sm_scale, workspace=c.workspace(splits))
+    torch.cuda.synchronize()
+    g_flags, g_out = host(flags, np.uint32), host(out, np.uint16)
+    assert np.array_equal(g_flags, o_flags)
+    et = np.uint8 if kv_dtype == "fp8" else np.uint16
+    assert np.array_equal(host(c.dkp, et), c.okp)
+    if not latent:
+        assert np.array_equal(host(c.dvp, et), c.ovp)
+    err = attn_error(g_out, o_out)
+    note(f"  step error {err:.3e}")
+    assert err <= ATTN_TOL
+    for r in np.flatnonzero(o_flags).tolist() + [3]:
+        assert not g_out[r].any()
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_fused_matches_separate_launches(kv_dtype):
+    """The fused launch and kv_tag_check + kv_append_* on two copies of one device cache: identical bytes."""
+    note(f"fused vs separate {kv_dtype}")
+    c, k_new, v_new, req, pos, _ = _fused_case(kv_dtype, False)
+    w = c.w
+    kp2, vp2 = c.dkp.clone(), c.dvp.clone()
+    f1 = torch.zeros(w.batch, dtype=torch.int32, device="cuda")
+    f2 = torch.full((w.batch,), 7, dtype=torch.int32, device="cuda")
+    dk, dv = dev(k_new), dev(v_new)
+    kv.kv_tag_check(c.dtags, c.dpt, c.dexp, c.dlens, w.page_size, f1)
+    if kv_dtype == "fp8":
+        kv.kv_append_fp8(c.desc, c.dkp, c.dvp, dk, dv, dev(req), dev(pos), c.dpt, f1, k_scale=c.d_k_scale,
+                         v_scale=c.d_v_scale)
+        kv.kv_tag_check_append_fp8(c.desc, kp2, vp2, dk, dv, c.dpt, c.dlens, c.dtags, c.dexp, f2,
+                                   k_scale=c.d_k_scale, v_scale=c.d_v_scale)
+    else:
+        kv.kv_append_bf16(c.desc, c.dkp, c.dvp, dk, dv, dev(req), dev(pos), c.dpt, f1)
+        kv.kv_tag_check_append_bf16(c.desc, kp2, vp2, dk, dv, c.dpt, c.dlens, c.dtags, c.dexp, f2)
+    torch.cuda.synchronize()
+    assert torch.equal(f1, f2)
+    assert torch.equal(c.dkp, kp2) and torch.equal(c.dvp, vp2)
