@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bf16", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads (GQA batch, long, latent)")
+    p.add_argument("--no-sweep", action="store_true", help="skip the batch sweep B = 1, 8, 16, 32, 64")
+    p.add_argument("--flush-mib", type=int, default=512,
+                   help="size of the write that evicts the 256 MB Infinity Cache before each flushed step")
     p.add_argument("--cpu-sample", type=int, default=8, help="requests in the CPU oracle sample")
     p.add_argument("--fp8-only-steps", action="store_true", help="time only the FP8 step (profiling runs)")
     p.add_argument("--unfused", action="store_true",
@@ -180,6 +183,33 @@ class DeviceCache:
         total_ms = t0.elapsed_time(t1)
         return dict(ms_per_step=total_ms / steps, wall_ms_per_step=1e3 * wall / steps)
 
+    def run_flushed(self, steps, warmup, flush):
+        """Per-step times with a cache-evicting write before every step, outside the event window:
+        events before the step, after the check (+ append) and after the attention."""
+        torch = self.torch
+        for _ in range(warmup):
+            flush.add_(1)
+            self.step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for e in evs:
+            flush.add_(1)
+            e[0].record()
+            if self.fused:
+                self.check_append()
+            else:
+                self.check()
+                self.append()
+            e[1].record()
+            self.attend()
+            e[2].record()
+        torch.cuda.synchronize()
+        per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in evs])
+        step = per.sum(axis=1)
+        return dict(step_ms=float(np.median(step)), step_ms_p95=float(np.percentile(step, 95)),
+                    attn_ms=float(np.median(per[:, 1])), attn_ms_p95=float(np.percentile(per[:, 1], 95)),
+                    check_append_ms=float(np.median(per[:, 0])))
+
     def breakdown(self, steps, tracker=True):
         """Per-kernel durations: an event before and after each launch of every step."""
         torch = self.torch
@@ -311,10 +341,26 @@ def main():
         log(f"{w.name}: inputs ready in {time.perf_counter() - t:.1f} s")
         return host, stale, elems, flops
 
-    def measure(w, kvd, host, stale, elems, steps, warmup, full=True):
+    flush = torch.zeros((args.flush_mib << 20) // 4, dtype=torch.int32, device="cuda")
+
+    def measure(w, kvd, host, stale, elems, steps, warmup, full=True, flushed=False):
         t = time.perf_counter()
         c = DeviceCache(w, kvd, host, torch, kv, fused=not args.unfused)
         log(f"{w.name} {kvd}: cache filled in {time.perf_counter() - t:.1f} s, splits={c.splits}")
+        elt = 1 if kvd == "fp8" else 2
+        if flushed:
+            r = c.run_flushed(steps, warmup, flush)
+            r["kv_bytes"] = elems * elt
+            r["gbs_attn"] = r["kv_bytes"] / (r["attn_ms"] * 1e-3) / 1e9
+            r["gbs_step"] = r["kv_bytes"] / (r["step_ms"] * 1e-3) / 1e9
+            r["splits"] = c.splits
+            flags = c.flags.cpu().numpy().view(np.uint32)
+            assert np.flatnonzero(flags).tolist() == stale.tolist(), "abort flags differ from the planted stale set"
+            log(f"{w.name} {kvd} flushed: " + json.dumps({k_: (round(v_, 4) if isinstance(v_, float) else v_)
+                                                          for k_, v_ in r.items()}))
+            del c
+            torch.cuda.empty_cache()
+            return r
         r = c.run(steps, warmup, tracker=True, graph=args.graph)
         if full:
             r["other"] = c.run(steps, warmup, tracker=True, graph=not args.graph)
@@ -323,7 +369,7 @@ def main():
         assert np.flatnonzero(flags).tolist() == stale.tolist(), "abort flags differ from the planted stale set"
         if full and not args.fp8_only_steps:
             r["no_tracker"] = c.run(steps, warmup, tracker=False, graph=args.graph)
-        elt = 1 if kvd == "fp8" else 2
+            r["flushed"] = c.run_flushed(steps, warmup, flush)
         r["kv_bytes"] = elems * elt
         r["gbs_step"] = r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
         r["gbs_attn"] = r["kv_bytes"] / (r["attn_ms_mean"] * 1e-3) / 1e9
@@ -342,6 +388,27 @@ def main():
         results[kvd] = measure(w, kvd, host, stale, kv_elems, args.steps, args.warmup)
     del host
     torch.cuda.empty_cache()
+
+    sweep = {}
+    if not args.no_sweep and not args.fp8_only_steps:
+        # B = 1 .. 64 at 8192 tokens, each step after a cache-evicting write: without it the smaller
+        # points (16.8 MB of FP8 KV at B = 1) would be read from the 256 MB Infinity Cache
+        for b in (1, 8, 16, 32, 64):
+            wb = wl.WORKLOADS[f"sweep_b{b}"]
+            hb, st_b, el_b, _ = prepare(wb, args.splits)
+            e = {}
+            for kvd in ("fp8", "bf16"):
+                r = measure(wb, kvd, hb, st_b, el_b, args.steps, 3, flushed=True)
+                e[kvd] = {"step_us": round(1e3 * r["step_ms"], 2), "step_us_p95": round(1e3 * r["step_ms_p95"], 2),
+                          "steps_per_s": round(1e3 / r["step_ms"], 1), "attn_us": round(1e3 * r["attn_ms"], 2),
+                          "attn_us_p95": round(1e3 * r["attn_ms_p95"], 2), "attn_gbs": round(r["gbs_attn"], 1),
+                          "attn_pct_hbm_peak": round(100 * r["gbs_attn"] / HBM_PEAK_GBS, 2),
+                          "check_append_us": round(1e3 * r["check_append_ms"], 2), "splits": r["splits"]}
+            e["fp8_speedup_step"] = round(e["bf16"]["step_us"] / e["fp8"]["step_us"], 3)
+            e["stale_requests"] = len(st_b)
+            sweep[f"B{b}"] = e
+            del hb
+            torch.cuda.empty_cache()
 
     extra = {}
     if not args.no_extra and not args.fp8_only_steps:
@@ -406,6 +473,13 @@ def main():
                    "eager back-to-back steps") + ", between two events on the launch stream",
         ("eager_ms_per_step" if args.graph else "graph_ms_per_step"): round(f8["other"]["ms_per_step"], 5),
     }
+    if "flushed" in f8:
+        fl = f8["flushed"]
+        line["flushed_step"] = {"step_us": round(1e3 * fl["step_ms"], 2), "step_us_p95": round(1e3 * fl["step_ms_p95"], 2),
+                                "attn_us": round(1e3 * fl["attn_ms"], 2),
+                                "note": f"median over steps each preceded by a {args.flush_mib} MiB write"}
+    if sweep:
+        line["batch_sweep_flushed"] = sweep
     if "no_tracker" in f8:
         nt = f8["no_tracker"]
         line["tracker_off"] = {"ms_per_step": round(nt["ms_per_step"], 5),

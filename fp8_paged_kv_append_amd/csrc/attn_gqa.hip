@@ -238,7 +238,7 @@ __device__ __forceinline__ void compute_tile(TileRegs<FP8>& T, const u32x4_t (&q
   float psum = 0.f;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    x[k] = exp2f(x[k] - m_use);
+    x[k] = __builtin_amdgcn_exp2f(x[k] - m_use);  // v_exp_f32: weights below 2^-126 flush to 0
     psum += x[k];
   }
   st.l += psum;
@@ -406,19 +406,25 @@ __global__ __launch_bounds__(kThreads) void attn_gqa_split_kernel(AttnArgs a) {
 
 // --- merge of the split partials ----------------------------------------------------------------
 
-__global__ __launch_bounds__(kD) void attn_merge_kernel(MergeArgs a) {
-  const int row = blockIdx.x;  // r * Hq + h
-  const int r = row / a.num_q_heads;
-  const int d = threadIdx.x;
+// One thread per 4 consecutive value dims of a (request, head) row, 16-byte loads of each split's
+// partial; the rows of one block are consecutive, so a block reads contiguous partials.
+constexpr int kMergeThreads = 128;
+
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(MergeArgs a) {
+  const int tpr = a.v_dim / 4;  // threads per row
+  const int64_t row = (int64_t)blockIdx.x * (kMergeThreads / tpr) + threadIdx.x / tpr;  // r * Hq + h
+  if (row >= a.rows) return;
+  const int d = 4 * (threadIdx.x % tpr);
+  const int r = (int)(row / a.num_q_heads);
   const int L = a.ctx_lens[r];
   const bool aborted = a.flags != nullptr && a.flags[r] != 0u;
-  uint16_t* out = a.out + (int64_t)row * a.v_dim;
+  u32x2_t* out = reinterpret_cast<u32x2_t*>(a.out + row * a.v_dim + d);
   if (aborted || L <= 0 || L > a.max_ctx || L > a.pt_stride * a.page_size) {
-    for (int e = d; e < a.v_dim; e += blockDim.x) out[e] = 0;
+    *out = u32x2_t{0u, 0u};
     return;
   }
   const int nvalid = min(a.num_splits, (L + a.chunk_tokens - 1) / a.chunk_tokens);
-  const float* lse = a.lse_part + (int64_t)row * a.num_splits;
+  const float* lse = a.lse_part + row * a.num_splits;
   float M = -INFINITY;
   bool nan = false;
   for (int c = 0; c < nvalid; ++c) {
@@ -426,17 +432,20 @@ __global__ __launch_bounds__(kD) void attn_merge_kernel(MergeArgs a) {
     nan |= x != x;
     M = fmaxf(M, x);
   }
-  for (int e = d; e < a.v_dim; e += blockDim.x) {
-    float o = 0.f, s = 0.f;
-    if (!nan && M != -INFINITY) {
-      for (int c = 0; c < nvalid; ++c) {
-        const float f = exp2f(lse[c] - M);
-        s += f;
-        o += f * a.o_part[((int64_t)row * a.num_splits + c) * a.v_dim + e];
-      }
+  f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+  float s = 0.f;
+  if (!nan && M != -INFINITY) {
+    const f32x4_t* part = reinterpret_cast<const f32x4_t*>(a.o_part + row * a.num_splits * a.v_dim + d);
+    const int stride = a.v_dim / 4;  // f32x4 per split row
+#pragma unroll 4
+    for (int c = 0; c < nvalid; ++c) {
+      const float f = exp2f(lse[c] - M);
+      s += f;
+      o += f * part[(int64_t)c * stride];
     }
-    out[e] = (uint16_t)(pack_bf16x2(s > 0.f ? o / s : 0.f, 0.f) & 0xFFFFu);
   }
+  const float inv = s > 0.f ? 1.f / s : 0.f;
+  *out = u32x2_t{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
 }
 
 hipError_t launch_attn_gqa(const AttnArgs& a, bool fp8, int batch, hipStream_t stream) {
@@ -463,8 +472,13 @@ hipError_t launch_attn_gqa(const AttnArgs& a, bool fp8, int batch, hipStream_t s
   return launch_merge(m, batch, stream);
 }
 
-hipError_t launch_merge(const MergeArgs& m, int batch, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(batch * m.num_q_heads), dim3(kD), 0, stream, m);
+hipError_t launch_merge(const MergeArgs& m_in, int batch, hipStream_t stream) {
+  MergeArgs m = m_in;
+  m.rows = (int64_t)batch * m.num_q_heads;
+  const int tpr = m.v_dim / 4;  // v_dim is 128 or 512: a power of two dividing 4 * kMergeThreads
+  const int64_t rows_per_block = kMergeThreads / tpr;
+  const int64_t blocks = (m.rows + rows_per_block - 1) / rows_per_block;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((uint32_t)blocks), dim3(kMergeThreads), 0, stream, m);
   return hipGetLastError();
 }
 

@@ -6,64 +6,108 @@
 // blog "Smaller, faster, safer: running Kimi and GLM at scale", section
 // "Quantized KV cache": the FP8 cache is converted as it is read), with one
 // cached vector serving as both key and value.  Unlike GQA this shape is bound
-// by the matrix units, not by HBM: 128 heads x (576 + 512) MACs per cached byte.
+// by the matrix units, not by HBM: 128 heads x (576 + 512) MACs per cached element.
 //
-// Block = (request r, 64-head group hg, split c), 8 waves: wave (hb, kh) works
-// on heads 16hb..16hb+15 of the group, half kh of the contraction and half kh
-// of the value dims.  The head groups of one (r, c) are 8 block ids apart, so
-// round-robin dispatch puts them on the same XCD and later reads of a tile hit
-// L2.  Each 32-token tile is copied once into LDS as stored (e4m3 bytes or
-// bf16), one padded row per token, into one of two buffers: the copy of tile
-// t+1 (whose global loads were issued during tile t-1) and the math of tile t
-// share one barrier.  With lane = 16*q + n:
-//  * S^T = C q^T: two 16-token blocks; wave (hb, kh) contracts dims
-//    288kh + 72q + 8kk + j (kk = 0..8) with A = C rows (lane (q, m) reads 8
-//    elements of token m, e4m3 converted to bf16 in registers) and B = q^T
-//    (lane (q, n) holds head n).  The two partial sums of a pair meet in LDS;
-//    fp32 addition commutes, so both waves hold the same scores and the same
-//    softmax state, bit for bit.
-//  * C layout: lane (q, n) holds head n's scores for tokens 16mb + 4q + i;
-//    the PV contraction slot (q, j) is token 16(j/4) + 4q + j%4, so the P it
-//    holds is already the B operand.
-//  * O^T += V^T P^T over value dims 256kh .. 256kh+255: the A operand (8 tokens
-//    at one value dim per lane) is read straight from the token rows with the
-//    gfx950 LDS transpose loads: ds_read_b64_tr_b8 gives lane 8h+e byte e of
-//    the 8-byte blocks named by lanes h, h+2, .., h+14 of its 16-lane group,
-//    ds_read_b64_tr_b16 gives lane 4a+e element e of the blocks named by
-//    lanes a, a+4, a+8, a+12.
-//  * 16 accumulator blocks per lane, column = head n: the online-softmax
-//    rescale is lane-local, and lazy (see below).
+// Block = (request r, split c, group of 128 query heads), 4 waves, one wave per
+// SIMD.  Wave w owns 32 heads over the whole contraction and all 512 value dims:
+// its q (144 VGPRs) and its O accumulators (256 registers, AGPRs) stay resident,
+// so every element a wave converts feeds a 32-head MFMA, and no partial sums
+// cross waves.  The latent pool is row-major ([page][slot][576]); each 32-token
+// tile is copied as stored into LDS by direct global->LDS loads (no VGPRs), into
+// a ring of NBUF buffers, NBUF-1 tiles ahead of the math; one barrier per tile.
+// A token row sits at LDS row sigma(t) with a 16-byte pad: both the row reads
+// of QK and the transpose reads of PV then touch every bank once per phase.
+// With lane l = 32*hh + n (n = head within the wave):
+//  * S^T = C q^T: v_mfma_f32_32x32x16_bf16, A = 32 token rows x 16 dims (lane
+//    reads 8 dims of row l%32), B = q^T (lane holds head n).  Contraction slot
+//    (k-step 2p+x, half hh, element e) is dim 32p + 16hh + 8x + e, so a lane
+//    reads 16 contiguous bytes of its row per pair of k-steps.
+//  * C layout: lane (hh, n) holds head n's scores for tokens 8(j/4) + 4hh + j%4
+//    (j = 0..15); the softmax is lane-local apart from one xor-32 shuffle.
+//  * O^T += V^T P^T per 32-dim block: B = P^T, slot (hh, e) of k-step ks is
+//    token 8(2ks + e/4) + 4hh + e%4 -- register 8ks + e of the scores, so the
+//    lane already holds its P.  A = V^T comes from the gfx950 LDS transpose
+//    loads: ds_read_b64_tr_b8 gives lane 8h+e of a 16-lane group byte e of the
+//    8-byte blocks named by lanes h, h+2, .., h+14; ds_read_b64_tr_b16 gives
+//    lane 4a+e element e of the blocks named by lanes a, a+4, a+8, a+12.
+//  * Online softmax in the log2 domain, lazy: the accumulators are rescaled
+//    only when a head's running max grows by more than 2^8.
 #include "kvfp8_device.h"
 #include "kvfp8_internal.h"
 
 namespace kvfp8 {
 
-constexpr int kLD = 576;            // latent width (score dim)
-constexpr int kLV = 512;            // value dim
-constexpr int kLT = 32;             // tokens per tile
-constexpr int kLWaves = 8;
+constexpr int kLD = kLatentDim;           // 576: latent width (score dim)
+constexpr int kLV = kLatentVDim;          // 512: value dim
+constexpr int kLT = kLatentTileTokens;    // 32 tokens per tile
+constexpr int kLWaves = 4;
 constexpr int kLThreads = kLWaves * kWave;
-constexpr int kLHeadsPerBlock = 64;
+constexpr int kLHW = 32;                  // heads per wave
 constexpr int kLPidWin = 1024;
-constexpr float kLazy = 8.f;        // log2-domain slack before the accumulators are rescaled
+constexpr float kLazy = 8.f;              // log2-domain slack before the accumulators are rescaled
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
-#define KVFP8_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+template <bool FP8>
+struct LCfg {
+  static constexpr int ELT = FP8 ? 1 : 2;
+  static constexpr int ROWB = kLD * ELT;                          // bytes per token row
+  static constexpr int RS = ROWB + 16;                            // LDS row stride
+  static constexpr int CH = ROWB / 16;                            // 16-byte chunks per row
+  static constexpr int SLOTS = RS / 16;                           // chunk slots per LDS row
+  static constexpr int NINST = (kLT * SLOTS + 63) / 64;           // 1 KiB copies per tile
+  static constexpr int NPW = (NINST + kLWaves - 1) / kLWaves;     // copies per wave per tile
+  static constexpr int BUF = NPW * kLWaves * 1024;                // bytes per tile buffer
+  static constexpr int NBUF = FP8 ? 4 : 3;                        // tile buffers
+};
+
+// LDS row of tile token t.  FP8: the 8 tokens a PV transpose read of one half-wave
+// gathers land on rows 2 apart (mod 16); BF16: its 4 tokens land on rows 4 apart.
+template <bool FP8>
+__device__ __forceinline__ int lat_row(int t) {
+  return FP8 ? 16 * (t >> 4) + 8 * ((t >> 3) & 1) + 2 * (t & 3) + ((t >> 2) & 1)
+             : 16 * (t >> 4) + 4 * (t & 3) + 2 * ((t >> 2) & 1) + ((t >> 3) & 1);
+}
+template <bool FP8>
+__device__ __forceinline__ int lat_tok(int row) {  // inverse of lat_row
+  const int u = row >> 4, x = row & 15;
+  return FP8 ? 16 * u + 8 * (x >> 3) + 4 * (x & 1) + ((x >> 1) & 3)
+             : 16 * u + 8 * (x & 1) + 4 * ((x >> 1) & 1) + (x >> 2);
+}
+// tile token of PV contraction slot k (0..15) of k-step ks
+__device__ __forceinline__ int pv_tok(int ks, int k) { return 8 * (2 * ks + ((k & 7) >> 2)) + 4 * (k >> 3) + (k & 3); }
+
+// 16 bytes per lane from global memory straight into LDS at lds_addr + 16*lane (lds_addr
+// wave-uniform, in M0).  Issued through asm so that the compiler does not treat every later LDS
+// read as possibly aliasing an in-flight copy (it would wait for all copies before each tile);
+// the copies are waited for explicitly with vm_wait before the barrier that publishes a tile.
+// M0 is reserved by the compiler, so the asm restores it.
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds_addr) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "v"(src), "s"(lds_addr)
+      : "memory");
+}
+
+// wait until at most N vector memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 template <bool FP8>
 __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs a) {
-  constexpr int ELT = FP8 ? 1 : 2;
-  constexpr int NI = kLD * ELT / 64;           // chunks per 64-byte slice of a row
-  constexpr int SUBCH = 16 * kLD * ELT / 16;   // 16-byte chunks per 16-token sub-page block
-  constexpr int NCH = 2 * SUBCH;               // chunks per 32-token tile
-  constexpr int NLD = (NCH + kLThreads - 1) / kLThreads;
-  constexpr int RS = kLD * ELT + 16;           // LDS bytes per token row (16 bytes of padding)
-  constexpr int BUF = kLT * RS;                // LDS bytes per tile buffer
-
-  __shared__ __align__(16) uint8_t s_tile[2 * BUF];
-  __shared__ __align__(16) f32x4_t s_part[kLWaves][2][kWave];  // partial scores of each wave
+  using C = LCfg<FP8>;
+  constexpr int ELT = C::ELT;
+  __shared__ __align__(1024) uint8_t s_tile[C::NBUF * C::BUF];
   __shared__ int s_pid[kLPidWin];
+  __shared__ int s_bad;
 
   // XCD-aware block decode: head groups of one (request, split) unit are 8 ids apart
   const int b = blockIdx.x;
@@ -74,13 +118,12 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   const int r = unit / a.num_splits, split = unit % a.num_splits;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int hb = wave >> 1, kh = wave & 1;
-  const int q4 = lane >> 4, n = lane & 15;
+  const int n = lane & 31, hh = lane >> 5;
   const int S = a.page_size;
   const int Hq = a.num_q_heads;
-  const int h0 = hg * kLHeadsPerBlock + hb * 16;       // this wave's first head
-  const bool active = h0 < Hq;                          // wave-uniform, equal within a pair
-  const int hb0 = hg * kLHeadsPerBlock, hb1 = min(Hq, hb0 + kLHeadsPerBlock);
+  const int hb0 = hg * kLatentHeadsPerBlock, hb1 = min(Hq, hb0 + kLatentHeadsPerBlock);
+  const int h0 = hb0 + wave * kLHW;     // this wave's first head
+  const bool active = h0 < Hq;          // wave-uniform
 
   const int L = a.ctx_lens[r];
   const bool aborted = a.flags != nullptr && a.flags[r] != 0u;
@@ -97,34 +140,60 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   if (c0 >= L) return;
   const int c1 = min(L, c0 + chunk);
 
-  // q^T operand: lane (q4, n) holds head h0+n, dims 288*kh + 72*q4 + 8*kk .. +8 for kk = 0..8
-  const int dim0 = 288 * kh + 72 * q4;
-  u32x4_t qv[9];
-  if (active) {
-    const uint16_t* qp = a.q + ((int64_t)r * Hq + h0 + n) * kLD + dim0;
+  // q^T operand: lane (hh, n) holds head h0+n, dims 32p + 16hh + 8x .. +8 as qv[2p + x]
+  u32x4_t qv[36];
+  if (h0 + n < Hq) {
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(a.q + ((int64_t)r * Hq + h0 + n) * kLD + 16 * hh);
 #pragma unroll
-    for (int kk = 0; kk < 9; ++kk) qv[kk] = *reinterpret_cast<const u32x4_t*>(qp + 8 * kk);
+    for (int p = 0; p < 18; ++p) {
+      qv[2 * p] = qp[4 * p];
+      qv[2 * p + 1] = qp[4 * p + 1];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 36; ++k) qv[k] = u32x4_t{0, 0, 0, 0};
   }
 
+  // q has landed before any tile copy is in flight: the loop below then carries no waits for it
+  vm_wait<0>();
+
   // LDS byte offsets this lane reads, relative to a tile buffer
-  const int qk_off = n * RS + dim0 * ELT;  // + 16*RS per token block, + 8*ELT bytes per k-step
-  int pv_off0, pv_off1 = 0;               // PV source addresses for this wave's first d-block
-  if (FP8) {
-    const int j = (lane & 15) >> 1, h = lane & 1;
-    pv_off0 = (16 * (j >> 2) + 4 * q4 + (j & 3)) * RS + 8 * h + 256 * kh;
-  } else {
-    const int jj = (lane & 15) >> 2, aa = lane & 3;
-    pv_off0 = (4 * q4 + jj) * RS + 8 * aa + 512 * kh;
-    pv_off1 = (16 + 4 * q4 + jj) * RS + 8 * aa + 512 * kh;
+  const int qk_off = lat_row<FP8>(n) * C::RS + 16 * hh * ELT;   // + 32*p*ELT per k-step pair
+  // PV source of k-step ks, read rd: pv_off + ks*16*RS + rd*RS (+ 32*db*ELT per d-block) -- the
+  // tokens of k-step 1 are those of k-step 0 plus 16 (LDS rows + 16), and the second BF16 read's
+  // tokens are the first's plus 8 (LDS row + 1), under lat_row
+  int pv_off;
+  {
+    const int g = lane >> 4;
+    if (FP8) {
+      const int h = lane & 1, i = (lane & 15) >> 1;
+      pv_off = lat_row<FP8>(pv_tok(0, 8 * (g >> 1) + i)) * C::RS + 16 * (g & 1) + 8 * h;
+    } else {
+      const int aa = lane & 3, i = (lane & 15) >> 2;
+      pv_off = lat_row<FP8>(pv_tok(0, 8 * (g >> 1) + i)) * C::RS + 2 * (16 * (g & 1) + 4 * aa);
+    }
+  }
+  // this lane's share of each tile copy: copy k of the wave fills LDS slots [64j, 64j+64),
+  // j = wave*NPW + k; slot 64j+lane is chunk c of LDS row rho = token lat_tok(rho), or padding
+  // two 16-bit entries per register: (token << 8) | chunk, or 0xFFFF for a padding slot
+  uint32_t cp_tc[(C::NPW + 1) / 2];
+#pragma unroll
+  for (int k = 0; k < (C::NPW + 1) / 2; ++k) cp_tc[k] = 0xFFFFFFFFu;
+#pragma unroll
+  for (int k = 0; k < C::NPW; ++k) {
+    const int slot = 64 * (wave * C::NPW + k) + lane;
+    const int rho = slot / C::SLOTS, c = slot % C::SLOTS;
+    const uint32_t e = (rho < kLT && c < C::CH) ? (uint32_t)((lat_tok<FP8>(rho) << 8) | c) : 0xFFFFu;
+    cp_tc[k >> 1] = (k & 1) ? ((cp_tc[k >> 1] & 0xFFFFu) | (e << 16)) : ((cp_tc[k >> 1] & 0xFFFF0000u) | e);
   }
 
   const int32_t* pt = a.page_table + (int64_t)r * a.pt_stride;
   const uint8_t* pool = reinterpret_cast<const uint8_t*>(a.pool);
   const float c_log2 = a.qk_scale_log2;
   float m_run = -INFINITY, l_run = 0.f;
-  f32x4_t acc[16];
+  f32x16_t acc[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < 16; ++db) acc[db] = f32x16_t{};
   bool bad = false;
 
   // at most kLPidWin - 1 pages of tokens per window: a window starting mid-page still fits kLPidWin ids
@@ -133,7 +202,7 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
     const int w1 = min(c1, w0 + win);
     const int e0 = w0 / S;
     const int ne = (w1 - 1) / S - e0 + 1;
-    __syncthreads();
+    __syncthreads();  // the previous window's ids and tiles are no longer read
     for (int i = threadIdx.x; i < ne; i += kLThreads) {
       int p = pt[e0 + i];
       if (p < 0 || p >= a.num_pages) {
@@ -145,98 +214,111 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
     __syncthreads();
     const int ntile = (w1 - w0 + kLT - 1) / kLT;
 
-    // This thread's chunks of one tile, in storage order; each goes to LDS row tok, bytes 16c.
-    u32x4_t raw[NLD];
-    int dst[NLD];
-    auto issue = [&](int t) {
+    // Copy tile t of the window into buffer bi: NPW 16-byte global->LDS loads per lane.  Every
+    // lane of every copy loads from inside the pool: tokens past the window end re-read the tile's
+    // first row (finite data, weight 0), padding slots and tiles past the end read the first
+    // row too, and a page id outside the pool reads the pool's first page (the request is zeroed).
+    auto copy_tile = [&](int t, int bi) {
       const int tb = w0 + t * kLT;
+      const bool live = t < ntile;
+      const int nv = live ? w1 - tb : 0;
+      const int tb_c = live ? tb : w0;
+      // the two 16-token halves of a tile each lie inside one page (tile starts are 32-aligned, S % 16 == 0)
+      const int pid0 = s_pid[tb_c / S - e0];
+      const int pid1 = nv > 16 ? s_pid[(tb_c + 16) / S - e0] : pid0;
+      const uint8_t* base0 = pool + (pid0 >= 0 ? ((int64_t)pid0 * S + tb_c % S) * C::ROWB : 0);
+      const uint8_t* base1 = nv > 16 ? pool + (pid1 >= 0 ? ((int64_t)pid1 * S + (tb_c + 16) % S) * C::ROWB : 0)
+                                     : base0;
+      const uint32_t dst = (uint32_t)(uintptr_t)((lds_u8*)(s_tile + bi * C::BUF) + 1024 * wave * C::NPW);
 #pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        const int pa = threadIdx.x + kLThreads * j;
-        const int sub = pa / SUBCH, p = pa % SUBCH;
-        const int i = p & 3, qq = (p >> 2) & 3, rest = p >> 4;
-        const int kq = rest % NI, s = rest / NI;
-        const int tok = 16 * sub + 4 * s + i;
-        dst[j] = pa < NCH ? tok * RS + 16 * (qq * NI + kq) : -1;
-        const int tok_sub = tb + 16 * sub;
-        int pid = -1;
-        if (t < ntile && pa < NCH && tok_sub < w1) pid = s_pid[min(tok_sub / S - e0, ne - 1)];
-        if (pid >= 0 && tb + tok < w1) {
-          const uint8_t* src = pool + ((int64_t)pid * S * kLD + (int64_t)(tok_sub % S) * kLD) * ELT + 16 * (int64_t)p;
-          raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
-        } else {
-          raw[j] = u32x4_t{0, 0, 0, 0};     // absent token: zeros (masked below)
-        }
+      for (int k = 0; k < C::NPW; ++k) {
+        const int tc = (int)((cp_tc[k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
+        const int tok = tc >> 8;
+        const bool ok = tc != 0xFFFF && tok < nv;
+        const int tt = ok ? tok : 0, cc = ok ? (tc & 255) : 0;
+        const uint8_t* src = (tt >= 16 ? base1 : base0) + (tt & 15) * C::ROWB + 16 * cc;
+        lds_copy16(src, dst + 1024 * k);
       }
     };
-    auto stage = [&](int buf) {
-#pragma unroll
-      for (int j = 0; j < NLD; ++j)
-        if (dst[j] >= 0) *reinterpret_cast<u32x4_t*>(&s_tile[buf * BUF + dst[j]]) = raw[j];
-    };
 
-    issue(0);
-    __syncthreads();  // the previous window's last tile is no longer read
-    stage(0);
-    issue(1);
+#pragma unroll
+    for (int t = 0; t < C::NBUF - 1; ++t) copy_tile(t, t);
     for (int t = 0; t < ntile; ++t) {
-      const int tb = w0 + t * kLT;
-      const int cur = t & 1;
-      __syncthreads();  // tile t is in LDS; buffer cur^1 and the score exchange are free
-      if (t + 1 < ntile) {
-        stage(cur ^ 1);
-        issue(t + 2);
-      }
-      const uint8_t* tile = &s_tile[cur * BUF];
-
-      // ---- partial S^T = C q^T over this wave's half of the dims, two 16-token blocks
-      f32x4_t sc[2];
-      if (active) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          f32x4_t ch[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-          const uint8_t* row = tile + qk_off + 16 * mb * RS;
-#pragma unroll
-          for (int kk = 0; kk < 9; ++kk) {
-            u32x4_t av;
-            if (FP8) {
-              const u32x2_t c8 = *reinterpret_cast<const u32x2_t*>(row + 8 * kk);
-              const u32x2_t lo = e4m3x4_to_bf16x4(c8[0]), hi = e4m3x4_to_bf16x4(c8[1]);
-              av = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-            } else {
-              av = *reinterpret_cast<const u32x4_t*>(row + 16 * kk);
-            }
-            ch[kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                                 __builtin_bit_cast(bf16x8_t, qv[kk]), ch[kk & 1], 0,
-                                                                 0, 0);
-          }
-          sc[mb] = ch[0] + ch[1];
-          s_part[wave][mb][lane] = sc[mb];
-        }
-      }
-      __syncthreads();  // both halves of every pair's scores are in LDS
+      vm_wait<C::NPW * (C::NBUF - 2)>();  // this wave's copies of tile t have landed
+      __syncthreads();                    // everyone's have; everyone is done with tile t-1
+      copy_tile(t + C::NBUF - 1, (t + C::NBUF - 1) % C::NBUF);
       if (!active) continue;
-      {
-        const f32x4_t o0 = s_part[wave ^ 1][0][lane], o1 = s_part[wave ^ 1][1][lane];
-        // same operands in the same order in both waves of the pair
-        sc[0] = kh == 0 ? sc[0] + o0 : o0 + sc[0];
-        sc[1] = kh == 0 ? sc[1] + o1 : o1 + sc[1];
+      const uint8_t* tile = s_tile + (t % C::NBUF) * C::BUF;
+      const lds_u8* lt = (const lds_u8*)tile;
+      const int nv = w1 - (w0 + t * kLT);  // valid tokens of this tile (may exceed 32)
+
+      // Operand reads run a fixed distance ahead of the math (QD k-step pairs for QK, PD steps
+      // for PV), each step fenced with sched_barrier so that the compiler keeps that order instead
+      // of waiting for every read right before its MFMA; the first PV reads are issued before the
+      // softmax, which does not need them.
+      constexpr int QD = FP8 ? 2 : 1, PD = FP8 ? 4 : 2;
+      auto qk_read = [&](int p, u32x4_t(&dst)[2]) {  // k-step pair p of this lane's token row
+        dst[0] = *reinterpret_cast<const u32x4_t*>(tile + qk_off + 32 * ELT * p);
+        if (!FP8) dst[1] = *reinterpret_cast<const u32x4_t*>(tile + qk_off + 64 * p + 16);
+      };
+      auto pv_read = [&](int i, u32x4_t& dst) {  // PV step i = 2*db + ks: 8 tokens at one value dim
+        const int db = i >> 1, ks = i & 1;
+        const lds_u8* src = lt + pv_off + ks * 16 * C::RS + 32 * ELT * db;
+        if (FP8) {
+          const i32x2_t t8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)src);
+          dst[0] = (uint32_t)t8[0];
+          dst[1] = (uint32_t)t8[1];
+        } else {
+          const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)src);
+          const i16x4_t t1 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(src + C::RS));
+          const u32x2_t u0 = __builtin_bit_cast(u32x2_t, t0), u1 = __builtin_bit_cast(u32x2_t, t1);
+          dst = u32x4_t{u0[0], u0[1], u1[0], u1[1]};
+        }
+      };
+
+      // ---- S^T = C q^T over all 576 dims, 36 k-steps
+      u32x4_t qb[QD + 1][2];
+#pragma unroll
+      for (int p = 0; p < QD; ++p) qk_read(p, qb[p]);
+      f32x16_t sc = f32x16_t{};
+#pragma unroll
+      for (int p = 0; p < 18; ++p) {
+        if (p + QD < 18) qk_read(p + QD, qb[(p + QD) % (QD + 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+        const u32x4_t(&raw)[2] = qb[p % (QD + 1)];
+        u32x4_t a0, a1;
+        if (FP8) {
+          const u32x2_t x0 = e4m3x4_to_bf16x4(raw[0][0]), x1 = e4m3x4_to_bf16x4(raw[0][1]);
+          const u32x2_t x2 = e4m3x4_to_bf16x4(raw[0][2]), x3 = e4m3x4_to_bf16x4(raw[0][3]);
+          a0 = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
+          a1 = u32x4_t{x2[0], x2[1], x3[0], x3[1]};
+        } else {
+          a0 = raw[0];
+          a1 = raw[1];
+        }
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0),
+                                                     __builtin_bit_cast(bf16x8_t, qv[2 * p]), sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1),
+                                                     __builtin_bit_cast(bf16x8_t, qv[2 * p + 1]), sc, 0, 0, 0);
       }
-      // ---- online softmax for head n over tokens 16mb + 4q4 + i.  The accumulators stay
-      // referenced to m_run until a tile's max exceeds it by more than kLazy (log2 units):
-      // p <= 2^kLazy meanwhile, exact up to rounding, and the rescale is rare.
-      float x[8];
+      // the scores are read by VALU: keep them in VGPRs, leaving the AGPRs to the 256 accumulators
+      asm volatile("" : "+v"(sc));
+      u32x4_t vb[PD + 1];
+#pragma unroll
+      for (int i = 0; i < PD; ++i) pv_read(i, vb[i]);
+      __builtin_amdgcn_sched_barrier(0);
+
+
+      // ---- online softmax for head n over tokens 8(j/4) + 4hh + j%4
+      float x[16];
       float tmax = -INFINITY;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool valid = tb + 16 * mb + 4 * q4 + i < w1;
-          const float v = valid ? sc[mb][i] * c_log2 : -INFINITY;
-          x[4 * mb + i] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+      for (int j = 0; j < 16; ++j) {
+        const bool valid = 8 * (j >> 2) + 4 * hh + (j & 3) < nv;
+        x[j] = valid ? sc[j] * c_log2 : -INFINITY;
+        tmax = fmaxf(tmax, x[j]);
+      }
       tmax = fmaxf(tmax, shfl_xor(tmax, 32));
       const bool grow = tmax > m_run + kLazy;  // m_run = -inf: any finite tile max grows it
       if (__any(grow)) {
@@ -244,68 +326,91 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
         const float alpha = grow ? exp2f(m_run - m_new) : 1.f;  // m_run = -inf -> 0
         l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < 16; ++db) acc[db] *= alpha;
+        for (int db = 0; db < 16; ++db) {
+          // the accumulators live in AGPRs; the empty asm statements pin that register class around
+          // the multiply, which would otherwise move all 256 of them into VGPRs
+          f32x16_t t = acc[db];
+          asm volatile("" : "+a"(t));
+          f32x16_t u = t * alpha;
+          asm volatile("" : "+v"(u));
+          t = u;
+          asm volatile("" : "+a"(t));
+          acc[db] = t;
+        }
         m_run = m_new;
       }
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
       float psum = 0.f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        x[k] = exp2f(x[k] - m_use);
-        psum += x[k];
+      for (int j = 0; j < 16; ++j) {
+        x[j] = __builtin_amdgcn_exp2f(x[j] - m_use);  // v_exp_f32: weights below 2^-126 flush to 0
+        psum += x[j];
       }
       l_run += psum;
-      const u32x4_t pp = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                          pack_bf16x2(x[6], x[7])};
-      // ---- O^T += V^T P^T, 16 blocks of 16 value dims, A operand by LDS transpose reads
-      __attribute__((address_space(3))) uint8_t* lt = (__attribute__((address_space(3))) uint8_t*)(tile);
+      u32x4_t pp[2];
 #pragma unroll
-      for (int db = 0; db < 16; ++db) {
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pp[ks][e] = pack_bf16x2(x[8 * ks + 2 * e], x[8 * ks + 2 * e + 1]);
+
+      // ---- O^T += V^T P^T, 16 blocks of 32 value dims x 2 k-steps of 16 tokens
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i + PD < 32) pv_read(i + PD, vb[(i + PD) % (PD + 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+        const u32x4_t& raw = vb[i % (PD + 1)];
         u32x4_t vv;
         if (FP8) {
-          const i32x2_t t8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(KVFP8_LDS(i32x2_t, lt + pv_off0 + 16 * db));
-          const u32x2_t lo = e4m3x4_to_bf16x4((uint32_t)t8[0]), hi = e4m3x4_to_bf16x4((uint32_t)t8[1]);
+          const u32x2_t lo = e4m3x4_to_bf16x4(raw[0]), hi = e4m3x4_to_bf16x4(raw[1]);
           vv = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
         } else {
-          const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(KVFP8_LDS(i16x4_t, lt + pv_off0 + 32 * db));
-          const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(KVFP8_LDS(i16x4_t, lt + pv_off1 + 32 * db));
-          const u32x2_t a0 = __builtin_bit_cast(u32x2_t, t0), a1 = __builtin_bit_cast(u32x2_t, t1);
-          vv = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+          vv = raw;
         }
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vv),
-                                                          __builtin_bit_cast(bf16x8_t, pp), acc[db], 0, 0, 0);
+        acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv),
+                                                              __builtin_bit_cast(bf16x8_t, pp[i & 1]), acc[i >> 1], 0,
+                                                              0, 0);
       }
     }
+    vm_wait<0>();  // copies issued past the window's last tile have landed before the buffers are reused
   }
 
-  // ---- write this wave's heads and value half (a page id outside the pool zeroes the request)
+  // ---- write this wave's heads (a page id outside the pool zeroes the request)
   __syncthreads();
-  if (threadIdx.x == 0) s_pid[0] = 0;
+  if (threadIdx.x == 0) s_bad = 0;
   __syncthreads();
-  if (bad) s_pid[0] = 1;
+  if (bad) s_bad = 1;
   __syncthreads();
-  const bool any_bad = s_pid[0] != 0;
+  const bool any_bad = s_bad != 0;
   if (!active) return;
-  l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
   const int h = h0 + n;
+  if (h >= Hq) return;
   const int64_t row = (int64_t)r * Hq + h;
   const float inv = l_run > 0.f ? a.v_scale / l_run : 0.f;
-  const int dv0 = 256 * kh + 4 * q4;
   if (a.num_splits == 1) {
 #pragma unroll
-    for (int db = 0; db < 16; ++db) {
-      const float o0 = any_bad ? 0.f : acc[db][0] * inv, o1 = any_bad ? 0.f : acc[db][1] * inv;
-      const float o2 = any_bad ? 0.f : acc[db][2] * inv, o3 = any_bad ? 0.f : acc[db][3] * inv;
-      const u32x2_t v2 = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-      *reinterpret_cast<u32x2_t*>(&a.out[row * kLV + dv0 + 16 * db]) = v2;
-    }
+    for (int db = 0; db < 16; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d0 = 32 * db + 8 * jg + 4 * hh;
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = any_bad ? 0.f : acc[db][4 * jg + i] * inv;
+        const u32x2_t v2 = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        *reinterpret_cast<u32x2_t*>(&a.out[row * kLV + d0]) = v2;
+      }
   } else {
     const int64_t slot = row * a.num_splits + split;
 #pragma unroll
     for (int db = 0; db < 16; ++db)
-      *reinterpret_cast<f32x4_t*>(&a.o_part[slot * kLV + dv0 + 16 * db]) = acc[db] * inv;
-    if (q4 == 0 && kh == 0) a.lse_part[slot] = any_bad ? NAN : (l_run == 0.f ? -INFINITY : m_run + __log2f(l_run));
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d0 = 32 * db + 8 * jg + 4 * hh;
+        const f32x4_t v4 = {acc[db][4 * jg] * inv, acc[db][4 * jg + 1] * inv, acc[db][4 * jg + 2] * inv,
+                            acc[db][4 * jg + 3] * inv};
+        *reinterpret_cast<f32x4_t*>(&a.o_part[slot * kLV + d0]) = v4;
+      }
+    if (hh == 0) a.lse_part[slot] = any_bad ? NAN : (l_run == 0.f ? -INFINITY : m_run + __log2f(l_run));
   }
 }
 

@@ -48,8 +48,9 @@ hipError_t launch_tag_check(const TagArgs& a, hipStream_t stream) {
 
 // ------------------------------------------------------------------ write path
 // Cloudflare post, section "Quantized KV cache": the cache holds e4m3 instead of bf16.
-// One wave per (token, KV head).  K rows go to the chunk-reordered sub-page block; V goes to
-// the transposed page block, one element per d row.
+// One wave per (token, KV head).  K rows go to the chunk-reordered sub-page block (a latent
+// pool, written with no V pool, is plain row-major); V goes to the transposed page block, one
+// element per d row.
 struct AppendTarget {
   int page, slot;
 };
@@ -79,7 +80,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   for (int d2 = lane; d2 < D / 2; d2 += kWave) {
     const uint32_t w = ksrc[d2];
     // elements 2*d2 and 2*d2+1 share a 16-byte chunk: one 2-element store
-    const int64_t o = k_elem_offset<FP8 ? 1 : 2>(t.page, h, t.slot, 2 * d2, H, S, D);
+    const int64_t o = a.v_pool ? k_elem_offset<FP8 ? 1 : 2>(t.page, h, t.slot, 2 * d2, H, S, D)
+                               : c_elem_offset(t.page, h, t.slot, 2 * d2, H, S, D);
     if (FP8) {
       const float x0 = bf16_bits_to_f32(w & 0xFFFFu) * a.k_inv;
       const float x1 = bf16_bits_to_f32(w >> 16) * a.k_inv;
@@ -177,7 +179,8 @@ __global__ __launch_bounds__(256) void check_append_kernel(TagArgs c, AppendArgs
     const int e = threadIdx.x + 256 * i;
     if (e < nk) {
       const int h = e / (D / 2), d2 = e % (D / 2);
-      const int64_t o = k_elem_offset<FP8 ? 1 : 2>(page, h, slot, 2 * d2, H, S, D);
+      const int64_t o = a.v_pool ? k_elem_offset<FP8 ? 1 : 2>(page, h, slot, 2 * d2, H, S, D)
+                                 : c_elem_offset(page, h, slot, 2 * d2, H, S, D);
       if (FP8) {
         const float x0 = bf16_bits_to_f32(kw[i] & 0xFFFFu) * a.k_inv;
         const float x1 = bf16_bits_to_f32(kw[i] >> 16) * a.k_inv;
@@ -231,7 +234,9 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   T* ko = reinterpret_cast<T*>(a.k_out) + ((int64_t)tok * H + h) * D;
   const T* kp = reinterpret_cast<const T*>(a.k_pool);
   for (int d = lane; d < D; d += kWave)
-    ko[d] = page < 0 ? T(0) : kp[k_elem_offset<sizeof(T)>(page, h, slot, d, H, S, D)];
+    ko[d] = page < 0 ? T(0)
+                     : kp[a.v_pool ? k_elem_offset<sizeof(T)>(page, h, slot, d, H, S, D)
+                                   : c_elem_offset(page, h, slot, d, H, S, D)];
   if (a.v_out == nullptr) return;
   T* vo = reinterpret_cast<T*>(a.v_out) + ((int64_t)tok * H + h) * Dv;
   const T* vp = reinterpret_cast<const T*>(a.v_pool);

@@ -96,6 +96,12 @@ __device__ __forceinline__ int64_t k_elem_offset(int page, int head, int slot, i
   return ((int64_t)page * H + head) * S * D + (int64_t)u * 16 * D + (int64_t)chunk * E + (d % E);
 }
 
+// Element offset of element (page, head, slot, d) of a latent pool (written with no V pool):
+// plain row-major [P][Hkv][S][D], so a tile of consecutive tokens of one page is contiguous.
+__device__ __forceinline__ int64_t c_elem_offset(int page, int head, int slot, int d, int H, int S, int D) {
+  return (((int64_t)page * H + head) * S + slot) * D + d;
+}
+
 template <typename T>
 __device__ __forceinline__ T shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, kWave);

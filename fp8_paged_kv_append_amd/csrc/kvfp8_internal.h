@@ -31,6 +31,7 @@ struct MergeArgs {
   const int32_t* ctx_lens;
   const uint32_t* flags;
   int32_t num_q_heads, v_dim, num_splits, chunk_tokens, max_ctx, pt_stride, page_size;
+  int64_t rows;  // batch * num_q_heads (set by launch_merge)
 };
 
 struct AppendArgs {
@@ -70,7 +71,7 @@ struct TagArgs {
 
 struct LatentArgs {
   const uint16_t* q;          // bf16 [B][Hq][576]
-  const void* pool;           // K-layout pool, one head, 576 wide
+  const void* pool;           // row-major pool [P][S][576]
   const int32_t* page_table;
   const int32_t* ctx_lens;
   const uint32_t* flags;
@@ -88,7 +89,7 @@ constexpr int kAttnTileTokens = 64;
 constexpr int kLatentTileTokens = 32;
 constexpr int kLatentDim = 576;
 constexpr int kLatentVDim = 512;
-constexpr int kLatentHeadsPerBlock = 64;
+constexpr int kLatentHeadsPerBlock = 128;
 
 hipError_t launch_attn_gqa(const AttnArgs& a, bool fp8, int batch, hipStream_t stream);
 hipError_t launch_attn_latent(const LatentArgs& a, bool fp8, hipStream_t stream);

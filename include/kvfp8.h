@@ -42,7 +42,9 @@
  *            ((s*NI + k)*4 + q)*4 + i.  (A wave reading one chunk of four
  *            tokens from each of four pages then reads four contiguous
  *            256-byte runs per instruction.)  D*bytes must be a multiple of 64.
- *    latent  the K-pool layout with one head and D = Dl; no V pool.
+ *    latent  [P][Hkv][S][Dl] row-major (Hkv = 1): a pool written or read with
+ *            no V pool (v_pool NULL) is a latent pool; the tokens of a page
+ *            are consecutive Dl-element rows.
  * Page table: int32 [B][pt_stride]; entry i of request r is the physical page
  * of its tokens [i*S, (i+1)*S).  Entries at or past ceil(L_r/S) are never read.
  * Context length L_r counts the token appended in the current step.
@@ -104,7 +106,7 @@ float kv_scale_from_absmax(uint32_t absmax_bits);
  * OCP E4M3 round-to-nearest-even, |value| > 448 saturating to +-448, NaN ->
  * 0x7F with the input's sign.  kv_append_bf16 copies the bf16 bits.
  *   k_new [N][Hkv][D], v_new [N][Hkv][Dv] (bf16).  v_pool/v_new may both be
- *   NULL (latent cache: only the K-layout pool is written).
+ *   NULL: the pool is then a latent pool (row-major layout above).
  *   abort_flags [B] or NULL (NULL = no-op tracker): tokens of a request whose
  *   flag is non-zero are skipped [T].  Tokens whose request is outside [0,B),
  *   whose position is outside [0, pt_stride*S) or whose page id is outside
@@ -194,8 +196,9 @@ int paged_decode_attn_bf16(const kvfp8_pool_desc* desc, const uint16_t* q, int32
 
 /* ---------------------------------------------------------------- latent (MLA-style) cache  [Q]
  * One cached vector c_t of width Dl = 576 per token, shared by every query
- * head (the pool: K layout, num_kv_heads = 1, head_dim = 576, v_dim = 512,
- * written by kv_append_* with v_pool = v_new = NULL).  For request r, head h:
+ * head (the pool: latent layout, num_kv_heads = 1, head_dim = 576,
+ * v_dim = 512, written by kv_append_* with v_pool = v_new = NULL).  For
+ * request r, head h:
  *   s_t = sm_scale * <q_h, c^_t>,  o_h = sum_t softmax(s)_t c^_t[0:512],
  * with c^ = dec(c) * scale for the FP8 cache (one per-tensor scale) and
  * c^ = c for BF16; fp32 result rounded to bf16.
@@ -220,7 +223,8 @@ int paged_decode_attn_latent_bf16(const kvfp8_pool_desc* desc, const uint16_t* q
  * Read back tokens through the page table: k_out [N][Hkv][D], v_out
  * [N][Hkv][Dv] (v_out NULL for the latent cache) receive the stored
  * elements of token (tok_req[n], tok_pos[n]); a token whose request,
- * position or page is out of range gets zero elements. */
+ * position or page is out of range gets zero elements.  v_pool NULL reads
+ * k_pool as a latent pool. */
 int kv_gather_fp8(const kvfp8_pool_desc* desc, const uint8_t* k_pool, const uint8_t* v_pool,
                   const int32_t* tok_req, const int32_t* tok_pos, int32_t n_tokens,
                   const int32_t* page_table, int32_t batch, int32_t pt_stride, uint8_t* k_out,

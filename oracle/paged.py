@@ -24,8 +24,10 @@ Readings where the pages are silent:
        tokens thus holds, for each k, four 64-byte runs (one per q) of four
        16-byte chunks (one per token).  S must be a multiple of 16 and a
        K row a multiple of 64 bytes.
-  Latent cache (one vector per token shared by all query heads):
-    C: the K layout with one head and D = Dl; no V pool.
+  Latent cache (one vector per token shared by all query heads; a pool
+  written with no V pool):
+    C: [P][Hkv][S][Dl] row-major (Hkv = 1), element (page, head, slot, d);
+       the tokens of a page are consecutive rows.
 * Flags, rewritten on every check (not sticky), uint32 per request:
     bit0 (1) a used entry's page tag differs from the expected tag;
     bit1 (2) a used entry's page id is outside [0, P), or the context needs
@@ -45,7 +47,7 @@ FLAG_BAD_PAGE = 2
 
 
 def k_offset(page, head, slot, d, num_kv_heads, page_size, head_dim, elt_bytes):
-    """Flat element offset of K (or latent) element (page, head, slot, d) in the chunk-reordered block."""
+    """Flat element offset of K element (page, head, slot, d) in the chunk-reordered block."""
     E = 16 // elt_bytes                      # elements per 16-byte chunk
     NI = head_dim * elt_bytes // 64          # chunks per 64-byte slice of a row
     slot = np.asarray(slot, dtype=np.int64)
@@ -57,6 +59,13 @@ def k_offset(page, head, slot, d, num_kv_heads, page_size, head_dim, elt_bytes):
     chunk = ((s * NI + k) * 4 + q) * 4 + i
     block = (np.int64(page) * num_kv_heads + head) * page_size * head_dim
     return block + u * 16 * head_dim + chunk * E + d % E
+
+
+def c_offset(page, head, slot, d, num_kv_heads, page_size, dim):
+    """Flat element offset of latent element (page, head, slot, d): row-major rows of `dim` elements."""
+    slot = np.asarray(slot, dtype=np.int64)
+    d = np.asarray(d, dtype=np.int64)
+    return ((np.int64(page) * num_kv_heads + head) * page_size + slot) * dim + d
 
 
 def v_offset(page, head, slot, d, num_kv_heads, page_size, v_dim):
@@ -126,7 +135,10 @@ def append(k_pool, v_pool, k_new, v_new, tok_req, tok_pos, page_table, num_kv_he
     d = np.arange(D, dtype=np.int64)[None, None, :]
     for a in range(0, idx.size, chunk):
         i, p, s = idx[a:a + chunk], page[a:a + chunk, None, None], slot[a:a + chunk, None, None]
-        k_pool[k_offset(p, h, s, d, H, page_size, D, elt)] = k_new[i]
+        if v_pool is None:
+            k_pool[c_offset(p, h, s, d, H, page_size, D)] = k_new[i]
+        else:
+            k_pool[k_offset(p, h, s, d, H, page_size, D, elt)] = k_new[i]
         if v_pool is not None:
             Dv = v_new.shape[2]
             dv = np.arange(Dv, dtype=np.int64)[None, None, :]
@@ -152,8 +164,12 @@ def gather(k_pool, v_pool, page_table, r, length, num_kv_heads, page_size, head_
     slot = t % page_size
     h = np.arange(num_kv_heads, dtype=np.int64)
     d = np.arange(head_dim, dtype=np.int64)
-    ko = k_offset(page[:, None, None], h[None, :, None], slot[:, None, None], d[None, None, :],
-                  num_kv_heads, page_size, head_dim, k_pool.dtype.itemsize)
+    if v_pool is None:
+        ko = c_offset(page[:, None, None], h[None, :, None], slot[:, None, None], d[None, None, :],
+                      num_kv_heads, page_size, head_dim)
+    else:
+        ko = k_offset(page[:, None, None], h[None, :, None], slot[:, None, None], d[None, None, :],
+                      num_kv_heads, page_size, head_dim, k_pool.dtype.itemsize)
     k = k_pool[ko]
     v = None
     if v_pool is not None:

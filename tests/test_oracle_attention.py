@@ -68,11 +68,12 @@ def test_equal_keys_give_mean_of_values(dtype):
     k_same = np.broadcast_to(k[:1], k.shape).copy()
     req, pos = wl.token_index(lens)
     if dtype == "fp8":
-        paged.append_fp8(st["k_pool"], None, k_same, None, req, pos, st["page_table"], 1, w.page_size,
+        # V is rewritten with its own rows (same codes); a call without the V pool would address a latent pool
+        paged.append_fp8(st["k_pool"], st["v_pool"], k_same, v, req, pos, st["page_table"], 1, w.page_size,
                          st["k_scale"], st["v_scale"])
         vhat = codec.e4m3_decode(codec.quantize_e4m3(v, st["v_scale"])) * np.float64(st["v_scale"])
     else:
-        paged.append(st["k_pool"], None, k_same, None, req, pos, st["page_table"], 1, w.page_size)
+        paged.append(st["k_pool"], st["v_pool"], k_same, v, req, pos, st["page_table"], 1, w.page_size)
         vhat = codec.f64_from_bf16(v)
     o = _attn(st, wl.queries(w))[0]
     ref = vhat[:, 0, :].mean(axis=0)

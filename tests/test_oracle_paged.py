@@ -102,6 +102,30 @@ def test_layout_offsets_by_hand():
     assert paged.v_offset(0, 0, 1, 0, 2, 4, 5) == 1
 
 
+def test_latent_layout_offsets_by_hand():
+    """A latent pool (no V pool) is row-major: element (page 3, slot 5, d 7) of a 576-wide, 16-slot pool
+    sits (3*16 + 5)*576 + 7 = 30535 elements in; a page's tokens are consecutive 576-element rows."""
+    assert paged.c_offset(3, 0, 5, 7, 1, 16, 576) == 30535
+    assert paged.c_offset(0, 0, 0, 0, 1, 64, 576) == 0
+    assert paged.c_offset(2, 0, 63, 575, 1, 64, 576) == 3 * 64 * 576 - 1   # last element of page 2
+    slot, d = np.meshgrid(np.arange(64), np.arange(576), indexing="ij")
+    assert np.array_equal(paged.c_offset(1, 0, slot, d, 1, 64, 576).ravel(), 64 * 576 + np.arange(64 * 576))
+
+
+def test_latent_append_writes_contiguous_rows():
+    """Appending into a latent pool (v_pool None) writes each token's whole row at row-major offsets."""
+    S, D, P = 16, 576, 4
+    cp = np.zeros(P * S * D, dtype=np.uint8)
+    pt = np.array([[3, 1]], dtype=np.int32)
+    rows = (np.arange(2 * D) % 251 + 1).astype(np.uint8).reshape(2, 1, D)
+    paged.append(cp, None, rows, None, [0, 0], [2, 17], pt, 1, S)   # slot 2 of page 3, slot 1 of page 1
+    assert np.array_equal(cp[(3 * S + 2) * D:(3 * S + 3) * D], rows[0, 0])
+    assert np.array_equal(cp[(1 * S + 1) * D:(1 * S + 2) * D], rows[1, 0])
+    assert cp.astype(np.int64).sum() == rows.astype(np.int64).sum()
+    k, v = paged.gather(cp, None, pt, 0, 18, 1, S, D, 0)
+    assert v is None and np.array_equal(k[17, 0], rows[1, 0]) and np.array_equal(k[2, 0], rows[0, 0])
+
+
 @pytest.mark.parametrize("S,D,elt", [(16, 128, 1), (16, 128, 2), (64, 128, 1), (32, 576, 1), (16, 576, 2), (16, 64, 1)])
 def test_k_layout_is_a_bijection_per_block(S, D, elt):
     slot, d = np.meshgrid(np.arange(S), np.arange(D), indexing="ij")
