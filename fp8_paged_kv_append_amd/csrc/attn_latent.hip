@@ -61,7 +61,7 @@ struct LCfg {
   static constexpr int NINST = (kLT * SLOTS + 63) / 64;           // 1 KiB copies per tile
   static constexpr int NPW = (NINST + kLWaves - 1) / kLWaves;     // copies per wave per tile
   static constexpr int BUF = NPW * kLWaves * 1024;                // bytes per tile buffer
-  static constexpr int NBUF = FP8 ? 4 : 3;                        // tile buffers
+  static constexpr int NBUF = FP8 ? 5 : 3;                        // tile buffers
 };
 
 // LDS row of tile token t.  FP8: the 8 tokens a PV transpose read of one half-wave
@@ -107,6 +107,7 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   constexpr int ELT = C::ELT;
   __shared__ __align__(1024) uint8_t s_tile[C::NBUF * C::BUF];
   __shared__ int s_pid[kLPidWin];
+  __shared__ f32x4_t s_sc[kLWaves][4][kWave];  // each wave's next-tile scores, parked across PV
   __shared__ int s_bad;
 
   // XCD-aware block decode: head groups of one (request, split) unit are 8 ids apart
@@ -175,16 +176,15 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   }
   // this lane's share of each tile copy: copy k of the wave fills LDS slots [64j, 64j+64),
   // j = wave*NPW + k; slot 64j+lane is chunk c of LDS row rho = token lat_tok(rho), or padding
-  // two 16-bit entries per register: (token << 8) | chunk, or 0xFFFF for a padding slot
-  uint32_t cp_tc[(C::NPW + 1) / 2];
-#pragma unroll
-  for (int k = 0; k < (C::NPW + 1) / 2; ++k) cp_tc[k] = 0xFFFFFFFFu;
+  // each entry: (token << 16) | byte offset of the chunk inside its 16-token half (token & 15
+  // rows in), or 0 for a padding slot (token 0, chunk 0: a harmless re-read)
+  uint32_t cp_tc[C::NPW];
 #pragma unroll
   for (int k = 0; k < C::NPW; ++k) {
     const int slot = 64 * (wave * C::NPW + k) + lane;
     const int rho = slot / C::SLOTS, c = slot % C::SLOTS;
-    const uint32_t e = (rho < kLT && c < C::CH) ? (uint32_t)((lat_tok<FP8>(rho) << 8) | c) : 0xFFFFu;
-    cp_tc[k >> 1] = (k & 1) ? ((cp_tc[k >> 1] & 0xFFFFu) | (e << 16)) : ((cp_tc[k >> 1] & 0xFFFF0000u) | e);
+    const int tok = lat_tok<FP8>(rho);
+    cp_tc[k] = (rho < kLT && c < C::CH) ? (uint32_t)((tok << 16) | ((tok & 15) * C::ROWB + 16 * c)) : 0u;
   }
 
   const int32_t* pt = a.page_table + (int64_t)r * a.pt_stride;
@@ -232,92 +232,100 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
       const uint32_t dst = (uint32_t)(uintptr_t)((lds_u8*)(s_tile + bi * C::BUF) + 1024 * wave * C::NPW);
 #pragma unroll
       for (int k = 0; k < C::NPW; ++k) {
-        const int tc = (int)((cp_tc[k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
-        const int tok = tc >> 8;
-        const bool ok = tc != 0xFFFF && tok < nv;
-        const int tt = ok ? tok : 0, cc = ok ? (tc & 255) : 0;
-        const uint8_t* src = (tt >= 16 ? base1 : base0) + (tt & 15) * C::ROWB + 16 * cc;
+        const uint32_t tc = cp_tc[k];
+        const int tok = (int)(tc >> 16);
+        const uint32_t off = tok < nv ? (tc & 0xFFFFu) : 0u;  // past the end: the tile's first row
+        const uint8_t* src = (tok < nv && tok >= 16 ? base1 : base0) + off;
         lds_copy16(src, dst + 1024 * k);
       }
     };
 
+    // Tiles are software-pipelined by one: iteration t publishes tile t+1 and computes its scores
+    // (QK MFMAs) while tile t's exponentials run between them, then accumulates tile t (PV).  The
+    // ring holds tile t (PV), tile t+1 (QK) and NBUF-2 tiles whose copies are in flight.
+    constexpr int QD = FP8 ? 3 : 1, PD = FP8 ? 4 : 2;  // operand reads ahead of the math
+    auto qk_read = [&](const uint8_t* tile, int p, u32x4_t(&dst)[2]) {  // k-step pair p of this lane's row
+      dst[0] = *reinterpret_cast<const u32x4_t*>(tile + qk_off + 32 * ELT * p);
+      if (!FP8) dst[1] = *reinterpret_cast<const u32x4_t*>(tile + qk_off + 64 * p + 16);
+    };
+    auto qk_cvt = [&](const u32x4_t(&raw)[2], u32x4_t(&op)[2]) {
+      if (FP8) {
+        const u32x2_t x0 = e4m3x4_to_bf16x4(raw[0][0]), x1 = e4m3x4_to_bf16x4(raw[0][1]);
+        const u32x2_t x2 = e4m3x4_to_bf16x4(raw[0][2]), x3 = e4m3x4_to_bf16x4(raw[0][3]);
+        op[0] = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
+        op[1] = u32x4_t{x2[0], x2[1], x3[0], x3[1]};
+      } else {
+        op[0] = raw[0];
+        op[1] = raw[1];
+      }
+    };
+    auto pv_read = [&](const lds_u8* lt, int i, u32x4_t& dst) {  // PV step i = 16*ks + db
+      const int db = i & 15, ks = i >> 4;
+      const lds_u8* src = lt + pv_off + ks * 16 * C::RS + 32 * ELT * db;
+      if (FP8) {
+        const i32x2_t t8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)src);
+        dst[0] = (uint32_t)t8[0];
+        dst[1] = (uint32_t)t8[1];
+      } else {
+        const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)src);
+        const i16x4_t t1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(src + C::RS));
+        const u32x2_t u0 = __builtin_bit_cast(u32x2_t, t0), u1 = __builtin_bit_cast(u32x2_t, t1);
+        dst = u32x4_t{u0[0], u0[1], u1[0], u1[1]};
+      }
+    };
+    auto pv_cvt = [&](const u32x4_t& raw) {
+      if (FP8) {
+        const u32x2_t lo = e4m3x4_to_bf16x4(raw[0]), hi = e4m3x4_to_bf16x4(raw[1]);
+        return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      }
+      return raw;
+    };
+
 #pragma unroll
-    for (int t = 0; t < C::NBUF - 1; ++t) copy_tile(t, t);
-    for (int t = 0; t < ntile; ++t) {
-      vm_wait<C::NPW * (C::NBUF - 2)>();  // this wave's copies of tile t have landed
+    for (int t = 0; t < C::NBUF - 2; ++t) copy_tile(t, t);
+    for (int t = -1; t < ntile; ++t) {
+      vm_wait<C::NPW * (C::NBUF - 3)>();  // this wave's copies of tile t+1 have landed
       __syncthreads();                    // everyone's have; everyone is done with tile t-1
       copy_tile(t + C::NBUF - 1, (t + C::NBUF - 1) % C::NBUF);
       if (!active) continue;
-      const uint8_t* tile = s_tile + (t % C::NBUF) * C::BUF;
-      const lds_u8* lt = (const lds_u8*)tile;
-      const int nv = w1 - (w0 + t * kLT);  // valid tokens of this tile (may exceed 32)
+      const bool has_cur = t >= 0;
+      // buffer offsets as opaque scalars: every LDS read is then base + lane offset + immediate,
+      // rather than one precomputed address per ring slot and step
+      uint32_t off_n = (uint32_t)(((t + 1) % C::NBUF) * C::BUF), off_c = (uint32_t)(((t + C::NBUF) % C::NBUF) * C::BUF);
+      asm volatile("" : "+s"(off_n), "+s"(off_c));
+      const uint8_t* tile_n = s_tile + off_n;
+      const lds_u8* lt_c = (const lds_u8*)(s_tile + off_c);
+      const int nv = w1 - (w0 + t * kLT);  // valid tokens of tile t (may exceed 32)
 
-      // Operand reads run a fixed distance ahead of the math (QD k-step pairs for QK, PD steps
-      // for PV), each step fenced with sched_barrier so that the compiler keeps that order instead
-      // of waiting for every read right before its MFMA; the first PV reads are issued before the
-      // softmax, which does not need them.
-      constexpr int QD = FP8 ? 2 : 1, PD = FP8 ? 4 : 2;
-      auto qk_read = [&](int p, u32x4_t(&dst)[2]) {  // k-step pair p of this lane's token row
-        dst[0] = *reinterpret_cast<const u32x4_t*>(tile + qk_off + 32 * ELT * p);
-        if (!FP8) dst[1] = *reinterpret_cast<const u32x4_t*>(tile + qk_off + 64 * p + 16);
-      };
-      auto pv_read = [&](int i, u32x4_t& dst) {  // PV step i = 2*db + ks: 8 tokens at one value dim
-        const int db = i >> 1, ks = i & 1;
-        const lds_u8* src = lt + pv_off + ks * 16 * C::RS + 32 * ELT * db;
-        if (FP8) {
-          const i32x2_t t8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)src);
-          dst[0] = (uint32_t)t8[0];
-          dst[1] = (uint32_t)t8[1];
-        } else {
-          const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)src);
-          const i16x4_t t1 =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(src + C::RS));
-          const u32x2_t u0 = __builtin_bit_cast(u32x2_t, t0), u1 = __builtin_bit_cast(u32x2_t, t1);
-          dst = u32x4_t{u0[0], u0[1], u1[0], u1[1]};
-        }
-      };
-
-      // ---- S^T = C q^T over all 576 dims, 36 k-steps
-      u32x4_t qb[QD + 1][2];
-#pragma unroll
-      for (int p = 0; p < QD; ++p) qk_read(p, qb[p]);
+      // ---- softmax of tile t, first part: masked scores (log2 domain), tile max, lazy rescale;
+      // the scores of head n are those of tokens 8(j/4) + 4hh + j%4 (computed in iteration t-1)
       f32x16_t sc = f32x16_t{};
+      if (has_cur) {
 #pragma unroll
-      for (int p = 0; p < 18; ++p) {
-        if (p + QD < 18) qk_read(p + QD, qb[(p + QD) % (QD + 1)]);
-        __builtin_amdgcn_sched_barrier(0);
-        const u32x4_t(&raw)[2] = qb[p % (QD + 1)];
-        u32x4_t a0, a1;
-        if (FP8) {
-          const u32x2_t x0 = e4m3x4_to_bf16x4(raw[0][0]), x1 = e4m3x4_to_bf16x4(raw[0][1]);
-          const u32x2_t x2 = e4m3x4_to_bf16x4(raw[0][2]), x3 = e4m3x4_to_bf16x4(raw[0][3]);
-          a0 = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
-          a1 = u32x4_t{x2[0], x2[1], x3[0], x3[1]};
-        } else {
-          a0 = raw[0];
-          a1 = raw[1];
+        for (int k = 0; k < 4; ++k) {
+          const f32x4_t v = s_sc[wave][k][lane];
+          sc[4 * k] = v[0];
+          sc[4 * k + 1] = v[1];
+          sc[4 * k + 2] = v[2];
+          sc[4 * k + 3] = v[3];
         }
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0),
-                                                     __builtin_bit_cast(bf16x8_t, qv[2 * p]), sc, 0, 0, 0);
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1),
-                                                     __builtin_bit_cast(bf16x8_t, qv[2 * p + 1]), sc, 0, 0, 0);
       }
-      // the scores are read by VALU: keep them in VGPRs, leaving the AGPRs to the 256 accumulators
-      asm volatile("" : "+v"(sc));
-      u32x4_t vb[PD + 1];
-#pragma unroll
-      for (int i = 0; i < PD; ++i) pv_read(i, vb[i]);
-      __builtin_amdgcn_sched_barrier(0);
-
-
-      // ---- online softmax for head n over tokens 8(j/4) + 4hh + j%4
       float x[16];
       float tmax = -INFINITY;
+      if (has_cur && nv >= kLT) {  // a full tile: no token to mask
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const bool valid = 8 * (j >> 2) + 4 * hh + (j & 3) < nv;
-        x[j] = valid ? sc[j] * c_log2 : -INFINITY;
-        tmax = fmaxf(tmax, x[j]);
+        for (int j = 0; j < 16; ++j) {
+          x[j] = sc[j] * c_log2;
+          tmax = fmaxf(tmax, x[j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const bool valid = has_cur && 8 * (j >> 2) + 4 * hh + (j & 3) < nv;
+          x[j] = valid ? sc[j] * c_log2 : -INFINITY;
+          tmax = fmaxf(tmax, x[j]);
+        }
       }
       tmax = fmaxf(tmax, shfl_xor(tmax, 32));
       const bool grow = tmax > m_run + kLazy;  // m_run = -inf: any finite tile max grows it
@@ -329,46 +337,76 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
         for (int db = 0; db < 16; ++db) {
           // the accumulators live in AGPRs; the empty asm statements pin that register class around
           // the multiply, which would otherwise move all 256 of them into VGPRs
-          f32x16_t t = acc[db];
-          asm volatile("" : "+a"(t));
-          f32x16_t u = t * alpha;
+          f32x16_t tv = acc[db];
+          asm volatile("" : "+a"(tv));
+          f32x16_t u = tv * alpha;
           asm volatile("" : "+v"(u));
-          t = u;
-          asm volatile("" : "+a"(t));
-          acc[db] = t;
+          tv = u;
+          asm volatile("" : "+a"(tv));
+          acc[db] = tv;
         }
         m_run = m_new;
       }
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      float psum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        x[j] = __builtin_amdgcn_exp2f(x[j] - m_use);  // v_exp_f32: weights below 2^-126 flush to 0
-        psum += x[j];
-      }
-      l_run += psum;
-      u32x4_t pp[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pp[ks][e] = pack_bf16x2(x[8 * ks + 2 * e], x[8 * ks + 2 * e + 1]);
 
-      // ---- O^T += V^T P^T, 16 blocks of 32 value dims x 2 k-steps of 16 tokens
+      // ---- S^T of tile t+1 = C q^T over all 576 dims (36 k-steps; past the last tile the reads
+      // hit a buffer with finite data and the result is unused).  Step p issues the read of pair
+      // p+QD, converts pair p+1 and one of tile t's exponentials while the MFMAs of pair p-1 run,
+      // then issues pair p's MFMAs.
+      float psum = 0.f;
+      u32x4_t qb[QD + 1][2];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (i + PD < 32) pv_read(i + PD, vb[(i + PD) % (PD + 1)]);
-        __builtin_amdgcn_sched_barrier(0);
-        const u32x4_t& raw = vb[i % (PD + 1)];
-        u32x4_t vv;
-        if (FP8) {
-          const u32x2_t lo = e4m3x4_to_bf16x4(raw[0]), hi = e4m3x4_to_bf16x4(raw[1]);
-          vv = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-        } else {
-          vv = raw;
+      for (int p = 0; p < QD; ++p) qk_read(tile_n, p, qb[p]);
+      u32x4_t qop[2][2];
+      qk_cvt(qb[0], qop[0]);
+      f32x16_t sn = f32x16_t{};
+      asm volatile("" : "+v"(sn));
+#pragma unroll
+      for (int p = 0; p < 18; ++p) {
+        if (p + QD < 18) qk_read(tile_n, p + QD, qb[(p + QD) % (QD + 1)]);
+        if (p + 1 < 18) qk_cvt(qb[(p + 1) % (QD + 1)], qop[(p + 1) & 1]);
+        if (p < 16) {
+          x[p] = __builtin_amdgcn_exp2f(x[p] - m_use);  // v_exp_f32: weights below 2^-126 flush to 0
+          psum += x[p];
         }
-        acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv),
-                                                              __builtin_bit_cast(bf16x8_t, pp[i & 1]), acc[i >> 1], 0,
-                                                              0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qop[p & 1][0]),
+                                                     __builtin_bit_cast(bf16x8_t, qv[2 * p]), sn, 0, 0, 0);
+        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qop[p & 1][1]),
+                                                     __builtin_bit_cast(bf16x8_t, qv[2 * p + 1]), sn, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the scores are read by VALU: keep them in VGPRs, leaving the AGPRs to the 256 accumulators;
+      // they wait in LDS while PV runs (the registers are needed there)
+      asm volatile("" : "+v"(sn));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s_sc[wave][k][lane] = f32x4_t{sn[4 * k], sn[4 * k + 1], sn[4 * k + 2], sn[4 * k + 3]};
+
+      if (has_cur) {
+        // ---- O^T += V^T P^T of tile t: 2 k-steps of 16 tokens x 16 blocks of 32 value dims (the
+        // two MFMAs of one accumulator 16 steps apart); step i reads step i+PD and converts step
+        // i+1 while the MFMA of step i-1 runs
+        u32x4_t vb[PD + 1];
+#pragma unroll
+        for (int i = 0; i < PD; ++i) pv_read(lt_c, i, vb[i]);
+        l_run += psum;
+        u32x4_t pp[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pp[ks][e] = pack_bf16x2(x[8 * ks + 2 * e], x[8 * ks + 2 * e + 1]);
+        u32x4_t vop[2];
+        vop[0] = pv_cvt(vb[0]);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          if (i + PD < 32) pv_read(lt_c, i + PD, vb[(i + PD) % (PD + 1)]);
+          if (i + 1 < 32) vop[(i + 1) & 1] = pv_cvt(vb[(i + 1) % (PD + 1)]);
+          __builtin_amdgcn_sched_barrier(0);
+          acc[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vop[i & 1]),
+                                                                __builtin_bit_cast(bf16x8_t, pp[i >> 4]),
+                                                                acc[i & 15], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     vm_wait<0>();  // copies issued past the window's last tile have landed before the buffers are reused
