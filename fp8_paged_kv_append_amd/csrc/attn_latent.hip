@@ -49,6 +49,7 @@ constexpr float kLazy = 8.f;              // log2-domain slack before the accumu
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 template <bool FP8>
@@ -141,25 +142,74 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   if (c0 >= L) return;
   const int c1 = min(L, c0 + chunk);
 
-  // q^T operand: lane (hh, n) holds head h0+n, dims 32p + 16hh + 8x .. +8 as qv[2p + x]
+  // q operand.  BF16 cache (bf16 MFMA): lane (hh, n) holds head h0+n, dims 32p + 16hh + 8x .. +8 as
+  // qv[2p + x].  FP8 cache: QK runs on FP8 MFMAs (v_mfma_f32_32x32x64_f8f6f4) over the cached e4m3 bytes
+  // as stored; q*s, with s a power of two per head that puts max|q*s| in [128, 256), is held as two e4m3
+  // terms hi + lo, lo = e4m3(q*s - hi) (exact for every element within 2^9 of the head's max |q|), and
+  // 1/s joins the score scale.  Lane (hh, n) holds dims 64ks + 32hh + b (b = 0..31) of k-step ks as byte b
+  // of qhi[ks] / qlo[ks].
   u32x4_t qv[36];
-  if (h0 + n < Hq) {
-    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(a.q + ((int64_t)r * Hq + h0 + n) * kLD + 16 * hh);
+  v8i_t qhi[9], qlo[9];
+  float q_unscale = 1.f;
+  const bool q_live = h0 + n < Hq;
+  if constexpr (FP8) {
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(a.q + ((int64_t)r * Hq + h0 + n) * kLD + 32 * hh);
+    float amax = 0.f;
+    if (q_live) {
 #pragma unroll
-    for (int p = 0; p < 18; ++p) {
-      qv[2 * p] = qp[4 * p];
-      qv[2 * p + 1] = qp[4 * p + 1];
+      for (int ks = 0; ks < 9; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4_t w = qp[8 * ks + i];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w[e] & 0xFFFFu)), fabsf(bf16_bits_to_f32(w[e] >> 16))));
+        }
     }
-  } else {
+    amax = fmaxf(amax, shfl_xor(amax, 32));
+    int ex;
+    frexpf(amax, &ex);  // amax < 2^ex
+    const float qs = ldexpf(1.f, 8 - ex);
+    q_unscale = ldexpf(1.f, ex - 8);
 #pragma unroll
-    for (int k = 0; k < 36; ++k) qv[k] = u32x4_t{0, 0, 0, 0};
+    for (int ks = 0; ks < 9; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4_t w = q_live ? qp[8 * ks + i] : u32x4_t{0, 0, 0, 0};  // dims 64ks + 32hh + 8i .. +8
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const float f0 = bf16_bits_to_f32(w[2 * h2] & 0xFFFFu) * qs, f1 = bf16_bits_to_f32(w[2 * h2] >> 16) * qs;
+          const float f2 = bf16_bits_to_f32(w[2 * h2 + 1] & 0xFFFFu) * qs;
+          const float f3 = bf16_bits_to_f32(w[2 * h2 + 1] >> 16) * qs;
+          int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+          hi = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, hi, true);
+          const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false), b1 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+          int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f0 - b0[0], f1 - b0[1], 0, false);
+          lo = __builtin_amdgcn_cvt_pk_fp8_f32(f2 - b1[0], f3 - b1[1], lo, true);
+          qhi[ks][2 * i + h2] = hi;
+          qlo[ks][2 * i + h2] = lo;
+        }
+      }
+  } else {
+    if (q_live) {
+      const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(a.q + ((int64_t)r * Hq + h0 + n) * kLD + 16 * hh);
+#pragma unroll
+      for (int p = 0; p < 18; ++p) {
+        qv[2 * p] = qp[4 * p];
+        qv[2 * p + 1] = qp[4 * p + 1];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 36; ++k) qv[k] = u32x4_t{0, 0, 0, 0};
+    }
   }
 
   // q has landed before any tile copy is in flight: the loop below then carries no waits for it
   vm_wait<0>();
 
   // LDS byte offsets this lane reads, relative to a tile buffer
-  const int qk_off = lat_row<FP8>(n) * C::RS + 16 * hh * ELT;   // + 32*p*ELT per k-step pair
+  // QK row reads: FP8 32 bytes at lat_row(n)*RS + 32hh + 64*ks; BF16 32 bytes at lat_row(n)*RS + 32hh + 64*p
+  const int qk_off = lat_row<FP8>(n) * C::RS + 32 * hh;
   // PV source of k-step ks, read rd: pv_off + ks*16*RS + rd*RS (+ 32*db*ELT per d-block) -- the
   // tokens of k-step 1 are those of k-step 0 plus 16 (LDS rows + 16), and the second BF16 read's
   // tokens are the first's plus 8 (LDS row + 1), under lat_row
@@ -189,7 +239,7 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
 
   const int32_t* pt = a.page_table + (int64_t)r * a.pt_stride;
   const uint8_t* pool = reinterpret_cast<const uint8_t*>(a.pool);
-  const float c_log2 = a.qk_scale_log2;
+  const float c_qk = a.qk_scale_log2 * q_unscale;  // log2-domain score scale (FP8: also undoes q's s)
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t acc[16];
 #pragma unroll
@@ -218,46 +268,47 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
     // lane of every copy loads from inside the pool: tokens past the window end re-read the tile's
     // first row (finite data, weight 0), padding slots and tiles past the end read the first
     // row too, and a page id outside the pool reads the pool's first page (the request is zeroed).
-    auto copy_tile = [&](int t, int bi) {
+    struct CopyTile {
+      const uint8_t* base0;
+      const uint8_t* base1;
+      uint32_t dst;
+      int nv;
+    };
+    auto copy_prep = [&](int t, int bi) {
+      CopyTile ct;
       const int tb = w0 + t * kLT;
       const bool live = t < ntile;
-      const int nv = live ? w1 - tb : 0;
+      ct.nv = live ? w1 - tb : 0;
       const int tb_c = live ? tb : w0;
       // the two 16-token halves of a tile each lie inside one page (tile starts are 32-aligned, S % 16 == 0)
-      const int pid0 = s_pid[tb_c / S - e0];
-      const int pid1 = nv > 16 ? s_pid[(tb_c + 16) / S - e0] : pid0;
-      const uint8_t* base0 = pool + (pid0 >= 0 ? ((int64_t)pid0 * S + tb_c % S) * C::ROWB : 0);
-      const uint8_t* base1 = nv > 16 ? pool + (pid1 >= 0 ? ((int64_t)pid1 * S + (tb_c + 16) % S) * C::ROWB : 0)
-                                     : base0;
-      const uint32_t dst = (uint32_t)(uintptr_t)((lds_u8*)(s_tile + bi * C::BUF) + 1024 * wave * C::NPW);
+      // wave-uniform: kept in SGPRs, so the copy state costs no VGPRs across QK and PV
+      const int pid0 = __builtin_amdgcn_readfirstlane(s_pid[tb_c / S - e0]);
+      const int pid1 = ct.nv > 16 ? __builtin_amdgcn_readfirstlane(s_pid[(tb_c + 16) / S - e0]) : pid0;
+      ct.base0 = pool + (pid0 >= 0 ? ((int64_t)pid0 * S + tb_c % S) * C::ROWB : 0);
+      ct.base1 = ct.nv > 16 ? pool + (pid1 >= 0 ? ((int64_t)pid1 * S + (tb_c + 16) % S) * C::ROWB : 0) : ct.base0;
+      ct.dst = (uint32_t)(uintptr_t)((lds_u8*)(s_tile + bi * C::BUF) + 1024 * wave * C::NPW);
+      return ct;
+    };
+    auto copy_one = [&](const CopyTile& ct, int k) {
+      const uint32_t tc = cp_tc[k];
+      const int tok = (int)(tc >> 16);
+      const uint32_t off = tok < ct.nv ? (tc & 0xFFFFu) : 0u;  // past the end: the tile's first row
+      const uint8_t* src = (tok < ct.nv && tok >= 16 ? ct.base1 : ct.base0) + off;
+      lds_copy16(src, ct.dst + 1024 * k);
+    };
+    auto copy_tile = [&](int t, int bi) {
+      const CopyTile ct = copy_prep(t, bi);
 #pragma unroll
-      for (int k = 0; k < C::NPW; ++k) {
-        const uint32_t tc = cp_tc[k];
-        const int tok = (int)(tc >> 16);
-        const uint32_t off = tok < nv ? (tc & 0xFFFFu) : 0u;  // past the end: the tile's first row
-        const uint8_t* src = (tok < nv && tok >= 16 ? base1 : base0) + off;
-        lds_copy16(src, dst + 1024 * k);
-      }
+      for (int k = 0; k < C::NPW; ++k) copy_one(ct, k);
     };
 
     // Tiles are software-pipelined by one: iteration t publishes tile t+1 and computes its scores
     // (QK MFMAs) while tile t's exponentials run between them, then accumulates tile t (PV).  The
     // ring holds tile t (PV), tile t+1 (QK) and NBUF-2 tiles whose copies are in flight.
-    constexpr int QD = FP8 ? 3 : 1, PD = FP8 ? 4 : 2;  // operand reads ahead of the math
-    auto qk_read = [&](const uint8_t* tile, int p, u32x4_t(&dst)[2]) {  // k-step pair p of this lane's row
-      dst[0] = *reinterpret_cast<const u32x4_t*>(tile + qk_off + 32 * ELT * p);
-      if (!FP8) dst[1] = *reinterpret_cast<const u32x4_t*>(tile + qk_off + 64 * p + 16);
-    };
-    auto qk_cvt = [&](const u32x4_t(&raw)[2], u32x4_t(&op)[2]) {
-      if (FP8) {
-        const u32x2_t x0 = e4m3x4_to_bf16x4(raw[0][0]), x1 = e4m3x4_to_bf16x4(raw[0][1]);
-        const u32x2_t x2 = e4m3x4_to_bf16x4(raw[0][2]), x3 = e4m3x4_to_bf16x4(raw[0][3]);
-        op[0] = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
-        op[1] = u32x4_t{x2[0], x2[1], x3[0], x3[1]};
-      } else {
-        op[0] = raw[0];
-        op[1] = raw[1];
-      }
+    constexpr int QD = FP8 ? 1 : 1, PD = FP8 ? 4 : 2;  // operand reads ahead of the math
+    auto qk_read = [&](const uint8_t* tile, int p, u32x4_t(&dst)[2]) {  // 32 bytes of this lane's row
+      dst[0] = *reinterpret_cast<const u32x4_t*>(tile + qk_off + 64 * p);
+      dst[1] = *reinterpret_cast<const u32x4_t*>(tile + qk_off + 64 * p + 16);
     };
     auto pv_read = [&](const lds_u8* lt, int i, u32x4_t& dst) {  // PV step i = 16*ks + db
       const int db = i & 15, ks = i >> 4;
@@ -312,21 +363,19 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
         }
       }
       float x[16];
-      float tmax = -INFINITY;
       if (has_cur && nv >= kLT) {  // a full tile: no token to mask
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          x[j] = sc[j] * c_log2;
-          tmax = fmaxf(tmax, x[j]);
-        }
+        for (int j = 0; j < 16; ++j) x[j] = sc[j] * c_qk;
       } else {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const bool valid = has_cur && 8 * (j >> 2) + 4 * hh + (j & 3) < nv;
-          x[j] = valid ? sc[j] * c_log2 : -INFINITY;
-          tmax = fmaxf(tmax, x[j]);
+          x[j] = valid ? sc[j] * c_qk : -INFINITY;
         }
       }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, x[j]);
       tmax = fmaxf(tmax, shfl_xor(tmax, 32));
       const bool grow = tmax > m_run + kLazy;  // m_run = -inf: any finite tile max grows it
       if (__any(grow)) {
@@ -349,32 +398,50 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
       }
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
-      // ---- S^T of tile t+1 = C q^T over all 576 dims (36 k-steps; past the last tile the reads
-      // hit a buffer with finite data and the result is unused).  Step p issues the read of pair
-      // p+QD, converts pair p+1 and one of tile t's exponentials while the MFMAs of pair p-1 run,
-      // then issues pair p's MFMAs.
+      // ---- S^T of tile t+1 = C q^T over all 576 dims (past the last tile the reads hit a buffer with
+      // finite data and the result is unused).  Step p issues the read QD steps ahead and one or two
+      // of tile t's exponentials while the MFMAs of step p-1 run, then issues step p's MFMAs.
       float psum = 0.f;
       u32x4_t qb[QD + 1][2];
 #pragma unroll
       for (int p = 0; p < QD; ++p) qk_read(tile_n, p, qb[p]);
-      u32x4_t qop[2][2];
-      qk_cvt(qb[0], qop[0]);
       f32x16_t sn = f32x16_t{};
       asm volatile("" : "+v"(sn));
+      if constexpr (FP8) {
+        // 9 k-steps of 64 dims, each two FP8 MFMAs (q hi and lo terms) over the raw cached bytes
 #pragma unroll
-      for (int p = 0; p < 18; ++p) {
-        if (p + QD < 18) qk_read(tile_n, p + QD, qb[(p + QD) % (QD + 1)]);
-        if (p + 1 < 18) qk_cvt(qb[(p + 1) % (QD + 1)], qop[(p + 1) & 1]);
-        if (p < 16) {
-          x[p] = __builtin_amdgcn_exp2f(x[p] - m_use);  // v_exp_f32: weights below 2^-126 flush to 0
-          psum += x[p];
+        for (int p = 0; p < 9; ++p) {
+          if (p + QD < 9) qk_read(tile_n, p + QD, qb[(p + QD) % (QD + 1)]);
+          if (p < 8) {
+            x[2 * p] = __builtin_amdgcn_exp2f(x[2 * p] - m_use);  // v_exp_f32: weights below 2^-126 flush to 0
+            x[2 * p + 1] = __builtin_amdgcn_exp2f(x[2 * p + 1] - m_use);
+            psum += x[2 * p] + x[2 * p + 1];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          const u32x4_t(&kr)[2] = qb[p % (QD + 1)];
+          const v8i_t av = {(int)kr[0][0], (int)kr[0][1], (int)kr[0][2], (int)kr[0][3],
+                            (int)kr[1][0], (int)kr[1][1], (int)kr[1][2], (int)kr[1][3]};
+          sn = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qhi[p], sn, 0, 0, 0, 0, 0, 0);
+          sn = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qlo[p], sn, 0, 0, 0, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qop[p & 1][0]),
-                                                     __builtin_bit_cast(bf16x8_t, qv[2 * p]), sn, 0, 0, 0);
-        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qop[p & 1][1]),
-                                                     __builtin_bit_cast(bf16x8_t, qv[2 * p + 1]), sn, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // 18 pairs of 16-dim k-steps on bf16 MFMAs
+#pragma unroll
+        for (int p = 0; p < 18; ++p) {
+          if (p + QD < 18) qk_read(tile_n, p + QD, qb[(p + QD) % (QD + 1)]);
+          if (p < 16) {
+            x[p] = __builtin_amdgcn_exp2f(x[p] - m_use);  // v_exp_f32: weights below 2^-126 flush to 0
+            psum += x[p];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          const u32x4_t(&raw)[2] = qb[p % (QD + 1)];
+          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, raw[0]),
+                                                       __builtin_bit_cast(bf16x8_t, qv[2 * p]), sn, 0, 0, 0);
+          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, raw[1]),
+                                                       __builtin_bit_cast(bf16x8_t, qv[2 * p + 1]), sn, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       // the scores are read by VALU: keep them in VGPRs, leaving the AGPRs to the 256 accumulators;
       // they wait in LDS while PV runs (the registers are needed there)
