@@ -93,3 +93,28 @@ def test_latent_full_size_sampled(kv_dtype):
         err = float(np.max(attention.row_rel_error(codec.f64_from_bf16(got[r]), ref)))
         note(f"  request {r}: row error {err:.3e}")
         assert err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_latent_query_dynamic_range(kv_dtype):
+    """Queries whose heads span 1e-3..1e3 in scale, with elements far below their head's max (beyond the
+    2^9 range that two e4m3 terms hold exactly in the FP8 path) and one all-zero head: rows still within
+    tolerance of the oracle, and the zero head gives the plain mean of the values."""
+    w = wl.WORKLOADS["latent"].with_(batch=3, num_q_heads=32, num_pages=60, ctx_lo=40, ctx_hi=300)
+    note(f"latent q dynamic range {kv_dtype}")
+    c = Case(w, kv_dtype)
+    c.fill_device()
+    rng = np.random.default_rng(11)
+    qf = wl.bf16_bits_to_f32(c.q).astype(np.float32)                      # [B][Hq][576]
+    head_scale = (10.0 ** rng.uniform(-3, 3, size=(1, w.num_q_heads, 1))).astype(np.float32)
+    tiny = rng.random(qf.shape) < 0.05                                     # 5% of elements ~1e-5 of the rest
+    qf = np.where(tiny, qf * 1e-5, qf) * head_scale
+    qf[:, 7, :] = 0.0
+    c.q = wl.to_bf16_bits(qf)
+    c.dq = dev(c.q)
+    got = _latent_attend(c)
+    _check(c, got)
+    # head 7 has zero scores: uniform weights, the output is the mean of the dequantised value rows
+    for r in range(w.batch):
+        ref = c.oracle_request(r)[7]
+        assert np.max(attention.row_rel_error(codec.f64_from_bf16(got[r, 7])[None], ref[None])) <= ATTN_TOL
