@@ -24,7 +24,8 @@ __all__ = ["KvFp8Error", "PoolDesc", "pool_desc", "kv_absmax_bf16", "kv_scale_fr
            "kv_tag_check_append_bf16", "paged_decode_attn_workspace_bytes",
            "paged_decode_attn_auto_splits", "paged_decode_attn_fp8", "paged_decode_attn_bf16",
            "paged_decode_attn_latent_auto_splits", "paged_decode_attn_latent_fp8",
-           "paged_decode_attn_latent_bf16", "kv_gather_fp8", "kv_gather_bf16", "decode_step", "lib"]
+           "paged_decode_attn_latent_bf16", "kv_gather_fp8", "kv_gather_bf16", "decode_step", "PageAllocator",
+           "lib"]
 
 
 class KvFp8Error(RuntimeError):
@@ -243,6 +244,51 @@ def kv_gather_bf16(desc: PoolDesc, k_pool, v_pool, tok_req, tok_pos, page_table,
         desc, _ptr(k_pool, _BF16, "k_pool"), _ptr(v_pool, _BF16, "v_pool", True), _ptr(tok_req, _I32, "tok_req"),
         _ptr(tok_pos, _I32, "tok_pos"), tok_req.numel(), _ptr(page_table, _I32, "page_table"), B, stride,
         _ptr(k_out, _BF16, "k_out"), _ptr(v_out, _BF16, "v_out", True), _stream(stream)), "kv_gather_bf16")
+
+
+# ----------------------------------------------------------------------------- page allocator
+
+class PageAllocator:
+    """The library's host-side page allocator (kv_page_alloc_*): a free list over a pool's pages whose
+    tags change each time a page is handed to a new owner.  The state lives in a numpy buffer owned here."""
+
+    def __init__(self, num_pages: int, initial_tags=None):
+        import numpy as np
+        n = lib().kv_page_alloc_state_bytes(num_pages)
+        if n == 0:
+            raise KvFp8Error(-2, "kv_page_alloc_state_bytes")
+        self.num_pages = num_pages
+        self._state = np.zeros((n + 3) // 4, dtype=np.uint32)
+        tags = None if initial_tags is None else np.ascontiguousarray(initial_tags, dtype=np.uint32)
+        if tags is not None and tags.shape != (num_pages,):
+            raise ValueError("initial_tags must have one entry per page")
+        _check(lib().kv_page_alloc_init(self._state.ctypes.data, self._state.nbytes, num_pages,
+                                        None if tags is None else tags.ctypes.data), "kv_page_alloc_init")
+        self._keep = tags
+
+    @property
+    def free_count(self) -> int:
+        return int(lib().kv_page_alloc_free_count(self._state.ctypes.data))
+
+    def alloc(self, n: int):
+        """n pages (int32) and their new tags (uint32); raises KvFp8Error(KVFP8_ERR_NOSPACE) if short."""
+        import numpy as np
+        pages = np.empty(n, dtype=np.int32)
+        tags = np.empty(n, dtype=np.uint32)
+        _check(lib().kv_page_alloc(self._state.ctypes.data, n, pages.ctypes.data, tags.ctypes.data), "kv_page_alloc")
+        return pages, tags
+
+    def free(self, pages):
+        import numpy as np
+        pages = np.ascontiguousarray(pages, dtype=np.int32)
+        _check(lib().kv_page_free(self._state.ctypes.data, pages.ctypes.data, pages.size), "kv_page_free")
+
+    def tags(self):
+        """The current tag of every page (host uint32 [P]), for upload to the device tag array."""
+        import numpy as np
+        out = np.empty(self.num_pages, dtype=np.uint32)
+        _check(lib().kv_page_alloc_tags(self._state.ctypes.data, out.ctypes.data), "kv_page_alloc_tags")
+        return out
 
 
 # ----------------------------------------------------------------------------- one decode step

@@ -9,7 +9,9 @@ LIB_PATH = os.path.join(_HERE, "libkvfp8.so")
 
 KVFP8_OK = 0
 STATUS = {0: "KVFP8_OK", -1: "KVFP8_ERR_NULL", -2: "KVFP8_ERR_SHAPE", -3: "KVFP8_ERR_UNSUPPORTED",
-          -4: "KVFP8_ERR_WORKSPACE", -5: "KVFP8_ERR_ALIGN", -6: "KVFP8_ERR_HIP", -7: "KVFP8_ERR_VALUE"}
+          -4: "KVFP8_ERR_WORKSPACE", -5: "KVFP8_ERR_ALIGN", -6: "KVFP8_ERR_HIP", -7: "KVFP8_ERR_VALUE",
+          -8: "KVFP8_ERR_NOSPACE"}
+KVFP8_ERR_NOSPACE = -8
 FLAG_TAG_MISMATCH = 1
 FLAG_BAD_PAGE = 2
 
@@ -48,6 +50,12 @@ PROTOTYPES = {
                                                _p, _sz, _p, _p]),
     "paged_decode_attn_latent_bf16": (C.c_int, [_desc, _p, _i32, _p, _p, _i32, _p, _i32, _i32, _p, _f32, _i32, _p,
                                                 _sz, _p, _p]),
+    "kv_page_alloc_state_bytes": (_sz, [_i32]),
+    "kv_page_alloc_init": (C.c_int, [_p, _sz, _i32, _p]),
+    "kv_page_alloc_free_count": (_i32, [_p]),
+    "kv_page_alloc": (C.c_int, [_p, _i32, _p, _p]),
+    "kv_page_free": (C.c_int, [_p, _p, _i32]),
+    "kv_page_alloc_tags": (C.c_int, [_p, _p]),
     "kv_gather_fp8": (C.c_int, [_desc, _p, _p, _p, _p, _i32, _p, _i32, _i32, _p, _p, _p]),
     "kv_gather_bf16": (C.c_int, [_desc, _p, _p, _p, _p, _i32, _p, _i32, _i32, _p, _p, _p]),
 }

@@ -303,6 +303,7 @@ const char* kvfp8_status_string(int s) {
     case KVFP8_ERR_ALIGN: return "pointer not 16-byte aligned";
     case KVFP8_ERR_HIP: return "HIP launch error";
     case KVFP8_ERR_VALUE: return "invalid scalar argument";
+    case KVFP8_ERR_NOSPACE: return "not enough free pages";
     default: return "unknown status";
   }
 }

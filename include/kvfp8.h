@@ -71,6 +71,7 @@ typedef struct ihipStream_t* hipStream_t;
 #define KVFP8_ERR_ALIGN (-5)       /* a pointer is not 16-byte aligned                 */
 #define KVFP8_ERR_HIP (-6)         /* the HIP runtime reported a launch error          */
 #define KVFP8_ERR_VALUE (-7)       /* a scalar argument is invalid (scale <= 0, NaN)   */
+#define KVFP8_ERR_NOSPACE (-8)     /* the page allocator has fewer free pages than asked */
 
 /* Abort-flag bits written by kv_tag_check (uint32 per request). */
 #define KVFP8_FLAG_TAG_MISMATCH 1u /* a used entry's page tag != the expected tag      */
@@ -218,6 +219,32 @@ int paged_decode_attn_latent_bf16(const kvfp8_pool_desc* desc, const uint16_t* q
                                   const int32_t* ctx_lens, int32_t batch, int32_t max_ctx_len,
                                   const uint32_t* abort_flags, float sm_scale, int32_t num_splits, void* workspace,
                                   size_t workspace_bytes, uint16_t* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------- page allocator  [T]
+ * Host-side free list over the P pages of a pool, holding the page tags of the
+ * integrity check (agentlenshq summary of the Cloudflare post, section "KV Cache
+ * 完整性检查"; xujun.org note, section "一个不能出错的共享缓存": a page's tag
+ * changes when the page gets a new owner, so a request still holding the old
+ * (page, tag) pair fails the next kv_tag_check and is aborted).
+ *   - Each allocation of a page adds 1 (mod 2^32) to its tag; freeing leaves the
+ *     tag as it is.  Pages come off a stack: last freed, first handed out; a
+ *     fresh allocator hands out 0, 1, 2, ... in order.
+ *   - The state is a caller-owned host buffer of kv_page_alloc_state_bytes(P)
+ *     bytes, 4-byte aligned, set up by kv_page_alloc_init (initial_tags: host
+ *     [P] or NULL for zeros).  Host memory only: no HIP call, no allocation,
+ *     not thread-safe.  Copy kv_page_alloc_tags to the device page_tags array
+ *     before the next kv_tag_check.
+ *   - kv_page_alloc: n pages into pages[n] with their new tags in tags[n]
+ *     (tags may be NULL); KVFP8_ERR_NOSPACE (nothing taken) if fewer than n are
+ *     free.  kv_page_free: KVFP8_ERR_VALUE (nothing freed) if any page is out of
+ *     range, not allocated, or listed twice.  kv_page_alloc_free_count returns
+ *     the number of free pages, or -1 for an uninitialised state. */
+size_t kv_page_alloc_state_bytes(int32_t num_pages);
+int kv_page_alloc_init(void* state, size_t state_bytes, int32_t num_pages, const uint32_t* initial_tags);
+int32_t kv_page_alloc_free_count(const void* state);
+int kv_page_alloc(void* state, int32_t n, int32_t* pages, uint32_t* tags);
+int kv_page_free(void* state, const int32_t* pages, int32_t n);
+int kv_page_alloc_tags(const void* state, uint32_t* tags);
 
 /* ---------------------------------------------------------------- test export
  * Read back tokens through the page table: k_out [N][Hkv][D], v_out

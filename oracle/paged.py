@@ -180,6 +180,51 @@ def gather(k_pool, v_pool, page_table, r, length, num_kv_heads, page_size, head_
     return k, v
 
 
+class PageAllocator:
+    """Free list over P pages with the integrity check's page tags (agentlenshq summary, section
+    "KV Cache 完整性检查"; xujun.org note, section "一个不能出错的共享缓存": a page's tag changes when
+    the page is reallocated, so an old holder's (page, tag) pair no longer matches).
+
+    Readings where the pages are silent: the tag is a uint32 generation counter that goes up by one
+    (mod 2**32) each time the page is handed out and is left alone on free; the free list is a stack
+    (last freed, first handed out) that starts as 0, 1, 2, ...; a request that cannot be met takes
+    nothing ("nospace"); a free that names a page out of range, not in use, or twice frees nothing.
+    """
+
+    NOSPACE = "nospace"
+    INVALID = "invalid"
+
+    def __init__(self, num_pages, initial_tags=None):
+        self.tags = (np.zeros(num_pages, dtype=np.uint32) if initial_tags is None
+                     else np.array(initial_tags, dtype=np.uint32))
+        self.free_list = list(range(num_pages - 1, -1, -1))   # last element = next handed out
+        self.in_use = [False] * num_pages
+
+    @property
+    def free_count(self):
+        return len(self.free_list)
+
+    def alloc(self, n):
+        if n > len(self.free_list):
+            return self.NOSPACE
+        pages = []
+        for _ in range(n):
+            p = self.free_list.pop()
+            self.in_use[p] = True
+            self.tags[p] = np.uint32((int(self.tags[p]) + 1) % 2 ** 32)
+            pages.append(p)
+        return np.array(pages, dtype=np.int32), self.tags[pages].copy()
+
+    def free(self, pages):
+        pages = [int(p) for p in pages]
+        if len(set(pages)) != len(pages) or any(p < 0 or p >= len(self.in_use) or not self.in_use[p] for p in pages):
+            return self.INVALID
+        for p in pages:
+            self.in_use[p] = False
+            self.free_list.append(p)
+        return None
+
+
 def kv_bytes(requests, tokens, layers, kv_heads, head_dim, bytes_per_element):
     """KV-cache size as the zdabc.icu article writes it (section "显存为什么会成为长上下文推理的瓶颈"):
     requests x tokens x layers x KV heads x head_dim x 2 (K and V) x bytes per element."""

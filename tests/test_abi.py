@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.kvfp8_abi_version() == 1
-    for s in range(-7, 1):
+    for s in range(-8, 1):
         assert lib.kvfp8_status_string(s).decode() not in ("", "unknown status")
     assert lib.kvfp8_status_string(5) == b"unknown status"
 
