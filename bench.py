@@ -48,6 +48,10 @@ def parse():
     p.add_argument("--no-bf16", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads (GQA batch, long, latent)")
     p.add_argument("--no-sweep", action="store_true", help="skip the batch sweep B = 1, 8, 16, 32, 64")
+    p.add_argument("--no-capacity", action="store_true",
+                   help="skip the fixed-budget admission of 8192-token requests (FP8 vs BF16)")
+    p.add_argument("--capacity-ref-batch", type=int, default=32,
+                   help="the byte budget is what this many 8192-token requests take in the BF16 cache")
     p.add_argument("--flush-mib", type=int, default=512,
                    help="size of the write that evicts the 256 MB Infinity Cache before each flushed step")
     p.add_argument("--cpu-sample", type=int, default=8, help="requests in the CPU oracle sample")
@@ -235,6 +239,37 @@ class DeviceCache:
                     step_ms_p95=float(np.percentile(per.sum(axis=1), 95)))
 
 
+def capacity_admission(kv, w, kvd, budget_bytes, seed=0):
+    """Admit requests of w.ctx_hi tokens through the library's page allocator until it reports too few free
+    pages (KVFP8_ERR_NOSPACE), with the pool sized to a byte budget.
+
+    A page costs its K and V elements plus three uint32 words: its tag, one page-table entry and one
+    expected-tag entry; the FP8 cache also keeps its two float scales.  Before admission the free list is
+    churned into a seeded random order (every page allocated once, then freed in a shuffled order), as in a
+    pool that has been serving for a while.  Returns the pool size, the admitted page table and the tags."""
+    S = w.page_size
+    elt = 1 if kvd == "fp8" else 2
+    page_bytes = S * w.num_kv_heads * (w.head_dim + w.v_dim) * elt + 3 * 4
+    fixed = 2 * 4 if kvd == "fp8" else 0
+    P = int((budget_bytes - fixed) // page_bytes)
+    alloc = kv.PageAllocator(P)
+    pages, _ = alloc.alloc(P)
+    alloc.free(np.random.default_rng(seed).permutation(pages))
+    need = -(-int(w.ctx_hi) // S)
+    rows = []
+    while True:
+        try:
+            p, _ = alloc.alloc(need)
+        except kv.KvFp8Error as e:
+            if e.status != kv.KVFP8_ERR_NOSPACE:
+                raise
+            break
+        rows.append(p)
+    table = np.stack(rows) if rows else np.zeros((0, need), dtype=np.int32)
+    return dict(num_pages=P, page_bytes=page_bytes, admitted=len(rows), pages_left=alloc.free_count,
+                token_capacity=P * S, page_table=table, tags=alloc.tags())
+
+
 def measured_traffic(workload, splits):
     """HBM bytes per launch of the FP8 attention kernel from the committed counter runs, or None when the
     kernel's sources changed since those counters were taken (or they cover another launch shape)."""
@@ -311,12 +346,16 @@ def main():
             a = a.view(np.int32)
         return torch.from_numpy(a).cuda()
 
-    def prepare(w, splits):
-        """Generate one workload's inputs on the host and move them to the device."""
+    def prepare(w, splits, table=None):
+        """Generate one workload's inputs on the host and move them to the device.  table = (page table,
+        page tags) from the page allocator replaces the drawn ones."""
         t = time.perf_counter()
         lens = wl.ctx_lens(w)
-        pt, _ = wl.page_table(w, lens)
-        tags = wl.page_tags(w)
+        if table is None:
+            pt, _ = wl.page_table(w, lens)
+            tags = wl.page_tags(w)
+        else:
+            pt, tags = table
         stale = wl.stale_requests(w)
         exp = wl.expected_tags(w, pt, lens, tags, stale)
         k, v = wl.all_kv(w, lens)
@@ -410,6 +449,39 @@ def main():
             del hb
             torch.cuda.empty_cache()
 
+    capacity = {}
+    if not args.no_capacity and not args.fp8_only_steps:
+        # one byte budget, what the BF16 cache needs for capacity_ref_batch requests of 8192 tokens; each
+        # cache admits requests through the page allocator until it runs out, then its step is timed at
+        # that concurrency (flushed, like the sweep)
+        wc0 = wl.WORKLOADS["sweep_b64"].with_(stale=False)
+        need = -(-int(wc0.ctx_hi) // wc0.page_size)
+        bf16_page = wc0.page_size * wc0.num_kv_heads * (wc0.head_dim + wc0.v_dim) * 2 + 3 * 4
+        budget = args.capacity_ref_batch * need * bf16_page
+        capacity = {"budget_bytes": budget,
+                    "budget": f"BF16 K/V pages plus per-page tag, page-table and expected-tag words of "
+                              f"{args.capacity_ref_batch} requests x {wc0.ctx_hi} tokens",
+                    "admission": "requests of 8192 tokens admitted through kv_page_alloc until KVFP8_ERR_NOSPACE, "
+                                 "free list churned into a seeded random order first"}
+        for kvd in ("fp8", "bf16"):
+            adm = capacity_admission(kv, wc0, kvd, budget)
+            wc = wc0.with_(name=f"capacity_{kvd}", batch=adm["admitted"], num_pages=adm["num_pages"])
+            hc, st_c, el_c, _ = prepare(wc, args.splits, table=(adm["page_table"], adm["tags"]))
+            r = measure(wc, kvd, hc, st_c, el_c, args.steps, 3, flushed=True)
+            capacity[kvd] = {"num_pages": adm["num_pages"], "token_capacity": adm["token_capacity"],
+                             "admitted_requests": adm["admitted"], "pages_left": adm["pages_left"],
+                             "step_us": round(1e3 * r["step_ms"], 2), "attn_us": round(1e3 * r["attn_ms"], 2),
+                             "attn_gbs": round(r["gbs_attn"], 1),
+                             "tokens_per_s": round(adm["admitted"] / (r["step_ms"] * 1e-3), 1),
+                             "splits": r["splits"]}
+            del hc
+            torch.cuda.empty_cache()
+        capacity["fp8_over_bf16"] = {
+            "admitted": round(capacity["fp8"]["admitted_requests"] / capacity["bf16"]["admitted_requests"], 3),
+            "tokens_per_s": round(capacity["fp8"]["tokens_per_s"] / capacity["bf16"]["tokens_per_s"], 3)}
+        capacity["note"] = ("tokens_per_s = admitted requests / flushed step time: one new token per request "
+                            "per step of one attention layer")
+
     extra = {}
     if not args.no_extra and not args.fp8_only_steps:
         for name in ("gqa_batch", "long", "latent"):
@@ -480,6 +552,8 @@ def main():
                                 "note": f"median over steps each preceded by a {args.flush_mib} MiB write"}
     if sweep:
         line["batch_sweep_flushed"] = sweep
+    if capacity:
+        line["capacity_fixed_budget"] = capacity
     if "no_tracker" in f8:
         nt = f8["no_tracker"]
         line["tracker_off"] = {"ms_per_step": round(nt["ms_per_step"], 5),

@@ -17,7 +17,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import FLAG_BAD_PAGE, FLAG_TAG_MISMATCH, PoolDesc  # noqa: F401
+from ._lib import FLAG_BAD_PAGE, FLAG_TAG_MISMATCH, KVFP8_ERR_NOSPACE, PoolDesc  # noqa: F401
 
 __all__ = ["KvFp8Error", "PoolDesc", "pool_desc", "kv_absmax_bf16", "kv_scale_from_absmax", "calibrate_scale",
            "kv_append_fp8", "kv_append_bf16", "kv_tag_check", "kv_tag_check_append_fp8",
