@@ -50,6 +50,13 @@ def parse():
     p.add_argument("--no-sweep", action="store_true", help="skip the batch sweep B = 1, 8, 16, 32, 64")
     p.add_argument("--no-capacity", action="store_true",
                    help="skip the fixed-budget admission of 8192-token requests (FP8 vs BF16)")
+    p.add_argument("--no-layers", action="store_true",
+                   help="skip the whole-step runs over a layer stack (eager and HIP-graph replays)")
+    p.add_argument("--layers", type=int, default=61, help="layers in the layer-stack step")
+    p.add_argument("--layer-batches", default="1,8,64",
+                   help="batch sizes of the layer-stack step (the latent cache runs those of them in {1, 64})")
+    p.add_argument("--layers-only", action="store_true",
+                   help="run only the layer-stack step (skips the headline workload's timing)")
     p.add_argument("--capacity-ref-batch", type=int, default=32,
                    help="the byte budget is what this many 8192-token requests take in the BF16 cache")
     p.add_argument("--flush-mib", type=int, default=512,
@@ -419,14 +426,82 @@ def main():
         torch.cuda.empty_cache()
         return r
 
+    def measure_layers(w, kvd, host, stale, n_layers, steps, warmup):
+        """One decode step over n_layers layers (each layer's pool a copy of layer 0's), as one
+        kv_decode_step_* call: eager, and replayed from captured HIP graphs, tracker on and off."""
+        c = DeviceCache(w, kvd, host, torch, kv, fused=True)
+        kps = torch.empty((n_layers, c.kp.numel()), dtype=c.kp.dtype, device="cuda")
+        kps.copy_(c.kp.unsqueeze(0).expand(n_layers, -1))
+        vps = None
+        if c.vp is not None:
+            vps = torch.empty((n_layers, c.vp.numel()), dtype=c.vp.dtype, device="cuda")
+            vps.copy_(c.vp.unsqueeze(0).expand(n_layers, -1))
+        c.kp = c.vp = None
+        q = c.q.unsqueeze(0).expand(n_layers, *c.q.shape).contiguous()
+        k_new = c.k_new.unsqueeze(0).expand(n_layers, *c.k_new.shape).contiguous()
+        v_new = None if c.v_new is None else c.v_new.unsqueeze(0).expand(n_layers, *c.v_new.shape).contiguous()
+        out = torch.empty((n_layers,) + tuple(c.out.shape), dtype=torch.int16, device="cuda")
+        fp8 = kvd == "fp8"
+        ks = [c.k_scale] * n_layers if fp8 else None
+        vs = [c.v_scale] * n_layers if fp8 and not w.latent else None
+
+        def one(tracker):
+            kv.decode_step_layers(c.desc, kvd, kps, vps, c.pt, c.lens, c.max_ctx, q, k_new, v_new, out,
+                                  page_tags=c.tags if tracker else None, expected_tags=c.exp if tracker else None,
+                                  abort_flags=c.flags if tracker else None, k_scales=ks, v_scales=vs,
+                                  workspace=c.ws)
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(steps):
+                fn()
+            t1.record()
+            torch.cuda.synchronize()
+            return 1e3 * t0.elapsed_time(t1) / steps
+
+        res = {"eager_us": timed(lambda: one(True))}
+        for tracker in (True, False):
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                one(tracker)
+            torch.cuda.current_stream().wait_stream(side)
+            with torch.cuda.graph(g):
+                one(tracker)
+            res["graph_us" if tracker else "graph_no_tracker_us"] = timed(g.replay)
+            del g
+        flags = c.flags.cpu().numpy().view(np.uint32)
+        assert np.flatnonzero(flags).tolist() == stale.tolist(), "abort flags differ from the planted stale set"
+        r = {k_: round(v_, 2) for k_, v_ in res.items()}
+        r["layers"] = n_layers
+        r["per_layer_us"] = round(res["graph_us"] / n_layers, 2)
+        r["steps_per_s"] = round(1e6 / res["graph_us"], 1)
+        r["tokens_per_s"] = round((w.batch - len(stale)) * 1e6 / res["graph_us"], 1)
+        r["check_overhead_pct"] = round(100 * (res["graph_us"] / res["graph_no_tracker_us"] - 1), 2)
+        r["splits"] = c.splits
+        log(f"{w.name} {kvd} x{n_layers} layers: " + json.dumps(r))
+        del c, kps, vps, q, k_new, v_new, out
+        torch.cuda.empty_cache()
+        return r
+
     w = wl.WORKLOADS[args.workload]
-    log(f"workload {w}")
-    host, stale, kv_elems, flops = prepare(w, args.splits)
     results = {}
-    for kvd in (["fp8"] if (args.no_bf16 or args.fp8_only_steps) else ["fp8", "bf16"]):
-        results[kvd] = measure(w, kvd, host, stale, kv_elems, args.steps, args.warmup)
-    del host
-    torch.cuda.empty_cache()
+    if args.layers_only:
+        args.no_sweep = args.no_capacity = args.no_extra = args.no_cpu_baseline = True
+        args.no_layers = False
+    else:
+        log(f"workload {w}")
+        host, stale, kv_elems, flops = prepare(w, args.splits)
+        for kvd in (["fp8"] if (args.no_bf16 or args.fp8_only_steps) else ["fp8", "bf16"]):
+            results[kvd] = measure(w, kvd, host, stale, kv_elems, args.steps, args.warmup)
+        del host
+        torch.cuda.empty_cache()
 
     sweep = {}
     if not args.no_sweep and not args.fp8_only_steps:
@@ -482,6 +557,32 @@ def main():
         capacity["note"] = ("tokens_per_s = admitted requests / flushed step time: one new token per request "
                             "per step of one attention layer")
 
+    layer_runs = {}
+    if not args.no_layers and not args.fp8_only_steps:
+        # the attention part of a whole decode step: args.layers layers sharing one page table and tag set
+        # (kv_decode_step_*: one check, then each layer's write + attention), timed eagerly (one library
+        # call per step) and as replays of a captured HIP graph, with the tracker on and off
+        n_l = args.layers
+        lb = [int(x) for x in args.layer_batches.split(",") if x]
+        for wname, batches in (("sweep_b64", lb), ("latent", [b for b in lb if b in (1, 64)])):
+            for b in batches:
+                base = wl.WORKLOADS[wname]
+                # no stale tags here: with the tracker on an aborted request would skip its work, which is
+                # not the check's cost
+                wb = base.with_(name=f"{wname}_layers_b{b}", batch=b,
+                                num_pages=b * (-(-int(base.ctx_hi) // base.page_size)), stale=False)
+                hb, st_b, el_b, _ = prepare(wb, 0)
+                e = {}
+                for kvd in ("fp8", "bf16"):
+                    r = measure_layers(wb, kvd, hb, st_b, n_l, max(10, args.steps // 2), 3)
+                    r["kv_gb_per_s"] = round(el_b * (1 if kvd == "fp8" else 2) * n_l / (r["graph_us"] * 1e-6) / 1e9, 1)
+                    e[kvd] = r
+                e["fp8_speedup_graph"] = round(e["bf16"]["graph_us"] / e["fp8"]["graph_us"], 3)
+                e["stale_requests"] = len(st_b)
+                layer_runs[f"{wname}_B{b}"] = e
+                del hb
+                torch.cuda.empty_cache()
+
     extra = {}
     if not args.no_extra and not args.fp8_only_steps:
         for name in ("gqa_batch", "long", "latent"):
@@ -506,6 +607,10 @@ def main():
             del he
             torch.cuda.empty_cache()
 
+    if args.layers_only:
+        print(json.dumps({"metric": "decode steps/s over a layer stack (one GPU)", "n_gpus": 1, "steps": args.steps,
+                          "layer_stack_step": layer_runs}), flush=True)
+        return
     f8 = results["fp8"]
     line = {
         "metric": METRIC,
@@ -554,6 +659,12 @@ def main():
         line["batch_sweep_flushed"] = sweep
     if capacity:
         line["capacity_fixed_budget"] = capacity
+    if layer_runs:
+        line["layer_stack_step"] = layer_runs | {
+            "note": f"one decode step over {args.layers} layers sharing one page table and tag set "
+                    "(kv_decode_step_*: the tag check once, fused with layer 0's write, then each layer's write "
+                    "and attention); graph_us = replay of a captured HIP graph of the whole step, eager_us = one "
+                    "library call per step; tokens_per_s = non-aborted requests x steps/s"}
     if "no_tracker" in f8:
         nt = f8["no_tracker"]
         line["tracker_off"] = {"ms_per_step": round(nt["ms_per_step"], 5),

@@ -17,14 +17,14 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import FLAG_BAD_PAGE, FLAG_TAG_MISMATCH, KVFP8_ERR_NOSPACE, PoolDesc  # noqa: F401
+from ._lib import FLAG_BAD_PAGE, FLAG_TAG_MISMATCH, KVFP8_ERR_NOSPACE, LayerStack, PoolDesc  # noqa: F401
 
 __all__ = ["KvFp8Error", "PoolDesc", "pool_desc", "kv_absmax_bf16", "kv_scale_from_absmax", "calibrate_scale",
            "kv_append_fp8", "kv_append_bf16", "kv_tag_check", "kv_tag_check_append_fp8",
            "kv_tag_check_append_bf16", "paged_decode_attn_workspace_bytes",
            "paged_decode_attn_auto_splits", "paged_decode_attn_fp8", "paged_decode_attn_bf16",
            "paged_decode_attn_latent_auto_splits", "paged_decode_attn_latent_fp8",
-           "paged_decode_attn_latent_bf16", "kv_gather_fp8", "kv_gather_bf16", "decode_step", "PageAllocator",
+           "paged_decode_attn_latent_bf16", "kv_gather_fp8", "kv_gather_bf16", "decode_step", "decode_step_layers", "PageAllocator",
            "lib"]
 
 
@@ -157,6 +157,58 @@ def paged_decode_attn_workspace_bytes(batch, num_q_heads, v_dim, num_splits) -> 
 
 def paged_decode_attn_auto_splits(batch, num_kv_heads, max_ctx_len) -> int:
     return int(lib().paged_decode_attn_auto_splits(int(batch), int(num_kv_heads), int(max_ctx_len)))
+
+
+def decode_step_layers(desc: PoolDesc, kv_dtype: str, k_pools, v_pools, page_table, ctx_lens, max_ctx_len: int,
+                       q, k_new, v_new, out, *, page_tags=None, expected_tags=None, abort_flags=None,
+                       k_scales=None, v_scales=None, sm_scale: Optional[float] = None, num_splits: int = 0,
+                       workspace=None, stream=None):
+    """One decode step over a stack of layers sharing the page table, tags and flags (kv_decode_step_*):
+    the tag check once, fused with layer 0's write, then each layer's write and attention in stream order.
+
+    k_pools/v_pools: [layers][pool elements] (v_pools None: the latent cache, v_new None too);
+    q [layers][B][Hq][D]; k_new/v_new [layers][B][Hkv][D|Dv]; out [layers][B][Hq][Dv];
+    k_scales/v_scales: per-layer floats (FP8).  page_tags None = no-op tracker."""
+    import numpy as np
+    if kv_dtype not in ("fp8", "bf16"):
+        raise ValueError(f"kv_dtype {kv_dtype!r}")
+    fp8 = kv_dtype == "fp8"
+    pool_t = _U8 if fp8 else _BF16
+    n_layers, B, Hq, D = q.shape
+    latent = v_pools is None
+    for name, t in (("k_pools", k_pools), ("v_pools", v_pools), ("k_new", k_new), ("v_new", v_new), ("out", out)):
+        if t is not None and t.shape[0] != n_layers:
+            raise ValueError(f"{name}: {t.shape[0]} layers, q has {n_layers}")
+    Hkv, Dk, Dv = desc.num_kv_heads, desc.head_dim, desc.v_dim
+    if D != Dk or k_new.numel() != n_layers * B * Hkv * Dk or out.numel() != n_layers * B * Hq * Dv or (
+            not latent and (v_new is None or v_new.numel() != n_layers * B * Hkv * Dv)):
+        raise ValueError("q, k_new, v_new and out must be [layers][B][heads][dim] stacks of the descriptor's shape")
+    if page_table.shape[0] != B or ctx_lens.numel() != B:
+        raise ValueError("page_table and ctx_lens need one row per request")
+    slots = desc.num_pages * desc.page_size * desc.num_kv_heads
+    if k_pools.numel() != n_layers * slots * desc.head_dim or (
+            not latent and v_pools.numel() != n_layers * slots * desc.v_dim):
+        raise ValueError("each layer's pool must hold exactly the pool the descriptor describes")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    ks = vs = None
+    if fp8:
+        if k_scales is None or (not latent and v_scales is None):
+            raise ValueError("the FP8 cache needs per-layer scales")
+        ks = np.ascontiguousarray(np.asarray(k_scales, dtype=np.float32).reshape(-1))
+        vs = None if latent else np.ascontiguousarray(np.asarray(v_scales, dtype=np.float32).reshape(-1))
+        if ks.size != n_layers or (vs is not None and vs.size != n_layers):
+            raise ValueError("one K (and V) scale per layer")
+    stack = LayerStack(n_layers, _ptr(k_pools, pool_t, "k_pools"), _ptr(v_pools, pool_t, "v_pools", True),
+                       _ptr(q, _BF16, "q"), _ptr(k_new, _BF16, "k_new"), _ptr(v_new, _BF16, "v_new", True),
+                       None if ks is None else ks.ctypes.data, None if vs is None else vs.ctypes.data,
+                       _ptr(out, _BF16, "out"))
+    ws, wsb = _ws(workspace)
+    f = lib().kv_decode_step_fp8 if fp8 else lib().kv_decode_step_bf16
+    _check(f(desc, stack, Hq, _ptr(page_table, _I32, "page_table"), page_table.shape[1],
+             _ptr(ctx_lens, _I32, "ctx_lens"), B, int(max_ctx_len), _ptr(page_tags, _U32, "page_tags", True),
+             _ptr(expected_tags, _U32, "expected_tags", True), _ptr(abort_flags, _U32, "abort_flags", True),
+             float(sm_scale), int(num_splits), ws, wsb, _stream(stream)), f"kv_decode_step_{kv_dtype}")
 
 
 def _ws(workspace):

@@ -21,6 +21,12 @@ class PoolDesc(C.Structure):
                 ("head_dim", C.c_int32), ("v_dim", C.c_int32)]
 
 
+class LayerStack(C.Structure):
+    _fields_ = [("num_layers", C.c_int32), ("k_pools", C.c_void_p), ("v_pools", C.c_void_p), ("q", C.c_void_p),
+                ("k_new", C.c_void_p), ("v_new", C.c_void_p), ("k_scales", C.c_void_p), ("v_scales", C.c_void_p),
+                ("out", C.c_void_p)]
+
+
 _p = C.c_void_p
 _i32 = C.c_int32
 _i64 = C.c_int64
@@ -39,6 +45,10 @@ PROTOTYPES = {
     "kv_tag_check": (C.c_int, [_p, _i32, _p, _p, _i32, _p, _i32, _i32, _p, _p]),
     "kv_tag_check_append_fp8": (C.c_int, [_desc, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _p, _f32, _f32, _p]),
     "kv_tag_check_append_bf16": (C.c_int, [_desc, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _p, _p]),
+    "kv_decode_step_fp8": (C.c_int, [_desc, C.POINTER(LayerStack), _i32, _p, _i32, _p, _i32, _i32, _p, _p, _p,
+                                     _f32, _i32, _p, _sz, _p]),
+    "kv_decode_step_bf16": (C.c_int, [_desc, C.POINTER(LayerStack), _i32, _p, _i32, _p, _i32, _i32, _p, _p, _p,
+                                      _f32, _i32, _p, _sz, _p]),
     "paged_decode_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "paged_decode_attn_auto_splits": (_i32, [_i32, _i32, _i32]),
     "paged_decode_attn_fp8": (C.c_int, [_desc, _p, _i32, _p, _p, _p, _i32, _p, _i32, _i32, _p, _f32, _f32,

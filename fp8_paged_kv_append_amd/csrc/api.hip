@@ -116,7 +116,7 @@ int attn_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_he
                 const void* v_pool, const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens,
                 int32_t batch, int32_t max_ctx_len, const uint32_t* flags, bool fp8, float k_scale,
                 float v_scale, float sm_scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
-                uint16_t* out, hipStream_t stream) {
+                uint16_t* out, hipStream_t stream, bool launch = true) {
   int st = check_pool(desc, true, fp8 ? 1 : 2);
   if (st) return st;
   if (batch < 0 || num_q_heads < 1 || pt_stride < 1 || num_splits < 0) return KVFP8_ERR_SHAPE;
@@ -164,6 +164,7 @@ int attn_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_he
   a.max_ctx = max_ctx_len;
   a.qk_scale_log2 = fp8 ? sm_scale * k_scale * kLog2e : sm_scale * kLog2e;
   a.v_scale = fp8 ? v_scale : 1.0f;
+  if (!launch) return KVFP8_OK;
   return launch_attn_gqa(a, fp8, batch, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
 }
 
@@ -171,13 +172,14 @@ int check_append_common(const kvfp8_pool_desc* desc, void* k_pool, void* v_pool,
                         const uint16_t* v_new, const int32_t* page_table, int32_t pt_stride,
                         const int32_t* ctx_lens, int32_t batch, const uint32_t* page_tags,
                         const uint32_t* expected_tags, uint32_t* abort_flags, bool fp8, float k_scale,
-                        float v_scale, hipStream_t stream) {
+                        float v_scale, hipStream_t stream, bool launch = true) {
+  // page_tags null: no check, abort_flags (may be null) only read -- see check_append_kernel
   int st = check_pool(desc, false, fp8 ? 1 : 2);
   if (st) return st;
   if (batch < 0 || pt_stride < 1) return KVFP8_ERR_SHAPE;
   if (batch == 0) return KVFP8_OK;
-  if (!k_pool || !k_new || !page_table || !ctx_lens || !page_tags || !expected_tags || !abort_flags)
-    return KVFP8_ERR_NULL;
+  if (!k_pool || !k_new || !page_table || !ctx_lens) return KVFP8_ERR_NULL;
+  if (page_tags && (!expected_tags || !abort_flags)) return KVFP8_ERR_NULL;
   if ((v_pool == nullptr) != (v_new == nullptr)) return KVFP8_ERR_NULL;
   if (!aligned16(k_pool) || !aligned16(k_new) || (v_pool && (!aligned16(v_pool) || !aligned16(v_new))))
     return KVFP8_ERR_ALIGN;
@@ -214,6 +216,7 @@ int check_append_common(const kvfp8_pool_desc* desc, void* k_pool, void* v_pool,
   a.v_dim = desc->v_dim;
   a.k_inv = fp8 ? 1.0f / k_scale : 1.0f;
   a.v_inv = fp8 && v_pool ? 1.0f / v_scale : 1.0f;
+  if (!launch) return KVFP8_OK;
   return launch_check_append(c, a, fp8, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
 }
 
@@ -236,7 +239,8 @@ int32_t latent_auto_splits(int32_t batch, int32_t num_q_heads, int32_t max_ctx) 
 int latent_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads, const void* pool,
                   const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens, int32_t batch,
                   int32_t max_ctx_len, const uint32_t* flags, bool fp8, float scale, float sm_scale,
-                  int32_t num_splits, void* workspace, size_t workspace_bytes, uint16_t* out, hipStream_t stream) {
+                  int32_t num_splits, void* workspace, size_t workspace_bytes, uint16_t* out, hipStream_t stream,
+                  bool launch = true) {
   int st = check_pool(desc, false, fp8 ? 1 : 2);
   if (st) return st;
   if (desc->num_kv_heads != 1 || desc->head_dim != kLatentDim || desc->v_dim != kLatentVDim)
@@ -284,7 +288,61 @@ int latent_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_
   a.n_hg = n_hg;
   a.qk_scale_log2 = (fp8 ? sm_scale * scale : sm_scale) * kLog2e;
   a.v_scale = fp8 ? scale : 1.0f;
+  if (!launch) return KVFP8_OK;
   return launch_attn_latent(a, fp8, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
+}
+
+// One decode step over a layer stack: every argument of every layer is checked (a dry pass of the
+// per-layer checks) before the first launch, so an error launches nothing; then, layer by layer,
+// the check + write launch (layer 0 checks when page_tags is given; later layers only read the
+// flags) and the attention launches.  Stream order carries the layer-to-layer dependency.
+int decode_step_common(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* layers, int32_t num_q_heads,
+                       const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens, int32_t batch,
+                       int32_t max_ctx_len, const uint32_t* page_tags, const uint32_t* expected_tags,
+                       uint32_t* abort_flags, bool fp8, float sm_scale, int32_t num_splits, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  if (desc == nullptr || layers == nullptr) return KVFP8_ERR_NULL;
+  const kvfp8_layer_stack& ls = *layers;
+  if (ls.num_layers < 1 || batch < 0 || num_q_heads < 1) return KVFP8_ERR_SHAPE;
+  if (!ls.k_pools || !ls.q || !ls.k_new || !ls.out) return KVFP8_ERR_NULL;
+  const bool latent = ls.v_pools == nullptr;
+  if (latent != (ls.v_new == nullptr)) return KVFP8_ERR_NULL;
+  if (fp8 && (!ls.k_scales || (!latent && !ls.v_scales))) return KVFP8_ERR_NULL;
+  if (page_tags && (!expected_tags || !abort_flags)) return KVFP8_ERR_NULL;
+  if (desc->num_pages < 1 || desc->page_size < 1 || desc->num_kv_heads < 1 || desc->head_dim < 1 || desc->v_dim < 0)
+    return KVFP8_ERR_SHAPE;
+  const int64_t elt = fp8 ? 1 : 2;
+  const int64_t slots = (int64_t)desc->num_pages * desc->page_size * desc->num_kv_heads;
+  const int64_t kpool_b = slots * desc->head_dim * elt, vpool_b = slots * desc->v_dim * elt;
+  const int64_t q_n = (int64_t)batch * num_q_heads * desc->head_dim;
+  const int64_t kn_n = (int64_t)batch * desc->num_kv_heads * desc->head_dim;
+  const int64_t vn_n = (int64_t)batch * desc->num_kv_heads * desc->v_dim;
+  const int64_t out_n = (int64_t)batch * num_q_heads * desc->v_dim;
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool launch = pass == 1;
+    for (int32_t l = 0; l < ls.num_layers; ++l) {
+      void* kp = static_cast<uint8_t*>(ls.k_pools) + l * kpool_b;
+      void* vp = latent ? nullptr : static_cast<uint8_t*>(ls.v_pools) + l * vpool_b;
+      const uint16_t* q = ls.q + l * q_n;
+      const uint16_t* kn = ls.k_new + l * kn_n;
+      const uint16_t* vn = latent ? nullptr : ls.v_new + l * vn_n;
+      uint16_t* out = ls.out + l * out_n;
+      const float ks = fp8 ? ls.k_scales[l] : 1.f;
+      const float vs = fp8 && !latent ? ls.v_scales[l] : 1.f;
+      int st = check_append_common(desc, kp, vp, kn, vn, page_table, pt_stride, ctx_lens, batch,
+                                   l == 0 ? page_tags : nullptr, expected_tags, abort_flags, fp8, ks, vs, stream,
+                                   launch);
+      if (st) return st;
+      st = latent ? latent_common(desc, q, num_q_heads, kp, page_table, pt_stride, ctx_lens, batch, max_ctx_len,
+                                  abort_flags, fp8, ks, sm_scale, num_splits, workspace, workspace_bytes, out, stream,
+                                  launch)
+                  : attn_common(desc, q, num_q_heads, kp, vp, page_table, pt_stride, ctx_lens, batch, max_ctx_len,
+                                abort_flags, fp8, ks, vs, sm_scale, num_splits, workspace, workspace_bytes, out,
+                                stream, launch);
+      if (st) return st;
+    }
+  }
+  return KVFP8_OK;
 }
 
 }  // namespace
@@ -363,6 +421,7 @@ int kv_tag_check_append_fp8(const kvfp8_pool_desc* desc, uint8_t* k_pool, uint8_
                             const int32_t* ctx_lens, int32_t batch, const uint32_t* page_tags,
                             const uint32_t* expected_tags, uint32_t* abort_flags, float k_scale, float v_scale,
                             hipStream_t stream) {
+  if (page_tags == nullptr) return KVFP8_ERR_NULL;
   return check_append_common(desc, k_pool, v_pool, k_new, v_new, page_table, pt_stride, ctx_lens, batch, page_tags,
                              expected_tags, abort_flags, true, k_scale, v_scale, stream);
 }
@@ -371,8 +430,28 @@ int kv_tag_check_append_bf16(const kvfp8_pool_desc* desc, uint16_t* k_pool, uint
                              const uint16_t* v_new, const int32_t* page_table, int32_t pt_stride,
                              const int32_t* ctx_lens, int32_t batch, const uint32_t* page_tags,
                              const uint32_t* expected_tags, uint32_t* abort_flags, hipStream_t stream) {
+  if (page_tags == nullptr) return KVFP8_ERR_NULL;
   return check_append_common(desc, k_pool, v_pool, k_new, v_new, page_table, pt_stride, ctx_lens, batch, page_tags,
                              expected_tags, abort_flags, false, 1.f, 1.f, stream);
+}
+
+int kv_decode_step_fp8(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* layers, int32_t num_q_heads,
+                       const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens, int32_t batch,
+                       int32_t max_ctx_len, const uint32_t* page_tags, const uint32_t* expected_tags,
+                       uint32_t* abort_flags, float sm_scale, int32_t num_splits, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  return decode_step_common(desc, layers, num_q_heads, page_table, pt_stride, ctx_lens, batch, max_ctx_len, page_tags,
+                            expected_tags, abort_flags, true, sm_scale, num_splits, workspace, workspace_bytes, stream);
+}
+
+int kv_decode_step_bf16(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* layers, int32_t num_q_heads,
+                        const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens, int32_t batch,
+                        int32_t max_ctx_len, const uint32_t* page_tags, const uint32_t* expected_tags,
+                        uint32_t* abort_flags, float sm_scale, int32_t num_splits, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  return decode_step_common(desc, layers, num_q_heads, page_table, pt_stride, ctx_lens, batch, max_ctx_len, page_tags,
+                            expected_tags, abort_flags, false, sm_scale, num_splits, workspace, workspace_bytes,
+                            stream);
 }
 
 size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t v_dim, int32_t num_splits) {

@@ -127,6 +127,9 @@ hipError_t launch_append(const AppendArgs& a, bool fp8, hipStream_t stream) {
 // pages exactly as tag_check_kernel does, and only when they are clear writes r's new token
 // (position ctx_lens[r] - 1) exactly as append_kernel would.  The new rows are loaded before the
 // check so their latency overlaps it.  Check before write is preserved inside the block.
+// With c.page_tags null there is no check: the flags (when given) were set by an earlier launch and
+// are only read -- the later layers of a step that shares one check -- and the page id of the
+// written slot is validated here instead.
 template <bool FP8>
 __global__ __launch_bounds__(256) void check_append_kernel(TagArgs c, AppendArgs a) {
   __shared__ uint32_t s_or[4];
@@ -143,36 +146,43 @@ __global__ __launch_bounds__(256) void check_append_kernel(TagArgs c, AppendArgs
     kw[i] = e < nk ? ksrc[e] : 0u;
     vw[i] = e < nv ? vsrc[e] : 0u;
   }
-  // ---- the check
   const int64_t L = c.ctx_lens[r];
-  uint32_t f = 0;
-  if (L > 0) {
-    const int64_t need = (L + c.page_size - 1) / c.page_size;
-    int64_t n = need;
-    if (need > c.pt_stride) {
-      f |= 2u;
-      n = c.pt_stride;
-    }
-    const int32_t* pt = c.page_table + (int64_t)r * c.pt_stride;
-    const uint32_t* ex = c.expected + (int64_t)r * c.pt_stride;
-    for (int64_t i = threadIdx.x; i < n; i += 256) {
-      const int32_t p = pt[i];
-      if (p < 0 || p >= c.num_pages)
+  if (c.page_tags == nullptr) {
+    // ---- no check: honour the flags an earlier launch wrote
+    if (L <= 0 || (c.flags != nullptr && c.flags[r] != 0u)) return;
+    if ((L - 1) / a.page_size >= a.pt_stride) return;
+  } else {
+    // ---- the check
+    uint32_t f = 0;
+    if (L > 0) {
+      const int64_t need = (L + c.page_size - 1) / c.page_size;
+      int64_t n = need;
+      if (need > c.pt_stride) {
         f |= 2u;
-      else if (c.page_tags[p] != ex[i])
-        f |= 1u;
+        n = c.pt_stride;
+      }
+      const int32_t* pt = c.page_table + (int64_t)r * c.pt_stride;
+      const uint32_t* ex = c.expected + (int64_t)r * c.pt_stride;
+      for (int64_t i = threadIdx.x; i < n; i += 256) {
+        const int32_t p = pt[i];
+        if (p < 0 || p >= c.num_pages)
+          f |= 2u;
+        else if (c.page_tags[p] != ex[i])
+          f |= 1u;
+      }
     }
-  }
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) f |= shfl_xor(f, m);
-  if ((threadIdx.x & 63) == 0) s_or[threadIdx.x >> 6] = f;
-  __syncthreads();
-  const uint32_t flag = s_or[0] | s_or[1] | s_or[2] | s_or[3];
-  if (threadIdx.x == 0) c.flags[r] = flag;
+    for (int m = 32; m >= 1; m >>= 1) f |= shfl_xor(f, m);
+    if ((threadIdx.x & 63) == 0) s_or[threadIdx.x >> 6] = f;
+    __syncthreads();
+    const uint32_t flag = s_or[0] | s_or[1] | s_or[2] | s_or[3];
+    if (threadIdx.x == 0) c.flags[r] = flag;
+    if (flag != 0u || L <= 0) return;
+  }
   // ---- the write, for a request whose pages all check out
-  if (flag != 0u || L <= 0) return;
   const int pos = (int)(L - 1);
-  const int page = a.page_table[(int64_t)r * a.pt_stride + pos / S];  // validated above
+  const int page = a.page_table[(int64_t)r * a.pt_stride + pos / S];  // in range: checked above
+  if (page < 0 || page >= a.num_pages) return;                         // (the no-check mode's guard)
   const int slot = pos % S;
 #pragma unroll
   for (int i = 0; i < kMaxPairs; ++i) {

@@ -220,6 +220,53 @@ int paged_decode_attn_latent_bf16(const kvfp8_pool_desc* desc, const uint16_t* q
                                   const uint32_t* abort_flags, float sm_scale, int32_t num_splits, void* workspace,
                                   size_t workspace_bytes, uint16_t* out, hipStream_t stream);
 
+/* ---------------------------------------------------------------- one decode step over a layer stack  [T][Q]
+ * The attention part of a decode step for num_layers layers that share one
+ * page table, one set of page tags, the context lengths and the abort flags
+ * (a page id names the same logical slot in every layer's pool).  Layer l's
+ * buffers are the l-th blocks of contiguous stacks:
+ *   k_pools  [layers][K pool] (the latent pool for the latent cache);
+ *   v_pools  [layers][V pool], or NULL for the latent cache (then v_new NULL);
+ *   q        bf16 [layers][B][Hq][D];   out bf16 [layers][B][Hq][Dv];
+ *   k_new    bf16 [layers][B][Hkv][D];  v_new bf16 [layers][B][Hkv][Dv];
+ *   k_scales, v_scales (host) float [layers]: per-tensor scales of each
+ *   layer's FP8 cache (the latent cache uses k_scales; both ignored, may be
+ *   NULL, for BF16).
+ * Launch order on `stream`: layer 0's check + write (kv_tag_check_append_*
+ * semantics; with page_tags NULL, the write only), layer 0's attention, then
+ * for each later layer its write, honouring the flags layer 0 left (read,
+ * not rewritten: the pages' tag check runs once per step, before any read),
+ * and its attention.  Each write puts request r's token at ctx_lens[r] - 1.
+ * page_tags NULL = no-op tracker: no check; abort_flags, when given, are
+ * only read.  Every layer's arguments are checked before the first launch,
+ * so an error status means nothing was enqueued.  The workspace is shared by
+ * the layers (stream order); size it as for one layer's attention.  Other
+ * shapes, limits and outputs as for the per-layer calls above.  In a model
+ * the layers' q and new rows come from the layer below; here they are given
+ * up front (the projections between layers are not this library's). */
+typedef struct kvfp8_layer_stack {
+  int32_t num_layers;
+  void* k_pools;
+  void* v_pools;
+  const uint16_t* q;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const float* k_scales; /* host */
+  const float* v_scales; /* host */
+  uint16_t* out;
+} kvfp8_layer_stack;
+
+int kv_decode_step_fp8(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* layers, int32_t num_q_heads,
+                       const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens, int32_t batch,
+                       int32_t max_ctx_len, const uint32_t* page_tags, const uint32_t* expected_tags,
+                       uint32_t* abort_flags, float sm_scale, int32_t num_splits, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+int kv_decode_step_bf16(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* layers, int32_t num_q_heads,
+                        const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens, int32_t batch,
+                        int32_t max_ctx_len, const uint32_t* page_tags, const uint32_t* expected_tags,
+                        uint32_t* abort_flags, float sm_scale, int32_t num_splits, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------- page allocator  [T]
  * Host-side free list over the P pages of a pool, holding the page tags of the
  * integrity check (agentlenshq summary of the Cloudflare post, section "KV Cache

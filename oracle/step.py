@@ -57,6 +57,38 @@ def decode_step(state, q_bits, k_new_bits, v_new_bits, tok_req, tok_pos, *, trac
     return flags, out
 
 
+def decode_step_layers(states, q_bits, k_new_bits, v_new_bits, tok_req, tok_pos, *, tracker=True):
+    """One decode step over several attention layers that share the page table, the page tags and the
+    context lengths (one page id names the same logical slot in every layer's pool).
+
+    The check runs once, first, over the shared pages, so it covers every read of the step (the
+    passages place it before any read, as its own batched pass); each layer then writes its new token
+    and attends with those flags.  states: one state dict per layer (see decode_step) whose page_table,
+    ctx_lens, page_tags and expected_tags are the same arrays; q_bits, k_new_bits, v_new_bits: one per
+    layer (v_new_bits entries None for the latent cache).  Returns (flags or None, [{r: fp64 [Hq][Dv]}
+    per layer]).
+    """
+    s0 = states[0]
+    flags = None
+    if tracker:
+        flags = paged.tag_check(s0["page_tags"], s0["page_table"], s0["expected_tags"], s0["ctx_lens"],
+                                s0["page_size"])
+    outs = []
+    for s, q, kn, vn in zip(states, q_bits, k_new_bits, v_new_bits):
+        if s["dtype"] == "fp8":
+            paged.append_fp8(s["k_pool"], s["v_pool"], kn, vn, tok_req, tok_pos, s["page_table"],
+                             s["num_kv_heads"], s["page_size"], s["k_scale"], s["v_scale"], flags)
+        else:
+            paged.append(s["k_pool"], s["v_pool"], kn, vn, tok_req, tok_pos, s["page_table"], s["num_kv_heads"],
+                         s["page_size"], flags)
+        outs.append(attention.decode_attention(
+            q, s["k_pool"], s["v_pool"], s["page_table"], s["ctx_lens"], num_kv_heads=s["num_kv_heads"],
+            page_size=s["page_size"], head_dim=s["head_dim"], v_dim=s["v_dim"], dtype=s["dtype"],
+            k_scale=s["k_scale"], v_scale=s["v_scale"], sm_scale=s["sm_scale"], flags=flags,
+            latent=s.get("latent", False)))
+    return flags, outs
+
+
 def output_bf16(o_f64):
     """The step's bf16 output: fp64 -> fp32 -> bf16 (round to nearest even at each step)."""
     return codec.bf16_from_f32(np.asarray(o_f64, dtype=np.float64).astype(np.float32))

@@ -101,5 +101,24 @@ def test_host_validation_codes(lib):
     assert f(d, A, 8, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 2, A, 64, A, None) == -4       # too small
     d64 = _lib.PoolDesc(16, 16, 1, 64, 64)
     assert f(d64, A, 8, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 0, None, 0, A, None) == -3
+    # one step over a layer stack: every layer checked before anything is enqueued
+    step = lib.kv_decode_step_fp8
+    sc = (C.c_float * 3)(1., 1., 1.)
+    bad = (C.c_float * 3)(1., 0., 1.)                               # layer 1's K scale is invalid
+    Ls = _lib.LayerStack(3, A, A, A, A, A, C.cast(sc, C.c_void_p), C.cast(sc, C.c_void_p), A)
+    args = (8, A, 16, A, 1, 256, A, A, A, 1., 0, A, 1 << 20, None)
+    assert step(d, None, *args) == -1
+    assert step(d, _lib.LayerStack(0, A, A, A, A, A, C.cast(sc, C.c_void_p), C.cast(sc, C.c_void_p), A), *args) == -2
+    assert step(d, _lib.LayerStack(3, A, A, A, A, A, None, None, A), *args) == -1     # FP8 needs the scales
+    assert step(d, _lib.LayerStack(3, A, A, A, A, A, C.cast(bad, C.c_void_p), C.cast(sc, C.c_void_p), A),
+                *args) == -7
+    assert step(d, _lib.LayerStack(3, A, A, A, A, A + 8, C.cast(sc, C.c_void_p), C.cast(sc, C.c_void_p), A),
+                *args) == -5                                        # layer 0's v_new misaligned
+    assert step(d, _lib.LayerStack(3, A, None, A, A, A, C.cast(sc, C.c_void_p), None, A), *args) == -1
+    assert step(d, Ls, 8, A, 16, A, 1, 256, A, None, A, 1., 0, A, 1 << 20, None) == -1   # tags w/o expected
+    assert step(d, Ls, 32, A, 16, A, 1, 256, A, A, A, 1., 0, A, 1 << 20, None) == -3    # group 32 > 16
+    assert step(d, Ls, 8, A, 16, A, 0, 256, A, A, A, 1., 0, A, 1 << 20, None) == 0      # empty batch
+    assert lib.kv_decode_step_bf16(d, _lib.LayerStack(2, A, A, A, A, A, None, None, A), 8, A, 15, A, 1, 256,
+                                   None, None, None, 1., 0, A, 1 << 20, None) == -2     # 15*16 < 256
     assert lib.paged_decode_attn_workspace_bytes(64, 64, 128, 1) == 0
     assert lib.paged_decode_attn_workspace_bytes(64, 64, 128, 2) == 64 * 64 * 2 * 129 * 4
