@@ -25,6 +25,8 @@ __all__ = ["KvFp8Error", "PoolDesc", "pool_desc", "kv_absmax_bf16", "kv_scale_fr
            "paged_decode_attn_auto_splits", "paged_decode_attn_fp8", "paged_decode_attn_bf16",
            "paged_decode_attn_latent_auto_splits", "paged_decode_attn_latent_fp8",
            "paged_decode_attn_latent_bf16", "kv_gather_fp8", "kv_gather_bf16", "decode_step", "decode_step_layers", "PageAllocator",
+           "w4_quantize_bf16", "w8_quantize_bf16", "wgemm_auto_splits", "wgemm_workspace_bytes", "w4a16_gemm",
+           "w8a16_gemm",
            "lib"]
 
 
@@ -278,6 +280,63 @@ def paged_decode_attn_latent_bf16(desc: PoolDesc, q, pool, page_table, ctx_lens,
         page_table.shape[1], _ptr(ctx_lens, _I32, "ctx_lens"), B, int(max_ctx_len),
         _ptr(abort_flags, _U32, "abort_flags", True), float(sm_scale), int(num_splits), ws, wsb,
         _ptr(out, _BF16, "out"), _stream(stream)), "paged_decode_attn_latent_bf16")
+
+
+# ----------------------------------------------------------------------------- weight-quantised GEMM
+
+def _wq_check(w_or_x, n, k, packed, scales, bits):
+    need = lib().w4_packed_bytes(n, k) if bits == 4 else lib().w8_packed_bytes(n, k)
+    if need == 0:
+        raise ValueError(f"unsupported weight shape {n} x {k} (N a multiple of 16, K of 256)")
+    if packed.numel() * packed.element_size() != need:
+        raise ValueError(f"packed codes: {packed.numel() * packed.element_size()} bytes, the layout needs {need}")
+    if scales.numel() != lib().wq_scales_count(n, k):
+        raise ValueError("scales: one bf16 per output channel and group of 128 input channels")
+
+
+def w4_quantize_bf16(w, packed, scales, stream=None):
+    """bf16 weights w [N][K] -> INT4 codes (packed, uint8 [N*K/2]) and bf16 group scales [N/16][K/128][16]."""
+    n, k = w.shape
+    _wq_check(w, n, k, packed, scales, 4)
+    _check(lib().w4_quantize_bf16(_ptr(w, _BF16, "w"), n, k, _ptr(packed, _U8, "packed"),
+                                  _ptr(scales, _BF16, "scales"), _stream(stream)), "w4_quantize_bf16")
+
+
+def w8_quantize_bf16(w, packed, scales, stream=None):
+    """bf16 weights w [N][K] -> e4m3 codes (packed, uint8 [N*K]) and bf16 group scales [N/16][K/128][16]."""
+    n, k = w.shape
+    _wq_check(w, n, k, packed, scales, 8)
+    _check(lib().w8_quantize_bf16(_ptr(w, _BF16, "w"), n, k, _ptr(packed, _U8, "packed"),
+                                  _ptr(scales, _BF16, "scales"), _stream(stream)), "w8_quantize_bf16")
+
+
+def wgemm_auto_splits(m, n, k) -> int:
+    return int(lib().wgemm_auto_splits(int(m), int(n), int(k)))
+
+
+def wgemm_workspace_bytes(m, n, k, num_splits) -> int:
+    return int(lib().wgemm_workspace_bytes(int(m), int(n), int(k), int(num_splits)))
+
+
+def _wgemm(bits, x, w_packed, scales, n, k, y, num_splits, workspace, stream):
+    m = x.shape[0]
+    if x.shape != (m, k) or y.shape != (m, n):
+        raise ValueError(f"x must be [M][{k}] and y [M][{n}]")
+    _wq_check(x, n, k, w_packed, scales, bits)
+    ws, wsb = _ws(workspace)
+    f = lib().w4a16_gemm if bits == 4 else lib().w8a16_gemm
+    _check(f(_ptr(x, _BF16, "x"), m, _ptr(w_packed, _U8, "w_packed"), _ptr(scales, _BF16, "scales"), int(n),
+             int(k), int(num_splits), ws, wsb, _ptr(y, _BF16, "y"), _stream(stream)), f"w{bits}a16_gemm")
+
+
+def w4a16_gemm(x, w_packed, scales, n, k, y, *, num_splits: int = 0, workspace=None, stream=None):
+    """y [M][N] (bf16) = x [M][K] (bf16) times the INT4 weights (packed by w4_quantize_bf16), transposed."""
+    _wgemm(4, x, w_packed, scales, n, k, y, num_splits, workspace, stream)
+
+
+def w8a16_gemm(x, w_packed, scales, n, k, y, *, num_splits: int = 0, workspace=None, stream=None):
+    """y [M][N] (bf16) = x [M][K] (bf16) times the FP8 weights (packed by w8_quantize_bf16), transposed."""
+    _wgemm(8, x, w_packed, scales, n, k, y, num_splits, workspace, stream)
 
 
 # ----------------------------------------------------------------------------- read back (tests)

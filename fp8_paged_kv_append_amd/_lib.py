@@ -66,6 +66,15 @@ PROTOTYPES = {
     "kv_page_alloc": (C.c_int, [_p, _i32, _p, _p]),
     "kv_page_free": (C.c_int, [_p, _p, _i32]),
     "kv_page_alloc_tags": (C.c_int, [_p, _p]),
+    "w4_packed_bytes": (_sz, [_i32, _i32]),
+    "w8_packed_bytes": (_sz, [_i32, _i32]),
+    "wq_scales_count": (_sz, [_i32, _i32]),
+    "w4_quantize_bf16": (C.c_int, [_p, _i32, _i32, _p, _p, _p]),
+    "w8_quantize_bf16": (C.c_int, [_p, _i32, _i32, _p, _p, _p]),
+    "wgemm_auto_splits": (_i32, [_i32, _i32, _i32]),
+    "wgemm_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "w4a16_gemm": (C.c_int, [_p, _i32, _p, _p, _i32, _i32, _i32, _p, _sz, _p, _p]),
+    "w8a16_gemm": (C.c_int, [_p, _i32, _p, _p, _i32, _i32, _i32, _p, _sz, _p, _p]),
     "kv_gather_fp8": (C.c_int, [_desc, _p, _p, _p, _p, _i32, _p, _i32, _i32, _p, _p, _p]),
     "kv_gather_bf16": (C.c_int, [_desc, _p, _p, _p, _p, _i32, _p, _i32, _i32, _p, _p, _p]),
 }

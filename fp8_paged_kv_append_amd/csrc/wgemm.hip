@@ -1,0 +1,531 @@
+// Weight-quantised decode GEMM on gfx950: y[M][N] = x[M][K] W^T with bf16 activations (M <= 64
+// requests) and weights stored as INT4 (W4A16) or FP8 e4m3 (W8A16) codes with one bf16 scale per
+// group of 128 input channels of an output channel.
+//
+// What it computes follows the pages' weight compression (Cloudflare post, section "Compressed model
+// weights"; agentlenshq summary, section "模型权重压缩以降低延迟"): decode streams every weight once per
+// token, so fewer weight bytes mean a faster step, and the 4-bit codes are expanded to a wider type
+// before the multiply.  Here the expansion happens in registers, right before bf16 matrix-core
+// instructions, and nothing expanded is ever written back.
+//
+// Storage (tile = 16 output channels x 128 input channels, tiles ordered [N/16][K/128]; inside a
+// tile lane l = 16*qq + nn owns channel 16t + nn and inputs 128g + 32j + 8qq + e, j 0..3, e 0..7,
+// which is exactly the B operand of v_mfma_f32_16x16x32_bf16 for k-step j):
+//  * INT4: 16 bytes per lane; dword j holds nibbles q + 8 with e = 2*(s%4) + s/4 in slot s, so
+//    (dword >> 4i) & 0x000F000F | 0x43004300 is the bf16 pair (128 + n_e, 128 + n_e+1) for e = 2i:
+//    two ALU operations expand two codes.  The values are q + 136; the bias is removed after the
+//    MFMAs of a group as 136 * (sum of the group's activations), computed once per block.
+//  * FP8: 32 bytes per lane, bytes 8j + e; expanded exactly to bf16 by the hardware conversion.
+// The group's partial sum (fp32, exact products) is scaled by the group's scale and accumulated in
+// fp32; the result is rounded to bf16.
+//
+// Work decomposition.  Block = 4 waves = 64 output channels x one split of the K range; wave w owns
+// output tile 4*blockIdx.x + w.  The activation rows of a 256-wide K chunk are staged in LDS (double
+// buffered, the next chunk's global loads issued a chunk ahead) and shared by the four waves; each
+// wave streams its own weight tiles with an 8-group register ring (8 KB of INT4 / 16 KB of FP8 in
+// flight per wave).  With several splits, fp32 partials go to the workspace and a second kernel
+// adds them in split order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvfp8.h"
+#include "../../include/wgemm.h"
+#include "kvfp8_device.h"
+
+namespace kvfp8 {
+namespace wq {
+
+constexpr int kGroup = 128;          // input channels per scale group
+constexpr int kChunk = 256;          // input channels staged in LDS per step (two groups)
+constexpr int kRing = 8;             // weight groups in flight per wave
+constexpr int kRowBytes = kChunk * 2 + 16;  // LDS row stride of the staged activations (padded)
+constexpr float kW4Bias = 136.0f;    // the expansion yields q + 136
+
+struct WgemmArgs {
+  const uint16_t* x;        // bf16 [M][K]
+  const uint8_t* w;         // packed codes
+  const uint16_t* s;        // bf16 scales [N/16][K/128][16]
+  float* part;              // fp32 [splits][M][N] (splits > 1)
+  uint16_t* y;              // bf16 [M][N]
+  int32_t M, N, K, splits, groups_per_split;
+};
+
+constexpr uint32_t kOOB = 0x80000000u;    // a buffer offset past every buffer (all < 2^31 bytes): loads give 0
+constexpr int kRsrcWord3 = 0x00020000;    // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kNT = 2;                    // cache policy of a load: non-temporal (weights are read once)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// bf16 pair of two INT4 codes (plus the bias 136) from the nibbles at bits 4i and 16 + 4i.
+__device__ __forceinline__ uint32_t w4_pair(uint32_t w, int i) {
+  return ((w >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
+}
+
+// One wave's stream of weight groups: codes and scales of output tile `tile`, groups g0 + g.  Every
+// load is issued unconditionally; a group past the split (or a tile past N) reads zeros through an
+// out-of-range buffer offset, so the loop is straight-line code and the compiler's load counters stay
+// exact (a conditional load would make it wait for every outstanding load).
+template <bool W4>
+struct WStream {
+  static constexpr int kB = W4 ? 16 : 32;   // code bytes per lane per group
+  __amdgpu_buffer_rsrc_t codes, scales;
+  uint32_t cbase, sbase;
+  int ng;
+  bool active;
+  __device__ WStream(const WgemmArgs& a, int tile, int g0, int ng_, int lane) {
+    const int KG = a.K / kGroup;
+    active = tile * 16 < a.N;
+    ng = ng_;
+    codes = make_rsrc(a.w, (uint32_t)((int64_t)a.N * a.K / (W4 ? 2 : 1)));
+    scales = make_rsrc(a.s, (uint32_t)((int64_t)a.N * KG * 2));
+    cbase = (uint32_t)((((int64_t)tile * KG + g0) * 64 + lane) * kB);
+    sbase = (uint32_t)((((int64_t)tile * KG + g0) * 16 + (lane & 15)) * 2);
+  }
+  __device__ __forceinline__ void load(u32x4_t (&w)[kB / 16], uint32_t& sraw, int g) const {
+    const bool ok = active && g < ng;
+    const uint32_t co = ok ? cbase + (uint32_t)g * 64 * kB : kOOB;
+#pragma unroll
+    for (int d = 0; d < kB / 16; ++d) w[d] = __builtin_amdgcn_raw_buffer_load_b128(codes, co + 16 * d, 0, kNT);
+    sraw = __builtin_amdgcn_raw_buffer_load_b16(scales, ok ? sbase + (uint32_t)g * 32 : kOOB, 0, 0);
+  }
+};
+
+// The B operand of k-step j (eight bf16 values e = 0..7) from one group's codes.
+template <bool W4>
+__device__ __forceinline__ u32x4_t expand(const u32x4_t (&w)[W4 ? 1 : 2], int j) {
+  u32x4_t b;
+  if constexpr (W4) {
+    const uint32_t wd = w[0][j];
+    b[0] = w4_pair(wd, 0);
+    b[1] = w4_pair(wd, 1);
+    b[2] = w4_pair(wd, 2);
+    b[3] = w4_pair(wd, 3);
+  } else {
+    const u32x2_t lo = e4m3x4_to_bf16x4(w[j >> 1][2 * (j & 1)]);
+    const u32x2_t hi = e4m3x4_to_bf16x4(w[j >> 1][2 * (j & 1) + 1]);
+    b[0] = lo[0];
+    b[1] = lo[1];
+    b[2] = hi[0];
+    b[3] = hi[1];
+  }
+  return b;
+}
+
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+// acc += s * (group sum - 136 * sum of the group's activations) for INT4 (the expansion's bias),
+// acc += s * group sum for FP8.
+template <bool W4>
+__device__ __forceinline__ void add_group(f32x4_t& acc, const f32x4_t& accg, float sc, const f32x4_t& xs) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    acc[r] = W4 ? fmaf(sc, fmaf(-kW4Bias, xs[r], accg[r]), acc[r]) : fmaf(sc, accg[r], acc[r]);
+}
+
+template <int MT>
+__device__ __forceinline__ void store_out(const WgemmArgs& a, const f32x4_t (&acc)[MT], int tile, int nn, int qq) {
+  if (tile * 16 >= a.N) return;
+  const int n = tile * 16 + nn;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 16 * mt + 4 * qq + r;
+      if (m >= a.M) continue;
+      if (a.splits == 1)
+        a.y[(int64_t)m * a.N + n] = (uint16_t)(pack_bf16x2(acc[mt][r], 0.f) & 0xFFFFu);
+      else
+        a.part[((int64_t)blockIdx.y * a.M + m) * a.N + n] = acc[mt][r];
+    }
+  }
+}
+
+// ---- M <= 16: the block's whole K range of the activations stays in LDS (rows 0..M-1, then the
+// group sums [group][16]); after one load the waves only stream weights, with no barrier.
+template <bool W4>
+__global__ __launch_bounds__(256) void wgemm_small_kernel(WgemmArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nn = lane & 15, qq = lane >> 4;
+  const int KG = a.K / kGroup;
+  const int g0 = blockIdx.y * a.groups_per_split;
+  const int ng = min(a.groups_per_split, KG - g0);
+  const int row_bytes = ng * kGroup * 2 + 16;
+  float* xs = reinterpret_cast<float*>(smem + a.M * row_bytes);
+
+  // activations: all loads of a batch in flight before the stores
+  {
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)((int64_t)a.M * a.K * 2));
+    const int per_row = ng * (kGroup / 8), total = a.M * per_row;
+    for (int base = 0; base < total; base += 256 * 8) {
+      u32x4_t v[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int i = base + 256 * t + tid, r = i / per_row, c = i % per_row;
+        v[t] = __builtin_amdgcn_raw_buffer_load_b128(
+            xr, i < total ? (uint32_t)(((int64_t)r * a.K + g0 * kGroup + 8 * c) * 2) : kOOB, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int i = base + 256 * t + tid;
+        if (i < total) *reinterpret_cast<u32x4_t*>(smem + (i / per_row) * row_bytes + 16 * (i % per_row)) = v[t];
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < a.M * ng; i += 256) {
+    const int r = i / ng, g = i % ng;
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < kGroup / 8; ++c) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + r * row_bytes + (g * kGroup + 8 * c) * 2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum += bf16_bits_to_f32(v[e] & 0xFFFFu) + bf16_bits_to_f32(v[e] >> 16);
+    }
+    xs[g * 16 + r] = sum;
+  }
+  __syncthreads();
+
+  const int tile = blockIdx.x * 4 + wave;
+  const WStream<W4> ws(a, tile, g0, ng, lane);
+  constexpr int kB = WStream<W4>::kB;
+  u32x4_t wr[kRing][kB / 16];
+  uint32_t sr[kRing];
+#pragma unroll
+  for (int u = 0; u < kRing; ++u) ws.load(wr[u], sr[u], u);
+
+  // rows >= M read row M-1: their results are never stored
+  const uint8_t* xa = smem + min(nn, a.M - 1) * row_bytes + 16 * qq;
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int base = 0; base < ng; base += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int gc = min(base + u, ng - 1);   // a group past the split has zero codes and scale
+      f32x4_t accg = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        accg = mfma_bf16(*reinterpret_cast<const u32x4_t*>(xa + (gc * kGroup + 32 * j) * 2), expand<W4>(wr[u], j),
+                         accg);
+      const f32x4_t x4 = *reinterpret_cast<const f32x4_t*>(&xs[gc * 16 + 4 * qq]);
+      add_group<W4>(acc, accg, bf16_bits_to_f32(sr[u]), x4);
+      ws.load(wr[u], sr[u], base + u + kRing);
+    }
+  }
+  f32x4_t out[1] = {acc};
+  store_out<1>(a, out, tile, nn, qq);
+}
+
+// ---- M > 16: activations staged per 256-wide chunk (two groups) through double-buffered LDS, the next
+// chunk's loads issued at the start of the current one; rows >= M and chunks past the split load zeros.
+template <int MT, bool W4>
+__global__ __launch_bounds__(256, 2) void wgemm_kernel(WgemmArgs a) {
+  constexpr int kRows = 16 * MT;
+  constexpr int kR = MT <= 2 ? kRing : kRing / 2;   // groups in flight (more rows: more work per byte)
+  __shared__ __align__(16) uint8_t s_x[2][kRows * kRowBytes];
+  __shared__ __align__(16) float s_xs[2][2][kRows];   // [buffer][group of the chunk][row]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nn = lane & 15, qq = lane >> 4;
+  const int KG = a.K / kGroup;
+  const int g0 = blockIdx.y * a.groups_per_split;
+  const int ng = min(a.groups_per_split, KG - g0);    // even
+  const int nch = ng / 2;
+
+  // ---- activation staging: thread -> (row 8p + tid/32, 16-byte column tid%32) of a chunk
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, (uint32_t)((int64_t)a.M * a.K * 2));
+  const int xr_row = tid >> 5, xr_col = tid & 31;
+  u32x4_t xr[2 * MT];
+  auto x_load = [&](int ch) {   // chunk ch of the split
+#pragma unroll
+    for (int p = 0; p < 2 * MT; ++p) {
+      const int row = 8 * p + xr_row;
+      const uint32_t off = (row < a.M && ch < nch)
+                               ? (uint32_t)(((int64_t)row * a.K + (int64_t)(g0 / 2 + ch) * kChunk + 8 * xr_col) * 2)
+                               : kOOB;
+      xr[p] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+    }
+  };
+  auto x_store = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < 2 * MT; ++p) {
+      const int row = 8 * p + xr_row;
+      *reinterpret_cast<u32x4_t*>(s_x[buf] + row * kRowBytes + 16 * xr_col) = xr[p];
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum += bf16_bits_to_f32(xr[p][i] & 0xFFFFu) + bf16_bits_to_f32(xr[p][i] >> 16);
+      // the 16 lanes of one (row, group) are lanes 16h..16h+15 of this wave
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) sum += __shfl_xor(sum, m);
+      if ((xr_col & 15) == 0) s_xs[buf][xr_col >> 4][row] = sum;
+    }
+  };
+
+  const int tile = blockIdx.x * 4 + wave;
+  const WStream<W4> ws(a, tile, g0, ng, lane);
+  constexpr int kB = WStream<W4>::kB;
+  u32x4_t wr[kR][kB / 16];
+  uint32_t sr[kR];
+#pragma unroll
+  for (int u = 0; u < kR; ++u) ws.load(wr[u], sr[u], u);
+  x_load(0);
+  x_store(0);
+  __syncthreads();
+
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int base = 0; base < ng; base += kR) {
+#pragma unroll
+    for (int u = 0; u < kR; ++u) {
+      const int buf = (u >> 1) & 1;           // chunk parity (base is a multiple of 4 groups)
+      const int gl = u & 1;                   // group inside the chunk
+      if (gl == 0) x_load((base + u) / 2 + 1);
+      f32x4_t accg[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) accg[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4_t b = expand<W4>(wr[u], j);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          accg[mt] = mfma_bf16(*reinterpret_cast<const u32x4_t*>(s_x[buf] + (16 * mt + nn) * kRowBytes +
+                                                                 (gl * kGroup + 32 * j + 8 * qq) * 2),
+                               b, accg[mt]);
+      }
+      const float sc = bf16_bits_to_f32(sr[u]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        add_group<W4>(acc[mt], accg[mt], sc, *reinterpret_cast<const f32x4_t*>(&s_xs[buf][gl][16 * mt + 4 * qq]));
+      ws.load(wr[u], sr[u], base + u + kR);
+      if (gl == 1) {
+        x_store(buf ^ 1);
+        __syncthreads();
+      }
+    }
+  }
+  store_out<MT>(a, acc, tile, nn, qq);
+}
+
+// y = bf16(sum over splits of the partials), splits added in order.
+__global__ __launch_bounds__(256) void wgemm_reduce_kernel(const float* part, int32_t splits, int64_t mn,
+                                                           uint16_t* y) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= mn) return;
+  f32x4_t s = *reinterpret_cast<const f32x4_t*>(part + i);
+  for (int sp = 1; sp < splits; ++sp) {
+    const f32x4_t p = *reinterpret_cast<const f32x4_t*>(part + (int64_t)sp * mn + i);
+    s += p;
+  }
+  u32x2_t o;
+  o[0] = pack_bf16x2(s[0], s[1]);
+  o[1] = pack_bf16x2(s[2], s[3]);
+  *reinterpret_cast<u32x2_t*>(y + i) = o;
+}
+
+// ---- quantise + pack: block = one 16 x 128 tile; thread (row nn = tid/16, 8-channel column c = tid%16)
+template <bool W4>
+__global__ __launch_bounds__(256) void wquant_kernel(const uint16_t* w, int32_t K, uint8_t* packed,
+                                                     uint16_t* scales) {
+  const int t = blockIdx.x, g = blockIdx.y, KG = K / kGroup;
+  const int tid = threadIdx.x, nn = tid >> 4, c = tid & 15;
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(w + (int64_t)(16 * t + nn) * K + g * kGroup + 8 * c);
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_bits_to_f32(v[i] & 0xFFFFu);
+    x[2 * i + 1] = bf16_bits_to_f32(v[i] >> 16);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  const uint32_t sb = pack_bf16x2(__fdiv_rn(amax, W4 ? 7.0f : kE4M3Max), 0.f) & 0xFFFFu;
+  const float s = bf16_bits_to_f32(sb);
+  const float inv = s > 0.f ? __fdiv_rn(1.0f, s) : 0.f;
+  // this thread holds inputs 8c..8c+7 of the group: k-step j = c/4, lane group qq = c%4
+  const int j = c >> 2, lane = 16 * (c & 3) + nn;
+  const int64_t tile = (int64_t)t * KG + g;
+  if (W4) {
+    uint32_t d = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float q = fminf(fmaxf(rintf(x[e] * inv), -8.f), 7.f);
+      const uint32_t nib = (uint32_t)((int)q + 8) & 0xFu;
+      const int slot = (e & 1) * 4 + (e >> 1);
+      d |= nib << (4 * slot);
+    }
+    reinterpret_cast<uint32_t*>(packed)[(tile * 64 + lane) * 4 + j] = d;
+  } else {
+    u32x2_t d;
+    d[0] = encode_e4m3x2(x[0] * inv, x[1] * inv) | (encode_e4m3x2(x[2] * inv, x[3] * inv) << 16);
+    d[1] = encode_e4m3x2(x[4] * inv, x[5] * inv) | (encode_e4m3x2(x[6] * inv, x[7] * inv) << 16);
+    reinterpret_cast<u32x2_t*>(packed)[(tile * 64 + lane) * 4 + j] = d;
+  }
+  if (c == 0) scales[tile * 16 + nn] = (uint16_t)sb;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int32_t n, int32_t k) {
+  if (n < 16 || k < kChunk || n % 16 != 0 || k % kChunk != 0) return KVFP8_ERR_SHAPE;
+  return KVFP8_OK;
+}
+
+int quantize_common(const uint16_t* w, int32_t n, int32_t k, uint8_t* packed, uint16_t* scales, bool w4,
+                    hipStream_t stream) {
+  if (!w || !packed || !scales) return KVFP8_ERR_NULL;
+  int st = check_shape(n, k);
+  if (st) return st;
+  if (!aligned16(w) || !aligned16(packed) || (reinterpret_cast<uintptr_t>(scales) & 1u)) return KVFP8_ERR_ALIGN;
+  const dim3 grid(n / 16, k / kGroup);
+  if (w4)
+    hipLaunchKernelGGL(wquant_kernel<true>, grid, dim3(256), 0, stream, w, k, packed, scales);
+  else
+    hipLaunchKernelGGL(wquant_kernel<false>, grid, dim3(256), 0, stream, w, k, packed, scales);
+  return hipGetLastError() == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
+}
+
+constexpr int64_t kTargetBlocks = 512;      // two blocks of four waves per CU
+constexpr size_t kSmallLdsMax = 64 * 1024;  // dynamic LDS of the M <= 16 kernel
+
+size_t small_lds_bytes(int32_t m, int32_t gps) { return (size_t)m * (gps * kGroup * 2 + 16) + (size_t)gps * 16 * 4; }
+
+int32_t auto_splits(int32_t m, int32_t n, int32_t k) {
+  if (m < 1 || n < 16 || k < kChunk) return 1;
+  const int64_t cols = (n / 16 + 3) / 4;
+  const int64_t chunks = k / kChunk;
+  int64_t s = (kTargetBlocks + cols - 1) / cols;
+  // at least four chunks (eight groups, one ring) per split
+  int64_t cap = chunks / 4;
+  if (cap < 1) cap = 1;
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  // M <= 16: the split's activations must fit the resident kernel's LDS
+  while (m <= 16 && s < chunks && small_lds_bytes(m, 2 * (int32_t)((chunks + s - 1) / s)) > kSmallLdsMax) ++s;
+  return (int32_t)s;
+}
+
+template <int MT, bool W4>
+void launch_mt(const WgemmArgs& a, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((wgemm_kernel<MT, W4>), grid, dim3(256), 0, stream, a);
+}
+
+int gemm_common(const uint16_t* x, int32_t m, const uint8_t* w, const uint16_t* scales, int32_t n, int32_t k,
+                int32_t num_splits, void* workspace, size_t workspace_bytes, uint16_t* y, bool w4,
+                hipStream_t stream) {
+  if (!x || !w || !scales || !y) return KVFP8_ERR_NULL;
+  if (m < 1 || m > 64 || num_splits < 0) return KVFP8_ERR_SHAPE;
+  int st = check_shape(n, k);
+  if (st) return st;
+  // buffer offsets are 32-bit with the top bit reserved for out-of-range loads
+  if ((int64_t)n * k >= (int64_t)1 << 31 || (int64_t)m * k * 2 >= (int64_t)1 << 31) return KVFP8_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (reinterpret_cast<uintptr_t>(scales) & 1u))
+    return KVFP8_ERR_ALIGN;
+  const int32_t chunks = k / kChunk;
+  int32_t splits = num_splits == 0 ? auto_splits(m, n, k) : num_splits;
+  if (splits > chunks) return KVFP8_ERR_SHAPE;
+  const int32_t cps = (chunks + splits - 1) / splits;   // chunks per split
+  splits = (chunks + cps - 1) / cps;                    // drop empty splits
+  WgemmArgs a;
+  a.x = x;
+  a.w = w;
+  a.s = scales;
+  a.y = y;
+  a.part = nullptr;
+  a.M = m;
+  a.N = n;
+  a.K = k;
+  a.splits = splits;
+  a.groups_per_split = 2 * cps;
+  if (splits > 1) {
+    const size_t need = wgemm_workspace_bytes(m, n, k, splits);
+    if (!workspace) return KVFP8_ERR_NULL;
+    if (workspace_bytes < need) return KVFP8_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KVFP8_ERR_ALIGN;
+    a.part = reinterpret_cast<float*>(workspace);
+  }
+  const dim3 grid((n / 16 + 3) / 4, splits);
+  const size_t lds = small_lds_bytes(m, a.groups_per_split);
+  if (m <= 16 && lds <= kSmallLdsMax) {
+    if (w4)
+      hipLaunchKernelGGL(wgemm_small_kernel<true>, grid, dim3(256), lds, stream, a);
+    else
+      hipLaunchKernelGGL(wgemm_small_kernel<false>, grid, dim3(256), lds, stream, a);
+  } else {
+    const int mt = (m + 15) / 16;
+    if (w4) {
+      if (mt == 1) launch_mt<1, true>(a, grid, stream);
+      else if (mt == 2) launch_mt<2, true>(a, grid, stream);
+      else if (mt == 3) launch_mt<3, true>(a, grid, stream);
+      else launch_mt<4, true>(a, grid, stream);
+    } else {
+      if (mt == 1) launch_mt<1, false>(a, grid, stream);
+      else if (mt == 2) launch_mt<2, false>(a, grid, stream);
+      else if (mt == 3) launch_mt<3, false>(a, grid, stream);
+      else launch_mt<4, false>(a, grid, stream);
+    }
+  }
+  if (hipGetLastError() != hipSuccess) return KVFP8_ERR_HIP;
+  if (splits > 1) {
+    const int64_t mn = (int64_t)m * n;                 // a multiple of 16
+    hipLaunchKernelGGL(wgemm_reduce_kernel, dim3((uint32_t)((mn / 4 + 255) / 256)), dim3(256), 0, stream,
+                       a.part, splits, mn, y);
+    if (hipGetLastError() != hipSuccess) return KVFP8_ERR_HIP;
+  }
+  return KVFP8_OK;
+}
+
+}  // namespace wq
+}  // namespace kvfp8
+
+using namespace kvfp8::wq;
+
+extern "C" {
+
+size_t w4_packed_bytes(int32_t n, int32_t k) {
+  return check_shape(n, k) ? 0 : (size_t)n * k / 2;
+}
+
+size_t w8_packed_bytes(int32_t n, int32_t k) {
+  return check_shape(n, k) ? 0 : (size_t)n * k;
+}
+
+size_t wq_scales_count(int32_t n, int32_t k) {
+  return check_shape(n, k) ? 0 : (size_t)n * (k / kGroup);
+}
+
+int w4_quantize_bf16(const uint16_t* w, int32_t n, int32_t k, uint8_t* packed, uint16_t* scales,
+                     hipStream_t stream) {
+  return quantize_common(w, n, k, packed, scales, true, stream);
+}
+
+int w8_quantize_bf16(const uint16_t* w, int32_t n, int32_t k, uint8_t* packed, uint16_t* scales,
+                     hipStream_t stream) {
+  return quantize_common(w, n, k, packed, scales, false, stream);
+}
+
+int32_t wgemm_auto_splits(int32_t m, int32_t n, int32_t k) { return auto_splits(m, n, k); }
+
+size_t wgemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t num_splits) {
+  if (m < 1 || n < 1 || k < 1 || num_splits <= 1) return 0;
+  return (size_t)num_splits * m * n * sizeof(float);
+}
+
+int w4a16_gemm(const uint16_t* x, int32_t m, const uint8_t* w_packed, const uint16_t* scales, int32_t n, int32_t k,
+               int32_t num_splits, void* workspace, size_t workspace_bytes, uint16_t* y, hipStream_t stream) {
+  return gemm_common(x, m, w_packed, scales, n, k, num_splits, workspace, workspace_bytes, y, true, stream);
+}
+
+int w8a16_gemm(const uint16_t* x, int32_t m, const uint8_t* w_packed, const uint16_t* scales, int32_t n, int32_t k,
+               int32_t num_splits, void* workspace, size_t workspace_bytes, uint16_t* y, hipStream_t stream) {
+  return gemm_common(x, m, w_packed, scales, n, k, num_splits, workspace, workspace_bytes, y, false, stream);
+}
+
+}  // extern "C"

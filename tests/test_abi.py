@@ -9,10 +9,12 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvfp8.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def _declared():
-    src = open(HEADER).read()
+    src = "\n".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
     return sorted(set(names))
@@ -27,10 +29,11 @@ def test_header_declares_the_entry_points():
 
 
 def test_header_compiles_as_c_and_cxx():
-    for lang, std in (("c", "-std=c11"), ("c++", "-std=c++17")):
-        r = subprocess.run(["gcc", "-x", lang, std, "-Wall", "-Werror", "-fsyntax-only", HEADER],
-                           capture_output=True, text=True)
-        assert r.returncode == 0, r.stderr
+    for h in HEADERS:
+        for lang, std in (("c", "-std=c11"), ("c++", "-std=c++17")):
+            r = subprocess.run(["gcc", "-x", lang, std, "-Wall", "-Werror", "-fsyntax-only", h],
+                               capture_output=True, text=True)
+            assert r.returncode == 0, (h, r.stderr)
 
 
 @pytest.fixture(scope="module")
@@ -120,5 +123,22 @@ def test_host_validation_codes(lib):
     assert step(d, Ls, 8, A, 16, A, 0, 256, A, A, A, 1., 0, A, 1 << 20, None) == 0      # empty batch
     assert lib.kv_decode_step_bf16(d, _lib.LayerStack(2, A, A, A, A, A, None, None, A), 8, A, 15, A, 1, 256,
                                    None, None, None, 1., 0, A, 1 << 20, None) == -2     # 15*16 < 256
+    # weight-quantised GEMM
+    assert lib.w4_packed_bytes(64, 256) == 64 * 128 and lib.w8_packed_bytes(64, 256) == 64 * 256
+    assert lib.w4_packed_bytes(24, 256) == 0 and lib.w8_packed_bytes(64, 384) == 0
+    assert lib.wq_scales_count(64, 512) == 64 * 4
+    assert lib.w4_quantize_bf16(A, 64, 200, A, A, None) == -2
+    assert lib.w4_quantize_bf16(None, 64, 256, A, A, None) == -1
+    assert lib.w8_quantize_bf16(A, 64, 256, A, A + 1, None) == -5
+    gm = lib.w4a16_gemm
+    assert gm(A, 0, A, A, 64, 256, 0, None, 0, A, None) == -2                 # M = 0
+    assert gm(A, 65, A, A, 64, 256, 0, None, 0, A, None) == -2                # M > 64
+    assert gm(A, 4, A, A, 64, 256, 2, None, 0, A, None) == -2                 # 2 splits > 1 chunk
+    assert gm(A, 4, A, A, 64, 512, 2, None, 0, A, None) == -1                 # no workspace
+    assert gm(A, 4, A, A, 64, 512, 2, A, 64, A, None) == -4                   # too small
+    assert lib.w8a16_gemm(A + 8, 4, A, A, 64, 256, 0, None, 0, A, None) == -5
+    assert lib.wgemm_workspace_bytes(4, 64, 512, 1) == 0
+    assert lib.wgemm_workspace_bytes(4, 64, 512, 2) == 2 * 4 * 64 * 4
+    assert 1 <= lib.wgemm_auto_splits(1, 8192, 8192) <= 32
     assert lib.paged_decode_attn_workspace_bytes(64, 64, 128, 1) == 0
     assert lib.paged_decode_attn_workspace_bytes(64, 64, 128, 2) == 64 * 64 * 2 * 129 * 4

@@ -1,0 +1,123 @@
+"""Weight-quantised decode GEMM on the GPU against the oracle (Cloudflare post, section "Compressed
+model weights"): the library's INT4 and FP8 quantisers are bit-exact to the oracle's (codes in the
+packed layout, scales), and y = x W^T matches the fp64 GEMM over the dequantised weights within the
+bf16-output tolerance, for M = 1..64, several split counts (ragged last split included) and, at the
+8192 x 8192 size the benchmark streams, on sampled output tiles."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_paged_kv_append_amd as kv
+from kvsynth import weights as wsyn
+from oracle import codec, wgemm
+from tests.gpu_util import dev, host, note
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2          # max |y - ref| / max |ref| per output row, bf16 result
+
+
+def _quantize_dev(w_bits, bits):
+    n, k = w_bits.shape
+    packed = torch.empty(n * k // (2 if bits == 4 else 1), dtype=torch.uint8, device="cuda")
+    scales = torch.empty(n * k // 128, dtype=torch.int16, device="cuda")
+    (kv.w4_quantize_bf16 if bits == 4 else kv.w8_quantize_bf16)(dev(w_bits), packed, scales)
+    torch.cuda.synchronize()
+    return packed, scales
+
+
+def _oracle_codes(w_bits, bits):
+    if bits == 4:
+        q, s = wgemm.quantize_w4(w_bits)
+        return wgemm.pack_w4(q), wgemm.pack_scales(s).ravel(), wgemm.dequant_w4(q, s)
+    c, s = wgemm.quantize_w8(w_bits)
+    return wgemm.pack_w8(c), wgemm.pack_scales(s).ravel(), wgemm.dequant_w8(c, s)
+
+
+def _row_err(y_bits, ref):
+    y = codec.f64_from_bf16(y_bits)
+    den = np.maximum(np.max(np.abs(ref), axis=1), 1e-30)
+    return float(np.max(np.max(np.abs(y - ref), axis=1) / den))
+
+
+def _gemm(bits, x, packed, scales, n, k, splits=0):
+    m = x.shape[0]
+    y = torch.empty((m, n), dtype=torch.int16, device="cuda")
+    s = splits or kv.wgemm_auto_splits(m, n, k)
+    nb = kv.wgemm_workspace_bytes(m, n, k, s)
+    ws = torch.empty(max(nb, 16) // 4 + 4, dtype=torch.float32, device="cuda")
+    (kv.w4a16_gemm if bits == 4 else kv.w8a16_gemm)(x, packed, scales, n, k, y, num_splits=splits, workspace=ws)
+    torch.cuda.synchronize()
+    return host(y, np.uint16)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("shape", ["tiny", "ragged"])
+def test_quantiser_bit_exact(bits, shape):
+    note(f"quantiser w{bits} {shape}")
+    sh = wsyn.SHAPES[shape]
+    w = wsyn.weights(sh)
+    w[3, 128:256] = 0                      # an all-zero group: scale 0, codes 0
+    packed, scales = _quantize_dev(w, bits)
+    o_packed, o_scales, _ = _oracle_codes(w, bits)
+    assert np.array_equal(host(packed, np.uint8), o_packed)
+    assert np.array_equal(host(scales, np.uint16), o_scales)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 40, 64])
+def test_gemm_matches_oracle(bits, m):
+    sh = wsyn.SHAPES["ragged"]                       # N = 320 (5 column blocks, the last one partly idle)
+    note(f"gemm w{bits} ragged m={m}")
+    w = wsyn.weights(sh)
+    packed, scales = _quantize_dev(w, bits)
+    o_packed, _, W = _oracle_codes(w, bits)
+    assert np.array_equal(host(packed, np.uint8), o_packed)
+    x = wsyn.activations(sh, m)
+    ref = wgemm.gemm(x, W)
+    dx = dev(x)
+    for splits in (0, 1, 2, 3, 5):                   # K = 1280: 5 chunks; 2 and 3 splits leave a short last one
+        err = _row_err(_gemm(bits, dx, packed, scales, sh.n, sh.k, splits), ref)
+        note(f"  splits={splits}: row error {err:.2e}")
+        assert err <= TOL
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemm_tiny_and_zero_rows(bits):
+    """K = 256 (one chunk, one split), an all-zero activation row and an all-zero weight group."""
+    sh = wsyn.SHAPES["tiny"]
+    note(f"gemm w{bits} tiny")
+    w = wsyn.weights(sh)
+    w[5, :128] = 0
+    packed, scales = _quantize_dev(w, bits)
+    _, _, W = _oracle_codes(w, bits)
+    x = wsyn.activations(sh, 3)
+    x[1] = 0
+    y = _gemm(bits, dev(x), packed, scales, sh.n, sh.k)
+    assert not y[1].any()
+    ref = wgemm.gemm(x, W)
+    assert _row_err(y[[0, 2]], ref[[0, 2]]) <= TOL
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("m", [1, 64])
+def test_gemm_full_size_sampled(bits, m):
+    """8192 x 8192 weights (one matrix of the benchmark's stack), the library's split choice: the codes of
+    sampled 16-row tiles bit-exact to the oracle's, and y on those tiles' columns within tolerance."""
+    sh = wsyn.SHAPES["stack_8k"]
+    note(f"gemm w{bits} 8192x8192 m={m}")
+    w = wsyn.weights(sh, layer=0)
+    packed, scales = _quantize_dev(w, bits)
+    x = wsyn.activations(sh, m)
+    y = _gemm(bits, dev(x), packed, scales, sh.n, sh.k)
+    hp, hs = host(packed, np.uint8), host(scales, np.uint16)
+    KG = sh.k // 128
+    tile_bytes = KG * 64 * (16 if bits == 4 else 32)
+    for t in (0, 137, 511):
+        o_packed, o_scales, W = _oracle_codes(w[16 * t:16 * t + 16], bits)
+        assert np.array_equal(hp[t * tile_bytes:(t + 1) * tile_bytes], o_packed), t
+        assert np.array_equal(hs[t * KG * 16:(t + 1) * KG * 16], o_scales), t
+        ref = wgemm.gemm(x, W)
+        err = _row_err(y[:, 16 * t:16 * t + 16], ref)
+        note(f"  tile {t}: row error {err:.2e}")
+        assert err <= TOL
