@@ -20,11 +20,12 @@
 // fp32; the result is rounded to bf16.
 //
 // Work decomposition.  Block = 4 waves = 64 output channels x one split of the K range; wave w owns
-// output tile 4*blockIdx.x + w.  The activation rows of a 256-wide K chunk are staged in LDS (double
-// buffered, the next chunk's global loads issued a chunk ahead) and shared by the four waves; each
+// output tile 4*blockIdx.x + w.  For M <= 16 the split's activation rows stay resident in LDS; above,
+// 256-wide K chunks are staged in LDS (double buffered, the next chunk's global loads issued a chunk
+// ahead).  Either way the four waves share them; each
 // wave streams its own weight tiles with an 8-group register ring (8 KB of INT4 / 16 KB of FP8 in
-// flight per wave).  With several splits, fp32 partials go to the workspace and a second kernel
-// adds them in split order.
+// flight per wave).  With several splits, fp32 partials go to the workspace and a second kernel adds
+// them in split order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,6 +41,8 @@ constexpr int kChunk = 256;          // input channels staged in LDS per step (t
 constexpr int kRing = 8;             // weight groups in flight per wave
 constexpr int kRowBytes = kChunk * 2 + 16;  // LDS row stride of the staged activations (padded)
 constexpr float kW4Bias = 136.0f;    // the expansion yields q + 136
+constexpr int kMaxGroupsChunked = 64;
+constexpr int kVmWait0 = 0x0F70;       // s_waitcnt vmcnt(0) (gfx9 encoding: expcnt, lgkmcnt left open)  // groups per split of the M > 16 kernel (its scales sit in LDS)
 
 struct WgemmArgs {
   const uint16_t* x;        // bf16 [M][K]
@@ -63,15 +66,16 @@ __device__ __forceinline__ uint32_t w4_pair(uint32_t w, int i) {
   return ((w >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
 }
 
-// One wave's stream of weight groups: codes and scales of output tile `tile`, groups g0 + g.  Every
-// load is issued unconditionally; a group past the split (or a tile past N) reads zeros through an
-// out-of-range buffer offset, so the loop is straight-line code and the compiler's load counters stay
-// exact (a conditional load would make it wait for every outstanding load).
+// One wave's stream of weight groups: the codes of output tile `tile`, groups g0 + g.  Every load is
+// issued unconditionally; a group past the split (or a tile past N) reads zeros through an out-of-range
+// buffer offset, so the loop is straight-line code.  Only these loads are counted by vmcnt inside the
+// loop (scales and activations come from LDS), which keeps the compiler's waits exact: a conditional
+// load, or a second load kind issued in another order before the loop, makes it wait for the whole ring.
 template <bool W4>
 struct WStream {
   static constexpr int kB = W4 ? 16 : 32;   // code bytes per lane per group
-  __amdgpu_buffer_rsrc_t codes, scales;
-  uint32_t cbase, sbase;
+  __amdgpu_buffer_rsrc_t codes;
+  uint32_t cbase;
   int ng;
   bool active;
   __device__ WStream(const WgemmArgs& a, int tile, int g0, int ng_, int lane) {
@@ -79,18 +83,29 @@ struct WStream {
     active = tile * 16 < a.N;
     ng = ng_;
     codes = make_rsrc(a.w, (uint32_t)((int64_t)a.N * a.K / (W4 ? 2 : 1)));
-    scales = make_rsrc(a.s, (uint32_t)((int64_t)a.N * KG * 2));
     cbase = (uint32_t)((((int64_t)tile * KG + g0) * 64 + lane) * kB);
-    sbase = (uint32_t)((((int64_t)tile * KG + g0) * 16 + (lane & 15)) * 2);
   }
-  __device__ __forceinline__ void load(u32x4_t (&w)[kB / 16], uint32_t& sraw, int g) const {
-    const bool ok = active && g < ng;
-    const uint32_t co = ok ? cbase + (uint32_t)g * 64 * kB : kOOB;
+  __device__ __forceinline__ void load(u32x4_t (&w)[kB / 16], int g) const {
+    const uint32_t co = (active && g < ng) ? cbase + (uint32_t)g * 64 * kB : kOOB;
 #pragma unroll
     for (int d = 0; d < kB / 16; ++d) w[d] = __builtin_amdgcn_raw_buffer_load_b128(codes, co + 16 * d, 0, kNT);
-    sraw = __builtin_amdgcn_raw_buffer_load_b16(scales, ok ? sbase + (uint32_t)g * 32 : kOOB, 0, 0);
   }
 };
+
+// The block's group scales -> LDS s_sc[tile of the block][group][16] (bf16), zeros past N or the split.
+__device__ __forceinline__ void load_scales(const WgemmArgs& a, int tile0, int ntiles, int g0, int ng, int gcap,
+                                            uint16_t* s_sc) {
+  const int KG = a.K / kGroup;
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.s, (uint32_t)((int64_t)a.N * KG * 2));
+  // ntiles x gcap groups x 32 bytes, 16 bytes per thread and pass
+  for (int i = threadIdx.x; i < ntiles * gcap * 2; i += 256) {
+    const int t = i / (gcap * 2), g = (i / 2) % gcap, h = i & 1;
+    const int tile = tile0 + t;
+    const bool ok = tile * 16 < a.N && g < ng;
+    const uint32_t off = ok ? (uint32_t)(((int64_t)tile * KG + g0 + g) * 32 + 16 * h) : kOOB;
+    *reinterpret_cast<u32x4_t*>(s_sc + (t * gcap + g) * 16 + 8 * h) = __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0);
+  }
+}
 
 // The B operand of k-step j (eight bf16 values e = 0..7) from one group's codes.
 template <bool W4>
@@ -145,18 +160,58 @@ __device__ __forceinline__ void store_out(const WgemmArgs& a, const f32x4_t (&ac
   }
 }
 
+// y = bf16(sum over splits of the partials), splits added in order.
+__global__ __launch_bounds__(256) void wgemm_reduce_kernel(const float* part, int32_t splits, int64_t mn,
+                                                           uint16_t* y) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= mn) return;
+  f32x4_t s = *reinterpret_cast<const f32x4_t*>(part + i);
+  for (int sp = 1; sp < splits; ++sp) s += *reinterpret_cast<const f32x4_t*>(part + (int64_t)sp * mn + i);
+  u32x2_t o;
+  o[0] = pack_bf16x2(s[0], s[1]);
+  o[1] = pack_bf16x2(s[2], s[3]);
+  *reinterpret_cast<u32x2_t*>(y + i) = o;
+}
+
 // ---- M <= 16: the block's whole K range of the activations stays in LDS (rows 0..M-1, then the
 // group sums [group][16]); after one load the waves only stream weights, with no barrier.
-template <bool W4>
+// WK = false: the block covers four output tiles, one per wave, each over the whole split.
+// WK = true: the block is one output tile and the four waves split its K range (wave w takes the w-th
+// quarter of the groups); they add their results through LDS in wave order -- a K split with neither
+// a workspace nor a second launch.
+template <bool W4, bool WK>
 __global__ __launch_bounds__(256) void wgemm_small_kernel(WgemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int kTiles = WK ? 1 : 4;
+  constexpr int kRingS = kRing;   // groups in flight per wave (16 measured slower: 14.2 vs 12.0 us)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nn = lane & 15, qq = lane >> 4;
   const int KG = a.K / kGroup;
   const int g0 = blockIdx.y * a.groups_per_split;
   const int ng = min(a.groups_per_split, KG - g0);
+  const int gcap = a.groups_per_split;
   const int row_bytes = ng * kGroup * 2 + 16;
-  float* xs = reinterpret_cast<float*>(smem + a.M * row_bytes);
+  float* xs = reinterpret_cast<float*>(smem + a.M * row_bytes);                        // [gcap][16]
+  uint16_t* s_sc = reinterpret_cast<uint16_t*>(smem + a.M * row_bytes + gcap * 64);      // [kTiles][gcap][16]
+  f32x4_t* s_red = reinterpret_cast<f32x4_t*>(smem + a.M * row_bytes + gcap * 64 + kTiles * gcap * 32);
+
+  // the wave's tile and groups
+  const int tile = WK ? blockIdx.x : blockIdx.x * 4 + wave;
+  const int gq = WK ? (ng + 3) / 4 : ng;
+  const int gw0 = WK ? wave * gq : 0;                    // first group of the wave inside the split
+  const int ngw = WK ? max(0, min(gq, ng - gw0)) : ng;
+  const int st = WK ? 0 : wave;                          // the wave's tile inside s_sc
+
+  // the weight ring first: its loads do not depend on the activations, so the two latencies overlap
+  const WStream<W4> ws(a, tile, g0 + gw0, ngw, lane);
+  constexpr int kB = WStream<W4>::kB;
+  u32x4_t wr[kRingS][kB / 16];
+#pragma unroll
+  for (int u = 0; u < kRingS; ++u) {
+    ws.load(wr[u], u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  load_scales(a, WK ? blockIdx.x : blockIdx.x * 4, kTiles, g0, ng, gcap, s_sc);
 
   // activations: all loads of a batch in flight before the stores
   {
@@ -174,47 +229,52 @@ __global__ __launch_bounds__(256) void wgemm_small_kernel(WgemmArgs a) {
       for (int t = 0; t < 8; ++t) {
         const int i = base + 256 * t + tid;
         if (i < total) *reinterpret_cast<u32x4_t*>(smem + (i / per_row) * row_bytes + 16 * (i % per_row)) = v[t];
+        // group sums on the way: a group of a row is 16 consecutive columns, i.e. 16 aligned lanes
+        // (per_row and 256 are multiples of 16); out-of-range lanes loaded zeros
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum += bf16_bits_to_f32(v[t][e] & 0xFFFFu) + bf16_bits_to_f32(v[t][e] >> 16);
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) sum += __shfl_xor(sum, m);
+        if (i < total && (tid & 15) == 0) xs[((i % per_row) >> 4) * 16 + i / per_row] = sum;
       }
     }
   }
+  // Retire every prologue load, including the out-of-range ones whose data is never read: the compiler
+  // does not wait for those, and left outstanding they make it wait for the whole ring inside the loop
+  // when their registers are reused.  (The builtin, unlike inline asm, updates the compiler's count.)
+  __builtin_amdgcn_s_waitcnt(kVmWait0);
   __syncthreads();
-  for (int i = tid; i < a.M * ng; i += 256) {
-    const int r = i / ng, g = i % ng;
-    float sum = 0.f;
-#pragma unroll
-    for (int c = 0; c < kGroup / 8; ++c) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + r * row_bytes + (g * kGroup + 8 * c) * 2);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sum += bf16_bits_to_f32(v[e] & 0xFFFFu) + bf16_bits_to_f32(v[e] >> 16);
-    }
-    xs[g * 16 + r] = sum;
-  }
-  __syncthreads();
-
-  const int tile = blockIdx.x * 4 + wave;
-  const WStream<W4> ws(a, tile, g0, ng, lane);
-  constexpr int kB = WStream<W4>::kB;
-  u32x4_t wr[kRing][kB / 16];
-  uint32_t sr[kRing];
-#pragma unroll
-  for (int u = 0; u < kRing; ++u) ws.load(wr[u], sr[u], u);
 
   // rows >= M read row M-1: their results are never stored
   const uint8_t* xa = smem + min(nn, a.M - 1) * row_bytes + 16 * qq;
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int base = 0; base < ng; base += kRing) {
+  for (int base = 0; base < ngw; base += kRingS) {
 #pragma unroll
-    for (int u = 0; u < kRing; ++u) {
-      const int gc = min(base + u, ng - 1);   // a group past the split has zero codes and scale
+    for (int u = 0; u < kRingS; ++u) {
+      const int gc = gw0 + min(base + u, ngw - 1);   // a group past the wave's range has zero codes and scale
+      u32x4_t av[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const u32x4_t*>(xa + (gc * kGroup + 32 * j) * 2);
+      const f32x4_t x4 = *reinterpret_cast<const f32x4_t*>(&xs[gc * 16 + 4 * qq]);
+      const float sc = bf16_bits_to_f32(s_sc[(st * gcap + gc) * 16 + nn]);
       f32x4_t accg = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        accg = mfma_bf16(*reinterpret_cast<const u32x4_t*>(xa + (gc * kGroup + 32 * j) * 2), expand<W4>(wr[u], j),
-                         accg);
-      const f32x4_t x4 = *reinterpret_cast<const f32x4_t*>(&xs[gc * 16 + 4 * qq]);
-      add_group<W4>(acc, accg, bf16_bits_to_f32(sr[u]), x4);
-      ws.load(wr[u], sr[u], base + u + kRing);
+      for (int j = 0; j < 4; ++j) accg = mfma_bf16(av[j], expand<W4>(wr[u], j), accg);
+      add_group<W4>(acc, accg, base + u < ngw ? sc : 0.f, x4);
+      // refill this slot now: without the fence the scheduler sinks all refills of the unrolled loop
+      // to its end, and every pass then waits a full memory latency for loads it has just issued
+      ws.load(wr[u], base + u + kRingS);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  }
+  if constexpr (WK) {
+    s_red[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    acc = s_red[lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) acc += s_red[w * 64 + lane];
   }
   f32x4_t out[1] = {acc};
   store_out<1>(a, out, tile, nn, qq);
@@ -228,6 +288,7 @@ __global__ __launch_bounds__(256, 2) void wgemm_kernel(WgemmArgs a) {
   constexpr int kR = MT <= 2 ? kRing : kRing / 2;   // groups in flight (more rows: more work per byte)
   __shared__ __align__(16) uint8_t s_x[2][kRows * kRowBytes];
   __shared__ __align__(16) float s_xs[2][2][kRows];   // [buffer][group of the chunk][row]
+  __shared__ __align__(16) uint16_t s_sc[4 * kMaxGroupsChunked * 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nn = lane & 15, qq = lane >> 4;
@@ -269,9 +330,12 @@ __global__ __launch_bounds__(256, 2) void wgemm_kernel(WgemmArgs a) {
   const WStream<W4> ws(a, tile, g0, ng, lane);
   constexpr int kB = WStream<W4>::kB;
   u32x4_t wr[kR][kB / 16];
-  uint32_t sr[kR];
 #pragma unroll
-  for (int u = 0; u < kR; ++u) ws.load(wr[u], sr[u], u);
+  for (int u = 0; u < kR; ++u) {
+    ws.load(wr[u], u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  load_scales(a, blockIdx.x * 4, 4, g0, ng, kMaxGroupsChunked, s_sc);
   x_load(0);
   x_store(0);
   __syncthreads();
@@ -298,11 +362,13 @@ __global__ __launch_bounds__(256, 2) void wgemm_kernel(WgemmArgs a) {
                                                                  (gl * kGroup + 32 * j + 8 * qq) * 2),
                                b, accg[mt]);
       }
-      const float sc = bf16_bits_to_f32(sr[u]);
+      const float sc = bf16_bits_to_f32(s_sc[(wave * kMaxGroupsChunked + min(base + u, kMaxGroupsChunked - 1)) * 16 + nn]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        add_group<W4>(acc[mt], accg[mt], sc, *reinterpret_cast<const f32x4_t*>(&s_xs[buf][gl][16 * mt + 4 * qq]));
-      ws.load(wr[u], sr[u], base + u + kR);
+        add_group<W4>(acc[mt], accg[mt], base + u < ng ? sc : 0.f,
+                      *reinterpret_cast<const f32x4_t*>(&s_xs[buf][gl][16 * mt + 4 * qq]));
+      ws.load(wr[u], base + u + kR);
+      __builtin_amdgcn_sched_barrier(0);
       if (gl == 1) {
         x_store(buf ^ 1);
         __syncthreads();
@@ -310,22 +376,6 @@ __global__ __launch_bounds__(256, 2) void wgemm_kernel(WgemmArgs a) {
     }
   }
   store_out<MT>(a, acc, tile, nn, qq);
-}
-
-// y = bf16(sum over splits of the partials), splits added in order.
-__global__ __launch_bounds__(256) void wgemm_reduce_kernel(const float* part, int32_t splits, int64_t mn,
-                                                           uint16_t* y) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= mn) return;
-  f32x4_t s = *reinterpret_cast<const f32x4_t*>(part + i);
-  for (int sp = 1; sp < splits; ++sp) {
-    const f32x4_t p = *reinterpret_cast<const f32x4_t*>(part + (int64_t)sp * mn + i);
-    s += p;
-  }
-  u32x2_t o;
-  o[0] = pack_bf16x2(s[0], s[1]);
-  o[1] = pack_bf16x2(s[2], s[3]);
-  *reinterpret_cast<u32x2_t*>(y + i) = o;
 }
 
 // ---- quantise + pack: block = one 16 x 128 tile; thread (row nn = tid/16, 8-channel column c = tid%16)
@@ -393,12 +443,24 @@ int quantize_common(const uint16_t* w, int32_t n, int32_t k, uint8_t* packed, ui
 }
 
 constexpr int64_t kTargetBlocks = 512;      // two blocks of four waves per CU
+
 constexpr size_t kSmallLdsMax = 64 * 1024;  // dynamic LDS of the M <= 16 kernel
 
-size_t small_lds_bytes(int32_t m, int32_t gps) { return (size_t)m * (gps * kGroup * 2 + 16) + (size_t)gps * 16 * 4; }
+// activations [M][gps*128 + 8] bf16, group sums [gps][16] fp32, scales [tiles][gps][16] bf16, and for
+// the in-block K split the four waves' results [4][64] f32x4
+size_t small_lds_bytes(int32_t m, int32_t gps, bool wk = false) {
+  return (size_t)m * (gps * kGroup * 2 + 16) + (size_t)gps * 16 * 4 + (size_t)(wk ? 1 : 4) * gps * 16 * 2 +
+         (wk ? 4 * 64 * 16 : 0);
+}
+
+// M <= 16 with enough output tiles to fill the chip: one split, K cut among a block's waves
+bool use_wk(int32_t m, int32_t n, int32_t k) {
+  return m <= 16 && n / 16 >= 256 && small_lds_bytes(m, k / kGroup, true) <= kSmallLdsMax;
+}
 
 int32_t auto_splits(int32_t m, int32_t n, int32_t k) {
   if (m < 1 || n < 16 || k < kChunk) return 1;
+  if (use_wk(m, n, k)) return 1;
   const int64_t cols = (n / 16 + 3) / 4;
   const int64_t chunks = k / kChunk;
   int64_t s = (kTargetBlocks + cols - 1) / cols;
@@ -407,8 +469,11 @@ int32_t auto_splits(int32_t m, int32_t n, int32_t k) {
   if (cap < 1) cap = 1;
   if (s > cap) s = cap;
   if (s < 1) s = 1;
-  // M <= 16: the split's activations must fit the resident kernel's LDS
-  while (m <= 16 && s < chunks && small_lds_bytes(m, 2 * (int32_t)((chunks + s - 1) / s)) > kSmallLdsMax) ++s;
+  // M <= 16: the split's activations must fit the resident kernel's LDS; M > 16: at most
+  // kMaxGroupsChunked groups per split (the chunked kernel keeps its split's scales in LDS)
+  while (s < chunks && (m <= 16 ? small_lds_bytes(m, 2 * (int32_t)((chunks + s - 1) / s)) > kSmallLdsMax
+                                : 2 * ((chunks + s - 1) / s) > kMaxGroupsChunked))
+    ++s;
   return (int32_t)s;
 }
 
@@ -453,11 +518,20 @@ int gemm_common(const uint16_t* x, int32_t m, const uint8_t* w, const uint16_t* 
   }
   const dim3 grid((n / 16 + 3) / 4, splits);
   const size_t lds = small_lds_bytes(m, a.groups_per_split);
-  if (m <= 16 && lds <= kSmallLdsMax) {
+  const bool wk = splits == 1 && m <= 16 && small_lds_bytes(m, a.groups_per_split, true) <= kSmallLdsMax;
+  const bool small = m <= 16 && lds <= kSmallLdsMax;
+  if (!wk && !small && a.groups_per_split > kMaxGroupsChunked) return KVFP8_ERR_UNSUPPORTED;
+  if (wk) {
+    const size_t lw = small_lds_bytes(m, a.groups_per_split, true);
     if (w4)
-      hipLaunchKernelGGL(wgemm_small_kernel<true>, grid, dim3(256), lds, stream, a);
+      hipLaunchKernelGGL((wgemm_small_kernel<true, true>), dim3(n / 16, 1), dim3(256), lw, stream, a);
     else
-      hipLaunchKernelGGL(wgemm_small_kernel<false>, grid, dim3(256), lds, stream, a);
+      hipLaunchKernelGGL((wgemm_small_kernel<false, true>), dim3(n / 16, 1), dim3(256), lw, stream, a);
+  } else if (small) {
+    if (w4)
+      hipLaunchKernelGGL((wgemm_small_kernel<true, false>), grid, dim3(256), lds, stream, a);
+    else
+      hipLaunchKernelGGL((wgemm_small_kernel<false, false>), grid, dim3(256), lds, stream, a);
   } else {
     const int mt = (m + 15) / 16;
     if (w4) {

@@ -67,7 +67,9 @@ int w8_quantize_bf16(const uint16_t* w, int32_t n, int32_t k, uint8_t* packed, u
 
 /* y bf16 [M][N] = x bf16 [M][K] times the packed weights, transposed.
  * num_splits: 0 = chosen by the library, else at most K/256; the K range is
- * cut into that many slices whose fp32 partials go to `workspace` (at least
+ * cut into that many slices (for M > 16 with more than 16 activation rows'
+ * worth of LDS, at most 8192 input channels per slice: KVFP8_ERR_UNSUPPORTED
+ * otherwise) whose fp32 partials go to `workspace` (at least
  * wgemm_workspace_bytes(M, N, K, splits) bytes; 0 and NULL allowed for one
  * split) and are added in split order by a second launch. */
 int32_t wgemm_auto_splits(int32_t m, int32_t n, int32_t k);

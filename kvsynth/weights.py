@@ -35,6 +35,7 @@ def _shapes() -> dict:
     s = {}
     s["tiny"] = GemmShape("tiny", n=64, k=256, seed=0)
     s["ragged"] = GemmShape("ragged", n=320, k=1280, seed=1)
+    s["wide"] = GemmShape("wide", n=4096, k=1280, seed=3)
     # a 16-matrix stack of 8192 x 8192 weights: 0.5 GB in INT4, 1 GB in FP8, so every step streams
     # from HBM (the 256 MB Infinity Cache cannot hold it)
     s["stack_8k"] = GemmShape("stack_8k", n=8192, k=8192, layers=16, seed=2)

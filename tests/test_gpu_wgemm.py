@@ -45,7 +45,7 @@ def _gemm(bits, x, packed, scales, n, k, splits=0):
     y = torch.empty((m, n), dtype=torch.int16, device="cuda")
     s = splits or kv.wgemm_auto_splits(m, n, k)
     nb = kv.wgemm_workspace_bytes(m, n, k, s)
-    ws = torch.empty(max(nb, 16) // 4 + 4, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(nb, 16) // 4 + 4, dtype=torch.float32, device="cuda")   # counter words start at zero
     (kv.w4a16_gemm if bits == 4 else kv.w8a16_gemm)(x, packed, scales, n, k, y, num_splits=splits, workspace=ws)
     torch.cuda.synchronize()
     return host(y, np.uint16)
@@ -83,6 +83,26 @@ def test_gemm_matches_oracle(bits, m):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("m", [1, 3, 16])
+def test_gemm_in_block_k_split(bits, m):
+    """N = 4096 output channels and one split: the four waves of a block cut K = 1280 (10 groups) into
+    3 + 3 + 3 + 1 groups and add their results through LDS; also with an explicit second split."""
+    sh = wsyn.SHAPES["wide"]
+    note(f"gemm w{bits} wide m={m}")
+    w = wsyn.weights(sh)
+    packed, scales = _quantize_dev(w, bits)
+    _, _, W = _oracle_codes(w, bits)
+    x = wsyn.activations(sh, m)
+    ref = wgemm.gemm(x, W)
+    dx = dev(x)
+    assert kv.wgemm_auto_splits(m, sh.n, sh.k) == 1
+    for splits in (0, 2):
+        err = _row_err(_gemm(bits, dx, packed, scales, sh.n, sh.k, splits), ref)
+        note(f"  splits={splits}: row error {err:.2e}")
+        assert err <= TOL
+
+
+@pytest.mark.parametrize("bits", [4, 8])
 def test_gemm_tiny_and_zero_rows(bits):
     """K = 256 (one chunk, one split), an all-zero activation row and an all-zero weight group."""
     sh = wsyn.SHAPES["tiny"]
@@ -100,7 +120,7 @@ def test_gemm_tiny_and_zero_rows(bits):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("m", [1, 64])
+@pytest.mark.parametrize("m", [1, 3, 64])
 def test_gemm_full_size_sampled(bits, m):
     """8192 x 8192 weights (one matrix of the benchmark's stack), the library's split choice: the codes of
     sampled 16-row tiles bit-exact to the oracle's, and y on those tiles' columns within tolerance."""
@@ -121,3 +141,56 @@ def test_gemm_full_size_sampled(bits, m):
         err = _row_err(y[:, 16 * t:16 * t + 16], ref)
         note(f"  tile {t}: row error {err:.2e}")
         assert err <= TOL
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_workspace_reuse_and_graph_replay(bits):
+    """One workspace serves calls of different shapes and split counts back to back with the same
+    results, and a captured graph of two GEMMs replays bit-identically to the eager calls."""
+    note(f"gemm w{bits} workspace reuse + graph")
+    shapes = [(wsyn.SHAPES["ragged"], 5, 5), (wsyn.SHAPES["ragged"], 33, 2), (wsyn.SHAPES["tiny"], 1, 1),
+              (wsyn.SHAPES["ragged"], 1, 3)]
+    ws = torch.zeros(1 << 20, dtype=torch.float32, device="cuda")
+    cases = []
+    for sh, m, splits in shapes:
+        w = wsyn.weights(sh)
+        packed, scales = _quantize_dev(w, bits)
+        _, _, W = _oracle_codes(w, bits)
+        x = wsyn.activations(sh, m)
+        cases.append((sh, dev(x), packed, scales, splits, wgemm.gemm(x, W)))
+    f = kv.w4a16_gemm if bits == 4 else kv.w8a16_gemm
+    outs = []
+    for rep in range(2):
+        for sh, dx, packed, scales, splits, ref in cases:
+            y = torch.empty((dx.shape[0], sh.n), dtype=torch.int16, device="cuda")
+            f(dx, packed, scales, sh.n, sh.k, y, num_splits=splits, workspace=ws)
+            torch.cuda.synchronize()
+            assert _row_err(host(y, np.uint16), ref) <= TOL, (sh.name, dx.shape[0], splits, rep)
+            outs.append(y)
+    for a_, b_ in zip(outs[:len(cases)], outs[len(cases):]):
+        assert torch.equal(a_, b_)
+    # graph of the first two cases
+    ys = [torch.empty((c[1].shape[0], c[0].n), dtype=torch.int16, device="cuda") for c in cases[:2]]
+
+    def run():
+        for (sh, dx, packed, scales, splits, _), y in zip(cases[:2], ys):
+            f(dx, packed, scales, sh.n, sh.k, y, num_splits=splits, workspace=ws)
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        run()
+    junk = torch.empty(1 << 20, dtype=torch.float32, device="cuda")
+    for i in range(4):
+        for y in ys:
+            y.fill_(0x5555)
+        junk.normal_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for y, want in zip(ys, outs[:2]):
+            assert torch.equal(y, want), i
