@@ -57,6 +57,9 @@ def parse():
                    help="batch sizes of the layer-stack step (the latent cache runs those of them in {1, 64})")
     p.add_argument("--layers-only", action="store_true",
                    help="run only the layer-stack step (skips the headline workload's timing)")
+    p.add_argument("--no-weights", action="store_true",
+                   help="skip the weight-quantised decode GEMM runs (INT4 vs FP8 weights)")
+    p.add_argument("--weights-only", action="store_true", help="run only the weight-quantised GEMM section")
     p.add_argument("--capacity-ref-batch", type=int, default=32,
                    help="the byte budget is what this many 8192-token requests take in the BF16 cache")
     p.add_argument("--flush-mib", type=int, default=512,
@@ -490,8 +493,86 @@ def main():
         torch.cuda.empty_cache()
         return r
 
+    def measure_weights(reps=20):
+        """The weight-quantised decode GEMM over a stack of 16 distinct 8192 x 8192 weight matrices
+        (0.5 GB of INT4 codes / 1 GB of FP8 codes, so every pass streams from HBM), y = x W^T for
+        M = 1..64 activation rows, INT4 (W4A16) and FP8 (W8A16) weights, the whole stack captured in
+        one HIP graph and timed by replay."""
+        from kvsynth import weights as wsyn
+        sh = wsyn.SHAPES["stack_8k"]
+        N, K, L = sh.n, sh.k, sh.layers
+        gen = torch.Generator(device="cuda")
+        out = {"workload": f"{L} weight matrices of {N} x {K} (bf16 N(0, 0.02^2) drawn on the device with a "
+                           f"seeded generator, quantised by the library), y = x W^T per matrix",
+               "bytes_per_matrix": {"int4": N * K // 2 + N * K // 128 * 2, "fp8": N * K + N * K // 128 * 2}}
+        for bits in (4, 8):
+            gen.manual_seed(sh.seed)
+            packs, scs = [], []
+            for _ in range(L):
+                wf = (torch.randn(N, K, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+                pk = torch.empty(N * K // (2 if bits == 4 else 1), dtype=torch.uint8, device="cuda")
+                sc = torch.empty(N * K // 128, dtype=torch.int16, device="cuda")
+                (kv.w4_quantize_bf16 if bits == 4 else kv.w8_quantize_bf16)(wf, pk, sc)
+                packs.append(pk)
+                scs.append(sc)
+                del wf
+            torch.cuda.synchronize()
+            f = kv.w4a16_gemm if bits == 4 else kv.w8a16_gemm
+            res = {}
+            for m in (1, 8, 16, 32, 64):
+                x = (torch.randn(m, K, device="cuda", generator=gen)).to(torch.bfloat16)
+                y = torch.empty(m, N, dtype=torch.bfloat16, device="cuda")
+                sp = kv.wgemm_auto_splits(m, N, K)
+                ws = torch.empty(max(kv.wgemm_workspace_bytes(m, N, K, sp), 16) // 4 + 4, dtype=torch.float32,
+                                 device="cuda")
+
+                def stack():
+                    for li in range(L):
+                        f(x, packs[li], scs[li], N, K, y, workspace=ws)
+
+                stack()
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    stack()
+                torch.cuda.current_stream().wait_stream(side)
+                with torch.cuda.graph(g):
+                    stack()
+                for _ in range(3):
+                    g.replay()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                us = 1e3 * e0.elapsed_time(e1) / (reps * L)
+                gbs = out["bytes_per_matrix"]["int4" if bits == 4 else "fp8"] / (us * 1e-6) / 1e9
+                res[f"M{m}"] = {"us_per_gemm": round(us, 2), "weight_gbs": round(gbs, 1),
+                                "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                                "stack_passes_per_s": round(1e6 / (us * L), 1),
+                                "tokens_per_s": round(m * 1e6 / (us * L), 1), "splits": sp}
+                log(f"weights w{bits} M={m}: {res[f'M{m}']}")
+                del g, x, y, ws
+            out["int4" if bits == 4 else "fp8"] = res
+            del packs, scs
+            torch.cuda.empty_cache()
+        out["int4_speedup"] = {mk: round(out["fp8"][mk]["us_per_gemm"] / out["int4"][mk]["us_per_gemm"], 3)
+                               for mk in out["int4"]}
+        out["note"] = ("tokens_per_s = M rows x passes over the stack per second (one token per request per "
+                       "pass); weight_gbs counts codes + scales; graph replay of the whole stack")
+        return out
+
     w = wl.WORKLOADS[args.workload]
     results = {}
+    if args.weights_only:
+        print(json.dumps({"metric": "weight-quantised decode GEMM (INT4 vs FP8 weights), one GPU",
+                          "weight_gemm": measure_weights()}), flush=True)
+        return
     if args.layers_only:
         args.no_sweep = args.no_capacity = args.no_extra = args.no_cpu_baseline = True
         args.no_layers = False
@@ -583,6 +664,10 @@ def main():
                 del hb
                 torch.cuda.empty_cache()
 
+    weight_runs = None
+    if not args.no_weights and not args.fp8_only_steps and not args.layers_only:
+        weight_runs = measure_weights()
+
     extra = {}
     if not args.no_extra and not args.fp8_only_steps:
         for name in ("gqa_batch", "long", "latent"):
@@ -659,6 +744,8 @@ def main():
         line["batch_sweep_flushed"] = sweep
     if capacity:
         line["capacity_fixed_budget"] = capacity
+    if weight_runs:
+        line["weight_gemm"] = weight_runs
     if layer_runs:
         line["layer_stack_step"] = layer_runs | {
             "note": f"one decode step over {args.layers} layers sharing one page table and tag set "

@@ -444,7 +444,7 @@ int quantize_common(const uint16_t* w, int32_t n, int32_t k, uint8_t* packed, ui
 
 constexpr int64_t kTargetBlocks = 512;      // two blocks of four waves per CU
 
-constexpr size_t kSmallLdsMax = 64 * 1024;  // dynamic LDS of the M <= 16 kernel
+constexpr size_t kSmallLdsMax = 80 * 1024;  // dynamic LDS of the M <= 16 kernel (two blocks fit a CU)
 
 // activations [M][gps*128 + 8] bf16, group sums [gps][16] fp32, scales [tiles][gps][16] bf16, and for
 // the in-block K split the four waves' results [4][64] f32x4
