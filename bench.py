@@ -12,7 +12,11 @@ excluded).
 
 Prints one JSON line (rank 0).  Metric: KV-read GB/s of the whole step
 (algorithmic bytes: sum over non-aborted requests of L * Hkv * D * 2 * bytes
-per element) and steps/s.
+per element) and steps/s.  Further sections of the line: the flushed batch
+sweep, admission under a fixed byte budget (FP8 vs BF16 through the page
+allocator), a whole decode step over a 61-layer stack (eager and HIP graph,
+tracker on and off), the INT4- vs FP8-weight decode GEMM, the other
+workloads (ragged batch, long context, latent cache) and the CPU oracle.
 """
 from __future__ import annotations
 
