@@ -41,8 +41,10 @@ constexpr int kChunk = 256;          // input channels staged in LDS per step (t
 constexpr int kRing = 8;             // weight groups in flight per wave
 constexpr int kRowBytes = kChunk * 2 + 16;  // LDS row stride of the staged activations (padded)
 constexpr float kW4Bias = 136.0f;    // the expansion yields q + 136
-constexpr int kMaxGroupsChunked = 64;
-constexpr int kVmWait0 = 0x0F70;       // s_waitcnt vmcnt(0) (gfx9 encoding: expcnt, lgkmcnt left open)  // groups per split of the M > 16 kernel (its scales sit in LDS)
+constexpr int kMaxGroupsChunked = 64;  // groups per split of the M > 16 kernel (its scales sit in LDS)
+// s_waitcnt immediate for vmcnt(n) alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
+// left at their maxima)
+constexpr int vm_wait_enc(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 struct WgemmArgs {
   const uint16_t* x;        // bf16 [M][K]
@@ -183,7 +185,7 @@ template <bool W4, bool WK>
 __global__ __launch_bounds__(256) void wgemm_small_kernel(WgemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int kTiles = WK ? 1 : 4;
-  constexpr int kRingS = kRing;   // groups in flight per wave (16 measured slower: 14.2 vs 12.0 us)
+  constexpr int kRingS = kRing;   // measured on 8192 x 8192: 4 and 8 alike, 12 and 16 slower
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nn = lane & 15, qq = lane >> 4;
   const int KG = a.K / kGroup;
@@ -202,48 +204,54 @@ __global__ __launch_bounds__(256) void wgemm_small_kernel(WgemmArgs a) {
   const int ngw = WK ? max(0, min(gq, ng - gw0)) : ng;
   const int st = WK ? 0 : wave;                          // the wave's tile inside s_sc
 
-  // the weight ring first: its loads do not depend on the activations, so the two latencies overlap
   const WStream<W4> ws(a, tile, g0 + gw0, ngw, lane);
   constexpr int kB = WStream<W4>::kB;
+  load_scales(a, WK ? blockIdx.x : blockIdx.x * 4, kTiles, g0, ng, gcap, s_sc);
+
+  // Activations, then the weight ring, then one wait that leaves exactly the ring outstanding: the
+  // loads retire in issue order, so the activations go first (their latency overlaps the ring's), and
+  // the wait -- the builtin, which the compiler's load counting sees -- also retires the out-of-range
+  // activation loads whose data is never read (left outstanding, they would make the compiler wait for
+  // the whole ring inside the loop).  Batches before the last (only when M * groups > 256) are plain.
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)((int64_t)a.M * a.K * 2));
+  const int per_row = ng * (kGroup / 8), total = a.M * per_row;
+  auto x_off = [&](int i) {
+    const int r = i / per_row, c = i % per_row;
+    return i < total ? (uint32_t)(((int64_t)r * a.K + g0 * kGroup + 8 * c) * 2) : kOOB;
+  };
+  auto x_put = [&](int i, const u32x4_t& v) {
+    if (i < total) *reinterpret_cast<u32x4_t*>(smem + (i / per_row) * row_bytes + 16 * (i % per_row)) = v;
+    // group sums on the way: a group of a row is 16 consecutive columns, i.e. 16 aligned lanes
+    // (per_row and 256 are multiples of 16); out-of-range lanes loaded zeros
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sum += bf16_bits_to_f32(v[e] & 0xFFFFu) + bf16_bits_to_f32(v[e] >> 16);
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) sum += __shfl_xor(sum, m);
+    if (i < total && (threadIdx.x & 15) == 0) xs[((i % per_row) >> 4) * 16 + i / per_row] = sum;
+  };
+  constexpr int kXB = 16;                                // activation loads per thread and batch
+  int xbase = 0;
+  for (; xbase + 256 * kXB < total; xbase += 256 * kXB) {
+    u32x4_t v[kXB];
+#pragma unroll
+    for (int t = 0; t < kXB; ++t) v[t] = __builtin_amdgcn_raw_buffer_load_b128(xr, x_off(xbase + 256 * t + tid), 0, 0);
+#pragma unroll
+    for (int t = 0; t < kXB; ++t) x_put(xbase + 256 * t + tid, v[t]);
+  }
+  u32x4_t v[kXB];
+#pragma unroll
+  for (int t = 0; t < kXB; ++t) v[t] = __builtin_amdgcn_raw_buffer_load_b128(xr, x_off(xbase + 256 * t + tid), 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   u32x4_t wr[kRingS][kB / 16];
 #pragma unroll
   for (int u = 0; u < kRingS; ++u) {
     ws.load(wr[u], u);
     __builtin_amdgcn_sched_barrier(0);
   }
-  load_scales(a, WK ? blockIdx.x : blockIdx.x * 4, kTiles, g0, ng, gcap, s_sc);
-
-  // activations: all loads of a batch in flight before the stores
-  {
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)((int64_t)a.M * a.K * 2));
-    const int per_row = ng * (kGroup / 8), total = a.M * per_row;
-    for (int base = 0; base < total; base += 256 * 8) {
-      u32x4_t v[8];
+  __builtin_amdgcn_s_waitcnt(vm_wait_enc(kRingS * (kB / 16)));
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int i = base + 256 * t + tid, r = i / per_row, c = i % per_row;
-        v[t] = __builtin_amdgcn_raw_buffer_load_b128(
-            xr, i < total ? (uint32_t)(((int64_t)r * a.K + g0 * kGroup + 8 * c) * 2) : kOOB, 0, 0);
-      }
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int i = base + 256 * t + tid;
-        if (i < total) *reinterpret_cast<u32x4_t*>(smem + (i / per_row) * row_bytes + 16 * (i % per_row)) = v[t];
-        // group sums on the way: a group of a row is 16 consecutive columns, i.e. 16 aligned lanes
-        // (per_row and 256 are multiples of 16); out-of-range lanes loaded zeros
-        float sum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sum += bf16_bits_to_f32(v[t][e] & 0xFFFFu) + bf16_bits_to_f32(v[t][e] >> 16);
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) sum += __shfl_xor(sum, m);
-        if (i < total && (tid & 15) == 0) xs[((i % per_row) >> 4) * 16 + i / per_row] = sum;
-      }
-    }
-  }
-  // Retire every prologue load, including the out-of-range ones whose data is never read: the compiler
-  // does not wait for those, and left outstanding they make it wait for the whole ring inside the loop
-  // when their registers are reused.  (The builtin, unlike inline asm, updates the compiler's count.)
-  __builtin_amdgcn_s_waitcnt(kVmWait0);
+  for (int t = 0; t < kXB; ++t) x_put(xbase + 256 * t + tid, v[t]);
   __syncthreads();
 
   // rows >= M read row M-1: their results are never stored
