@@ -63,6 +63,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// Sum over the 16 lanes of each DPP row (lanes 16h..16h+15), every lane of the row receiving it: quad
+// permutations [1,0,3,2] and [2,3,0,1] give the quad sum, rotations by 4 and 8 inside the row add the
+// other quads.  All VALU (a __shfl_xor compiles to an LDS permute: a round trip per step).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp<0x124>(v);   // row_ror:4
+  v += dpp<0x128>(v);   // row_ror:8
+  return v;
+}
+
+// Sum of the eight bf16 values of a 16-byte load (a bf16 widens to fp32 by a shift or a mask).
+__device__ __forceinline__ float sum8_bf16(const u32x4_t& v) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s += __uint_as_float(v[e] << 16) + __uint_as_float(v[e] & 0xFFFF0000u);
+  return s;
+}
+
 // bf16 pair of two INT4 codes (plus the bias 136) from the nibbles at bits 4i and 16 + 4i.
 __device__ __forceinline__ uint32_t w4_pair(uint32_t w, int i) {
   return ((w >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
@@ -223,11 +246,7 @@ __global__ __launch_bounds__(256) void wgemm_small_kernel(WgemmArgs a) {
     if (i < total) *reinterpret_cast<u32x4_t*>(smem + (i / per_row) * row_bytes + 16 * (i % per_row)) = v;
     // group sums on the way: a group of a row is 16 consecutive columns, i.e. 16 aligned lanes
     // (per_row and 256 are multiples of 16); out-of-range lanes loaded zeros
-    float sum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sum += bf16_bits_to_f32(v[e] & 0xFFFFu) + bf16_bits_to_f32(v[e] >> 16);
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) sum += __shfl_xor(sum, m);
+    const float sum = row_sum16(sum8_bf16(v));
     if (i < total && (threadIdx.x & 15) == 0) xs[((i % per_row) >> 4) * 16 + i / per_row] = sum;
   };
   constexpr int kXB = 16;                                // activation loads per thread and batch
@@ -307,29 +326,29 @@ __global__ __launch_bounds__(256, 2) void wgemm_kernel(WgemmArgs a) {
 
   // ---- activation staging: thread -> (row 8p + tid/32, 16-byte column tid%32) of a chunk
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, (uint32_t)((int64_t)a.M * a.K * 2));
+  // Two register sets: chunk c's rows are loaded at the start of chunk c - 2 and stored to LDS at the
+  // end of chunk c - 1.  Loads retire in issue order, so the store's wait also retires every weight
+  // load issued before them; loading two chunks ahead keeps the weight loads of the last two chunks in
+  // flight through that wait (one chunk ahead left only the newest two groups in flight).
   const int xr_row = tid >> 5, xr_col = tid & 31;
-  u32x4_t xr[2 * MT];
-  auto x_load = [&](int ch) {   // chunk ch of the split
+  u32x4_t xr[2][2 * MT];
+  auto x_load = [&](int set, int ch) {   // chunk ch of the split into register set `set`
 #pragma unroll
     for (int p = 0; p < 2 * MT; ++p) {
       const int row = 8 * p + xr_row;
       const uint32_t off = (row < a.M && ch < nch)
                                ? (uint32_t)(((int64_t)row * a.K + (int64_t)(g0 / 2 + ch) * kChunk + 8 * xr_col) * 2)
                                : kOOB;
-      xr[p] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+      xr[set][p] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
     }
   };
-  auto x_store = [&](int buf) {
+  auto x_store = [&](int set, int buf) {
 #pragma unroll
     for (int p = 0; p < 2 * MT; ++p) {
       const int row = 8 * p + xr_row;
-      *reinterpret_cast<u32x4_t*>(s_x[buf] + row * kRowBytes + 16 * xr_col) = xr[p];
-      float sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sum += bf16_bits_to_f32(xr[p][i] & 0xFFFFu) + bf16_bits_to_f32(xr[p][i] >> 16);
+      *reinterpret_cast<u32x4_t*>(s_x[buf] + row * kRowBytes + 16 * xr_col) = xr[set][p];
       // the 16 lanes of one (row, group) are lanes 16h..16h+15 of this wave
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) sum += __shfl_xor(sum, m);
+      const float sum = row_sum16(sum8_bf16(xr[set][p]));
       if ((xr_col & 15) == 0) s_xs[buf][xr_col >> 4][row] = sum;
     }
   };
@@ -344,8 +363,9 @@ __global__ __launch_bounds__(256, 2) void wgemm_kernel(WgemmArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   }
   load_scales(a, blockIdx.x * 4, 4, g0, ng, kMaxGroupsChunked, s_sc);
-  x_load(0);
-  x_store(0);
+  x_load(0, 0);
+  x_load(1, 1);
+  x_store(0, 0);
   __syncthreads();
 
   f32x4_t acc[MT];
@@ -357,7 +377,7 @@ __global__ __launch_bounds__(256, 2) void wgemm_kernel(WgemmArgs a) {
     for (int u = 0; u < kR; ++u) {
       const int buf = (u >> 1) & 1;           // chunk parity (base is a multiple of 4 groups)
       const int gl = u & 1;                   // group inside the chunk
-      if (gl == 0) x_load((base + u) / 2 + 1);
+      if (gl == 0) x_load(buf, (base + u) / 2 + 2);
       f32x4_t accg[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) accg[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -378,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void wgemm_kernel(WgemmArgs a) {
       ws.load(wr[u], base + u + kR);
       __builtin_amdgcn_sched_barrier(0);
       if (gl == 1) {
-        x_store(buf ^ 1);
+        x_store(buf ^ 1, buf ^ 1);
         __syncthreads();
       }
     }
@@ -402,8 +422,10 @@ __global__ __launch_bounds__(256) void wquant_kernel(const uint16_t* w, int32_t 
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  amax = fmaxf(amax, dpp<0xB1>(amax));    // max over the 16 lanes of the DPP row (one output channel)
+  amax = fmaxf(amax, dpp<0x4E>(amax));
+  amax = fmaxf(amax, dpp<0x124>(amax));
+  amax = fmaxf(amax, dpp<0x128>(amax));
   const uint32_t sb = pack_bf16x2(__fdiv_rn(amax, W4 ? 7.0f : kE4M3Max), 0.f) & 0xFFFFu;
   const float s = bf16_bits_to_f32(sb);
   const float inv = s > 0.f ? __fdiv_rn(1.0f, s) : 0.f;
