@@ -137,6 +137,10 @@ def test_host_validation_codes(lib):
     assert gm(A, 4, A, A, 64, 512, 2, None, 0, A, None) == -1                 # no workspace
     assert gm(A, 4, A, A, 64, 512, 2, A, 64, A, None) == -4                   # too small
     assert lib.w8a16_gemm(A + 8, 4, A, A, 64, 256, 0, None, 0, A, None) == -5
+    # M > 16 keeps a split's scales in LDS: at most 64 groups (8192 inputs) per split
+    assert gm(A, 32, A, A, 64, 16384, 1, None, 0, A, None) == -3
+    assert 2 <= lib.wgemm_auto_splits(32, 64, 16384)                           # the library's own choice fits
+    assert lib.w4_packed_bytes(65536, 65536) == 65536 * 65536 // 2
     assert lib.wgemm_workspace_bytes(4, 64, 512, 1) == 0
     assert lib.wgemm_workspace_bytes(4, 64, 512, 2) == 2 * 4 * 64 * 4
     assert 1 <= lib.wgemm_auto_splits(1, 8192, 8192) <= 32
