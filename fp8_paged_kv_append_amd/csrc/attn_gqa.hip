@@ -267,6 +267,7 @@ __global__ __launch_bounds__(kThreads) void attn_gqa_split_kernel(AttnArgs a) {
   __shared__ float s_l[kWaves][16];
   __shared__ float s_acc[kWaves][16][kD];
   __shared__ int s_bad;
+  __shared__ float s_knew[kD], s_vnew[kD], s_snew[16];
 
   const int L = a.ctx_lens[r];
   const bool aborted = a.flags != nullptr && a.flags[r] != 0u;
@@ -281,7 +282,11 @@ __global__ __launch_bounds__(kThreads) void attn_gqa_split_kernel(AttnArgs a) {
     return;  // the merge kernel zeroes the rows itself
   }
   if (c0 >= L) return;  // past this request's context: the merge does not read this split
-  const int c1 = min(L, c0 + chunk);
+  // With the step's token passed in, the tiles stop before it (position L - 1) and the block whose
+  // chunk holds it writes it and adds it to its softmax in the epilogue: nothing reads it back.
+  const bool fold = a.k_new != nullptr;
+  const bool owner = fold && L - 1 < c0 + chunk;
+  const int c1 = min(fold ? L - 1 : L, c0 + chunk);
 
   // q^T operand: lane (q4, n) holds head g*G+n, dims 32*q4 .. 32*q4+31 (zero for padding heads)
   u32x4_t qv[4];
@@ -360,12 +365,57 @@ __global__ __launch_bounds__(kThreads) void attn_gqa_split_kernel(AttnArgs a) {
 #undef KVFP8_ISSUE
   }
 
+  // ---- the step's token (owner block): quantise it as the append does, write it into its page, keep
+  // its decoded K and V of this head in LDS
+  if (owner) {
+    const int pos = L - 1;
+    const int page = pt[pos / S];
+    const bool ok = page >= 0 && page < a.num_pages;
+    if (!ok) bad = true;
+    const int slot = pos % S, H = a.num_kv_heads;
+    for (int d = threadIdx.x; d < kD; d += kThreads) {
+      const uint32_t kb = a.k_new[((int64_t)r * H + g) * kD + d], vb = a.v_new[((int64_t)r * H + g) * kD + d];
+      const int64_t ko = ok ? k_elem_offset<FP8 ? 1 : 2>(page, g, slot, d, H, S, kD) : 0;
+      const int64_t vo = ((int64_t)page * H + g) * kD * S + (int64_t)d * S + slot;
+      if (FP8) {
+        const uint32_t kc = encode_e4m3x2(bf16_bits_to_f32(kb) * a.k_inv, 0.f) & 0xFFu;
+        const uint32_t vc = encode_e4m3x2(bf16_bits_to_f32(vb) * a.v_inv, 0.f) & 0xFFu;
+        if (ok) {
+          const_cast<uint8_t*>(kpool)[ko] = (uint8_t)kc;
+          const_cast<uint8_t*>(vpool)[vo] = (uint8_t)vc;
+        }
+        s_knew[d] = e4m3_to_f32(kc);
+        s_vnew[d] = e4m3_to_f32(vc);
+      } else {
+        if (ok) {
+          reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(kpool))[ko] = (uint16_t)kb;
+          reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(vpool))[vo] = (uint16_t)vb;
+        }
+        s_knew[d] = bf16_bits_to_f32(kb);
+        s_vnew[d] = bf16_bits_to_f32(vb);
+      }
+    }
+  }
+
   // ---- merge the four waves
   float l_run = st.l;
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
   if (threadIdx.x == 0) s_bad = 0;
   __syncthreads();
+  if (owner) {
+    // its score per head, log2 domain like the tiles': threads 16 hn .. 16 hn + 15 take 8 dims each
+    const int hn = threadIdx.x >> 4, part = threadIdx.x & 15;
+    float dot = 0.f;
+    if (hn < G) {
+      const uint16_t* qh = a.q + ((int64_t)r * a.num_q_heads + g * G + hn) * kD + 8 * part;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot += bf16_bits_to_f32(qh[e]) * s_knew[8 * part + e];
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) dot += shfl_xor(dot, m);
+    if (hn < G && part == 0) s_snew[hn] = dot * c_log2;
+  }
   if (q4 == 0) {
     s_m[wave][n] = st.m;
     s_l[wave][n] = l_run;
@@ -383,6 +433,7 @@ __global__ __launch_bounds__(kThreads) void attn_gqa_split_kernel(AttnArgs a) {
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][hn]);
+    if (owner) M = fmaxf(M, s_snew[hn]);
     float lsum = 0.f, o = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
@@ -390,6 +441,11 @@ __global__ __launch_bounds__(kThreads) void attn_gqa_split_kernel(AttnArgs a) {
         const float f = exp2f(s_m[w][hn] - M);
         lsum += s_l[w][hn] * f;
         o += s_acc[w][hn][d] * f;
+      }
+      if (owner) {
+        const float f = exp2f(s_snew[hn] - M);
+        lsum += f;
+        o += s_vnew[d] * f;
       }
     }
     const int64_t row = (int64_t)r * Hq + g * G + hn;

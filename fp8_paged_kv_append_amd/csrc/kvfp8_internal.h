@@ -22,6 +22,12 @@ struct AttnArgs {
   int32_t max_ctx;
   float qk_scale_log2;        // sm_scale * k_scale * log2(e)
   float v_scale;
+  // Optional: this step's new token of every request (bf16 rows [B][Hkv][D] / [B][Hkv][Dv]), written
+  // at position ctx_lens[r] - 1 by the block whose chunk holds it and folded into that block's softmax
+  // from registers (null: the token is already in the pool).  k_inv, v_inv: fl32(1/scale) (FP8).
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  float k_inv, v_inv;
 };
 
 struct MergeArgs {

@@ -237,6 +237,12 @@ int paged_decode_attn_latent_bf16(const kvfp8_pool_desc* desc, const uint16_t* q
  * for each later layer its write, honouring the flags layer 0 left (read,
  * not rewritten: the pages' tag check runs once per step, before any read),
  * and its attention.  Each write puts request r's token at ctx_lens[r] - 1.
+ * For the GQA cache a later layer's write is done by its attention launch:
+ * the block whose split holds position ctx_lens[r] - 1 quantises the token
+ * as kv_append_fp8 does, stores it, and adds it to its softmax from the
+ * values it holds (the pool contents after the step are the same).  A
+ * request with ctx_lens[r] > max_ctx_len is a caller error: its rows are
+ * zero and later GQA layers do not write its token.
  * page_tags NULL = no-op tracker: no check; abort_flags, when given, are
  * only read.  Every layer's arguments are checked before the first launch,
  * so an error status means nothing was enqueued.  The workspace is shared by

@@ -1,5 +1,6 @@
 """One decode step over a stack of layers through kv_decode_step_* (one launch sequence: the tag check
-once, fused with layer 0's write, then every layer's write and attention), against the oracle's
+once, fused with layer 0's write, then every layer's write and attention; for the GQA cache, layers
+after the first write the token from the attention launch), against the oracle's
 multi-layer step: flags and every layer's pools bit-exact, every layer's attention within tolerance,
 aborted and empty requests zero in every layer (agentlenshq summary, section "KV Cache 完整性检查":
 one batched check before any read).  The same step captured in a HIP graph replays bit-identically."""
@@ -22,15 +23,18 @@ LAYERS = 3
 class Stack:
     """LAYERS layers over one page table / tag set: oracle pools (numpy) and device stacks side by side."""
 
-    def __init__(self, kv_dtype, latent, stale=(1, 6), hole=True):
+    def __init__(self, kv_dtype, latent, stale=(1, 6), hole=True, lens=None, splits=0):
         if latent:
             w = wl.WORKLOADS["latent"].with_(batch=9, num_q_heads=16, num_pages=400, ctx_lo=1, ctx_hi=600)
         else:
             w = wl.WORKLOADS["sweep_b16"].with_(batch=9, num_pages=2000, ctx_lo=1, ctx_hi=700)
         self.w, self.kv_dtype, self.latent = w, kv_dtype, latent
         fp8 = kv_dtype == "fp8"
-        lens = wl.ctx_lens(w)
-        lens[3] = 0
+        if lens is None:
+            lens = wl.ctx_lens(w)
+            lens[3] = 0
+        else:
+            lens = np.asarray(lens, dtype=np.int32)
         pt, _ = wl.page_table(w, lens)
         tags = wl.page_tags(w)
         exp = wl.expected_tags(w, pt, lens, tags, np.asarray(stale, dtype=np.int64))
@@ -95,9 +99,10 @@ class Stack:
         self.dv_new = None if latent else dev(np.stack(self.v_new))
         self.max_ctx = int(lens.max())
         B, Hq = w.batch, w.num_q_heads
-        if latent:
+        self.splits = splits
+        if splits == 0 and latent:
             splits = kv.paged_decode_attn_latent_auto_splits(B, Hq, self.max_ctx)
-        else:
+        elif splits == 0:
             splits = kv.paged_decode_attn_auto_splits(B, w.num_kv_heads, self.max_ctx)
         n = kv.paged_decode_attn_workspace_bytes(B, Hq, w.v_dim, splits)
         self.ws = torch.empty(max(n, 16) // 4 + 4, dtype=torch.float32, device="cuda")
@@ -111,7 +116,7 @@ class Stack:
                               abort_flags=self.flags if tracker else None,
                               k_scales=self.ks if self.kv_dtype == "fp8" else None,
                               v_scales=self.vs if self.kv_dtype == "fp8" and not self.latent else None,
-                              sm_scale=self.sm_scale, workspace=self.ws)
+                              sm_scale=self.sm_scale, num_splits=self.splits, workspace=self.ws)
 
     def oracle(self, tracker=True):
         B = self.w.batch
@@ -140,6 +145,30 @@ def test_layer_stack_step_matches_oracle(kv_dtype, latent):
         assert err <= ATTN_TOL
         for r in np.flatnonzero(o_flags).tolist() + [3]:
             assert not g_out[l, r].any()
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_layer_stack_token_at_chunk_edges(kv_dtype, splits):
+    """Layers after the first write the step's token from their attention launch, in the block whose
+    split holds position L - 1.  Lengths put that position alone in its split (129, 257, 385 with
+    128-token splits), last in one (128, 512), first of the context (L = 1) and mid-tile; pools
+    bit-exact and outputs within tolerance in every layer."""
+    note(f"layer stack chunk edges {kv_dtype} splits={splits}")
+    lens = [1, 129, 0, 128, 512, 385, 64, 65, 257]
+    s = Stack(kv_dtype, False, stale=(6,), hole=False, lens=lens, splits=splits)
+    s.run()
+    torch.cuda.synchronize()
+    o_flags, o_outs = s.oracle()
+    assert np.array_equal(host(s.flags, np.uint32), o_flags)
+    g_out = host(s.out, np.uint16)
+    for l in range(LAYERS):
+        assert np.array_equal(host(s.dkp[l], s.et), s.states[l]["k_pool"]), l
+        assert np.array_equal(host(s.dvp[l], s.et), s.states[l]["v_pool"]), l
+        err = attn_error(g_out[l], o_outs[l])
+        note(f"  layer {l}: error {err:.3e}")
+        assert err <= ATTN_TOL
+        assert not g_out[l, 6].any() and not g_out[l, 2].any()
 
 
 @pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
