@@ -71,7 +71,10 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=8, help="requests in the CPU oracle sample")
     p.add_argument("--fp8-only-steps", action="store_true", help="time only the FP8 step (profiling runs)")
     p.add_argument("--unfused", action="store_true",
-                   help="tag check and append as two launches instead of kv_tag_check_append_*")
+                   help="tag check, append and attention as three launches")
+    p.add_argument("--two-launch", action="store_true",
+                   help="kv_tag_check_append_* then the attention (default: kv_decode_step_* over one layer, "
+                        "which for the GQA cache is one launch: check, write and attention)")
     p.add_argument("--graph", action="store_true",
                    help="time replays of a captured HIP graph of one step (default: eager launches)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -82,9 +85,11 @@ def parse():
 class DeviceCache:
     """One workload's cache on the device (FP8 or BF16), filled through the library's append."""
 
-    def __init__(self, w, kv_dtype, host, torch, kv, fused=True):
+    def __init__(self, w, kv_dtype, host, torch, kv, fused=True, one_launch=True):
         self.w, self.kv_dtype, self.torch, self.kv = w, kv_dtype, torch, kv
         self.fused = fused
+        # the library's whole step (kv_decode_step_* over one layer): one launch for the GQA cache
+        self.one_launch = fused and one_launch and not w.latent
         nk = w.num_pages * w.num_kv_heads * w.page_size * w.head_dim
         nv = w.num_pages * w.num_kv_heads * w.page_size * w.v_dim
         tdt = torch.uint8 if kv_dtype == "fp8" else torch.int16
@@ -157,7 +162,19 @@ class DeviceCache:
             kv.paged_decode_attn_bf16(self.desc, self.q, self.kp, self.vp, self.pt, self.lens, self.max_ctx,
                                       self.out, f, num_splits=self.splits, workspace=self.ws)
 
+    def lib_step(self, tracker=True):
+        """kv_decode_step_* over this one layer: for the GQA cache a single launch in which every block
+        checks its request's page tags, the block holding position L - 1 writes the new token, and the
+        attention runs (plus the merge when split)."""
+        self.kv.decode_step(self.desc, self.kv_dtype, self.kp, self.vp, self.pt, self.lens, self.max_ctx, self.q,
+                            self.k_new, self.v_new, None, None, self.out, page_tags=self.tags if tracker else None,
+                            expected_tags=self.exp if tracker else None, abort_flags=self.flags if tracker else None,
+                            k_scale=self.k_scale, v_scale=self.v_scale, num_splits=self.splits, workspace=self.ws)
+
     def step(self, tracker=True):
+        if self.one_launch:
+            self.lib_step(tracker)
+            return
         if tracker and self.fused:
             self.check_append()
         else:
@@ -213,6 +230,11 @@ class DeviceCache:
         for e in evs:
             flush.add_(1)
             e[0].record()
+            if self.one_launch:  # the whole step is the one launch: it lands in the attention column
+                e[1].record()
+                self.lib_step()
+                e[2].record()
+                continue
             if self.fused:
                 self.check_append()
             else:
@@ -235,6 +257,12 @@ class DeviceCache:
         torch.cuda.synchronize()
         for e in evs:
             e[0].record()
+            if self.one_launch:  # one launch: check, write and attention are in the attention column
+                e[1].record()
+                e[2].record()
+                self.lib_step(tracker)
+                e[3].record()
+                continue
             if tracker and self.fused:
                 self.check_append()
             elif tracker:
@@ -398,7 +426,7 @@ def main():
 
     def measure(w, kvd, host, stale, elems, steps, warmup, full=True, flushed=False):
         t = time.perf_counter()
-        c = DeviceCache(w, kvd, host, torch, kv, fused=not args.unfused)
+        c = DeviceCache(w, kvd, host, torch, kv, fused=not args.unfused, one_launch=not args.two_launch)
         log(f"{w.name} {kvd}: cache filled in {time.perf_counter() - t:.1f} s, splits={c.splits}")
         elt = 1 if kvd == "fp8" else 2
         if flushed:
@@ -602,7 +630,9 @@ def main():
                           "steps_per_s": round(1e3 / r["step_ms"], 1), "attn_us": round(1e3 * r["attn_ms"], 2),
                           "attn_us_p95": round(1e3 * r["attn_ms_p95"], 2), "attn_gbs": round(r["gbs_attn"], 1),
                           "attn_pct_hbm_peak": round(100 * r["gbs_attn"] / HBM_PEAK_GBS, 2),
-                          "check_append_us": round(1e3 * r["check_append_ms"], 2), "splits": r["splits"]}
+                          "splits": r["splits"]}
+                if args.unfused or args.two_launch:
+                    e[kvd]["check_append_us"] = round(1e3 * r["check_append_ms"], 2)
             e["fp8_speedup_step"] = round(e["bf16"]["step_us"] / e["fp8"]["step_us"], 3)
             e["stale_requests"] = len(st_b)
             sweep[f"B{b}"] = e
@@ -701,6 +731,22 @@ def main():
                           "layer_stack_step": layer_runs}), flush=True)
         return
     f8 = results["fp8"]
+    if args.unfused or args.two_launch:
+        step_desc = (("tag check + append(1 token/request)" if args.unfused else
+                      "fused tag check + append(1 token/request)") + " + attention (+ merge when split)")
+        kernel_desc = "paged_decode_attn_fp8 (split kernel, plus the merge kernel when splits > 1)"
+        breakdown = (({"tag_check": round(f8["check_ms"], 5), "append": round(f8["append_ms"], 5)}
+                      if args.unfused else {"tag_check_append": round(f8["check_ms"], 5)}) |
+                     {"attention": round(f8["attn_ms"], 5), "step_p95": round(f8["step_ms_p95"], 5),
+                      "note": "events around each launch of eager steps"})
+    else:
+        step_desc = ("one launch (kv_decode_step_fp8 over one layer): every block checks its request's page tags, "
+                     "the block holding position L-1 writes the new token (1 token/request), attention "
+                     "(+ merge when split)")
+        kernel_desc = ("attn_gqa_split_kernel<fp8> with the tag check and the token write in the same launch "
+                       "(plus the merge kernel when splits > 1)")
+        breakdown = {"one_launch_step": round(f8["attn_ms"], 5), "step_p95": round(f8["step_ms_p95"], 5),
+                     "note": "events around the step's launch, eager steps"}
     line = {
         "metric": METRIC,
         "value": round(f8["gbs_step"], 1),
@@ -723,18 +769,14 @@ def main():
                    "batch": w.batch, "ctx": int(w.ctx_hi), "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
                    "splits": f8["splits"],
-                   "step": ("tag check + append(1 token/request)" if args.unfused else
-                            "fused tag check + append(1 token/request)") + " + attention (+ merge when split)"},
+                   "step": step_desc},
         "roofline": {"bound": "hbm", "achieved": round(f8["gbs_attn"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(f8["gbs_attn"] / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name, f8["splits"]),
                      "algorithmic_bytes": f8["kv_bytes"],
-                     "kernel": "paged_decode_attn_fp8 (split kernel, plus the merge kernel when splits > 1)",
+                     "kernel": kernel_desc,
                      "attn_ms_mean": round(f8["attn_ms_mean"], 5), "attn_ms_p95": round(f8["attn_ms_p95"], 5)},
-        "step_breakdown_ms": ({"tag_check": round(f8["check_ms"], 5), "append": round(f8["append_ms"], 5)}
-                              if args.unfused else {"tag_check_append": round(f8["check_ms"], 5)}) |
-                             {"attention": round(f8["attn_ms"], 5), "step_p95": round(f8["step_ms_p95"], 5),
-                              "note": "events around each launch of eager steps"},
+        "step_breakdown_ms": breakdown,
         "timing": ("steps replayed from a captured HIP graph of one step" if args.graph else
                    "eager back-to-back steps") + ", between two events on the launch stream",
         ("eager_ms_per_step" if args.graph else "graph_ms_per_step"): round(f8["other"]["ms_per_step"], 5),
@@ -753,8 +795,8 @@ def main():
     if layer_runs:
         line["layer_stack_step"] = layer_runs | {
             "note": f"one decode step over {args.layers} layers sharing one page table and tag set "
-                    "(kv_decode_step_*: the tag check once, fused with layer 0's write, then each layer's write "
-                    "and attention); graph_us = replay of a captured HIP graph of the whole step, eager_us = one "
+                    "(kv_decode_step_*: GQA, one launch per layer that writes the layer's token, layer 0's also running "
+                    "the tag check; latent, a check + write launch (the check in layer 0 only) and the attention); graph_us = replay of a captured HIP graph of the whole step, eager_us = one "
                     "library call per step; tokens_per_s = non-aborted requests x steps/s"}
     if "no_tracker" in f8:
         nt = f8["no_tracker"]

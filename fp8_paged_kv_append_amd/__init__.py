@@ -411,37 +411,43 @@ def decode_step(desc: PoolDesc, kv_dtype: str, k_pool, v_pool, page_table, ctx_l
     """One attention layer's decode step, in stream order: tag check -> append -> attention.
 
     With page_tags/expected_tags given, the batched check writes abort_flags
-    first and both later launches honour them; with page_tags None (the
-    no-op tracker) no check runs and abort_flags is passed through (None =
-    no flags).  tok_req/tok_pos None means one new token per request, at
-    position ctx_lens[r] - 1: the check and the write then run as one launch
-    (kv_tag_check_append_*), which needs the tracker.
+    first and the write and the attention honour them; with page_tags None
+    (the no-op tracker) no check runs and abort_flags is passed through
+    (None = no flags).  tok_req/tok_pos None means one new token per
+    request, at position ctx_lens[r] - 1: the step is then kv_decode_step_*
+    over this one layer, a single launch for the GQA cache (every block
+    checks its request's pages before reading any, the block holding
+    position L - 1 writes the token), a check + write launch and the
+    attention for the latent cache.  Otherwise three launches: kv_tag_check,
+    kv_append_*, the attention.
     """
     if kv_dtype not in ("fp8", "bf16"):
         raise ValueError(f"kv_dtype {kv_dtype!r}")
     if page_tags is not None and (expected_tags is None or abort_flags is None):
         raise ValueError("the tag check needs expected_tags and an abort_flags buffer")
-    fused = tok_req is None and tok_pos is None
-    if fused and page_tags is None:
-        raise ValueError("tok_req/tok_pos None (fused check + write) needs page_tags")
-    if fused and kv_dtype == "fp8":
-        kv_tag_check_append_fp8(desc, k_pool, v_pool, k_new, v_new, page_table, ctx_lens, page_tags, expected_tags,
-                                abort_flags, k_scale=k_scale, v_scale=v_scale, stream=stream)
-    elif fused:
-        kv_tag_check_append_bf16(desc, k_pool, v_pool, k_new, v_new, page_table, ctx_lens, page_tags, expected_tags,
-                                 abort_flags, stream=stream)
-    elif page_tags is not None:
+    if (tok_req is None) != (tok_pos is None):
+        raise ValueError("tok_req and tok_pos are given together or not at all")
+    if tok_req is None:
+        fp8 = kv_dtype == "fp8"
+        latent = v_pool is None
+        decode_step_layers(desc, kv_dtype, k_pool.reshape(1, -1), None if latent else v_pool.reshape(1, -1),
+                           page_table, ctx_lens, max_ctx_len, q.unsqueeze(0), k_new.unsqueeze(0),
+                           None if latent else v_new.unsqueeze(0), out.unsqueeze(0), page_tags=page_tags,
+                           expected_tags=expected_tags, abort_flags=abort_flags,
+                           k_scales=[k_scale] if fp8 else None,
+                           v_scales=[v_scale] if fp8 and not latent else None, sm_scale=sm_scale,
+                           num_splits=num_splits, workspace=workspace, stream=stream)
+        return
+    if page_tags is not None:
         kv_tag_check(page_tags, page_table, expected_tags, ctx_lens, desc.page_size, abort_flags, stream=stream)
     if kv_dtype == "fp8":
-        if not fused:
-            kv_append_fp8(desc, k_pool, v_pool, k_new, v_new, tok_req, tok_pos, page_table, abort_flags,
-                          k_scale=k_scale, v_scale=v_scale, stream=stream)
+        kv_append_fp8(desc, k_pool, v_pool, k_new, v_new, tok_req, tok_pos, page_table, abort_flags,
+                      k_scale=k_scale, v_scale=v_scale, stream=stream)
         paged_decode_attn_fp8(desc, q, k_pool, v_pool, page_table, ctx_lens, max_ctx_len, out, abort_flags,
                               k_scale=k_scale, v_scale=v_scale, sm_scale=sm_scale, num_splits=num_splits,
                               workspace=workspace, stream=stream)
     else:
-        if not fused:
-            kv_append_bf16(desc, k_pool, v_pool, k_new, v_new, tok_req, tok_pos, page_table, abort_flags,
-                           stream=stream)
+        kv_append_bf16(desc, k_pool, v_pool, k_new, v_new, tok_req, tok_pos, page_table, abort_flags,
+                       stream=stream)
         paged_decode_attn_bf16(desc, q, k_pool, v_pool, page_table, ctx_lens, max_ctx_len, out, abort_flags,
                                sm_scale=sm_scale, num_splits=num_splits, workspace=workspace, stream=stream)

@@ -117,7 +117,8 @@ int attn_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_he
                 int32_t batch, int32_t max_ctx_len, const uint32_t* flags, bool fp8, float k_scale,
                 float v_scale, float sm_scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
                 uint16_t* out, hipStream_t stream, bool launch = true, const uint16_t* k_new = nullptr,
-                const uint16_t* v_new = nullptr) {
+                const uint16_t* v_new = nullptr, const uint32_t* page_tags = nullptr,
+                const uint32_t* expected_tags = nullptr, uint32_t* flags_out = nullptr) {
   int st = check_pool(desc, true, fp8 ? 1 : 2);
   if (st) return st;
   if (batch < 0 || num_q_heads < 1 || pt_stride < 1 || num_splits < 0) return KVFP8_ERR_SHAPE;
@@ -172,6 +173,12 @@ int attn_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_he
   a.v_new = v_new;
   a.k_inv = fp8 ? 1.0f / k_scale : 1.0f;  // fl32(1/scale), as the append computes it
   a.v_inv = fp8 ? 1.0f / v_scale : 1.0f;
+  // the tag check in the same launch: it writes the flags instead of reading them
+  if (page_tags && (!expected_tags || !flags_out)) return KVFP8_ERR_NULL;
+  a.page_tags = page_tags;
+  a.expected = expected_tags;
+  a.flags_out = flags_out;
+  if (page_tags) a.flags = nullptr;
   if (!launch) return KVFP8_OK;
   return launch_attn_gqa(a, fp8, batch, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
 }
@@ -301,12 +308,12 @@ int latent_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_
 }
 
 // One decode step over a layer stack: every argument of every layer is checked (a dry pass of the
-// per-layer checks) before the first launch, so an error launches nothing; then layer 0's check +
-// write launch (a check when page_tags is given) and its attention, and for each later layer one
-// attention launch that also writes the layer's token (GQA: the block whose split holds position
-// L - 1 writes it and adds it to its softmax from registers) or, for the latent cache, a write
-// launch that only reads the flags and the attention.  Stream order carries the layer-to-layer
-// dependency.
+// per-layer checks) before the first launch, so an error launches nothing.  GQA cache: one attention
+// launch per layer (plus the merge when split) that also writes the layer's token -- the block whose
+// split holds position L - 1 writes it and adds it to its softmax from registers -- and, in layer 0
+// with page_tags given, runs the tag check first in every block and stores the flags that the later
+// layers read.  Latent cache: per layer a check + write launch (the check in layer 0 only), then the
+// attention.  Stream order carries the layer-to-layer dependency.
 int decode_step_common(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* layers, int32_t num_q_heads,
                        const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens, int32_t batch,
                        int32_t max_ctx_len, const uint32_t* page_tags, const uint32_t* expected_tags,
@@ -340,20 +347,21 @@ int decode_step_common(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* lay
       uint16_t* out = ls.out + l * out_n;
       const float ks = fp8 ? ls.k_scales[l] : 1.f;
       const float vs = fp8 && !latent ? ls.v_scales[l] : 1.f;
-      // GQA layers after the first: the attention launch writes the token itself (one launch per layer)
-      const bool fold = !latent && l > 0;
+      // GQA: one attention launch per layer that also writes the layer's token (and, in layer 0, runs
+      // the tag check); latent: a check + write launch, then the attention
+      const uint32_t* tags = l == 0 ? page_tags : nullptr;
       int st = KVFP8_OK;
-      if (!fold || !launch)  // the dry pass checks the write's arguments for every layer
-        st = check_append_common(desc, kp, vp, kn, vn, page_table, pt_stride, ctx_lens, batch,
-                                 l == 0 ? page_tags : nullptr, expected_tags, abort_flags, fp8, ks, vs, stream,
-                                 launch && !fold);
+      if (latent || !launch)  // the dry pass checks the write's arguments for every layer
+        st = check_append_common(desc, kp, vp, kn, vn, page_table, pt_stride, ctx_lens, batch, tags, expected_tags,
+                                 abort_flags, fp8, ks, vs, stream, launch);
       if (st) return st;
       st = latent ? latent_common(desc, q, num_q_heads, kp, page_table, pt_stride, ctx_lens, batch, max_ctx_len,
                                   abort_flags, fp8, ks, sm_scale, num_splits, workspace, workspace_bytes, out, stream,
                                   launch)
                   : attn_common(desc, q, num_q_heads, kp, vp, page_table, pt_stride, ctx_lens, batch, max_ctx_len,
-                                abort_flags, fp8, ks, vs, sm_scale, num_splits, workspace, workspace_bytes, out,
-                                stream, launch, fold ? kn : nullptr, fold ? vn : nullptr);
+                                tags ? nullptr : abort_flags, fp8, ks, vs, sm_scale, num_splits, workspace,
+                                workspace_bytes, out, stream, launch, kn, vn, tags, expected_tags,
+                                tags ? abort_flags : nullptr);
       if (st) return st;
     }
   }

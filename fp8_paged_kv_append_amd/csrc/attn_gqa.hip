@@ -254,7 +254,9 @@ __device__ __forceinline__ void compute_tile(TileRegs<FP8>& T, const u32x4_t (&q
 }
 
 template <bool FP8>
-__global__ __launch_bounds__(kThreads) void attn_gqa_split_kernel(AttnArgs a) {
+// At least two waves per SIMD (eight per CU, two blocks): the register budget the tile pipeline is
+// written for.
+__global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
   // wave index in an SGPR: the tile loop is then a scalar loop, not an exec-masked one
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -268,27 +270,13 @@ __global__ __launch_bounds__(kThreads) void attn_gqa_split_kernel(AttnArgs a) {
   __shared__ float s_acc[kWaves][16][kD];
   __shared__ int s_bad;
   __shared__ float s_knew[kD], s_vnew[kD], s_snew[16];
+  __shared__ uint16_t s_kcode[kD], s_vcode[kD];
+  __shared__ int s_newpage;
+  __shared__ uint32_t s_flag[kWaves];
 
   const int L = a.ctx_lens[r];
-  const bool aborted = a.flags != nullptr && a.flags[r] != 0u;
-  const bool bad_len = L <= 0 || L > a.max_ctx || L > a.pt_stride * S;
-  const int chunk = a.chunk_tiles * kTile;
-  const int c0 = split * chunk;
-  if (aborted || bad_len) {
-    if (a.num_splits == 1) {  // rows of this group are zero
-      for (int e = threadIdx.x; e < G * kD; e += kThreads)
-        a.out[((int64_t)r * a.num_q_heads + g * G + e / kD) * kD + e % kD] = 0;
-    }
-    return;  // the merge kernel zeroes the rows itself
-  }
-  if (c0 >= L) return;  // past this request's context: the merge does not read this split
-  // With the step's token passed in, the tiles stop before it (position L - 1) and the block whose
-  // chunk holds it writes it and adds it to its softmax in the epilogue: nothing reads it back.
-  const bool fold = a.k_new != nullptr;
-  const bool owner = fold && L - 1 < c0 + chunk;
-  const int c1 = min(fold ? L - 1 : L, c0 + chunk);
-
-  // q^T operand: lane (q4, n) holds head g*G+n, dims 32*q4 .. 32*q4+31 (zero for padding heads)
+  // q^T operand: lane (q4, n) holds head g*G+n, dims 32*q4 .. 32*q4+31 (zero for padding heads);
+  // issued first, so that its latency overlaps the tag check
   u32x4_t qv[4];
   if (n < G) {
     const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(
@@ -299,6 +287,89 @@ __global__ __launch_bounds__(kThreads) void attn_gqa_split_kernel(AttnArgs a) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qv[kk] = u32x4_t{0, 0, 0, 0};
   }
+
+  // The step's token, when passed in, belongs to position L - 1: the block whose chunk holds it
+  // writes it into its page and adds it to its softmax from LDS (its tiles stop before it, so
+  // nothing reads it back).  Its rows and its page id are loaded now, staged after the check.
+  const int chunk = a.chunk_tiles * kTile;
+  const int c0 = split * chunk;
+  const bool fold = a.k_new != nullptr;
+  const bool owner = fold && L > 0 && c0 <= L - 1 && L - 1 < c0 + chunk;
+  uint32_t kb = 0, vb = 0;
+  int newpage = -1;
+  if (owner) {
+    const int64_t row = ((int64_t)r * a.num_kv_heads + g) * kD;
+    if (threadIdx.x < kD) {
+      kb = a.k_new[row + threadIdx.x];
+      vb = a.v_new[row + threadIdx.x];
+    }
+    if ((L - 1) / S < a.pt_stride) newpage = a.page_table[(int64_t)r * a.pt_stride + (L - 1) / S];
+  }
+
+  uint32_t checked = 0;
+  bool pid_ready = false;  // s_pid already holds the first window's page ids (split 0, from the check)
+  if (a.page_tags != nullptr) {
+    // the tag check of every page request r's context spans, before any of them is read: bit 0 a
+    // page whose tag differs from the one the request recorded, bit 1 a page id out of the pool or
+    // a context longer than the page table
+    uint32_t f = 0;
+    if (L > 0) {
+      const int64_t need = ((int64_t)L + S - 1) / S;
+      const int64_t np = min(need, (int64_t)a.pt_stride);
+      if (need > a.pt_stride) f |= 2u;
+      const int32_t* ptr = a.page_table + (int64_t)r * a.pt_stride;
+      const uint32_t* ex = a.expected + (int64_t)r * a.pt_stride;
+      // split 0 keeps the ids it checks: its first window starts at entry 0 and, for a request that
+      // passes, spans at most the `need` entries checked here
+      pid_ready = split == 0 && np <= kPidWin;
+      for (int64_t i = threadIdx.x; i < np; i += kThreads) {
+        const int32_t p = ptr[i];
+        const bool ok = p >= 0 && p < a.num_pages;
+        if (!ok)
+          f |= 2u;
+        else if (a.page_tags[p] != ex[i])
+          f |= 1u;
+        if (pid_ready) s_pid[i] = ok ? p : -1;
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) f |= shfl_xor(f, m);
+    if (lane == 0) s_flag[wave] = f;
+    __syncthreads();
+    checked = s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3];
+    if (split == 0 && g == 0 && threadIdx.x == 0) a.flags_out[r] = checked;
+  }
+  if (owner) {  // quantised as the append does; the decoded values are what the pool will hold
+    if (threadIdx.x < kD) {
+      const int d = threadIdx.x;
+      if (FP8) {
+        const uint32_t kc = encode_e4m3x2(bf16_bits_to_f32(kb) * a.k_inv, 0.f) & 0xFFu;
+        const uint32_t vc = encode_e4m3x2(bf16_bits_to_f32(vb) * a.v_inv, 0.f) & 0xFFu;
+        s_kcode[d] = (uint16_t)kc;
+        s_vcode[d] = (uint16_t)vc;
+        s_knew[d] = e4m3_to_f32(kc);
+        s_vnew[d] = e4m3_to_f32(vc);
+      } else {
+        s_kcode[d] = (uint16_t)kb;
+        s_vcode[d] = (uint16_t)vb;
+        s_knew[d] = bf16_bits_to_f32(kb);
+        s_vnew[d] = bf16_bits_to_f32(vb);
+      }
+    }
+    if (threadIdx.x == 0) s_newpage = newpage;
+  }
+  const bool aborted = checked != 0u || (a.flags != nullptr && a.flags[r] != 0u);
+  const bool bad_len = L <= 0 || L > a.max_ctx || L > a.pt_stride * S;
+  if (aborted || bad_len) {
+    if (a.num_splits == 1) {  // rows of this group are zero
+      for (int e = threadIdx.x; e < G * kD; e += kThreads)
+        a.out[((int64_t)r * a.num_q_heads + g * G + e / kD) * kD + e % kD] = 0;
+    }
+    return;  // the merge kernel zeroes the rows itself
+  }
+  if (c0 >= L) return;  // past this request's context: the merge does not read this split
+  const int c1 = min(fold ? L - 1 : L, c0 + chunk);
+
 
   const int32_t* pt = a.page_table + (int64_t)r * a.pt_stride;
   const uint8_t* kpool = reinterpret_cast<const uint8_t*>(a.k_pool);
@@ -321,7 +392,8 @@ __global__ __launch_bounds__(kThreads) void attn_gqa_split_kernel(AttnArgs a) {
     const int e0 = w0 / S;
     const int ne = (w1 - 1) / S - e0 + 1;  // entries of the pages holding [w0, w1)
     __syncthreads();                       // the previous window's ids are no longer read
-    for (int i = threadIdx.x; i < ne; i += kThreads) {
+    const bool have = pid_ready && w0 == 0;
+    for (int i = threadIdx.x; i < ne && !have; i += kThreads) {
       int p = pt[e0 + i];
       if (p < 0 || p >= a.num_pages) {
         bad = true;
@@ -365,38 +437,6 @@ __global__ __launch_bounds__(kThreads) void attn_gqa_split_kernel(AttnArgs a) {
 #undef KVFP8_ISSUE
   }
 
-  // ---- the step's token (owner block): quantise it as the append does, write it into its page, keep
-  // its decoded K and V of this head in LDS
-  if (owner) {
-    const int pos = L - 1;
-    const int page = pt[pos / S];
-    const bool ok = page >= 0 && page < a.num_pages;
-    if (!ok) bad = true;
-    const int slot = pos % S, H = a.num_kv_heads;
-    for (int d = threadIdx.x; d < kD; d += kThreads) {
-      const uint32_t kb = a.k_new[((int64_t)r * H + g) * kD + d], vb = a.v_new[((int64_t)r * H + g) * kD + d];
-      const int64_t ko = ok ? k_elem_offset<FP8 ? 1 : 2>(page, g, slot, d, H, S, kD) : 0;
-      const int64_t vo = ((int64_t)page * H + g) * kD * S + (int64_t)d * S + slot;
-      if (FP8) {
-        const uint32_t kc = encode_e4m3x2(bf16_bits_to_f32(kb) * a.k_inv, 0.f) & 0xFFu;
-        const uint32_t vc = encode_e4m3x2(bf16_bits_to_f32(vb) * a.v_inv, 0.f) & 0xFFu;
-        if (ok) {
-          const_cast<uint8_t*>(kpool)[ko] = (uint8_t)kc;
-          const_cast<uint8_t*>(vpool)[vo] = (uint8_t)vc;
-        }
-        s_knew[d] = e4m3_to_f32(kc);
-        s_vnew[d] = e4m3_to_f32(vc);
-      } else {
-        if (ok) {
-          reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(kpool))[ko] = (uint16_t)kb;
-          reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(vpool))[vo] = (uint16_t)vb;
-        }
-        s_knew[d] = bf16_bits_to_f32(kb);
-        s_vnew[d] = bf16_bits_to_f32(vb);
-      }
-    }
-  }
-
   // ---- merge the four waves
   float l_run = st.l;
   l_run += shfl_xor(l_run, 16);
@@ -404,17 +444,36 @@ __global__ __launch_bounds__(kThreads) void attn_gqa_split_kernel(AttnArgs a) {
   if (threadIdx.x == 0) s_bad = 0;
   __syncthreads();
   if (owner) {
-    // its score per head, log2 domain like the tiles': threads 16 hn .. 16 hn + 15 take 8 dims each
-    const int hn = threadIdx.x >> 4, part = threadIdx.x & 15;
-    float dot = 0.f;
-    if (hn < G) {
-      const uint16_t* qh = a.q + ((int64_t)r * a.num_q_heads + g * G + hn) * kD + 8 * part;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dot += bf16_bits_to_f32(qh[e]) * s_knew[8 * part + e];
+    // the token into its page (a bad page id only marks the rows, as a bad page of the tiles does)
+    const int page = s_newpage;
+    const bool ok = page >= 0 && page < a.num_pages;
+    if (!ok) bad = true;
+    if (ok && threadIdx.x < kD) {
+      const int d = threadIdx.x, slot = (L - 1) % S, H = a.num_kv_heads;
+      const int64_t ko = k_elem_offset<FP8 ? 1 : 2>(page, g, slot, d, H, S, kD);
+      const int64_t vo = ((int64_t)page * H + g) * kD * S + (int64_t)d * S + slot;
+      if (FP8) {
+        const_cast<uint8_t*>(kpool)[ko] = (uint8_t)s_kcode[d];
+        const_cast<uint8_t*>(vpool)[vo] = (uint8_t)s_vcode[d];
+      } else {
+        reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(kpool))[ko] = s_kcode[d];
+        reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(vpool))[vo] = s_vcode[d];
+      }
     }
+    // its score per head, log2 domain like the tiles', from the q operand lane (q4, n) holds:
+    // head n, dims 32 q4 + 8 kk + j
+    float dot = 0.f;
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1) dot += shfl_xor(dot, m);
-    if (hn < G && part == 0) s_snew[hn] = dot * c_log2;
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = qv[kk][e];
+        const int d = 32 * q4 + 8 * kk + 2 * e;
+        dot += __uint_as_float(w << 16) * s_knew[d] + __uint_as_float(w & 0xFFFF0000u) * s_knew[d + 1];
+      }
+    dot += shfl_xor(dot, 16);
+    dot += shfl_xor(dot, 32);
+    if (q4 == 0 && n < G) s_snew[n] = dot * c_log2;
   }
   if (q4 == 0) {
     s_m[wave][n] = st.m;
@@ -517,7 +576,7 @@ hipError_t launch_attn_gqa(const AttnArgs& a, bool fp8, int batch, hipStream_t s
   m.lse_part = a.lse_part;
   m.out = a.out;
   m.ctx_lens = a.ctx_lens;
-  m.flags = a.flags;
+  m.flags = a.page_tags != nullptr ? a.flags_out : a.flags;
   m.num_q_heads = a.num_q_heads;
   m.v_dim = kD;
   m.num_splits = a.num_splits;

@@ -28,6 +28,12 @@ struct AttnArgs {
   const uint16_t* k_new;
   const uint16_t* v_new;
   float k_inv, v_inv;
+  // Optional: the pages' tag check in the same launch (page_tags non-null; flags then null).  Every
+  // block checks all pages of its request before it reads any; block (split 0, head 0) stores the
+  // request's flag in flags_out, which the merge launch reads.
+  const uint32_t* page_tags;  // [P]
+  const uint32_t* expected;   // [B][pt_stride]
+  uint32_t* flags_out;        // [B]
 };
 
 struct MergeArgs {

@@ -237,12 +237,15 @@ int paged_decode_attn_latent_bf16(const kvfp8_pool_desc* desc, const uint16_t* q
  * for each later layer its write, honouring the flags layer 0 left (read,
  * not rewritten: the pages' tag check runs once per step, before any read),
  * and its attention.  Each write puts request r's token at ctx_lens[r] - 1.
- * For the GQA cache a later layer's write is done by its attention launch:
- * the block whose split holds position ctx_lens[r] - 1 quantises the token
- * as kv_append_fp8 does, stores it, and adds it to its softmax from the
- * values it holds (the pool contents after the step are the same).  A
- * request with ctx_lens[r] > max_ctx_len is a caller error: its rows are
- * zero and later GQA layers do not write its token.
+ * For the GQA cache every layer is ONE attention launch (plus the merge
+ * launch when split): in layer 0 with page_tags given, every block first
+ * checks all pages of its request (kv_tag_check semantics, before it reads
+ * any page) and block (split 0, head 0) stores the request's flag; the
+ * block whose split holds position ctx_lens[r] - 1 quantises the token as
+ * kv_append_fp8 does, stores it, and adds it to its softmax from the values
+ * it holds.  Flags, pools and outputs are those of the launch order above.
+ * A request with ctx_lens[r] > max_ctx_len is a caller error: its rows are
+ * zero and the GQA layers do not write its token.
  * page_tags NULL = no-op tracker: no check; abort_flags, when given, are
  * only read.  Every layer's arguments are checked before the first launch,
  * so an error status means nothing was enqueued.  The workspace is shared by

@@ -11,13 +11,19 @@ from tests.gpu_util import ATTN_TOL, Case, attn_error, dev, host, note
 pytestmark = pytest.mark.gpu
 
 
-def _device_step(c, k_new, v_new, req, pos, tracker=True, num_splits=0):
+def _device_step(c, k_new, v_new, req, pos, tracker=True, num_splits=0, one_launch=False):
+    """The step through decode_step: three launches with explicit token positions, or with one_launch
+    (positions implicit at L - 1) kv_decode_step_* over one layer -- one launch for the GQA cache."""
     w = c.w
+    if one_launch:
+        assert np.array_equal(pos, c.lens[req] - 1)
+        req = pos = None
     out = c.out_tensor()
     flags = torch.full((w.batch,), -1, dtype=torch.int32, device="cuda") if tracker else None
     splits = num_splits or kv.paged_decode_attn_auto_splits(w.batch, w.num_kv_heads, c.max_ctx)
     kv.decode_step(c.desc, c.kv_dtype, c.dkp, c.dvp, c.dpt, c.dlens, c.max_ctx, c.dq, dev(k_new),
-                   None if v_new is None else dev(v_new), dev(req), dev(pos), out,
+                   None if v_new is None else dev(v_new), None if req is None else dev(req),
+                   None if pos is None else dev(pos), out,
                    page_tags=c.dtags if tracker else None, expected_tags=c.dexp if tracker else None,
                    abort_flags=flags, k_scale=c.d_k_scale, v_scale=c.d_v_scale, sm_scale=c.sm_scale,
                    num_splits=num_splits, workspace=c.workspace(splits))
@@ -25,11 +31,13 @@ def _device_step(c, k_new, v_new, req, pos, tracker=True, num_splits=0):
     return (None if flags is None else host(flags, np.uint32)), host(out, np.uint16)
 
 
+@pytest.mark.parametrize("one_launch", [False, True])
 @pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
-def test_step_with_stale_request(kv_dtype):
-    """16 requests, one with a stale expected tag: its flag is set, its page is not written, its rows are 0."""
+def test_step_with_stale_request(kv_dtype, one_launch):
+    """16 requests, one with a stale expected tag: its flag is set, its page is not written, its rows are 0
+    (three launches, or one launch that checks, writes and attends)."""
     w = wl.WORKLOADS["sweep_b16"].with_(num_pages=3000, ctx_lo=700, ctx_hi=700)
-    note(f"step stale {kv_dtype}")
+    note(f"step stale {kv_dtype} one_launch={one_launch}")
     c = Case(w, kv_dtype)
     c.fill_device()
     k_new, v_new, req, pos = c.step_inputs()
@@ -39,7 +47,7 @@ def test_step_with_stale_request(kv_dtype):
               expected_tags=c.exp, num_kv_heads=w.num_kv_heads, page_size=w.page_size, head_dim=w.head_dim,
               v_dim=w.v_dim, k_scale=c.o_k_scale, v_scale=c.o_v_scale, sm_scale=c.sm_scale, latent=False)
     o_flags, o_out = step.decode_step(st, c.q, k_new, v_new, req, pos)
-    g_flags, g_out = _device_step(c, k_new, v_new, req, pos)
+    g_flags, g_out = _device_step(c, k_new, v_new, req, pos, one_launch=one_launch)
     assert np.array_equal(g_flags, o_flags)
     assert np.flatnonzero(g_flags).tolist() == c.stale.tolist()
     et = np.uint8 if kv_dtype == "fp8" else np.uint16
@@ -50,14 +58,14 @@ def test_step_with_stale_request(kv_dtype):
     for r in c.stale:
         assert not g_out[r].any()
     # the no-op tracker: no check, every request attended
-    g2_flags, g2_out = _device_step(c, k_new, v_new, req, pos, tracker=False)
+    g2_flags, g2_out = _device_step(c, k_new, v_new, req, pos, tracker=False, one_launch=one_launch)
     assert g2_flags is None and all(g2_out[r].any() for r in range(w.batch))
 
 
 @pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
 def test_full_size_64x8192_sampled(kv_dtype):
     """The 64 x 8192 workload (64/8 heads, page 16, 40k-page pool) at full size, in the bench's launch
-    configuration: all flags bit-exact, scales bit-exact, sampled requests' pages byte-exact and their
+    configuration (one launch: check, write and attention): all flags bit-exact, scales bit-exact, sampled requests' pages byte-exact and their
     attention rows within tolerance of the oracle."""
     w = wl.WORKLOADS["sweep_b64"]
     note(f"full 64x8192 {kv_dtype}: generating")
@@ -66,7 +74,7 @@ def test_full_size_64x8192_sampled(kv_dtype):
     note("  filling")
     c.fill_device()
     k_new, v_new, req, pos = c.step_inputs()
-    g_flags, g_out = _device_step(c, k_new, v_new, req, pos)
+    g_flags, g_out = _device_step(c, k_new, v_new, req, pos, one_launch=True)
     o_flags = paged.tag_check(c.tags, c.pt, c.exp, c.lens, w.page_size)
     assert np.array_equal(g_flags, o_flags) and o_flags.sum() > 0
     sample = sorted(set([0, 17, 63] + c.stale.tolist()))
@@ -112,12 +120,15 @@ def _fused_case(kv_dtype, latent):
     return c, k_new, v_new, req, pos, hole
 
 
-@pytest.mark.parametrize("latent", [False, True])
+@pytest.mark.parametrize("latent,two_launch", [(False, False), (False, True), (True, True)])
 @pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
-def test_fused_check_append_step(kv_dtype, latent):
-    """decode_step with implicit tokens (kv_tag_check_append_* then attention): flags and both pools
-    bit-exact to the oracle's check -> append, attention rows within tolerance, faulty requests zero."""
-    note(f"fused check+append {kv_dtype} latent={latent}")
+def test_fused_check_append_step(kv_dtype, latent, two_launch):
+    """One token per request at L - 1, the check and the write fused: for the GQA cache as one launch
+    (decode_step with implicit tokens: every attention block checks its request's pages, the block
+    holding L - 1 writes the token) or as kv_tag_check_append_* then the attention; the latent cache
+    takes the latter.  Flags and both pools bit-exact to the oracle's check -> append, attention rows
+    within tolerance, faulty requests zero."""
+    note(f"fused check+append {kv_dtype} latent={latent} two_launch={two_launch}")
     c, k_new, v_new, req, pos, hole = _fused_case(kv_dtype, latent)
     w = c.w
     st = dict(dtype=kv_dtype, k_pool=c.okp, v_pool=c.ovp, page_table=c.pt, ctx_lens=c.lens, page_tags=c.tags,
@@ -140,6 +151,19 @@ def test_fused_check_append_step(kv_dtype, latent):
         else:
             kv.paged_decode_attn_latent_bf16(c.desc, c.dq, c.dkp, c.dpt, c.dlens, c.max_ctx, out, flags,
                                              sm_scale=c.sm_scale, workspace=ws)
+    elif two_launch:
+        splits = kv.paged_decode_attn_auto_splits(w.batch, w.num_kv_heads, c.max_ctx)
+        ws = c.workspace(splits)
+        if kv_dtype == "fp8":
+            kv.kv_tag_check_append_fp8(c.desc, c.dkp, c.dvp, dev(k_new), dev(v_new), c.dpt, c.dlens, c.dtags, c.dexp,
+                                       flags, k_scale=c.d_k_scale, v_scale=c.d_v_scale)
+            kv.paged_decode_attn_fp8(c.desc, c.dq, c.dkp, c.dvp, c.dpt, c.dlens, c.max_ctx, out, flags,
+                                     k_scale=c.d_k_scale, v_scale=c.d_v_scale, sm_scale=c.sm_scale, workspace=ws)
+        else:
+            kv.kv_tag_check_append_bf16(c.desc, c.dkp, c.dvp, dev(k_new), dev(v_new), c.dpt, c.dlens, c.dtags,
+                                        c.dexp, flags)
+            kv.paged_decode_attn_bf16(c.desc, c.dq, c.dkp, c.dvp, c.dpt, c.dlens, c.max_ctx, out, flags,
+                                      sm_scale=c.sm_scale, workspace=ws)
     else:
         splits = kv.paged_decode_attn_auto_splits(w.batch, w.num_kv_heads, c.max_ctx)
         kv.decode_step(c.desc, kv_dtype, c.dkp, c.dvp, c.dpt, c.dlens, c.max_ctx, c.dq, dev(k_new), dev(v_new),
