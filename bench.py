@@ -4,8 +4,12 @@
 A step is one pass of the whole hot path for one attention layer over one
 batch: the batched page-tag check, the append of every request's new token
 (quantised to e4m3 for the FP8 cache) and paged decode attention (split
-kernel + log-sum-exp merge when the context is split).  Inputs are resident
-in HBM before timing starts.  Default workload: 64 requests x 8192 tokens,
+kernel + log-sum-exp merge when the context is split).  By default the step
+is kv_decode_step_* over that one layer, which for the GQA cache is a single
+launch: every attention block checks its request's page tags before reading
+any page, and the block holding position L-1 writes the new token
+(--two-launch: check + write launch, then attention; --unfused: three
+launches).  Inputs are resident in HBM before timing starts.  Default workload: 64 requests x 8192 tokens,
 64 query / 8 KV heads, head_dim 128, page size 16, 40,000-page pool, one
 stale expected tag (1% of requests, that request aborted and its bytes
 excluded).
