@@ -205,3 +205,47 @@ def test_fused_matches_separate_launches(kv_dtype):
     torch.cuda.synchronize()
     assert torch.equal(f1, f2)
     assert torch.equal(c.dkp, kp2) and torch.equal(c.dvp, vp2)
+
+
+@pytest.mark.parametrize("num_splits", [0, 3])
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_one_launch_length_beyond_max_ctx(kv_dtype, num_splits):
+    """A request longer than max_ctx_len is a caller error.  In the one-launch step its pages are still
+    checked (its flag is the tag check's), its rows are zero and its token is not written; a stale
+    request is aborted as usual and the others match the oracle, pools byte for byte."""
+    note(f"one launch, L > max_ctx {kv_dtype} splits={num_splits}")
+    w = wl.WORKLOADS["sweep_b16"].with_(batch=4, num_pages=3000, ctx_lo=300, ctx_hi=600)
+    lens = np.array([300, 500, 400, 350], dtype=np.int32)
+    max_ctx = 450                                          # request 1 exceeds it
+    c = Case(w, kv_dtype, lens=lens, stale=[3])
+    c.fill_device()
+    k_new, v_new, req, pos = c.step_inputs()
+    k_new, v_new = k_new ^ np.uint16(0x0040), v_new ^ np.uint16(0x0040)   # a write shows
+    o_flags = paged.tag_check(c.tags, c.pt, c.exp, c.lens, w.page_size)
+    assert o_flags.tolist() == [0, 0, 0, paged.FLAG_TAG_MISMATCH]
+    skip = o_flags.copy()
+    skip[1] = 1                                            # the caller error: not written, zero rows
+    if kv_dtype == "fp8":
+        paged.append_fp8(c.okp, c.ovp, k_new, v_new, req, pos, c.pt, w.num_kv_heads, w.page_size, c.o_k_scale,
+                         c.o_v_scale, skip)
+    else:
+        paged.append(c.okp, c.ovp, k_new, v_new, req, pos, c.pt, w.num_kv_heads, w.page_size, skip)
+    ref = attention.decode_attention(c.q, c.okp, c.ovp, c.pt, c.lens, num_kv_heads=w.num_kv_heads,
+                                     page_size=w.page_size, head_dim=w.head_dim, v_dim=w.v_dim, dtype=kv_dtype,
+                                     k_scale=c.o_k_scale, v_scale=c.o_v_scale, sm_scale=c.sm_scale, flags=skip,
+                                     requests=[0, 2])
+    flags = torch.full((w.batch,), -1, dtype=torch.int32, device="cuda")
+    out = c.out_tensor()
+    splits = num_splits or kv.paged_decode_attn_auto_splits(w.batch, w.num_kv_heads, max_ctx)
+    kv.decode_step(c.desc, kv_dtype, c.dkp, c.dvp, c.dpt, c.dlens, max_ctx, c.dq, dev(k_new), dev(v_new), None, None,
+                   out, page_tags=c.dtags, expected_tags=c.dexp, abort_flags=flags, k_scale=c.d_k_scale,
+                   v_scale=c.d_v_scale, sm_scale=c.sm_scale, num_splits=num_splits, workspace=c.workspace(splits))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(flags, np.uint32), o_flags)
+    et = np.uint8 if kv_dtype == "fp8" else np.uint16
+    assert np.array_equal(host(c.dkp, et), c.okp) and np.array_equal(host(c.dvp, et), c.ovp)
+    g_out = host(out, np.uint16)
+    assert not g_out[1].any() and not g_out[3].any()
+    err = attn_error(g_out, ref)
+    note(f"  step error {err:.3e}")
+    assert err <= ATTN_TOL
