@@ -244,10 +244,13 @@ __global__ __launch_bounds__(256) void wgemm_small_kernel(WgemmArgs a) {
   };
   auto x_put = [&](int i, const u32x4_t& v) {
     if (i < total) *reinterpret_cast<u32x4_t*>(smem + (i / per_row) * row_bytes + 16 * (i % per_row)) = v;
-    // group sums on the way: a group of a row is 16 consecutive columns, i.e. 16 aligned lanes
-    // (per_row and 256 are multiples of 16); out-of-range lanes loaded zeros
-    const float sum = row_sum16(sum8_bf16(v));
-    if (i < total && (threadIdx.x & 15) == 0) xs[((i % per_row) >> 4) * 16 + i / per_row] = sum;
+    // INT4: group sums on the way (the code bias is removed with them; FP8 codes carry none): a group
+    // of a row is 16 consecutive columns, i.e. 16 aligned lanes (per_row and 256 are multiples of 16);
+    // out-of-range lanes loaded zeros
+    if constexpr (W4) {
+      const float sum = row_sum16(sum8_bf16(v));
+      if (i < total && (threadIdx.x & 15) == 0) xs[((i % per_row) >> 4) * 16 + i / per_row] = sum;
+    }
   };
   constexpr int kXB = 16;                                // activation loads per thread and batch
   int xbase = 0;
@@ -347,9 +350,11 @@ __global__ __launch_bounds__(256, 2) void wgemm_kernel(WgemmArgs a) {
     for (int p = 0; p < 2 * MT; ++p) {
       const int row = 8 * p + xr_row;
       *reinterpret_cast<u32x4_t*>(s_x[buf] + row * kRowBytes + 16 * xr_col) = xr[set][p];
-      // the 16 lanes of one (row, group) are lanes 16h..16h+15 of this wave
-      const float sum = row_sum16(sum8_bf16(xr[set][p]));
-      if ((xr_col & 15) == 0) s_xs[buf][xr_col >> 4][row] = sum;
+      // INT4 only: the 16 lanes of one (row, group) are lanes 16h..16h+15 of this wave
+      if constexpr (W4) {
+        const float sum = row_sum16(sum8_bf16(xr[set][p]));
+        if ((xr_col & 15) == 0) s_xs[buf][xr_col >> 4][row] = sum;
+      }
     }
   };
 
