@@ -119,11 +119,11 @@ struct WStream {
 
 // The block's group scales -> LDS s_sc[tile of the block][group][16] (bf16), zeros past N or the split.
 __device__ __forceinline__ void load_scales(const WgemmArgs& a, int tile0, int ntiles, int g0, int ng, int gcap,
-                                            uint16_t* s_sc) {
+                                            uint16_t* s_sc, int nthreads = 256) {
   const int KG = a.K / kGroup;
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.s, (uint32_t)((int64_t)a.N * KG * 2));
   // ntiles x gcap groups x 32 bytes, 16 bytes per thread and pass
-  for (int i = threadIdx.x; i < ntiles * gcap * 2; i += 256) {
+  for (int i = threadIdx.x; i < ntiles * gcap * 2; i += nthreads) {
     const int t = i / (gcap * 2), g = (i / 2) % gcap, h = i & 1;
     const int tile = tile0 + t;
     const bool ok = tile * 16 < a.N && g < ng;
@@ -312,13 +312,17 @@ __global__ __launch_bounds__(256) void wgemm_small_kernel(WgemmArgs a) {
 
 // ---- M > 16: activations staged per 256-wide chunk (two groups) through double-buffered LDS, the next
 // chunk's loads issued at the start of the current one; rows >= M and chunks past the split load zeros.
-template <int MT, bool W4>
-__global__ __launch_bounds__(256, 2) void wgemm_kernel(WgemmArgs a) {
+// WB waves per block, one 16-channel tile each; the block stages each activation chunk (and, for
+// INT4, its group sums) once for all of them, so more waves per block stage less per output channel.
+template <int MT, bool W4, int WB>
+__global__ __launch_bounds__(64 * WB, 8 / WB) void wgemm_kernel(WgemmArgs a) {
   constexpr int kRows = 16 * MT;
   constexpr int kR = MT <= 2 ? kRing : kRing / 2;   // groups in flight (more rows: more work per byte)
+  constexpr int kThr = 64 * WB;
+  constexpr int kXP = kRows / (kThr / 32);          // staging passes: kThr / 32 rows of 32 x 16 bytes each
   __shared__ __align__(16) uint8_t s_x[2][kRows * kRowBytes];
   __shared__ __align__(16) float s_xs[2][2][kRows];   // [buffer][group of the chunk][row]
-  __shared__ __align__(16) uint16_t s_sc[4 * kMaxGroupsChunked * 16];
+  __shared__ __align__(16) uint16_t s_sc[WB * kMaxGroupsChunked * 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nn = lane & 15, qq = lane >> 4;
@@ -327,18 +331,18 @@ __global__ __launch_bounds__(256, 2) void wgemm_kernel(WgemmArgs a) {
   const int ng = min(a.groups_per_split, KG - g0);    // even
   const int nch = ng / 2;
 
-  // ---- activation staging: thread -> (row 8p + tid/32, 16-byte column tid%32) of a chunk
+  // ---- activation staging: thread -> (row (kThr/32) p + tid/32, 16-byte column tid%32) of a chunk
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, (uint32_t)((int64_t)a.M * a.K * 2));
   // Two register sets: chunk c's rows are loaded at the start of chunk c - 2 and stored to LDS at the
   // end of chunk c - 1.  Loads retire in issue order, so the store's wait also retires every weight
   // load issued before them; loading two chunks ahead keeps the weight loads of the last two chunks in
   // flight through that wait (one chunk ahead left only the newest two groups in flight).
   const int xr_row = tid >> 5, xr_col = tid & 31;
-  u32x4_t xr[2][2 * MT];
+  u32x4_t xr[2][kXP];
   auto x_load = [&](int set, int ch) {   // chunk ch of the split into register set `set`
 #pragma unroll
-    for (int p = 0; p < 2 * MT; ++p) {
-      const int row = 8 * p + xr_row;
+    for (int p = 0; p < kXP; ++p) {
+      const int row = (kThr / 32) * p + xr_row;
       const uint32_t off = (row < a.M && ch < nch)
                                ? (uint32_t)(((int64_t)row * a.K + (int64_t)(g0 / 2 + ch) * kChunk + 8 * xr_col) * 2)
                                : kOOB;
@@ -347,8 +351,8 @@ __global__ __launch_bounds__(256, 2) void wgemm_kernel(WgemmArgs a) {
   };
   auto x_store = [&](int set, int buf) {
 #pragma unroll
-    for (int p = 0; p < 2 * MT; ++p) {
-      const int row = 8 * p + xr_row;
+    for (int p = 0; p < kXP; ++p) {
+      const int row = (kThr / 32) * p + xr_row;
       *reinterpret_cast<u32x4_t*>(s_x[buf] + row * kRowBytes + 16 * xr_col) = xr[set][p];
       // INT4 only: the 16 lanes of one (row, group) are lanes 16h..16h+15 of this wave
       if constexpr (W4) {
@@ -358,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void wgemm_kernel(WgemmArgs a) {
     }
   };
 
-  const int tile = blockIdx.x * 4 + wave;
+  const int tile = blockIdx.x * WB + wave;
   const WStream<W4> ws(a, tile, g0, ng, lane);
   constexpr int kB = WStream<W4>::kB;
   u32x4_t wr[kR][kB / 16];
@@ -367,7 +371,7 @@ __global__ __launch_bounds__(256, 2) void wgemm_kernel(WgemmArgs a) {
     ws.load(wr[u], u);
     __builtin_amdgcn_sched_barrier(0);
   }
-  load_scales(a, blockIdx.x * 4, 4, g0, ng, kMaxGroupsChunked, s_sc);
+  load_scales(a, blockIdx.x * WB, WB, g0, ng, kMaxGroupsChunked, s_sc, kThr);
   x_load(0, 0);
   x_load(1, 1);
   x_store(0, 0);
@@ -512,9 +516,14 @@ int32_t auto_splits(int32_t m, int32_t n, int32_t k) {
   return (int32_t)s;
 }
 
+// Waves (16-channel tiles) per block of the M > 16 kernel: eight halve the activation staging per
+// channel, which INT4 (group sums included) always gains from; FP8 from three row tiles up (measured
+// on 8192 x 8192: INT4 M=64 28.9 -> 26.2 us, FP8 M=64 27.9 -> 25.4 us, FP8 M=32 24.2 -> 25.5 us).
 template <int MT, bool W4>
-void launch_mt(const WgemmArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((wgemm_kernel<MT, W4>), grid, dim3(256), 0, stream, a);
+void launch_mt(const WgemmArgs& a, int32_t n, int32_t splits, hipStream_t stream) {
+  constexpr int WB = (W4 || MT >= 3) ? 8 : 4;
+  const dim3 grid((n / 16 + WB - 1) / WB, splits);
+  hipLaunchKernelGGL((wgemm_kernel<MT, W4, WB>), grid, dim3(64 * WB), 0, stream, a);
 }
 
 int gemm_common(const uint16_t* x, int32_t m, const uint8_t* w, const uint16_t* scales, int32_t n, int32_t k,
@@ -570,15 +579,15 @@ int gemm_common(const uint16_t* x, int32_t m, const uint8_t* w, const uint16_t* 
   } else {
     const int mt = (m + 15) / 16;
     if (w4) {
-      if (mt == 1) launch_mt<1, true>(a, grid, stream);
-      else if (mt == 2) launch_mt<2, true>(a, grid, stream);
-      else if (mt == 3) launch_mt<3, true>(a, grid, stream);
-      else launch_mt<4, true>(a, grid, stream);
+      if (mt == 1) launch_mt<1, true>(a, n, splits, stream);
+      else if (mt == 2) launch_mt<2, true>(a, n, splits, stream);
+      else if (mt == 3) launch_mt<3, true>(a, n, splits, stream);
+      else launch_mt<4, true>(a, n, splits, stream);
     } else {
-      if (mt == 1) launch_mt<1, false>(a, grid, stream);
-      else if (mt == 2) launch_mt<2, false>(a, grid, stream);
-      else if (mt == 3) launch_mt<3, false>(a, grid, stream);
-      else launch_mt<4, false>(a, grid, stream);
+      if (mt == 1) launch_mt<1, false>(a, n, splits, stream);
+      else if (mt == 2) launch_mt<2, false>(a, n, splits, stream);
+      else if (mt == 3) launch_mt<3, false>(a, n, splits, stream);
+      else launch_mt<4, false>(a, n, splits, stream);
     }
   }
   if (hipGetLastError() != hipSuccess) return KVFP8_ERR_HIP;
