@@ -38,6 +38,17 @@
 // The four waves merge their (m, l, O) through LDS; with one split the block
 // writes bf16 output, otherwise normalised fp32 partials and lse for the merge
 // kernel.
+//
+// The same launch can be the whole decode step of a layer (Cloudflare blog,
+// section "Quantized KV cache", for the conversion on read; the tag check of
+// the agentlenshq summary, section "KV Cache 完整性检查"): with page tags given,
+// every block first checks all pages of its request (the flag bits of the
+// batched check) before it reads any of them, and block (split 0, head 0)
+// stores the flag; with the step's new rows given, the block whose chunk holds
+// position L - 1 quantises the token as the append does (staged in LDS at the
+// start), stores it in its page in the epilogue, and adds its score and value
+// to the merged softmax -- its tiles stop before L - 1, so nothing reads the
+// token back.
 #include "kvfp8_device.h"
 #include "kvfp8_internal.h"
 
