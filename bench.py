@@ -117,6 +117,9 @@ class DeviceCache:
         self.s_req, self.s_pos = host["ds_req"], host["ds_pos"]
         self.out = torch.empty((w.batch, w.num_q_heads, w.v_dim), dtype=torch.int16, device="cuda")
         self.flags = torch.zeros(w.batch, dtype=torch.int32, device="cuda")
+        # latent: with no requested count the library picks per cache type (FP8 and BF16 work on different
+        # head groups); the workspace is sized with the public bound, which covers both
+        self.lat_splits = host["splits"] if w.latent else None
         if host["splits"]:
             self.splits = host["splits"]
         elif w.latent:
@@ -154,10 +157,10 @@ class DeviceCache:
         kv, w = self.kv, self.w
         if w.latent and self.kv_dtype == "fp8":
             kv.paged_decode_attn_latent_fp8(self.desc, self.q, self.kp, self.pt, self.lens, self.max_ctx, self.out, f,
-                                            scale=self.k_scale, num_splits=self.splits, workspace=self.ws)
+                                            scale=self.k_scale, num_splits=self.lat_splits, workspace=self.ws)
         elif w.latent:
             kv.paged_decode_attn_latent_bf16(self.desc, self.q, self.kp, self.pt, self.lens, self.max_ctx, self.out,
-                                             f, num_splits=self.splits, workspace=self.ws)
+                                             f, num_splits=self.lat_splits, workspace=self.ws)
         elif self.kv_dtype == "fp8":
             kv.paged_decode_attn_fp8(self.desc, self.q, self.kp, self.vp, self.pt, self.lens, self.max_ctx,
                                      self.out, f, k_scale=self.k_scale, v_scale=self.v_scale,
@@ -720,6 +723,8 @@ def main():
                      "attn_ms": round(r["attn_ms_mean"], 5), "attn_gbs": round(r["gbs_attn"], 1),
                      "attn_pct_hbm_peak": round(100 * r["gbs_attn"] / HBM_PEAK_GBS, 2), "splits": r["splits"]}
                 if we.latent:
+                    e["splits"] = f"library choice per cache type (at most {r['splits']})" if not we.num_splits else \
+                        r["splits"]
                     tf = fl_e / (r["attn_ms_mean"] * 1e-3) / 1e12
                     e["attn_tflops"] = round(tf, 1)
                     e["mfma_roofline"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,

@@ -519,13 +519,20 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   }
 }
 
-hipError_t launch_attn_latent(const LatentArgs& a, bool fp8, hipStream_t stream) {
+hipError_t launch_attn_latent_pairs(const LatentArgs& a, hipStream_t stream);  // attn_latent_pairs.hip
+
+hipError_t launch_attn_latent(const LatentArgs& a, bool fp8, bool pairs, hipStream_t stream) {
   const int units = a.batch * a.num_splits;
   const int blocks = ((units + 7) / 8) * 8 * a.n_hg;
-  if (fp8)
+  // FP8 at small grids: the wave-pair kernel (two waves per SIMD, 64 heads per block)
+  if (fp8 && pairs) {
+    hipError_t e0 = launch_attn_latent_pairs(a, stream);
+    if (e0 != hipSuccess) return e0;
+  } else if (fp8) {
     hipLaunchKernelGGL(attn_latent_split_kernel<true>, dim3(blocks), dim3(kLThreads), 0, stream, a);
-  else
+  } else {
     hipLaunchKernelGGL(attn_latent_split_kernel<false>, dim3(blocks), dim3(kLThreads), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
   MergeArgs m;

@@ -104,7 +104,8 @@ constexpr int kLatentVDim = 512;
 constexpr int kLatentHeadsPerBlock = 128;
 
 hipError_t launch_attn_gqa(const AttnArgs& a, bool fp8, int batch, hipStream_t stream);
-hipError_t launch_attn_latent(const LatentArgs& a, bool fp8, hipStream_t stream);
+// pairs (FP8 only): the wave-pair kernel on 64-head groups (a.n_hg counts them) instead of the 128-head one
+hipError_t launch_attn_latent(const LatentArgs& a, bool fp8, bool pairs, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& m, int batch, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, bool fp8, hipStream_t stream);

@@ -207,7 +207,11 @@ int paged_decode_attn_bf16(const kvfp8_pool_desc* desc, const uint16_t* q, int32
  *   Page ids, lengths, abort flags, splits and workspace behave as for
  *   paged_decode_attn_fp8 (with 32-token tiles: num_splits at most
  *   ceil(max_ctx_len/32); workspace from
- *   paged_decode_attn_workspace_bytes(B, Hq, 512, splits)). */
+ *   paged_decode_attn_workspace_bytes(B, Hq, 512, splits)).  With
+ *   num_splits = 0 each cache type picks its own count (the FP8 kernel works
+ *   on 64 heads per block, the BF16 one on 128);
+ *   paged_decode_attn_latent_auto_splits returns the larger of the two, so a
+ *   workspace sized with it fits either. */
 int32_t paged_decode_attn_latent_auto_splits(int32_t batch, int32_t num_q_heads, int32_t max_ctx_len);
 int paged_decode_attn_latent_fp8(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads,
                                  const uint8_t* pool, const int32_t* page_table, int32_t pt_stride,
