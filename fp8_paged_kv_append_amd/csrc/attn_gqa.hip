@@ -553,6 +553,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(MergeArgs a) 
   const float* lse = a.lse_part + row * a.num_splits;
   float M = -INFINITY;
   bool nan = false;
+  // unrolled by 16 here and below: with few rows (one request, many splits) each thread's loads in
+  // flight are all the memory-level parallelism there is
+#pragma unroll 16
   for (int c = 0; c < nvalid; ++c) {
     const float x = lse[c];
     nan |= x != x;
@@ -563,7 +566,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(MergeArgs a) 
   if (!nan && M != -INFINITY) {
     const f32x4_t* part = reinterpret_cast<const f32x4_t*>(a.o_part + row * a.num_splits * a.v_dim + d);
     const int stride = a.v_dim / 4;  // f32x4 per split row
-#pragma unroll 4
+#pragma unroll 16
     for (int c = 0; c < nvalid; ++c) {
       const float f = exp2f(lse[c] - M);
       s += f;
