@@ -249,3 +249,50 @@ def test_one_launch_length_beyond_max_ctx(kv_dtype, num_splits):
     err = attn_error(g_out, ref)
     note(f"  step error {err:.3e}")
     assert err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("name", ["gqa_batch", "long"])
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_full_size_other_gqa_workloads_sampled(kv_dtype, name):
+    """The ragged batch (32 requests of 1024-8192 tokens, 40k-page pool, the library's split choice) and the
+    long context (4 x 131072 tokens, page 64, 32 splits, K outliers x20 against the outlier-free scale) at
+    full size, in the bench's launch configuration (one launch, plus the merge when split): flags bit-exact,
+    sampled requests' pages byte-exact (their first and last pages, where the step's token sits) and their
+    attention rows within tolerance of the oracle."""
+    w = wl.WORKLOADS[name]
+    note(f"full {name} {kv_dtype}: generating")
+    c = Case(w, kv_dtype, oracle_fill=False)
+    assert c.d_k_scale == float(c.o_k_scale) and c.d_v_scale == float(c.o_v_scale)
+    note("  filling")
+    c.fill_device()
+    k_new, v_new, req, pos = c.step_inputs()
+    g_flags, g_out = _device_step(c, k_new, v_new, req, pos, num_splits=w.num_splits, one_launch=True)
+    o_flags = paged.tag_check(c.tags, c.pt, c.exp, c.lens, w.page_size)
+    assert np.array_equal(g_flags, o_flags)
+    if name == "gqa_batch":   # the longest and the shortest request, and one between
+        order = np.argsort(c.lens, kind="stable")
+        sample = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2])})
+    else:
+        sample = [w.batch - 1]                                   # ~1 min of oracle work each
+    et = np.uint8 if kv_dtype == "fp8" else np.uint16
+    g = kv.kv_gather_fp8 if kv_dtype == "fp8" else kv.kv_gather_bf16
+    for r in sample:
+        note(f"  request {r} (L = {int(c.lens[r])})")
+        assert not g_flags[r]
+        a, b = int(c.off[r]), int(c.off[r + 1])
+        S = w.page_size
+        idx = np.r_[a:min(b, a + S), max(a, b - S):b]          # first and last page of the request
+        didx = dev(idx.astype(np.int64))
+        ko = torch.empty((idx.size, w.num_kv_heads, w.head_dim), dtype=c.dkp.dtype, device="cuda")
+        vo = torch.empty((idx.size, w.num_kv_heads, w.v_dim), dtype=c.dkp.dtype, device="cuda")
+        g(c.desc, c.dkp, c.dvp, c.dreq[didx].contiguous(), c.dpos[didx].contiguous(), c.dpt, ko, vo)
+        torch.cuda.synchronize()
+        if kv_dtype == "fp8":
+            assert np.array_equal(host(ko, et), codec.quantize_e4m3(c.k[idx], c.o_k_scale))
+            assert np.array_equal(host(vo, et), codec.quantize_e4m3(c.v[idx], c.o_v_scale))
+        else:
+            assert np.array_equal(host(ko, et), c.k[idx]) and np.array_equal(host(vo, et), c.v[idx])
+        ref = c.oracle_request(r)
+        err = float(np.max(attention.row_rel_error(codec.f64_from_bf16(g_out[r]), ref)))
+        note(f"    row error {err:.3e}")
+        assert err <= ATTN_TOL
