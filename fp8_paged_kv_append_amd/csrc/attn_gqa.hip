@@ -551,27 +551,50 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(MergeArgs a) 
   }
   const int nvalid = min(a.num_splits, (L + a.chunk_tokens - 1) / a.chunk_tokens);
   const float* lse = a.lse_part + row * a.num_splits;
-  float M = -INFINITY;
-  bool nan = false;
-  // unrolled by 16 here and below: with few rows (one request, many splits) each thread's loads in
-  // flight are all the memory-level parallelism there is
-#pragma unroll 16
-  for (int c = 0; c < nvalid; ++c) {
-    const float x = lse[c];
-    nan |= x != x;
-    M = fmaxf(M, x);
-  }
+  const f32x4_t* part = reinterpret_cast<const f32x4_t*>(a.o_part + row * a.num_splits * a.v_dim + d);
+  const int stride = a.v_dim / 4;  // f32x4 per split row
+  // Splits in groups of 16 whose lse values and partials are all loaded before any is used: one
+  // memory round trip per group (with few rows, one request and many splits, the loads each thread
+  // has in flight are all the memory-level parallelism there is).  Groups after the first rescale
+  // the running sums to the new maximum, as the online softmax does.
+  constexpr int kGroup = 16;
+  float M = -INFINITY, s = 0.f;
   f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-  float s = 0.f;
-  if (!nan && M != -INFINITY) {
-    const f32x4_t* part = reinterpret_cast<const f32x4_t*>(a.o_part + row * a.num_splits * a.v_dim + d);
-    const int stride = a.v_dim / 4;  // f32x4 per split row
-#pragma unroll 16
-    for (int c = 0; c < nvalid; ++c) {
-      const float f = exp2f(lse[c] - M);
-      s += f;
-      o += f * part[(int64_t)c * stride];
+  bool nan = false;
+  for (int c0 = 0; c0 < nvalid; c0 += kGroup) {
+    float x[kGroup];
+    f32x4_t p[kGroup];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      if (c0 + j < nvalid) {
+        x[j] = lse[c0 + j];
+        p[j] = part[(int64_t)(c0 + j) * stride];
+      } else {
+        x[j] = -INFINITY;
+        p[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
     }
+    float gm = M;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      nan |= x[j] != x[j];
+      gm = fmaxf(gm, x[j]);
+    }
+    if (gm == -INFINITY) continue;  // nothing but empty splits so far
+    const float rs = exp2f(M - gm);  // 0 while M is still -inf
+    s *= rs;
+    o *= rs;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const float f = exp2f(x[j] - gm);
+      s += f;
+      o += f * p[j];
+    }
+    M = gm;
+  }
+  if (nan) {  // a bad page seen by some split: the row is zero
+    s = 0.f;
+    o = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   const float inv = s > 0.f ? 1.f / s : 0.f;
   *out = u32x2_t{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
