@@ -536,6 +536,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
 // partial; the rows of one block are consecutive, so a block reads contiguous partials.
 constexpr int kMergeThreads = 128;
 
+template <int kGroup>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(MergeArgs a) {
   const int tpr = a.v_dim / 4;  // threads per row
   const int64_t row = (int64_t)blockIdx.x * (kMergeThreads / tpr) + threadIdx.x / tpr;  // r * Hq + h
@@ -553,11 +554,11 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(MergeArgs a) 
   const float* lse = a.lse_part + row * a.num_splits;
   const f32x4_t* part = reinterpret_cast<const f32x4_t*>(a.o_part + row * a.num_splits * a.v_dim + d);
   const int stride = a.v_dim / 4;  // f32x4 per split row
-  // Splits in groups of 16 whose lse values and partials are all loaded before any is used: one
-  // memory round trip per group (with few rows, one request and many splits, the loads each thread
-  // has in flight are all the memory-level parallelism there is).  Groups after the first rescale
-  // the running sums to the new maximum, as the online softmax does.
-  constexpr int kGroup = 16;
+  // Splits in groups of kGroup (4, 8 or 16: the split count rounded up, at most 16) whose lse values
+  // and partials are all loaded before any is used: one memory round trip per group (with few rows,
+  // one request and many splits, the loads each thread has in flight are all the memory-level
+  // parallelism there is; with few splits a small group keeps registers and ALU work down).  Groups
+  // after the first rescale the running sums to the new maximum, as the online softmax does.
   float M = -INFINITY, s = 0.f;
   f32x4_t o = {0.f, 0.f, 0.f, 0.f};
   bool nan = false;
@@ -630,7 +631,12 @@ hipError_t launch_merge(const MergeArgs& m_in, int batch, hipStream_t stream) {
   const int tpr = m.v_dim / 4;  // v_dim is 128 or 512: a power of two dividing 4 * kMergeThreads
   const int64_t rows_per_block = kMergeThreads / tpr;
   const int64_t blocks = (m.rows + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((uint32_t)blocks), dim3(kMergeThreads), 0, stream, m);
+  if (m.num_splits <= 4)
+    hipLaunchKernelGGL(attn_merge_kernel<4>, dim3((uint32_t)blocks), dim3(kMergeThreads), 0, stream, m);
+  else if (m.num_splits <= 8)
+    hipLaunchKernelGGL(attn_merge_kernel<8>, dim3((uint32_t)blocks), dim3(kMergeThreads), 0, stream, m);
+  else
+    hipLaunchKernelGGL(attn_merge_kernel<16>, dim3((uint32_t)blocks), dim3(kMergeThreads), 0, stream, m);
   return hipGetLastError();
 }
 
