@@ -161,6 +161,9 @@ __device__ __forceinline__ f32x4_t mfma_pv<false>(const VRow<false>& v, int kb, 
 
 // Page ids of the block's token range are staged in LDS, at most kPidWin entries at a time.
 constexpr int kPidWin = 2048;
+// Page-table entries per thread whose loads are issued together (the first batch with the context
+// length itself).
+constexpr int kPtBatch = 4;
 
 // One tile's loads for one lane, plus what the softmax needs to mask it.
 template <bool FP8>
@@ -285,6 +288,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
   __shared__ int s_newpage;
   __shared__ uint32_t s_flag[kWaves];
 
+  const int chunk = a.chunk_tiles * kTile;
+  const int c0 = split * chunk;
+  const bool check = a.page_tags != nullptr;
+  const int32_t* pt = a.page_table + (int64_t)r * a.pt_stride;
+  const uint32_t* ex = check ? a.expected + (int64_t)r * a.pt_stride : nullptr;
+  // Page-table words the block reads whatever the context length turns out to be are loaded
+  // together with that length, not after it: with the check, the row's first kPtBatch * kThreads
+  // entries (all checked); without it, the first entries of this split's chunk (its first
+  // page-id window).  Every row holds pt_stride entries, so these loads stay inside the table;
+  // no KV page is read before its tag has been checked.
+  const int64_t sbase = check ? 0 : c0 / S;
+  int32_t sp[kPtBatch];
+  uint32_t se[kPtBatch];
+#pragma unroll
+  for (int j = 0; j < kPtBatch; ++j) {
+    const int64_t i = sbase + threadIdx.x + j * kThreads;
+    const bool in = i < a.pt_stride;
+    sp[j] = in ? pt[i] : -1;
+    se[j] = (check && in) ? ex[i] : 0u;
+  }
   const int L = a.ctx_lens[r];
   // q^T operand: lane (q4, n) holds head g*G+n, dims 32*q4 .. 32*q4+31 (zero for padding heads);
   // issued first, so that its latency overlaps the tag check
@@ -302,8 +325,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
   // The step's token, when passed in, belongs to position L - 1: the block whose chunk holds it
   // writes it into its page and adds it to its softmax from LDS (its tiles stop before it, so
   // nothing reads it back).  Its rows and its page id are loaded now, staged after the check.
-  const int chunk = a.chunk_tiles * kTile;
-  const int c0 = split * chunk;
   const bool fold = a.k_new != nullptr;
   const bool owner = fold && L > 0 && c0 <= L - 1 && L - 1 < c0 + chunk;
   uint32_t kb = 0, vb = 0;
@@ -317,30 +338,60 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
     if ((L - 1) / S < a.pt_stride) newpage = a.page_table[(int64_t)r * a.pt_stride + (L - 1) / S];
   }
 
+  // this block's token range and its first page-id window ([c0, c1) is empty past the context)
+  const int c1 = min(fold ? L - 1 : L, c0 + chunk);
+  // tokens per page-id window: a multiple of the tile, at most kPidWin - 1 pages long, so that even
+  // a window that does not start on a page boundary touches at most kPidWin pages
+  const int win = ((kPidWin - 1) * S / kTile) * kTile;
+  const int fe0 = c0 / S;
+  const int fne = c0 < c1 ? (min(c1, c0 + win) - 1) / S - fe0 + 1 : 0;
+
   uint32_t checked = 0;
-  bool pid_ready = false;  // s_pid already holds the first window's page ids (split 0, from the check)
-  if (a.page_tags != nullptr) {
+  if (check) {
     // the tag check of every page request r's context spans, before any of them is read: bit 0 a
     // page whose tag differs from the one the request recorded, bit 1 a page id out of the pool or
-    // a context longer than the page table
+    // a context longer than the page table.  Entries go in batches of kPtBatch per thread whose
+    // loads, then tag gathers, are all issued before any is used; the entries of this block's
+    // first window are staged in LDS on the way (for a request that passes they lie inside the
+    // `need` entries checked here).
     uint32_t f = 0;
     if (L > 0) {
       const int64_t need = ((int64_t)L + S - 1) / S;
       const int64_t np = min(need, (int64_t)a.pt_stride);
       if (need > a.pt_stride) f |= 2u;
-      const int32_t* ptr = a.page_table + (int64_t)r * a.pt_stride;
-      const uint32_t* ex = a.expected + (int64_t)r * a.pt_stride;
-      // split 0 keeps the ids it checks: its first window starts at entry 0 and, for a request that
-      // passes, spans at most the `need` entries checked here
-      pid_ready = split == 0 && np <= kPidWin;
-      for (int64_t i = threadIdx.x; i < np; i += kThreads) {
-        const int32_t p = ptr[i];
-        const bool ok = p >= 0 && p < a.num_pages;
-        if (!ok)
-          f |= 2u;
-        else if (a.page_tags[p] != ex[i])
-          f |= 1u;
-        if (pid_ready) s_pid[i] = ok ? p : -1;
+      for (int64_t base = 0; base < np; base += kPtBatch * kThreads) {
+        int32_t pg[kPtBatch];
+        uint32_t ev[kPtBatch], tv[kPtBatch];
+#pragma unroll
+        for (int jj = 0; jj < kPtBatch; ++jj) {
+          const int64_t i = base + threadIdx.x + jj * kThreads;
+          if (base == 0) {
+            pg[jj] = sp[jj];
+            ev[jj] = se[jj];
+          } else {
+            pg[jj] = i < np ? pt[i] : -1;
+            ev[jj] = i < np ? ex[i] : 0u;
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < kPtBatch; ++jj) {
+          const int64_t i = base + threadIdx.x + jj * kThreads;
+          const bool ok = pg[jj] >= 0 && pg[jj] < a.num_pages;
+          tv[jj] = (i < np && ok) ? a.page_tags[pg[jj]] : 0u;
+        }
+#pragma unroll
+        for (int jj = 0; jj < kPtBatch; ++jj) {
+          const int64_t i = base + threadIdx.x + jj * kThreads;
+          if (i < np) {
+            const bool ok = pg[jj] >= 0 && pg[jj] < a.num_pages;
+            if (!ok)
+              f |= 2u;
+            else if (tv[jj] != ev[jj])
+              f |= 1u;
+            const int64_t k = i - fe0;
+            if (k >= 0 && k < fne) s_pid[k] = ok ? pg[jj] : -1;
+          }
+        }
       }
     }
 #pragma unroll
@@ -379,10 +430,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
     return;  // the merge kernel zeroes the rows itself
   }
   if (c0 >= L) return;  // past this request's context: the merge does not read this split
-  const int c1 = min(fold ? L - 1 : L, c0 + chunk);
 
-
-  const int32_t* pt = a.page_table + (int64_t)r * a.pt_stride;
   const uint8_t* kpool = reinterpret_cast<const uint8_t*>(a.k_pool);
   const uint8_t* vpool = reinterpret_cast<const uint8_t*>(a.v_pool);
   const int64_t blk = (int64_t)S * kD;  // elements per (page, head) block
@@ -395,22 +443,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
   for (int j = 0; j < 8; ++j) st.acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   bool bad = false;
 
-  // tokens per page-id window: a multiple of the tile, at most kPidWin - 1 pages long, so that even
-  // a window that does not start on a page boundary touches at most kPidWin pages
-  const int win = ((kPidWin - 1) * S / kTile) * kTile;
   for (int w0 = c0; w0 < c1; w0 += win) {
     const int w1 = min(c1, w0 + win);
     const int e0 = w0 / S;
     const int ne = (w1 - 1) / S - e0 + 1;  // entries of the pages holding [w0, w1)
     __syncthreads();                       // the previous window's ids are no longer read
-    const bool have = pid_ready && w0 == 0;
-    for (int i = threadIdx.x; i < ne && !have; i += kThreads) {
-      int p = pt[e0 + i];
-      if (p < 0 || p >= a.num_pages) {
-        bad = true;
-        p = -1;
+    if (!(check && w0 == c0)) {            // with the check, the first window's ids are staged;
+      const bool first = w0 == c0;         // without it, its first batch was loaded with L
+      for (int base = 0; base < ne; base += kPtBatch * kThreads) {
+#pragma unroll
+        for (int jj = 0; jj < kPtBatch; ++jj) {
+          const int i = base + threadIdx.x + jj * kThreads;
+          if (i < ne) {
+            int p = (first && base == 0) ? sp[jj] : pt[e0 + i];
+            if (p < 0 || p >= a.num_pages) {
+              bad = true;
+              p = -1;
+            }
+            s_pid[i] = p;
+          }
+        }
       }
-      s_pid[i] = p;
     }
     __syncthreads();
     const int ntile = (w1 - w0 + kTile - 1) / kTile;
