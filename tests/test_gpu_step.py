@@ -296,3 +296,49 @@ def test_full_size_other_gqa_workloads_sampled(kv_dtype, name):
         err = float(np.max(attention.row_rel_error(codec.f64_from_bf16(g_out[r]), ref)))
         note(f"    row error {err:.3e}")
         assert err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("num_splits", [1, 3])
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_long_rows_page_id_batches_and_windows(kv_dtype, num_splits):
+    """Contexts of 40,000, 17,000 and 33,000 tokens at page 16 (2,500, 1,063 and 2,063 pages): blocks stage
+    page ids in batches of 1,024 entries, so these rows take a second (and third) batch, and at one split the
+    40,000- and 33,000-token chunks span more than one 2,047-page id window.  Request 2 has a stale tag past
+    its first 1,024 entries.  Checked against the oracle: the one-launch step with the check in the launch
+    (flags, pools and rows), the same step with no tracker, and plain attention reading the flags."""
+    w = wl.WORKLOADS["sweep_b16"].with_(batch=3, num_q_heads=8, num_kv_heads=1, num_pages=6000, ctx_lo=1, ctx_hi=1,
+                                        stale=False)
+    lens = np.array([40000, 17000, 33000], dtype=np.int32)
+    note(f"long rows {kv_dtype} splits={num_splits}")
+    c = Case(w, kv_dtype, lens=lens, stale=[])
+    c.fill_device()
+    c.exp[2, 1500] = c.exp[2, 1500] - np.uint32(1)       # stale, in the second batch of 1,024 entries
+    c.dexp = dev(c.exp)
+    k_new, v_new, req, pos = c.step_inputs()
+    k_new = k_new ^ np.uint16(0x0040)                     # a skipped write stays visible
+    st = dict(dtype=kv_dtype, k_pool=c.okp, v_pool=c.ovp, page_table=c.pt, ctx_lens=c.lens, page_tags=c.tags,
+              expected_tags=c.exp, num_kv_heads=w.num_kv_heads, page_size=w.page_size, head_dim=w.head_dim,
+              v_dim=w.v_dim, k_scale=c.o_k_scale, v_scale=c.o_v_scale, sm_scale=c.sm_scale, latent=False)
+    o_flags, o_out = step.decode_step(st, c.q, k_new, v_new, req, pos)
+    assert o_flags.tolist() == [0, 0, 1]
+    g_flags, g_out = _device_step(c, k_new, v_new, req, pos, num_splits=num_splits, one_launch=True)
+    assert np.array_equal(g_flags, o_flags)
+    et = np.uint8 if kv_dtype == "fp8" else np.uint16
+    assert np.array_equal(host(c.dkp, et), c.okp) and np.array_equal(host(c.dvp, et), c.ovp)
+    assert not g_out[2].any()
+    err = attn_error(g_out, {r: o_out[r] for r in (0, 1)})
+    note(f"  tracker on: error {err:.3e}")
+    assert err <= ATTN_TOL
+    # plain attention reading the flags the step wrote
+    got = c.attend(flags=dev(g_flags.view(np.int32)), num_splits=num_splits)
+    assert not got[2].any()
+    err = attn_error(got, {r: o_out[r] for r in (0, 1)})
+    note(f"  flags read: error {err:.3e}")
+    assert err <= ATTN_TOL
+    # no tracker: every request attended (request 2 too), the pools already hold the step's tokens of 0 and 1
+    _, g2_out = _device_step(c, k_new, v_new, req, pos, tracker=False, num_splits=num_splits, one_launch=True)
+    _, o2_out = step.decode_step(st, c.q, k_new, v_new, req, pos, tracker=False)
+    err = attn_error(g2_out, o2_out)
+    note(f"  no tracker: error {err:.3e}")
+    assert err <= ATTN_TOL
+    assert np.array_equal(host(c.dkp, et), c.okp) and np.array_equal(host(c.dvp, et), c.ovp)
