@@ -263,7 +263,7 @@ int latent_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_
                   const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens, int32_t batch,
                   int32_t max_ctx_len, const uint32_t* flags, bool fp8, float scale, float sm_scale,
                   int32_t num_splits, void* workspace, size_t workspace_bytes, uint16_t* out, hipStream_t stream,
-                  bool launch = true) {
+                  bool launch = true, const uint16_t* c_new = nullptr) {
   int st = check_pool(desc, false, fp8 ? 1 : 2);
   if (st) return st;
   if (desc->num_kv_heads != 1 || desc->head_dim != kLatentDim || desc->v_dim != kLatentVDim)
@@ -316,6 +316,9 @@ int latent_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_
   a.n_hg = n_hg;
   a.qk_scale_log2 = (fp8 ? sm_scale * scale : sm_scale) * kLog2e;
   a.v_scale = fp8 ? scale : 1.0f;
+  if (c_new && !aligned16(c_new)) return KVFP8_ERR_ALIGN;
+  a.c_new = c_new;
+  a.c_inv = fp8 ? 1.0f / scale : 1.0f;  // fl32(1/scale), as the append computes it
   if (!launch) return KVFP8_OK;
   return launch_attn_latent(a, fp8, pairs, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
 }
@@ -361,16 +364,18 @@ int decode_step_common(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* lay
       const float ks = fp8 ? ls.k_scales[l] : 1.f;
       const float vs = fp8 && !latent ? ls.v_scales[l] : 1.f;
       // GQA: one attention launch per layer that also writes the layer's token (and, in layer 0, runs
-      // the tag check); latent: a check + write launch, then the attention
+      // the tag check).  Latent: layer 0 a check + write launch, then the attention; later layers one
+      // attention launch that also writes the layer's token (the block(s) holding position L - 1 store
+      // it before copying any tile, and read it back with the rest)
       const uint32_t* tags = l == 0 ? page_tags : nullptr;
       int st = KVFP8_OK;
-      if (latent || !launch)  // the dry pass checks the write's arguments for every layer
+      if ((latent && l == 0) || !launch)  // the dry pass checks the write's arguments for every layer
         st = check_append_common(desc, kp, vp, kn, vn, page_table, pt_stride, ctx_lens, batch, tags, expected_tags,
                                  abort_flags, fp8, ks, vs, stream, launch);
       if (st) return st;
       st = latent ? latent_common(desc, q, num_q_heads, kp, page_table, pt_stride, ctx_lens, batch, max_ctx_len,
                                   abort_flags, fp8, ks, sm_scale, num_splits, workspace, workspace_bytes, out, stream,
-                                  launch)
+                                  launch, l > 0 ? kn : nullptr)
                   : attn_common(desc, q, num_q_heads, kp, vp, page_table, pt_stride, ctx_lens, batch, max_ctx_len,
                                 tags ? nullptr : abort_flags, fp8, ks, vs, sm_scale, num_splits, workspace,
                                 workspace_bytes, out, stream, launch, kn, vn, tags, expected_tags,

@@ -204,7 +204,15 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
     }
   }
 
-  // q has landed before any tile copy is in flight: the loop below then carries no waits for it
+  // The step's token (later layers of a decode step), stored before any tile copy by the block(s)
+  // whose chunk holds position L - 1 (all head groups of that chunk store the same bytes); the wait
+  // below also retires these stores, and the barrier that opens the window loop orders them before
+  // every wave's copies, which then read the token back like any other row.
+  const bool tok_bad = a.c_new != nullptr && c0 <= L - 1 && L - 1 < c0 + chunk &&
+                       !store_latent_row<FP8, kLD>(a, r, L, kLThreads);
+
+  // q has landed (and the token's stores are done) before any tile copy is in flight: the loop
+  // below then carries no waits for them
   vm_wait<0>();
 
   // LDS byte offsets this lane reads, relative to a tile buffer
@@ -244,7 +252,7 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   f32x16_t acc[16];
 #pragma unroll
   for (int db = 0; db < 16; ++db) acc[db] = f32x16_t{};
-  bool bad = false;
+  bool bad = tok_bad;
 
   // at most kLPidWin - 1 pages of tokens per window: a window starting mid-page still fits kLPidWin ids
   const int win = ((kLPidWin - 1) * S / kLT) * kLT;

@@ -204,7 +204,12 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_latent_pair_kernel(LatentAr
     qsh = i32x2p_t{t0[0], t1[0]};
     qsl = i32x2p_t{t0[1], t1[1]};
   }
-  pair_vm_wait<0>();  // q has landed before any tile copy is in flight
+  // The step's token (later layers of a decode step), stored before any tile copy by both head-group
+  // blocks whose chunk holds position L - 1 (the same bytes); the wait below also retires these
+  // stores, and the barrier that opens the window loop orders them before every wave's copies.
+  const bool tok_bad = a.c_new != nullptr && c0 <= L - 1 && L - 1 < c0 + chunk &&
+                       !store_latent_row<true, kPD>(a, r, L, kPThreads);
+  pair_vm_wait<0>();  // q has landed (and the token's stores are done) before any tile copy is in flight
 
   // LDS offsets this lane reads inside a tile buffer (token block mb: token 16 mb + n at lrow)
   const int qk_off0 = lrow(n) * kRS + 256 * x + 32 * q4, qk_off1 = lrow(16 + n) * kRS + 256 * x + 32 * q4;  // + 128 j
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_latent_pair_kernel(LatentAr
 #pragma unroll
   for (int db = 0; db < 16; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   f32x4_t own[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};  // this wave's partial, next tile
-  bool bad = false;
+  bool bad = tok_bad;
 
   const int win = ((kPPidWin - 1) * S / kPT) * kPT;
   for (int w0 = c0; w0 < c1; w0 += win) {

@@ -49,6 +49,32 @@ __device__ __forceinline__ float clamp448(float x) {
   return fabsf(x) > kE4M3Max ? copysignf(kE4M3Max, x) : x;
 }
 
+__device__ __forceinline__ uint32_t encode_e4m3x2(float a, float b);
+
+// The step's new row of request r (DIM elements, bf16 bits at a.c_new + r * DIM) quantised as the
+// append does and stored at position L - 1 of a row-major latent pool [page][slot][DIM].  Only the
+// stores are issued here: the caller waits for them (vmcnt, which counts stores on this GPU family)
+// and crosses a barrier before anything reads the row back.  Returns false, writing nothing, for a
+// page id outside the pool or past the page table.
+template <bool FP8, int DIM, class Args>
+__device__ __forceinline__ bool store_latent_row(const Args& a, int r, int L, int nthreads) {
+  const int S = a.page_size;
+  const int e = (L - 1) / S;
+  const int page = e < a.pt_stride ? a.page_table[(int64_t)r * a.pt_stride + e] : -1;
+  if (page < 0 || page >= a.num_pages) return false;
+  const int64_t row = ((int64_t)page * S + (L - 1) % S) * DIM;
+  const uint16_t* src = a.c_new + (int64_t)r * DIM;
+  for (int d = threadIdx.x; d < DIM; d += nthreads) {
+    const uint32_t x = src[d];
+    if (FP8)
+      reinterpret_cast<uint8_t*>(const_cast<void*>(a.pool))[row + d] =
+          (uint8_t)(encode_e4m3x2(__uint_as_float(x << 16) * a.c_inv, 0.f) & 0xFFu);
+    else
+      reinterpret_cast<uint16_t*>(const_cast<void*>(a.pool))[row + d] = (uint16_t)x;
+  }
+  return true;
+}
+
 __device__ __forceinline__ uint32_t encode_e4m3x2(float a, float b) {
   uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
   uint32_t c0 = e4m3_clamp_nan_fix(a, w & 0xFFu);

@@ -95,6 +95,12 @@ struct LatentArgs {
   int32_t num_splits, max_ctx, batch, n_hg;
   float qk_scale_log2;        // sm_scale * scale * log2(e)
   float v_scale;
+  // Optional (later layers of a decode step): this step's new latent row of every request (bf16
+  // [B][576]), written at position ctx_lens[r] - 1 by the block(s) whose chunk holds it before they
+  // copy any tile, so their copies read it back (null: the token is already in the pool).  c_inv:
+  // fl32(1/scale) for the FP8 cache, as the append computes it.
+  const uint16_t* c_new;
+  float c_inv;
 };
 
 constexpr int kAttnTileTokens = 64;

@@ -147,16 +147,18 @@ def test_layer_stack_step_matches_oracle(kv_dtype, latent):
             assert not g_out[l, r].any()
 
 
+@pytest.mark.parametrize("latent", [False, True])
 @pytest.mark.parametrize("splits", [1, 4])
 @pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
-def test_layer_stack_token_at_chunk_edges(kv_dtype, splits):
-    """Layers after the first write the step's token from their attention launch, in the block whose
-    split holds position L - 1.  Lengths put that position alone in its split (129, 257, 385 with
-    128-token splits), last in one (128, 512), first of the context (L = 1) and mid-tile; pools
-    bit-exact and outputs within tolerance in every layer."""
-    note(f"layer stack chunk edges {kv_dtype} splits={splits}")
+def test_layer_stack_token_at_chunk_edges(kv_dtype, splits, latent):
+    """Layers after the first write the step's token from their attention launch, in the block(s) whose
+    split holds position L - 1 (GQA: added from LDS; latent: stored before the tile copies and read
+    back).  Lengths put that position alone in its split (129, 257, 385 with 128-token splits), last in
+    one (128, 512), first of the context (L = 1) and mid-tile; pools bit-exact and outputs within
+    tolerance in every layer.  Latent FP8 runs the wave-pair kernel here, latent BF16 the 128-head one."""
+    note(f"layer stack chunk edges {kv_dtype} splits={splits} latent={latent}")
     lens = [1, 129, 0, 128, 512, 385, 64, 65, 257]
-    s = Stack(kv_dtype, False, stale=(6,), hole=False, lens=lens, splits=splits)
+    s = Stack(kv_dtype, latent, stale=(6,), hole=False, lens=lens, splits=splits)
     s.run()
     torch.cuda.synchronize()
     o_flags, o_outs = s.oracle()
@@ -164,18 +166,20 @@ def test_layer_stack_token_at_chunk_edges(kv_dtype, splits):
     g_out = host(s.out, np.uint16)
     for l in range(LAYERS):
         assert np.array_equal(host(s.dkp[l], s.et), s.states[l]["k_pool"]), l
-        assert np.array_equal(host(s.dvp[l], s.et), s.states[l]["v_pool"]), l
+        if not latent:
+            assert np.array_equal(host(s.dvp[l], s.et), s.states[l]["v_pool"]), l
         err = attn_error(g_out[l], o_outs[l])
         note(f"  layer {l}: error {err:.3e}")
         assert err <= ATTN_TOL
         assert not g_out[l, 6].any() and not g_out[l, 2].any()
 
 
+@pytest.mark.parametrize("latent", [False, True])
 @pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
-def test_layer_stack_no_op_tracker(kv_dtype):
+def test_layer_stack_no_op_tracker(kv_dtype, latent):
     """page_tags None: no check, nothing flagged; stale requests are written and attended in every layer."""
-    note(f"layer stack no-op tracker {kv_dtype}")
-    s = Stack(kv_dtype, False, hole=False)
+    note(f"layer stack no-op tracker {kv_dtype} latent={latent}")
+    s = Stack(kv_dtype, latent, hole=False)
     s.run(tracker=False)
     torch.cuda.synchronize()
     o_flags, o_outs = s.oracle(tracker=False)
@@ -183,7 +187,8 @@ def test_layer_stack_no_op_tracker(kv_dtype):
     g_out = host(s.out, np.uint16)
     for l in range(LAYERS):
         assert np.array_equal(host(s.dkp[l], s.et), s.states[l]["k_pool"]), l
-        assert np.array_equal(host(s.dvp[l], s.et), s.states[l]["v_pool"]), l
+        if not latent:
+            assert np.array_equal(host(s.dvp[l], s.et), s.states[l]["v_pool"]), l
         assert attn_error(g_out[l], o_outs[l]) <= ATTN_TOL
         assert g_out[l, 1].any() and g_out[l, 6].any()
 
