@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8.0 TB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix peak
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 matrix peak
 METRIC = "decode-attn KV-read GB/s (% of HBM peak) + steps/s, FP8 vs BF16 KV cache"
 
 
@@ -727,9 +728,18 @@ def main():
                         r["splits"]
                     tf = fl_e / (r["attn_ms_mean"] * 1e-3) / 1e12
                     e["attn_tflops"] = round(tf, 1)
-                    e["mfma_roofline"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
-                                          "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                                          "flops_per_launch": fl_e}
+                    # FP8 cache: QK (576 of every 1088 flops per cached element and head) runs on FP8
+                    # MFMAs, PV on bf16 ones, so the peak is that mix's: both parts at their own rate
+                    if kvd == "fp8":
+                        qk = we.head_dim / (we.head_dim + we.v_dim)
+                        peak = 1.0 / (qk / FP8_MFMA_PEAK_TFLOPS + (1.0 - qk) / BF16_MFMA_PEAK_TFLOPS)
+                        peak_note = "QK on FP8 MFMAs (5.0 PFLOP/s), PV on bf16 MFMAs (2.5 PFLOP/s)"
+                    else:
+                        peak = BF16_MFMA_PEAK_TFLOPS
+                        peak_note = "QK and PV on bf16 MFMAs (2.5 PFLOP/s)"
+                    e["mfma_roofline"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": round(peak, 1),
+                                          "unit": "TFLOP/s", "frac": round(tf / peak, 4), "flops_per_launch": fl_e,
+                                          "peak_is": peak_note}
                 ex[kvd] = e
             extra[name] = ex
             del he
