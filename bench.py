@@ -5,7 +5,7 @@ A step is one pass of the whole hot path for one attention layer over one
 batch: the batched page-tag check, the append of every request's new token
 (quantised to e4m3 for the FP8 cache) and paged decode attention (split
 kernel + log-sum-exp merge when the context is split).  By default the step
-is kv_decode_step_* over that one layer, which for the GQA cache is a single
+is kv_decode_step_* over that one layer, which is a single
 launch: every attention block checks its request's page tags before reading
 any page, and the block holding position L-1 writes the new token
 (--two-launch: check + write launch, then attention; --unfused: three
@@ -79,7 +79,7 @@ def parse():
                    help="tag check, append and attention as three launches")
     p.add_argument("--two-launch", action="store_true",
                    help="kv_tag_check_append_* then the attention (default: kv_decode_step_* over one layer, "
-                        "which for the GQA cache is one launch: check, write and attention)")
+                        "one launch: check, write and attention; BF16 latent: a check + write launch first)")
     p.add_argument("--graph", action="store_true",
                    help="time replays of a captured HIP graph of one step (default: eager launches)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -93,8 +93,9 @@ class DeviceCache:
     def __init__(self, w, kv_dtype, host, torch, kv, fused=True, one_launch=True):
         self.w, self.kv_dtype, self.torch, self.kv = w, kv_dtype, torch, kv
         self.fused = fused
-        # the library's whole step (kv_decode_step_* over one layer): one launch for the GQA cache
-        self.one_launch = fused and one_launch and not w.latent
+        # the library's whole step (kv_decode_step_* over one layer): one launch (plus the merge when split);
+        # the BF16 latent cache keeps a check + write launch before it
+        self.one_launch = fused and one_launch
         nk = w.num_pages * w.num_kv_heads * w.page_size * w.head_dim
         nv = w.num_pages * w.num_kv_heads * w.page_size * w.v_dim
         tdt = torch.uint8 if kv_dtype == "fp8" else torch.int16
@@ -171,13 +172,14 @@ class DeviceCache:
                                       self.out, f, num_splits=self.splits, workspace=self.ws)
 
     def lib_step(self, tracker=True):
-        """kv_decode_step_* over this one layer: for the GQA cache a single launch in which every block
-        checks its request's page tags, the block holding position L - 1 writes the new token, and the
-        attention runs (plus the merge when split)."""
+        """kv_decode_step_* over this one layer: a single launch in which every block checks its request's
+        page tags, the block(s) holding position L - 1 write the new token, and the attention runs (plus
+        the merge when split); GQA and latent caches alike."""
         self.kv.decode_step(self.desc, self.kv_dtype, self.kp, self.vp, self.pt, self.lens, self.max_ctx, self.q,
                             self.k_new, self.v_new, None, None, self.out, page_tags=self.tags if tracker else None,
                             expected_tags=self.exp if tracker else None, abort_flags=self.flags if tracker else None,
-                            k_scale=self.k_scale, v_scale=self.v_scale, num_splits=self.splits, workspace=self.ws)
+                            k_scale=self.k_scale, v_scale=self.v_scale,
+                            num_splits=self.lat_splits if self.w.latent else self.splits, workspace=self.ws)
 
     def step(self, tracker=True):
         if self.one_launch:

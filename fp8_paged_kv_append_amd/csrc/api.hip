@@ -263,7 +263,8 @@ int latent_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_
                   const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens, int32_t batch,
                   int32_t max_ctx_len, const uint32_t* flags, bool fp8, float scale, float sm_scale,
                   int32_t num_splits, void* workspace, size_t workspace_bytes, uint16_t* out, hipStream_t stream,
-                  bool launch = true, const uint16_t* c_new = nullptr) {
+                  bool launch = true, const uint16_t* c_new = nullptr, const uint32_t* page_tags = nullptr,
+                  const uint32_t* expected_tags = nullptr, uint32_t* flags_out = nullptr) {
   int st = check_pool(desc, false, fp8 ? 1 : 2);
   if (st) return st;
   if (desc->num_kv_heads != 1 || desc->head_dim != kLatentDim || desc->v_dim != kLatentVDim)
@@ -319,6 +320,12 @@ int latent_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_
   if (c_new && !aligned16(c_new)) return KVFP8_ERR_ALIGN;
   a.c_new = c_new;
   a.c_inv = fp8 ? 1.0f / scale : 1.0f;  // fl32(1/scale), as the append computes it
+  // the tag check in the same launch: it writes the flags instead of reading them
+  if (page_tags && (!expected_tags || !flags_out)) return KVFP8_ERR_NULL;
+  a.page_tags = page_tags;
+  a.expected = expected_tags;
+  a.flags_out = flags_out;
+  if (page_tags) a.flags = nullptr;
   if (!launch) return KVFP8_OK;
   return launch_attn_latent(a, fp8, pairs, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
 }
@@ -363,19 +370,26 @@ int decode_step_common(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* lay
       uint16_t* out = ls.out + l * out_n;
       const float ks = fp8 ? ls.k_scales[l] : 1.f;
       const float vs = fp8 && !latent ? ls.v_scales[l] : 1.f;
-      // GQA: one attention launch per layer that also writes the layer's token (and, in layer 0, runs
-      // the tag check).  Latent: layer 0 a check + write launch, then the attention; later layers one
-      // attention launch that also writes the layer's token (the block(s) holding position L - 1 store
-      // it before copying any tile, and read it back with the rest)
+      // Every layer is one attention launch (plus the merge when split) that also writes the layer's
+      // token and, in layer 0 with page_tags given, runs the tag check in every block first.  GQA: the
+      // block holding position L - 1 adds the token to its softmax from registers; latent: the
+      // block(s) holding it store it before copying any tile and read it back with the rest.  The
+      // BF16 latent cache checks and writes layer 0 in a launch of its own instead: measured faster
+      // at 64 x 4096 (132.5-132.9 us per single-layer step against 135.0-136.1 with the check in its
+      // attention blocks), where the FP8 cache gains from the one launch (130.1-130.9 against
+      // 133.3-133.4 us)
+      const bool own_write = latent && !fp8 && l == 0;
       const uint32_t* tags = l == 0 ? page_tags : nullptr;
       int st = KVFP8_OK;
-      if ((latent && l == 0) || !launch)  // the dry pass checks the write's arguments for every layer
+      if (!launch || own_write)  // the dry pass checks the write's arguments for every layer
         st = check_append_common(desc, kp, vp, kn, vn, page_table, pt_stride, ctx_lens, batch, tags, expected_tags,
                                  abort_flags, fp8, ks, vs, stream, launch);
       if (st) return st;
+      if (own_write) tags = nullptr;
       st = latent ? latent_common(desc, q, num_q_heads, kp, page_table, pt_stride, ctx_lens, batch, max_ctx_len,
-                                  abort_flags, fp8, ks, sm_scale, num_splits, workspace, workspace_bytes, out, stream,
-                                  launch, l > 0 ? kn : nullptr)
+                                  tags ? nullptr : abort_flags, fp8, ks, sm_scale, num_splits, workspace,
+                                  workspace_bytes, out, stream, launch, own_write ? nullptr : kn, tags,
+                                  expected_tags, tags ? abort_flags : nullptr)
                   : attn_common(desc, q, num_q_heads, kp, vp, page_table, pt_stride, ctx_lens, batch, max_ctx_len,
                                 tags ? nullptr : abort_flags, fp8, ks, vs, sm_scale, num_splits, workspace,
                                 workspace_bytes, out, stream, launch, kn, vn, tags, expected_tags,

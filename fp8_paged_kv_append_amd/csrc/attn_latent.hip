@@ -102,7 +102,10 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <bool FP8>
+// CHECK: the launch also runs the tag check (a.page_tags non-null).  A variant of its own, so that the
+// launches without it keep the register allocation of the kernel without the check code (the
+// 128-head kernel uses the whole register file).
+template <bool FP8, bool CHECK>
 __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs a) {
   using C = LCfg<FP8>;
   constexpr int ELT = C::ELT;
@@ -110,6 +113,7 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   __shared__ int s_pid[kLPidWin];
   __shared__ f32x4_t s_sc[kLWaves][4][kWave];  // each wave's next-tile scores, parked across PV
   __shared__ int s_bad;
+  __shared__ uint32_t s_flag[kLWaves];
 
   // XCD-aware block decode: head groups of one (request, split) unit are 8 ids apart
   const int b = blockIdx.x;
@@ -128,7 +132,12 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   const bool active = h0 < Hq;          // wave-uniform
 
   const int L = a.ctx_lens[r];
-  const bool aborted = a.flags != nullptr && a.flags[r] != 0u;
+  uint32_t checked = 0;
+  if constexpr (CHECK) {  // the check in this launch: before any page of r is read or written
+    checked = block_tag_check<kLWaves>(a, r, L, s_flag);
+    if (split == 0 && hg == 0 && threadIdx.x == 0) a.flags_out[r] = checked;
+  }
+  const bool aborted = checked != 0u || (a.flags != nullptr && a.flags[r] != 0u);
   const bool bad_len = L <= 0 || L > a.max_ctx || L > a.pt_stride * S;
   const int chunk = a.chunk_tiles * kLT;
   const int c0 = split * chunk;
@@ -537,9 +546,15 @@ hipError_t launch_attn_latent(const LatentArgs& a, bool fp8, bool pairs, hipStre
     hipError_t e0 = launch_attn_latent_pairs(a, stream);
     if (e0 != hipSuccess) return e0;
   } else if (fp8) {
-    hipLaunchKernelGGL(attn_latent_split_kernel<true>, dim3(blocks), dim3(kLThreads), 0, stream, a);
+    if (a.page_tags != nullptr)
+      hipLaunchKernelGGL((attn_latent_split_kernel<true, true>), dim3(blocks), dim3(kLThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_latent_split_kernel<true, false>), dim3(blocks), dim3(kLThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(attn_latent_split_kernel<false>, dim3(blocks), dim3(kLThreads), 0, stream, a);
+    if (a.page_tags != nullptr)
+      hipLaunchKernelGGL((attn_latent_split_kernel<false, true>), dim3(blocks), dim3(kLThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_latent_split_kernel<false, false>), dim3(blocks), dim3(kLThreads), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
@@ -548,7 +563,7 @@ hipError_t launch_attn_latent(const LatentArgs& a, bool fp8, bool pairs, hipStre
   m.lse_part = a.lse_part;
   m.out = a.out;
   m.ctx_lens = a.ctx_lens;
-  m.flags = a.flags;
+  m.flags = a.page_tags != nullptr ? a.flags_out : a.flags;
   m.num_q_heads = a.num_q_heads;
   m.v_dim = kLV;
   m.num_splits = a.num_splits;

@@ -118,6 +118,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_latent_pair_kernel(LatentAr
   __shared__ int s_pid[kPPidWin];
   __shared__ f32x4_t s_sc[2][kPW][2][kWave];   // [tile parity][wave][token block][lane]: partial scores
   __shared__ int s_bad;
+  __shared__ uint32_t s_flag[kPW];
 
   // XCD-aware block decode: head groups of one (request, split) unit are 8 ids apart
   const int n_hg = (a.num_q_heads + kPHB - 1) / kPHB;
@@ -138,7 +139,12 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_latent_pair_kernel(LatentAr
   const bool active = h0 < Hq;                   // wave-uniform (Hq is a multiple of 16)
 
   const int L = a.ctx_lens[r];
-  const bool aborted = a.flags != nullptr && a.flags[r] != 0u;
+  uint32_t checked = 0;
+  if (a.page_tags != nullptr) {  // the check in this launch: before any page of r is read or written
+    checked = block_tag_check<kPW>(a, r, L, s_flag);
+    if (split == 0 && hg == 0 && threadIdx.x == 0) a.flags_out[r] = checked;
+  }
+  const bool aborted = checked != 0u || (a.flags != nullptr && a.flags[r] != 0u);
   const bool bad_len = L <= 0 || L > a.max_ctx || L > a.pt_stride * S;
   const int chunk = a.chunk_tiles * kPT;
   const int c0 = split * chunk;

@@ -49,32 +49,6 @@ __device__ __forceinline__ float clamp448(float x) {
   return fabsf(x) > kE4M3Max ? copysignf(kE4M3Max, x) : x;
 }
 
-__device__ __forceinline__ uint32_t encode_e4m3x2(float a, float b);
-
-// The step's new row of request r (DIM elements, bf16 bits at a.c_new + r * DIM) quantised as the
-// append does and stored at position L - 1 of a row-major latent pool [page][slot][DIM].  Only the
-// stores are issued here: the caller waits for them (vmcnt, which counts stores on this GPU family)
-// and crosses a barrier before anything reads the row back.  Returns false, writing nothing, for a
-// page id outside the pool or past the page table.
-template <bool FP8, int DIM, class Args>
-__device__ __forceinline__ bool store_latent_row(const Args& a, int r, int L, int nthreads) {
-  const int S = a.page_size;
-  const int e = (L - 1) / S;
-  const int page = e < a.pt_stride ? a.page_table[(int64_t)r * a.pt_stride + e] : -1;
-  if (page < 0 || page >= a.num_pages) return false;
-  const int64_t row = ((int64_t)page * S + (L - 1) % S) * DIM;
-  const uint16_t* src = a.c_new + (int64_t)r * DIM;
-  for (int d = threadIdx.x; d < DIM; d += nthreads) {
-    const uint32_t x = src[d];
-    if (FP8)
-      reinterpret_cast<uint8_t*>(const_cast<void*>(a.pool))[row + d] =
-          (uint8_t)(encode_e4m3x2(__uint_as_float(x << 16) * a.c_inv, 0.f) & 0xFFu);
-    else
-      reinterpret_cast<uint16_t*>(const_cast<void*>(a.pool))[row + d] = (uint16_t)x;
-  }
-  return true;
-}
-
 __device__ __forceinline__ uint32_t encode_e4m3x2(float a, float b) {
   uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
   uint32_t c0 = e4m3_clamp_nan_fix(a, w & 0xFFu);
@@ -132,5 +106,61 @@ template <typename T>
 __device__ __forceinline__ T shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }
+
+// The step's new row of request r (DIM elements, bf16 bits at a.c_new + r * DIM) quantised as the
+// append does and stored at position L - 1 of a row-major latent pool [page][slot][DIM].  Only the
+// stores are issued here: the caller waits for them (vmcnt, which counts stores on this GPU family)
+// and crosses a barrier before anything reads the row back.  Returns false, writing nothing, for a
+// page id outside the pool or past the page table.
+template <bool FP8, int DIM, class Args>
+__device__ __forceinline__ bool store_latent_row(const Args& a, int r, int L, int nthreads) {
+  const int S = a.page_size;
+  const int e = (L - 1) / S;
+  const int page = e < a.pt_stride ? a.page_table[(int64_t)r * a.pt_stride + e] : -1;
+  if (page < 0 || page >= a.num_pages) return false;
+  const int64_t row = ((int64_t)page * S + (L - 1) % S) * DIM;
+  const uint16_t* src = a.c_new + (int64_t)r * DIM;
+  for (int d = threadIdx.x; d < DIM; d += nthreads) {
+    const uint32_t x = src[d];
+    if (FP8)
+      reinterpret_cast<uint8_t*>(const_cast<void*>(a.pool))[row + d] =
+          (uint8_t)(encode_e4m3x2(__uint_as_float(x << 16) * a.c_inv, 0.f) & 0xFFu);
+    else
+      reinterpret_cast<uint16_t*>(const_cast<void*>(a.pool))[row + d] = (uint16_t)x;
+  }
+  return true;
+}
+
+// The tag check of every page request r's context spans, by a whole block (NW waves), before any
+// of them is read or written: bit 0 a page whose tag differs from the one the request recorded,
+// bit 1 a page id outside the pool or a context longer than the page table.  Returns the request's
+// flag to every thread (s_flag: NW words of LDS).
+template <int NW, class Args>
+__device__ __forceinline__ uint32_t block_tag_check(const Args& a, int r, int L, uint32_t* s_flag) {
+  uint32_t f = 0;
+  if (L > 0) {
+    const int64_t need = ((int64_t)L + a.page_size - 1) / a.page_size;
+    const int64_t np = need < a.pt_stride ? need : (int64_t)a.pt_stride;
+    if (need > a.pt_stride) f |= 2u;
+    const int32_t* pt = a.page_table + (int64_t)r * a.pt_stride;
+    const uint32_t* ex = a.expected + (int64_t)r * a.pt_stride;
+    for (int64_t i = threadIdx.x; i < np; i += NW * kWave) {
+      const int32_t p = pt[i];
+      if (p < 0 || p >= a.num_pages)
+        f |= 2u;
+      else if (a.page_tags[p] != ex[i])
+        f |= 1u;
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) f |= shfl_xor(f, m);
+  if ((threadIdx.x & (kWave - 1)) == 0) s_flag[threadIdx.x / kWave] = f;
+  __syncthreads();
+  uint32_t all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) all |= s_flag[w];
+  return all;
+}
+
 
 }  // namespace kvfp8

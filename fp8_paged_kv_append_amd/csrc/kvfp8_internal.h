@@ -101,6 +101,12 @@ struct LatentArgs {
   // fl32(1/scale) for the FP8 cache, as the append computes it.
   const uint16_t* c_new;
   float c_inv;
+  // Optional: the pages' tag check in the same launch (page_tags non-null; flags then null).  Every
+  // block checks all pages of its request before it reads or writes any; block (split 0, head group
+  // 0) stores the request's flag in flags_out, which the merge launch reads.
+  const uint32_t* page_tags;  // [P]
+  const uint32_t* expected;   // [B][pt_stride]
+  uint32_t* flags_out;        // [B]
 };
 
 constexpr int kAttnTileTokens = 64;

@@ -247,10 +247,12 @@ int paged_decode_attn_latent_bf16(const kvfp8_pool_desc* desc, const uint16_t* q
  * any page) and block (split 0, head 0) stores the request's flag; the
  * block whose split holds position ctx_lens[r] - 1 quantises the token as
  * kv_append_fp8 does, stores it, and adds it to its softmax from the values
- * it holds.  For the latent cache layer 0 keeps its check + write launch
- * and every later layer is one attention launch (plus the merge) in which
- * the block(s) whose split holds position ctx_lens[r] - 1 quantise and store
- * the token before copying any tile of it, then read it back with the rest.
+ * it holds.  For the latent cache every layer is likewise one attention
+ * launch (plus the merge) in which the block(s) whose split holds position
+ * ctx_lens[r] - 1 quantise and store the token before copying any tile of
+ * it, then read it back with the rest; FP8 layer 0 with page_tags given runs
+ * the check in every block first, BF16 layer 0 keeps a check + write launch
+ * before its attention.
  * Flags, pools and outputs are those of the launch order above.
  * A request with ctx_lens[r] > max_ctx_len is a caller error: its rows are
  * zero and the GQA layers and later latent layers do not write its token.
