@@ -320,8 +320,10 @@ int latent_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_
   if (c_new && !aligned16(c_new)) return KVFP8_ERR_ALIGN;
   a.c_new = c_new;
   a.c_inv = fp8 ? 1.0f / scale : 1.0f;  // fl32(1/scale), as the append computes it
-  // the tag check in the same launch: it writes the flags instead of reading them
+  // the tag check in the same launch: it writes the flags instead of reading them (FP8 only; for the
+  // BF16 cache the check is a launch of its own)
   if (page_tags && (!expected_tags || !flags_out)) return KVFP8_ERR_NULL;
+  if (page_tags && !fp8) return KVFP8_ERR_UNSUPPORTED;
   a.page_tags = page_tags;
   a.expected = expected_tags;
   a.flags_out = flags_out;

@@ -550,11 +550,8 @@ hipError_t launch_attn_latent(const LatentArgs& a, bool fp8, bool pairs, hipStre
       hipLaunchKernelGGL((attn_latent_split_kernel<true, true>), dim3(blocks), dim3(kLThreads), 0, stream, a);
     else
       hipLaunchKernelGGL((attn_latent_split_kernel<true, false>), dim3(blocks), dim3(kLThreads), 0, stream, a);
-  } else {
-    if (a.page_tags != nullptr)
-      hipLaunchKernelGGL((attn_latent_split_kernel<false, true>), dim3(blocks), dim3(kLThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_latent_split_kernel<false, false>), dim3(blocks), dim3(kLThreads), 0, stream, a);
+  } else {  // BF16: the check runs in a launch of its own (the host never asks for it here)
+    hipLaunchKernelGGL((attn_latent_split_kernel<false, false>), dim3(blocks), dim3(kLThreads), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
