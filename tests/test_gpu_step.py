@@ -342,3 +342,45 @@ def test_long_rows_page_id_batches_and_windows(kv_dtype, num_splits):
     note(f"  no tracker: error {err:.3e}")
     assert err <= ATTN_TOL
     assert np.array_equal(host(c.dkp, et), c.okp) and np.array_equal(host(c.dvp, et), c.ovp)
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_latent_one_launch_step_128_head_kernel(kv_dtype):
+    """The latent step through kv_decode_step_* over one layer at a grid large enough for the 128-head kernel
+    (64 requests, 128 heads, 4 splits): for the FP8 cache one launch whose blocks check their request's pages
+    and store the token, for BF16 a check + write launch and the attention.  Stale tags, a page-table hole
+    and an empty request; flags and the pool bit-exact to the oracle's check -> append, every row within
+    tolerance, faulty requests zero."""
+    w = wl.WORKLOADS["latent"].with_(batch=64, num_q_heads=128, num_pages=1200, ctx_lo=256, ctx_hi=700)
+    note(f"latent one-launch step, 128-head kernel, {kv_dtype}")
+    lens = wl.ctx_lens(w)
+    lens[3] = 0
+    c = Case(w, kv_dtype, lens=lens, stale=[1, 6])
+    c.fill_device()
+    hole = 5
+    c.pt[hole, (int(c.lens[hole]) - 1) // w.page_size // 2] = -1
+    c.dpt = dev(c.pt)
+    k_new, _, req, pos = c.step_inputs()
+    k_new = k_new ^ np.uint16(0x0040)
+    st = dict(dtype=kv_dtype, k_pool=c.okp, v_pool=None, page_table=c.pt, ctx_lens=c.lens, page_tags=c.tags,
+              expected_tags=c.exp, num_kv_heads=w.num_kv_heads, page_size=w.page_size, head_dim=w.head_dim,
+              v_dim=w.v_dim, k_scale=c.o_k_scale, v_scale=c.o_v_scale, sm_scale=c.sm_scale, latent=True)
+    o_flags, o_out = step.decode_step(st, c.q, k_new, None, req, pos)
+    assert o_flags[hole] == paged.FLAG_BAD_PAGE and o_flags[1] and o_flags[6] and not o_flags[3]
+    flags = torch.full((w.batch,), -1, dtype=torch.int32, device="cuda")
+    out = c.out_tensor()
+    splits = kv.paged_decode_attn_latent_auto_splits(w.batch, w.num_q_heads, c.max_ctx)
+    assert splits == 4
+    kv.decode_step(c.desc, kv_dtype, c.dkp, None, c.dpt, c.dlens, c.max_ctx, c.dq, dev(k_new), None, None, None, out,
+                   page_tags=c.dtags, expected_tags=c.dexp, abort_flags=flags, k_scale=c.d_k_scale,
+                   v_scale=c.d_v_scale, sm_scale=c.sm_scale, workspace=c.workspace(splits))
+    torch.cuda.synchronize()
+    g_flags, g_out = host(flags, np.uint32), host(out, np.uint16)
+    assert np.array_equal(g_flags, o_flags)
+    et = np.uint8 if kv_dtype == "fp8" else np.uint16
+    assert np.array_equal(host(c.dkp, et), c.okp)
+    err = attn_error(g_out, o_out)
+    note(f"  step error {err:.3e}")
+    assert err <= ATTN_TOL
+    for r in np.flatnonzero(o_flags).tolist() + [3]:
+        assert not g_out[r].any()
