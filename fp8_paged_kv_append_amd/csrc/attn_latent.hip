@@ -32,6 +32,11 @@
 //    lane 4a+e element e of the blocks named by lanes a, a+4, a+8, a+12.
 //  * Online softmax in the log2 domain, lazy: the accumulators are rescaled
 //    only when a head's running max grows by more than 2^8.
+// In a decode step the same launch may also store the step's token (the
+// block(s) whose split holds position L - 1 quantise it and store it into its
+// page before their first tile copy, then read it back like any other row) and,
+// for the FP8 cache, check the request's page tags first (every block, before
+// it reads or writes any page; a variant of its own, CHECK).
 #include "kvfp8_device.h"
 #include "kvfp8_internal.h"
 

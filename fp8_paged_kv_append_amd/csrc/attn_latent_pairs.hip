@@ -25,6 +25,10 @@
 //    dim offset 8 h: lane 8 h + e then receives dim 8 h + e of the 8 tokens.
 //  * Online softmax in the log2 domain with the lazy rescale (only when a
 //    head's running max grows by more than 2^8).
+// In a decode step the same launch may also check the request's page tags
+// (every block, before it reads or writes any page) and store the step's token
+// (both head-group blocks of the split holding position L - 1, the same bytes,
+// before their first tile copy), as attn_latent_split_kernel does.
 #include "kvfp8_device.h"
 #include "kvfp8_internal.h"
 
