@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="sweep_b64")
     p.add_argument("--splits", type=int, default=0, help="0 = library choice")
+    p.add_argument("--batch", type=int, default=0,
+                   help="requests of the main workload (0 = the workload's own; its page pool is kept)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bf16", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads (GQA batch, long, latent)")
@@ -610,6 +612,8 @@ def main():
         return out
 
     w = wl.WORKLOADS[args.workload]
+    if args.batch:
+        w = w.with_(name=f"{w.name}_b{args.batch}", batch=args.batch)
     results = {}
     if args.weights_only:
         print(json.dumps({"metric": "weight-quantised decode GEMM (INT4 vs FP8 weights), one GPU",
