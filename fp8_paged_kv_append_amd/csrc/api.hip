@@ -258,8 +258,15 @@ int32_t latent_auto_splits(int32_t batch, int32_t num_q_heads, int32_t max_ctx, 
   return (int32_t)s;
 }
 
-bool latent_use_pairs(bool fp8, int32_t batch, int32_t num_q_heads, int32_t splits128) {
-  return fp8 && (int64_t)batch * latent_head_groups(num_q_heads, false) * splits128 < kTargetBlocks;
+// FP8: the wave-pair kernel while its splits are at most 1024 tokens.  Measured at 4096 tokens per
+// request, pair kernel against 128-head kernel, each at its own split count: B=1 (32 splits) 31.4
+// against 35.7 us, B=8 (16 against 32) 43.6 against 56.5, B=16 (8 against 16) 57.7 against 67.0,
+// B=32 (4 against 8) 83.5-84.0 against 87.2-88.0; at B=64 (2048-token splits against 4 splits of the
+// 128-head kernel) 143-145 against 130-134 us, where each of the two head-group blocks copying every
+// tile into its own LDS costs more than the second wave per SIMD gains.
+constexpr int32_t kPairMaxSplitTokens = 1024;
+bool latent_use_pairs(bool fp8, int32_t max_ctx, int32_t pair_splits) {
+  return fp8 && pair_splits > 0 && ((int64_t)max_ctx + pair_splits - 1) / pair_splits <= kPairMaxSplitTokens;
 }
 
 int latent_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads, const void* pool,
@@ -281,12 +288,12 @@ int latent_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_
   if (!aligned16(q) || !aligned16(pool) || !aligned16(out)) return KVFP8_ERR_ALIGN;
   if (!good_scale(scale) || !good_scale(sm_scale)) return KVFP8_ERR_VALUE;
   const int32_t tiles = (int32_t)(((int64_t)max_ctx_len + kLatentTileTokens - 1) / kLatentTileTokens);
-  // FP8: the wave-pair kernel when the 128-head kernel's grid would leave CUs idle (few requests:
-  // its split count is capped by the context), e.g. 61-layer steps at B=1 51.8 -> 40.2 us per layer;
-  // at 64 x 4096 the 128-head kernel is as fast and steadier (131 us against 128-145 us)
-  const int32_t s128 = num_splits == 0 ? latent_auto_splits(batch, num_q_heads, max_ctx_len, false) : num_splits;
-  const bool pairs = latent_use_pairs(fp8, batch, num_q_heads, s128);
-  int32_t splits = num_splits == 0 && pairs ? latent_auto_splits(batch, num_q_heads, max_ctx_len, true) : s128;
+  // FP8: the wave-pair kernel while its splits stay short (latent_use_pairs), else the 128-head
+  // kernel; each with its own split count unless the caller gives one
+  const int32_t sp = num_splits == 0 ? latent_auto_splits(batch, num_q_heads, max_ctx_len, true) : num_splits;
+  const bool pairs = latent_use_pairs(fp8, max_ctx_len, sp);
+  int32_t splits = pairs ? sp : (num_splits == 0 ? latent_auto_splits(batch, num_q_heads, max_ctx_len, false)
+                                                 : num_splits);
   if (splits > tiles) return KVFP8_ERR_SHAPE;
   const int32_t chunk_tiles = (tiles + splits - 1) / splits;
   splits = (tiles + chunk_tiles - 1) / chunk_tiles;
@@ -547,7 +554,8 @@ int paged_decode_attn_bf16(const kvfp8_pool_desc* desc, const uint16_t* q, int32
 int32_t paged_decode_attn_latent_auto_splits(int32_t batch, int32_t num_q_heads, int32_t max_ctx_len) {
   // the larger of the two caches' choices, so that a workspace sized with it fits either
   const int32_t b = latent_auto_splits(batch, num_q_heads, max_ctx_len, false);
-  const int32_t f = latent_use_pairs(true, batch, num_q_heads, b) ? latent_auto_splits(batch, num_q_heads, max_ctx_len, true) : b;
+  const int32_t p = latent_auto_splits(batch, num_q_heads, max_ctx_len, true);
+  const int32_t f = latent_use_pairs(true, max_ctx_len, p) ? p : b;
   return f > b ? f : b;
 }
 

@@ -346,12 +346,13 @@ def test_long_rows_page_id_batches_and_windows(kv_dtype, num_splits):
 
 @pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
 def test_latent_one_launch_step_128_head_kernel(kv_dtype):
-    """The latent step through kv_decode_step_* over one layer at a grid large enough for the 128-head kernel
-    (64 requests, 128 heads, 4 splits): for the FP8 cache one launch whose blocks check their request's pages
-    and store the token, for BF16 a check + write launch and the attention.  Stale tags, a page-table hole
-    and an empty request; flags and the pool bit-exact to the oracle's check -> append, every row within
-    tolerance, faulty requests zero."""
-    w = wl.WORKLOADS["latent"].with_(batch=64, num_q_heads=128, num_pages=1200, ctx_lo=256, ctx_hi=700)
+    """The latent step through kv_decode_step_* over one layer where the library picks the 128-head kernel
+    (64 requests of 2,100-2,600 tokens, 128 heads: the wave-pair kernel's splits would exceed 1,024 tokens;
+    4 splits): for the FP8 cache one launch whose blocks check their request's pages and store the token,
+    for BF16 a check + write launch and the attention.  Stale tags, a page-table hole and an empty request;
+    flags and the pool bit-exact to the oracle's check -> append, every row within tolerance, faulty
+    requests zero."""
+    w = wl.WORKLOADS["latent"].with_(batch=64, num_q_heads=128, num_pages=3000, ctx_lo=2100, ctx_hi=2600)
     note(f"latent one-launch step, 128-head kernel, {kv_dtype}")
     lens = wl.ctx_lens(w)
     lens[3] = 0
