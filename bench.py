@@ -355,8 +355,8 @@ def cpu_baseline(w, n_req, min_seconds=10.0):
     k, v = wl.all_kv(ws, lens)
     req, pos = wl.token_index(lens)
     ks, vs = codec.calibrate_scale(k), codec.calibrate_scale(v)
-    kp, vp = wl.pool_bytes(ws, "k", 1), wl.pool_bytes(ws, "v", 1)
-    paged.append_fp8(kp, vp, k, v, req, pos, pt, ws.num_kv_heads, ws.page_size, ks, vs)
+    kp, vp = wl.pool_init(ws, "k", 1), wl.pool_init(ws, "v", 1)
+    paged.append_fp8(kp, vp, k, v, req, pos, pt, ks, vs)
     tags = wl.page_tags(ws)
     st = dict(dtype="fp8", k_pool=kp, v_pool=vp, page_table=pt, ctx_lens=lens, page_tags=tags,
               expected_tags=wl.expected_tags(ws, pt, lens, tags), num_kv_heads=ws.num_kv_heads,

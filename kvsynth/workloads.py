@@ -254,3 +254,12 @@ def pool_bytes(w: Workload, which: str, elt_bytes: int, num_pages: Optional[int]
         n = p * w.num_kv_heads * w.page_size * w.v_dim * elt_bytes
         sid = _S_POOL_V
     return np.frombuffer(_rng(w.seed, sid, elt_bytes).bytes(n), dtype=np.uint8).copy()
+
+
+def pool_init(w: Workload, which: str, elt_bytes: int, num_pages: Optional[int] = None) -> np.ndarray:
+    """The same random bytes as pool_bytes, viewed as a pool in logical order [P][Hkv][S][D]
+    (uint8 elements for elt_bytes 1, uint16 for 2)."""
+    p = w.num_pages if num_pages is None else num_pages
+    d = w.head_dim if which == "k" else w.v_dim
+    flat = pool_bytes(w, which, elt_bytes, p)
+    return flat.view(np.uint8 if elt_bytes == 1 else np.uint16).reshape(p, w.num_kv_heads, w.page_size, d)

@@ -59,8 +59,8 @@ def decode_attention(q_bits, k_pool, v_pool, page_table, ctx_lens, *, num_kv_hea
                      flags=None, requests=None, latent=False):
     """Paged decode attention for the listed requests (all by default).
 
-    q_bits: bf16 bits [B][Hq][D].  Pools: flat element arrays (e4m3 codes
-    when dtype == "fp8", bf16 bits when "bf16") in the layout of oracle.paged.
+    q_bits: bf16 bits [B][Hq][D].  Pools: logical [P][Hkv][S][D] element arrays
+    (e4m3 codes when dtype == "fp8", bf16 bits when "bf16"), as oracle.paged keeps them.
     Returns {r: fp64 [Hq][Dv]}; aborted requests (flags[r] != 0) and L <= 0
     give zero rows.
     """
@@ -77,11 +77,11 @@ def decode_attention(q_bits, k_pool, v_pool, page_table, ctx_lens, *, num_kv_hea
             continue
         q = codec.f64_from_bf16(q_bits[r])
         if latent:
-            c, _ = paged.gather(k_pool, None, page_table, r, L, 1, page_size, head_dim, v_dim)
+            c, _ = paged.gather(k_pool, None, page_table, r, L)
             c = dequant_rows(c, dtype, k_scale)[:, 0, :]            # [L][Dl]
             out[r] = softmax_attention(q, c, c[:, :v_dim], sm_scale)
         else:
-            k, v = paged.gather(k_pool, v_pool, page_table, r, L, num_kv_heads, page_size, head_dim, v_dim)
+            k, v = paged.gather(k_pool, v_pool, page_table, r, L)
             out[r] = request_attention(q, dequant_rows(k, dtype, k_scale), dequant_rows(v, dtype, v_scale),
                                        num_kv_heads, sm_scale)
     return out

@@ -34,11 +34,10 @@ def decode_step(state, q_bits, k_new_bits, v_new_bits, tok_req, tok_pos, *, trac
                                 s["page_size"])
     if s["dtype"] == "fp8":
         paged.append_fp8(s["k_pool"], s["v_pool"], k_new_bits, v_new_bits, tok_req, tok_pos,
-                         s["page_table"], s["num_kv_heads"], s["page_size"], s["k_scale"],
-                         s["v_scale"], flags)
+                         s["page_table"], s["k_scale"], s["v_scale"], flags)
     else:
         paged.append(s["k_pool"], s["v_pool"], k_new_bits, v_new_bits, tok_req, tok_pos, s["page_table"],
-                     s["num_kv_heads"], s["page_size"], flags)
+                     flags)
     B = q_bits.shape[0]
     reqs = list(range(B)) if requests is None else list(requests)
 
@@ -77,10 +76,9 @@ def decode_step_layers(states, q_bits, k_new_bits, v_new_bits, tok_req, tok_pos,
     for s, q, kn, vn in zip(states, q_bits, k_new_bits, v_new_bits):
         if s["dtype"] == "fp8":
             paged.append_fp8(s["k_pool"], s["v_pool"], kn, vn, tok_req, tok_pos, s["page_table"],
-                             s["num_kv_heads"], s["page_size"], s["k_scale"], s["v_scale"], flags)
+                             s["k_scale"], s["v_scale"], flags)
         else:
-            paged.append(s["k_pool"], s["v_pool"], kn, vn, tok_req, tok_pos, s["page_table"], s["num_kv_heads"],
-                         s["page_size"], flags)
+            paged.append(s["k_pool"], s["v_pool"], kn, vn, tok_req, tok_pos, s["page_table"], flags)
         outs.append(attention.decode_attention(
             q, s["k_pool"], s["v_pool"], s["page_table"], s["ctx_lens"], num_kv_heads=s["num_kv_heads"],
             page_size=s["page_size"], head_dim=s["head_dim"], v_dim=s["v_dim"], dtype=s["dtype"],

@@ -18,15 +18,8 @@ slower.  They give neither the grouping nor the scale format.  Readings taken he
   code = E(fl32(w * fl32(1/s))) with the KV cache's e4m3 encoder (RNE, saturating); weight s * dec(code);
 * weights are finite (the offline quantiser is not defined on NaN or infinity).
 
-Storage (the pages fix none; this is the library's layout, written out here as plain index rules):
-* codes are grouped in tiles of 16 output channels x 128 input channels, tile (t, g) for channels
-  n in [16t, 16t+16), k in [128g, 128g+128), tiles ordered t-major: tile index t * (K/128) + g;
-* inside a tile, 64 lanes l = 16*qq + nn (qq in 0..3, nn in 0..15) each own output channel 16t + nn
-  and, for j in 0..3 and e in 0..7, input channel k = 128g + 32j + 8qq + e;
-* INT4: 16 bytes per lane, dword j holds the 8 codes of (j, e) as unsigned nibbles q + 8, e = 2*(s%4)
-  + s//4 in nibble slot s (bits 4s..4s+3 of the little-endian dword);
-* FP8: 32 bytes per lane, byte 8j + e holds the code of (j, e);
-* scales: bf16 [N/16][K/128][16], element (t, g, nn) = scale of output channel 16t + nn in group g.
+Codes and scales are held in their logical order (codes [N][K], scales [N][K/128]); how the library
+packs them for its loads is not the oracle's concern.
 """
 from __future__ import annotations
 
@@ -35,7 +28,6 @@ import numpy as np
 from . import codec
 
 G = 128                 # input channels per quantisation group
-TILE_N = 16             # output channels per storage tile
 INT4_MAX = 7.0
 
 
@@ -90,75 +82,6 @@ def dequant_w8(codes, s_bits):
     N, K = codes.shape
     s = codec.f64_from_bf16(s_bits)
     return (codec.e4m3_decode(codes).reshape(N, K // G, G) * s[:, :, None]).reshape(N, K)
-
-
-# ----------------------------------------------------------------------------- storage layout
-
-def _lane_index(N, K):
-    """For every (n, k): (tile index, lane, j, e) of the storage rule."""
-    n = np.arange(N)[:, None]
-    k = np.arange(K)[None, :]
-    t, nn = n // TILE_N, n % TILE_N
-    g, kk = k // G, k % G
-    j, qq, e = kk // 32, (kk % 32) // 8, kk % 8
-    tile = t * (K // G) + g
-    lane = 16 * qq + nn
-    return np.broadcast_arrays(tile, lane, j, e)
-
-
-def _check_shape(N, K):
-    if N % TILE_N or K % G:
-        raise ValueError(f"N = {N} must be a multiple of {TILE_N} and K = {K} of {G}")
-
-
-def pack_w4(q):
-    """int8 codes [N][K] -> packed bytes (N*K/2) in the library's INT4 layout."""
-    N, K = q.shape
-    _check_shape(N, K)
-    tile, lane, j, e = _lane_index(N, K)
-    slot = (e % 2) * 4 + e // 2                     # inverse of e = 2*(s%4) + s//4
-    nib = (q.astype(np.int64) + 8) & 0xF
-    byte = (tile * 64 + lane) * 16 + 4 * j + slot // 2
-    shift = 4 * (slot % 2)
-    out = np.zeros(N * K // 2, dtype=np.int64)
-    np.add.at(out, byte.ravel(), (nib << shift).ravel())
-    return out.astype(np.uint8)
-
-
-def unpack_w4(packed, N, K):
-    _check_shape(N, K)
-    tile, lane, j, e = _lane_index(N, K)
-    slot = (e % 2) * 4 + e // 2
-    byte = (tile * 64 + lane) * 16 + 4 * j + slot // 2
-    nib = (np.asarray(packed, dtype=np.uint8)[byte].astype(np.int64) >> (4 * (slot % 2))) & 0xF
-    return (nib - 8).astype(np.int8)
-
-
-def pack_w8(codes):
-    N, K = codes.shape
-    _check_shape(N, K)
-    tile, lane, j, e = _lane_index(N, K)
-    out = np.zeros(N * K, dtype=np.uint8)
-    out[((tile * 64 + lane) * 32 + 8 * j + e).ravel()] = np.asarray(codes, dtype=np.uint8).ravel()
-    return out
-
-
-def unpack_w8(packed, N, K):
-    _check_shape(N, K)
-    tile, lane, j, e = _lane_index(N, K)
-    return np.asarray(packed, dtype=np.uint8)[(tile * 64 + lane) * 32 + 8 * j + e]
-
-
-def pack_scales(s_bits):
-    """bf16 bits [N][K/G] -> [N/16][K/G][16]."""
-    N, KG = s_bits.shape
-    return np.ascontiguousarray(np.asarray(s_bits, dtype=np.uint16).reshape(N // TILE_N, TILE_N, KG)
-                                .transpose(0, 2, 1))
-
-
-def unpack_scales(s_packed, N, K):
-    return np.ascontiguousarray(np.asarray(s_packed, dtype=np.uint16).reshape(N // TILE_N, K // G, TILE_N)
-                                .transpose(0, 2, 1).reshape(N, K // G))
 
 
 # ----------------------------------------------------------------------------- the GEMM

@@ -15,6 +15,7 @@ import torch
 import fp8_paged_kv_append_amd as kv
 from kvsynth import workloads as wl
 from oracle import attention, codec, paged
+from tests import layout
 
 
 def note(msg: str):
@@ -64,17 +65,22 @@ class Case:
             self.o_v_scale = codec.calibrate_scale(self.v)
         else:
             self.o_v_scale = self.o_k_scale
+        # the device pools start as random bytes in the library's layout; the oracle's logical pools
+        # start as the same elements, mapped by the test-side layout rules
+        self.kind_k = "latent" if w.latent else "k"
         self.kp0 = wl.pool_bytes(w, "k", self.elt)
         self.vp0 = None if w.latent else wl.pool_bytes(w, "v", self.elt)
+        self.et = np.uint8 if self.elt == 1 else np.uint16
+        self.k_shape = (w.num_pages, w.num_kv_heads, w.page_size, w.head_dim)
+        self.v_shape = (w.num_pages, w.num_kv_heads, w.page_size, w.v_dim)
         if oracle_fill:
-            self.okp = self.kp0.copy() if self.elt == 1 else self.kp0.copy().view(np.uint16)
-            self.ovp = None if w.latent else (self.vp0.copy() if self.elt == 1 else self.vp0.copy().view(np.uint16))
+            self.okp = layout.from_device(self.kp0.view(self.et), self.kind_k, self.k_shape, self.elt)
+            self.ovp = None if w.latent else layout.from_device(self.vp0.view(self.et), "v", self.v_shape, self.elt)
             if kv_dtype == "fp8":
-                paged.append_fp8(self.okp, self.ovp, self.k, self.v, self.req, self.pos, self.pt, w.num_kv_heads,
-                                 w.page_size, self.o_k_scale, self.o_v_scale)
+                paged.append_fp8(self.okp, self.ovp, self.k, self.v, self.req, self.pos, self.pt, self.o_k_scale,
+                                 self.o_v_scale)
             else:
-                paged.append(self.okp, self.ovp, self.k, self.v, self.req, self.pos, self.pt, w.num_kv_heads,
-                             w.page_size)
+                paged.append(self.okp, self.ovp, self.k, self.v, self.req, self.pos, self.pt)
 
         # ---- device
         self.desc = kv.pool_desc(w.num_pages, w.page_size, w.num_kv_heads, w.head_dim, w.v_dim)
@@ -99,6 +105,19 @@ class Case:
                 del dkc
         else:
             self.d_k_scale = self.d_v_scale = 1.0
+
+    def device_k(self, t=None) -> np.ndarray:
+        """The device K (or latent) pool mapped to the oracle's logical order [P][Hkv][S][D]."""
+        return layout.from_device(host(self.dkp if t is None else t, self.et), self.kind_k, self.k_shape, self.elt)
+
+    def device_v(self, t=None) -> np.ndarray:
+        return layout.from_device(host(self.dvp if t is None else t, self.et), "v", self.v_shape, self.elt)
+
+    def pools_match(self) -> bool:
+        """Device pools equal the oracle's, element by element (pages never written included)."""
+        if not np.array_equal(self.device_k(), self.okp):
+            return False
+        return self.w.latent or np.array_equal(self.device_v(), self.ovp)
 
     def fill_device(self):
         if self.kv_dtype == "fp8":

@@ -10,6 +10,7 @@ import torch
 import fp8_paged_kv_append_amd as kv
 from kvsynth import workloads as wl
 from oracle import attention, codec, paged, step
+from tests import layout
 from tests.gpu_util import Case, dev, host, note
 
 pytestmark = pytest.mark.gpu
@@ -34,12 +35,13 @@ def test_encode_every_bf16_value(scale):
     dk = torch.zeros(P * S * D, dtype=torch.uint8, device="cuda")
     dvp = torch.zeros(P * S * D, dtype=torch.uint8, device="cuda")
     kv.kv_append_fp8(desc, dk, dvp, dev(x), dev(xv), dev(req), dev(pos), dev(pt), k_scale=scale, v_scale=scale)
-    ok = np.zeros(P * S * D, dtype=np.uint8)
-    ov = np.zeros(P * S * D, dtype=np.uint8)
-    paged.append_fp8(ok, ov, x, xv, req, pos, pt, 1, S, np.float32(scale), np.float32(scale))
-    gk, gv = host(dk, np.uint8), host(dvp, np.uint8)
+    ok = np.zeros((P, 1, S, D), dtype=np.uint8)
+    ov = np.zeros((P, 1, S, D), dtype=np.uint8)
+    paged.append_fp8(ok, ov, x, xv, req, pos, pt, np.float32(scale), np.float32(scale))
+    gk = layout.from_device(host(dk, np.uint8), "k", ok.shape, 1)
+    gv = layout.from_device(host(dvp, np.uint8), "v", ov.shape, 1)
     bad = np.flatnonzero(gk != ok)
-    assert bad.size == 0, f"{bad.size} K codes differ, e.g. input {x.ravel()[bad[:5]]} got {gk[bad[:5]]} want {ok[bad[:5]]}"
+    assert bad.size == 0, f"{bad.size} K codes differ, e.g. got {gk.ravel()[bad[:5]]} want {ok.ravel()[bad[:5]]}"
     assert np.array_equal(gv, ov)
 
 
@@ -51,19 +53,19 @@ def test_decode_every_code_single_token(v_scale):
     note(f"decode all codes, v_scale={v_scale}")
     S, D, B, G = 16, 128, 2, 4
     P = 4
-    kp = np.random.Generator(np.random.PCG64(1)).integers(0, 0x78, P * S * D, dtype=np.uint8)  # finite K
-    vp = np.zeros(P * D * S, dtype=np.uint8)
+    kp = np.random.Generator(np.random.PCG64(1)).integers(0, 0x78, (P, 1, S, D), dtype=np.uint8)  # finite K
+    vp = np.zeros((P, 1, S, D), dtype=np.uint8)
     pt = np.array([[3], [1]], dtype=np.int32)
     codes = np.arange(256, dtype=np.uint8).reshape(2, D)
     for r in range(B):
-        paged.append(np.zeros(P * S * D, dtype=np.uint8), vp, codes[r].reshape(1, 1, D), codes[r].reshape(1, 1, D),
-                     [r], [0], pt, 1, S)
+        paged.append(np.zeros_like(kp), vp, codes[r].reshape(1, 1, D), codes[r].reshape(1, 1, D), [r], [0], pt)
     q = wl.to_bf16_bits(np.random.Generator(np.random.PCG64(2)).standard_normal((B, G, D)).astype(np.float32))
     lens = np.ones(B, dtype=np.int32)
     desc = kv.pool_desc(P, S, 1, D)
     out = torch.empty((B, G, D), dtype=torch.int16, device="cuda")
-    kv.paged_decode_attn_fp8(desc, dev(q), dev(kp), dev(vp), dev(pt), dev(lens), 1, out, k_scale=0.5,
-                             v_scale=v_scale, num_splits=1)
+    kv.paged_decode_attn_fp8(desc, dev(q), dev(layout.to_device(kp, "k", 1)), dev(layout.to_device(vp, "v", 1)),
+                             dev(pt), dev(lens), 1, out, k_scale=0.5, v_scale=v_scale, sm_scale=D ** -0.5,
+                             num_splits=1)
     got = host(out, np.uint16)
     ref = attention.decode_attention(q, kp, vp, pt, lens, num_kv_heads=1, page_size=S, head_dim=D, v_dim=D,
                                      dtype="fp8", k_scale=np.float32(0.5), v_scale=np.float32(v_scale))
@@ -93,10 +95,8 @@ def test_fill_whole_pool_bytes(kv_dtype, name, kw):
     assert c.d_k_scale == float(c.o_k_scale) and c.d_v_scale == float(c.o_v_scale)
     c.fill_device()
     torch.cuda.synchronize()
-    et = np.uint8 if kv_dtype == "fp8" else np.uint16
-    assert np.array_equal(host(c.dkp, et), c.okp)
-    if not w.latent:
-        assert np.array_equal(host(c.dvp, et), c.ovp)
+    et = c.et
+    assert c.pools_match()
     # read back through the page table
     ko = torch.empty((len(c.req), w.num_kv_heads, w.head_dim), dtype=c.dkp.dtype, device="cuda")
     vo = None if w.latent else torch.empty((len(c.req), w.num_kv_heads, w.v_dim), dtype=c.dkp.dtype, device="cuda")
@@ -104,8 +104,7 @@ def test_fill_whole_pool_bytes(kv_dtype, name, kw):
     g(c.desc, c.dkp, c.dvp, c.dreq, c.dpos, c.dpt, ko, vo)
     torch.cuda.synchronize()
     for r in range(w.batch):
-        ok_, ov_ = paged.gather(c.okp, c.ovp, c.pt, r, int(c.lens[r]), w.num_kv_heads, w.page_size, w.head_dim,
-                                w.v_dim)
+        ok_, ov_ = paged.gather(c.okp, c.ovp, c.pt, r, int(c.lens[r]))
         a, b = c.off[r], c.off[r + 1]
         assert np.array_equal(host(ko, et)[a:b], ok_)
         if not w.latent:
@@ -123,21 +122,23 @@ def test_append_skips_flagged_and_out_of_range(kv_dtype):
     req = np.array([0, 1, 1, 2, 2, 7, 3], dtype=np.int32)
     pos = np.array([1, 0, 17, 2, 20, 0, 40], dtype=np.int32)   # r1@17 -> entry -1; r2@20 -> page 9; r7; pos 40
     flags = np.array([1, 0, 0, 0], dtype=np.uint32)
-    kp0 = rng.integers(0, 256, P * H * S * D * (1 if kv_dtype == "fp8" else 2), dtype=np.uint8).view(et)
-    vp0 = rng.integers(0, 256, P * H * S * D * (1 if kv_dtype == "fp8" else 2), dtype=np.uint8).view(et)
+    elt = 1 if kv_dtype == "fp8" else 2
+    kp0 = rng.integers(0, 256, P * H * S * D * elt, dtype=np.uint8).view(et).reshape(P, H, S, D)
+    vp0 = rng.integers(0, 256, P * H * S * D * elt, dtype=np.uint8).view(et).reshape(P, H, S, D)
     desc = kv.pool_desc(P, S, H, D)
-    dk, dvv = dev(kp0), dev(vp0)
+    dk, dvv = dev(layout.to_device(kp0, "k", elt)), dev(layout.to_device(vp0, "v", elt))
     if kv_dtype == "fp8":
         kv.kv_append_fp8(desc, dk, dvv, dev(rows), dev(rows), dev(req), dev(pos), dev(pt), dev(flags),
                          k_scale=0.01, v_scale=0.02)
         ok, ov = kp0.copy(), vp0.copy()
-        paged.append_fp8(ok, ov, rows, rows, req, pos, pt, H, S, np.float32(0.01), np.float32(0.02), flags)
+        paged.append_fp8(ok, ov, rows, rows, req, pos, pt, np.float32(0.01), np.float32(0.02), flags)
     else:
         kv.kv_append_bf16(desc, dk, dvv, dev(rows), dev(rows), dev(req), dev(pos), dev(pt), dev(flags))
         ok, ov = kp0.copy(), vp0.copy()
-        paged.append(ok, ov, rows, rows, req, pos, pt, H, S, flags)
+        paged.append(ok, ov, rows, rows, req, pos, pt, flags)
     torch.cuda.synchronize()
-    assert np.array_equal(host(dk, et), ok) and np.array_equal(host(dvv, et), ov)
+    assert np.array_equal(layout.from_device(host(dk, et), "k", ok.shape, elt), ok)
+    assert np.array_equal(layout.from_device(host(dvv, et), "v", ov.shape, elt), ov)
     assert not np.array_equal(ok, kp0)          # something was written
 
 

@@ -49,7 +49,7 @@ def test_latent_ragged(kv_dtype, hq):
     c.fill_device()
     torch.cuda.synchronize()
     et = np.uint8 if kv_dtype == "fp8" else np.uint16
-    assert np.array_equal(host(c.dkp, et), c.okp)
+    assert np.array_equal(c.device_k(), c.okp)
     outs = []
     for splits in (0, 1, 2, 5):
         got = _latent_attend(c, num_splits=splits)

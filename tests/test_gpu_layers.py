@@ -13,6 +13,7 @@ import torch
 import fp8_paged_kv_append_amd as kv
 from kvsynth import workloads as wl
 from oracle import codec, paged, step
+from tests import layout
 from tests.gpu_util import ATTN_TOL, attn_error, dev, host, note
 
 pytestmark = pytest.mark.gpu
@@ -52,13 +53,11 @@ class Stack:
             k, v = wl.all_kv(wl_, lens)
             ks = codec.calibrate_scale(k) if fp8 else np.float32(1)
             vs = (ks if latent else codec.calibrate_scale(v)) if fp8 else np.float32(1)
-            kp = wl.pool_bytes(w, "k", elt)
-            vp = None if latent else wl.pool_bytes(w, "v", elt)
-            if not fp8:
-                kp = kp.view(np.uint16)
-                vp = None if latent else vp.view(np.uint16)
-            # device: this layer's pools filled through the library's append
-            dk_l, dv_l = dev(kp), None if latent else dev(vp)
+            kp = wl.pool_init(w, "k", elt)
+            vp = None if latent else wl.pool_init(w, "v", elt)
+            # device: this layer's pools, the same elements in the library's layout, filled through its append
+            dk_l = dev(layout.to_device(kp, "latent" if latent else "k", elt))
+            dv_l = None if latent else dev(layout.to_device(vp, "v", elt))
             if fp8:
                 k_s = kv.calibrate_scale(dev(k))
                 v_s = k_s if latent else kv.calibrate_scale(dev(v))
@@ -74,9 +73,9 @@ class Stack:
             vs_d.append(float(vs))
             # oracle: the same fill
             if fp8:
-                paged.append_fp8(kp, vp, k, v, req, pos, pt, w.num_kv_heads, w.page_size, ks, vs)
+                paged.append_fp8(kp, vp, k, v, req, pos, pt, ks, vs)
             else:
-                paged.append(kp, vp, k, v, req, pos, pt, w.num_kv_heads, w.page_size)
+                paged.append(kp, vp, k, v, req, pos, pt)
             self.states.append(dict(dtype=kv_dtype, k_pool=kp, v_pool=vp, page_table=pt, ctx_lens=lens,
                                     page_tags=tags, expected_tags=exp, num_kv_heads=w.num_kv_heads,
                                     page_size=w.page_size, head_dim=w.head_dim, v_dim=w.v_dim, k_scale=ks,
@@ -98,6 +97,19 @@ class Stack:
         self.dk_new = dev(np.stack(self.k_new))
         self.dv_new = None if latent else dev(np.stack(self.v_new))
         self.max_ctx = int(lens.max())
+        self.latent, self.elt = latent, elt
+
+    def layer_pools_match(self, l):
+        """Layer l's device pools, mapped to logical order, equal the oracle's element by element."""
+        st = self.states[l]
+        k = layout.from_device(host(self.dkp[l], self.et), "latent" if self.latent else "k", st["k_pool"].shape,
+                               self.elt)
+        if not np.array_equal(k, st["k_pool"]):
+            return False
+        if self.latent:
+            return True
+        v = layout.from_device(host(self.dvp[l], self.et), "v", st["v_pool"].shape, self.elt)
+        return np.array_equal(v, st["v_pool"])
         B, Hq = w.batch, w.num_q_heads
         self.splits = splits
         if splits == 0 and latent:
@@ -137,9 +149,7 @@ def test_layer_stack_step_matches_oracle(kv_dtype, latent):
     assert g_flags[1] and g_flags[6] and g_flags[s.hole] == paged.FLAG_BAD_PAGE and not g_flags[3]
     g_out = host(s.out, np.uint16)
     for l in range(LAYERS):
-        assert np.array_equal(host(s.dkp[l], s.et), s.states[l]["k_pool"]), l
-        if not latent:
-            assert np.array_equal(host(s.dvp[l], s.et), s.states[l]["v_pool"]), l
+        assert s.layer_pools_match(l), l
         err = attn_error(g_out[l], o_outs[l])
         note(f"  layer {l}: error {err:.3e}")
         assert err <= ATTN_TOL
@@ -165,9 +175,7 @@ def test_layer_stack_token_at_chunk_edges(kv_dtype, splits, latent):
     assert np.array_equal(host(s.flags, np.uint32), o_flags)
     g_out = host(s.out, np.uint16)
     for l in range(LAYERS):
-        assert np.array_equal(host(s.dkp[l], s.et), s.states[l]["k_pool"]), l
-        if not latent:
-            assert np.array_equal(host(s.dvp[l], s.et), s.states[l]["v_pool"]), l
+        assert s.layer_pools_match(l), l
         err = attn_error(g_out[l], o_outs[l])
         note(f"  layer {l}: error {err:.3e}")
         assert err <= ATTN_TOL
@@ -186,9 +194,7 @@ def test_layer_stack_no_op_tracker(kv_dtype, latent):
     assert o_flags is None
     g_out = host(s.out, np.uint16)
     for l in range(LAYERS):
-        assert np.array_equal(host(s.dkp[l], s.et), s.states[l]["k_pool"]), l
-        if not latent:
-            assert np.array_equal(host(s.dvp[l], s.et), s.states[l]["v_pool"]), l
+        assert s.layer_pools_match(l), l
         assert attn_error(g_out[l], o_outs[l]) <= ATTN_TOL
         assert g_out[l, 1].any() and g_out[l, 6].any()
 

@@ -51,7 +51,7 @@ def test_step_with_stale_request(kv_dtype, one_launch):
     assert np.array_equal(g_flags, o_flags)
     assert np.flatnonzero(g_flags).tolist() == c.stale.tolist()
     et = np.uint8 if kv_dtype == "fp8" else np.uint16
-    assert np.array_equal(host(c.dkp, et), c.okp) and np.array_equal(host(c.dvp, et), c.ovp)
+    assert c.pools_match()
     err = attn_error(g_out, o_out)
     note(f"  step error {err:.3e}")
     assert err <= ATTN_TOL
@@ -173,9 +173,9 @@ def test_fused_check_append_step(kv_dtype, latent, two_launch):
     g_flags, g_out = host(flags, np.uint32), host(out, np.uint16)
     assert np.array_equal(g_flags, o_flags)
     et = np.uint8 if kv_dtype == "fp8" else np.uint16
-    assert np.array_equal(host(c.dkp, et), c.okp)
+    assert np.array_equal(c.device_k(), c.okp)
     if not latent:
-        assert np.array_equal(host(c.dvp, et), c.ovp)
+        assert np.array_equal(c.device_v(), c.ovp)
     err = attn_error(g_out, o_out)
     note(f"  step error {err:.3e}")
     assert err <= ATTN_TOL
@@ -226,10 +226,9 @@ def test_one_launch_length_beyond_max_ctx(kv_dtype, num_splits):
     skip = o_flags.copy()
     skip[1] = 1                                            # the caller error: not written, zero rows
     if kv_dtype == "fp8":
-        paged.append_fp8(c.okp, c.ovp, k_new, v_new, req, pos, c.pt, w.num_kv_heads, w.page_size, c.o_k_scale,
-                         c.o_v_scale, skip)
+        paged.append_fp8(c.okp, c.ovp, k_new, v_new, req, pos, c.pt, c.o_k_scale, c.o_v_scale, skip)
     else:
-        paged.append(c.okp, c.ovp, k_new, v_new, req, pos, c.pt, w.num_kv_heads, w.page_size, skip)
+        paged.append(c.okp, c.ovp, k_new, v_new, req, pos, c.pt, skip)
     ref = attention.decode_attention(c.q, c.okp, c.ovp, c.pt, c.lens, num_kv_heads=w.num_kv_heads,
                                      page_size=w.page_size, head_dim=w.head_dim, v_dim=w.v_dim, dtype=kv_dtype,
                                      k_scale=c.o_k_scale, v_scale=c.o_v_scale, sm_scale=c.sm_scale, flags=skip,
@@ -243,7 +242,7 @@ def test_one_launch_length_beyond_max_ctx(kv_dtype, num_splits):
     torch.cuda.synchronize()
     assert np.array_equal(host(flags, np.uint32), o_flags)
     et = np.uint8 if kv_dtype == "fp8" else np.uint16
-    assert np.array_equal(host(c.dkp, et), c.okp) and np.array_equal(host(c.dvp, et), c.ovp)
+    assert c.pools_match()
     g_out = host(out, np.uint16)
     assert not g_out[1].any() and not g_out[3].any()
     err = attn_error(g_out, ref)
@@ -324,7 +323,7 @@ def test_long_rows_page_id_batches_and_windows(kv_dtype, num_splits):
     g_flags, g_out = _device_step(c, k_new, v_new, req, pos, num_splits=num_splits, one_launch=True)
     assert np.array_equal(g_flags, o_flags)
     et = np.uint8 if kv_dtype == "fp8" else np.uint16
-    assert np.array_equal(host(c.dkp, et), c.okp) and np.array_equal(host(c.dvp, et), c.ovp)
+    assert c.pools_match()
     assert not g_out[2].any()
     err = attn_error(g_out, {r: o_out[r] for r in (0, 1)})
     note(f"  tracker on: error {err:.3e}")
@@ -341,7 +340,7 @@ def test_long_rows_page_id_batches_and_windows(kv_dtype, num_splits):
     err = attn_error(g2_out, o2_out)
     note(f"  no tracker: error {err:.3e}")
     assert err <= ATTN_TOL
-    assert np.array_equal(host(c.dkp, et), c.okp) and np.array_equal(host(c.dvp, et), c.ovp)
+    assert c.pools_match()
 
 
 @pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
@@ -379,7 +378,7 @@ def test_latent_one_launch_step_128_head_kernel(kv_dtype):
     g_flags, g_out = host(flags, np.uint32), host(out, np.uint16)
     assert np.array_equal(g_flags, o_flags)
     et = np.uint8 if kv_dtype == "fp8" else np.uint16
-    assert np.array_equal(host(c.dkp, et), c.okp)
+    assert np.array_equal(c.device_k(), c.okp)
     err = attn_error(g_out, o_out)
     note(f"  step error {err:.3e}")
     assert err <= ATTN_TOL

@@ -10,6 +10,7 @@ import torch
 import fp8_paged_kv_append_amd as kv
 from kvsynth import weights as wsyn
 from oracle import codec, wgemm
+from tests import layout
 from tests.gpu_util import dev, host, note
 
 pytestmark = pytest.mark.gpu
@@ -27,11 +28,18 @@ def _quantize_dev(w_bits, bits):
 
 
 def _oracle_codes(w_bits, bits):
+    """The oracle's codes [N][K] and scales [N][K/128] in logical order, and the weights they stand for."""
     if bits == 4:
         q, s = wgemm.quantize_w4(w_bits)
-        return wgemm.pack_w4(q), wgemm.pack_scales(s).ravel(), wgemm.dequant_w4(q, s)
+        return q, s, wgemm.dequant_w4(q, s)
     c, s = wgemm.quantize_w8(w_bits)
-    return wgemm.pack_w8(c), wgemm.pack_scales(s).ravel(), wgemm.dequant_w8(c, s)
+    return c, s, wgemm.dequant_w8(c, s)
+
+
+def _device_codes(packed_bytes, scales_bits, n, k, bits):
+    """Device codes and scales mapped from the library's packed layout to logical order."""
+    codes = (layout.unpack_w4 if bits == 4 else layout.unpack_w8)(packed_bytes, n, k)
+    return codes, layout.unpack_scales(scales_bits, n, k)
 
 
 def _row_err(y_bits, ref):
@@ -59,9 +67,10 @@ def test_quantiser_bit_exact(bits, shape):
     w = wsyn.weights(sh)
     w[3, 128:256] = 0                      # an all-zero group: scale 0, codes 0
     packed, scales = _quantize_dev(w, bits)
-    o_packed, o_scales, _ = _oracle_codes(w, bits)
-    assert np.array_equal(host(packed, np.uint8), o_packed)
-    assert np.array_equal(host(scales, np.uint16), o_scales)
+    o_codes, o_scales, _ = _oracle_codes(w, bits)
+    g_codes, g_scales = _device_codes(host(packed, np.uint8), host(scales, np.uint16), sh.n, sh.k, bits)
+    assert np.array_equal(g_codes, o_codes)
+    assert np.array_equal(g_scales, o_scales)
 
 
 @pytest.mark.parametrize("bits", [4, 8])
@@ -71,8 +80,8 @@ def test_gemm_matches_oracle(bits, m):
     note(f"gemm w{bits} ragged m={m}")
     w = wsyn.weights(sh)
     packed, scales = _quantize_dev(w, bits)
-    o_packed, _, W = _oracle_codes(w, bits)
-    assert np.array_equal(host(packed, np.uint8), o_packed)
+    o_codes, _, W = _oracle_codes(w, bits)
+    assert np.array_equal(_device_codes(host(packed, np.uint8), host(scales, np.uint16), sh.n, sh.k, bits)[0], o_codes)
     x = wsyn.activations(sh, m)
     ref = wgemm.gemm(x, W)
     dx = dev(x)
@@ -134,9 +143,11 @@ def test_gemm_full_size_sampled(bits, m):
     KG = sh.k // 128
     tile_bytes = KG * 64 * (16 if bits == 4 else 32)
     for t in (0, 137, 511):
-        o_packed, o_scales, W = _oracle_codes(w[16 * t:16 * t + 16], bits)
-        assert np.array_equal(hp[t * tile_bytes:(t + 1) * tile_bytes], o_packed), t
-        assert np.array_equal(hs[t * KG * 16:(t + 1) * KG * 16], o_scales), t
+        o_codes, o_scales, W = _oracle_codes(w[16 * t:16 * t + 16], bits)
+        g_codes, g_scales = _device_codes(hp[t * tile_bytes:(t + 1) * tile_bytes], hs[t * KG * 16:(t + 1) * KG * 16],
+                                          16, sh.k, bits)
+        assert np.array_equal(g_codes, o_codes), t
+        assert np.array_equal(g_scales, o_scales), t
         ref = wgemm.gemm(x, W)
         err = _row_err(y[:, 16 * t:16 * t + 16], ref)
         note(f"  tile {t}: row error {err:.2e}")

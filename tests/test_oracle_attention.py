@@ -15,17 +15,14 @@ def _cache(w, dtype, lens=None, pool_pages=None):
     k, v = wl.all_kv(w, lens, threads=1)
     req, pos = wl.token_index(lens)
     elt = 1 if dtype == "fp8" else 2
-    kp = wl.pool_bytes(w, "k", elt)
-    vp = None if w.latent else wl.pool_bytes(w, "v", elt)
-    if dtype == "bf16":
-        kp = kp.view(np.uint16)
-        vp = None if vp is None else vp.view(np.uint16)
+    kp = wl.pool_init(w, "k", elt)
+    vp = None if w.latent else wl.pool_init(w, "v", elt)
     ks = codec.calibrate_scale(k) if dtype == "fp8" else np.float32(1)
     vs = (codec.calibrate_scale(v) if not w.latent else ks) if dtype == "fp8" else np.float32(1)
     if dtype == "fp8":
-        paged.append_fp8(kp, vp, k, v, req, pos, pt, w.num_kv_heads, w.page_size, ks, vs)
+        paged.append_fp8(kp, vp, k, None if w.latent else v, req, pos, pt, ks, vs)
     else:
-        paged.append(kp, vp, k, v, req, pos, pt, w.num_kv_heads, w.page_size)
+        paged.append(kp, vp, k, None if w.latent else v, req, pos, pt)
     tags = wl.page_tags(w)
     st = dict(dtype=dtype, k_pool=kp, v_pool=vp, page_table=pt, ctx_lens=lens, page_tags=tags,
               expected_tags=wl.expected_tags(w, pt, lens, tags), num_kv_heads=w.num_kv_heads,
@@ -69,11 +66,11 @@ def test_equal_keys_give_mean_of_values(dtype):
     req, pos = wl.token_index(lens)
     if dtype == "fp8":
         # V is rewritten with its own rows (same codes); a call without the V pool would address a latent pool
-        paged.append_fp8(st["k_pool"], st["v_pool"], k_same, v, req, pos, st["page_table"], 1, w.page_size,
-                         st["k_scale"], st["v_scale"])
+        paged.append_fp8(st["k_pool"], st["v_pool"], k_same, v, req, pos, st["page_table"], st["k_scale"],
+                         st["v_scale"])
         vhat = codec.e4m3_decode(codec.quantize_e4m3(v, st["v_scale"])) * np.float64(st["v_scale"])
     else:
-        paged.append(st["k_pool"], st["v_pool"], k_same, v, req, pos, st["page_table"], 1, w.page_size)
+        paged.append(st["k_pool"], st["v_pool"], k_same, v, req, pos, st["page_table"])
         vhat = codec.f64_from_bf16(v)
     o = _attn(st, wl.queries(w))[0]
     ref = vhat[:, 0, :].mean(axis=0)
@@ -81,58 +78,79 @@ def test_equal_keys_give_mean_of_values(dtype):
         np.testing.assert_allclose(o[h], ref, rtol=0, atol=1e-13)
 
 
-def _k_index(page, h, slot, d, H, S, D, elt):
-    """K element position, written out from the layout rule (16-token sub-pages, 16-byte chunks)."""
-    per_chunk = 16 // elt
-    ni = D * elt // 64
-    sub, tok = divmod(slot, 16)
-    grp, i = divmod(tok, 4)
-    q, k = divmod(d // per_chunk, ni)
-    return (page * H + h) * S * D + sub * 16 * D + (((grp * ni + k) * 4 + q) * 4 + i) * per_chunk + d % per_chunk
+def _decoder(dtype):
+    if dtype == "fp8":
+        return lambda c: float(codec.e4m3_decode([c])[0])
+    return lambda b: float(codec.f32_from_bf16([b])[0])
+
+
+def _softmax_rows(q, keys, values):
+    """Pure-Python softmax attention of one query row over lists of key and value rows."""
+    scores = [sum(a * b for a, b in zip(q, kk)) for kk in keys]
+    mx = max(scores)
+    e = [math.exp(s - mx) for s in scores]
+    z = sum(e)
+    o = [0.0] * len(values[0])
+    for t, vv in enumerate(values):
+        for d, x in enumerate(vv):
+            o[d] += e[t] / z * x
+    return o
 
 
 def _brute_force(q_bits, k_pool, v_pool, pt, lens, H, S, D, Dv, Hq, dtype, ks, vs, sm):
     """Pure-Python loops straight from the definition, reading the pools element by element."""
-    elt = 1 if dtype == "fp8" else 2
-    dec = (lambda c: float(codec.e4m3_decode([c])[0])) if dtype == "fp8" else \
-          (lambda b: float(codec.f32_from_bf16([b])[0]))
+    dec = _decoder(dtype)
     out = []
     G = Hq // H
     for r in range(len(lens)):
         rows = []
         for h in range(Hq):
             g = h // G
-            q = [float(codec.f32_from_bf16([q_bits[r, h, d]])[0]) for d in range(D)]
-            scores = []
+            q = [sm * float(codec.f32_from_bf16([q_bits[r, h, d]])[0]) for d in range(D)]
+            keys, values = [], []
             for t in range(lens[r]):
                 page, slot = int(pt[r, t // S]), t % S
-                kk = [dec(k_pool[_k_index(page, g, slot, d, H, S, D, elt)]) * ks for d in range(D)]
-                scores.append(sm * sum(a * b for a, b in zip(q, kk)))
-            mx = max(scores)
-            e = [math.exp(s - mx) for s in scores]
-            z = sum(e)
-            o = [0.0] * Dv
-            for t in range(lens[r]):
-                page, slot = int(pt[r, t // S]), t % S
-                for d in range(Dv):
-                    o[d] += e[t] / z * dec(v_pool[((page * H + g) * Dv + d) * S + slot]) * vs
-            rows.append(o)
+                keys.append([dec(k_pool[page, g, slot, d]) * ks for d in range(D)])
+                values.append([dec(v_pool[page, g, slot, d]) * vs for d in range(Dv)])
+            rows.append(_softmax_rows(q, keys, values))
         out.append(rows)
     return np.array(out)
 
 
 @pytest.mark.parametrize("dtype", ["fp8", "bf16"])
 def test_brute_force_tiny_shapes(dtype):
-    w = wl.Workload("bf", batch=3, num_q_heads=4, num_kv_heads=2, head_dim=64, v_dim=16, page_size=16,
+    w = wl.Workload("bf", batch=3, num_q_heads=4, num_kv_heads=2, head_dim=16, v_dim=16, page_size=16,
                     num_pages=12, ctx_lo=1, ctx_hi=40, seed=99)
     lens = np.array([40, 17, 1], dtype=np.int32)
     st, k, v, _ = _cache(w, dtype, lens=lens)
     q = wl.queries(w)
     got = _attn(st, q)
-    ref = _brute_force(q, st["k_pool"], st["v_pool"], st["page_table"], lens, 2, 16, 64, 16, 4, dtype,
+    ref = _brute_force(q, st["k_pool"], st["v_pool"], st["page_table"], lens, 2, 16, 16, 16, 4, dtype,
                        float(st["k_scale"]), float(st["v_scale"]), st["sm_scale"])
     for r in range(3):
         np.testing.assert_allclose(got[r], ref[r], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
+def test_brute_force_latent_tiny_shapes(dtype):
+    """Latent cache: every head scores against the whole cached vector and averages its first Dv dims."""
+    w = wl.Workload("bfl", batch=3, num_q_heads=4, num_kv_heads=1, head_dim=24, v_dim=16, page_size=16,
+                    num_pages=10, ctx_lo=1, ctx_hi=40, seed=98, latent=True)
+    lens = np.array([33, 1, 16], dtype=np.int32)
+    st, k, _, _ = _cache(w, dtype, lens=lens)
+    q = wl.queries(w)
+    got = _attn(st, q)
+    dec = _decoder(dtype)
+    sc = float(st["k_scale"])
+    for r in range(3):
+        for h in range(4):
+            qq = [st["sm_scale"] * float(codec.f32_from_bf16([q[r, h, d]])[0]) for d in range(24)]
+            rows = []
+            for t in range(lens[r]):
+                page, slot = int(st["page_table"][r, t // 16]), t % 16
+                rows.append([dec(st["k_pool"][page, 0, slot, d]) * sc for d in range(24)])
+            ref = _softmax_rows(qq, rows, [row[:16] for row in rows])
+            np.testing.assert_allclose(got[r][h], ref, rtol=1e-12, atol=1e-13)
 
 
 def test_score_shift_invariance():
@@ -165,12 +183,10 @@ def test_physical_page_permutation_invariance():
     # move every page to another physical slot and rewrite the table: identical output
     P = w.num_pages
     perm = np.random.Generator(np.random.PCG64(3)).permutation(P)
-    blk = w.num_kv_heads * w.page_size * w.head_dim
     kp2 = np.empty_like(st["k_pool"])
     vp2 = np.empty_like(st["v_pool"])
-    for p in range(P):
-        kp2[perm[p] * blk:(perm[p] + 1) * blk] = st["k_pool"][p * blk:(p + 1) * blk]
-        vp2[perm[p] * blk:(perm[p] + 1) * blk] = st["v_pool"][p * blk:(p + 1) * blk]
+    kp2[perm] = st["k_pool"]
+    vp2[perm] = st["v_pool"]
     st2 = dict(st, k_pool=kp2, v_pool=vp2, page_table=np.where(st["page_table"] >= 0,
                                                                perm[np.maximum(st["page_table"], 0)], -1))
     o2 = _attn(st2, q)[0]
@@ -179,7 +195,7 @@ def test_physical_page_permutation_invariance():
 
 def test_gqa_group_mapping_against_single_head_runs():
     """Head h of a 4-head/2-group cache equals a 1-KV-head run over group h // 2."""
-    w = wl.Workload("g", batch=1, num_q_heads=4, num_kv_heads=2, head_dim=64, v_dim=16, page_size=16,
+    w = wl.Workload("g", batch=1, num_q_heads=4, num_kv_heads=2, head_dim=16, v_dim=16, page_size=16,
                     num_pages=4, ctx_lo=20, ctx_hi=20, seed=11)
     st, k, v, lens = _cache(w, "bf16")
     q = wl.queries(w)
@@ -206,7 +222,7 @@ def test_aborted_and_empty_requests_give_zero_rows():
 
 def test_latent_matches_gqa_formula():
     """The latent cache is one shared K of width 576 whose first 512 dims are V."""
-    w = wl.Workload("lat", batch=2, num_q_heads=4, num_kv_heads=1, head_dim=64, v_dim=16, page_size=16,
+    w = wl.Workload("lat", batch=2, num_q_heads=4, num_kv_heads=1, head_dim=24, v_dim=16, page_size=16,
                     num_pages=8, ctx_lo=30, ctx_hi=30, seed=12, latent=True)
     st, k, _, lens = _cache(w, "fp8")
     q = wl.queries(w)
@@ -214,7 +230,7 @@ def test_latent_matches_gqa_formula():
     off = np.concatenate([[0], np.cumsum(lens)])
     for r in range(2):
         c = codec.e4m3_decode(codec.quantize_e4m3(k[off[r]:off[r + 1], 0], st["k_scale"])) * np.float64(st["k_scale"])
-        ref = attention.softmax_attention(codec.f64_from_bf16(q[r]), c, c[:, :16], 1 / math.sqrt(64))
+        ref = attention.softmax_attention(codec.f64_from_bf16(q[r]), c, c[:, :16], 1 / math.sqrt(24))
         np.testing.assert_allclose(o[r], ref, rtol=1e-13, atol=1e-14)
 
 
@@ -236,12 +252,11 @@ def test_decode_step_order_check_before_append():
     r = int(stale[0])
     assert not out[r].any()
     # the flagged request's last page is untouched; another request's changed
-    blk = w.num_kv_heads * w.page_size * w.head_dim
     p_stale = st["page_table"][r, (lens[r] - 1) // w.page_size]
-    assert np.array_equal(st["k_pool"][p_stale * blk:(p_stale + 1) * blk], kp_before[p_stale * blk:(p_stale + 1) * blk])
+    assert np.array_equal(st["k_pool"][p_stale], kp_before[p_stale])
     r2 = (r + 1) % w.batch
     p2 = st["page_table"][r2, (lens[r2] - 1) // w.page_size]
-    assert not np.array_equal(st["k_pool"][p2 * blk:(p2 + 1) * blk], kp_before[p2 * blk:(p2 + 1) * blk])
+    assert not np.array_equal(st["k_pool"][p2], kp_before[p2])
     # the step without a tracker writes every request and zeroes none
     flags2, out2 = step.decode_step(st, wl.queries(w), k_new, v_new, np.arange(w.batch, dtype=np.int32),
                                     lens - 1, tracker=False)

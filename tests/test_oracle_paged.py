@@ -79,76 +79,43 @@ def test_tag_check_bad_page_ids_and_lengths():
 
 # ----------------------------------------------------------------------------- layout / append / gather
 
-def test_layout_offsets_by_hand():
-    """Hand-worked offsets of the pool layout."""
-    # e4m3 K, Hkv=2, S=16, D=64 (one 64-byte slice per row, NI=1): element (page 2, head 1, slot 13, d 37)
-    #   block (2*2+1)*16*64 = 5120; token 13 = 4*3+1 (s=3, i=1); chunk 37//16 = 2 (q=2, k=0)
-    #   chunk position ((3*1+0)*4+2)*4+1 = 57 -> 5120 + 57*16 + 37%16 = 6037
-    assert paged.k_offset(2, 1, 13, 37, 2, 16, 64, 1) == 6037
-    # e4m3 K, Hkv=1, S=32, D=64: (page 1, head 0, slot 17, d 0) -> 2048 + sub-page 1 (1024) + chunk 1 (16)
-    assert paged.k_offset(1, 0, 17, 0, 1, 32, 64, 1) == 3088
-    # bf16 K, Hkv=1, S=16, D=128 (8 elements a chunk, NI=4): (page 0, head 0, slot 5, d 100)
-    #   token 5 (s=1, i=1); chunk 100//8 = 12 (q=3, k=0); position ((1*4+0)*4+3)*4+1 = 77 -> 77*8 + 4
-    assert paged.k_offset(0, 0, 5, 100, 1, 16, 128, 2) == 620
-    # e4m3 K, D=128 (NI=2): the 32 bytes lane group q reads of token 4s+i start at 512s + 64q + 16i
-    # (first half, k=0) and 256 bytes later (second half, k=1)
-    for s_ in range(4):
-        for q in range(4):
-            for i in range(4):
-                assert paged.k_offset(0, 0, 4 * s_ + i, 32 * q, 1, 16, 128, 1) == 512 * s_ + 64 * q + 16 * i
-                assert paged.k_offset(0, 0, 4 * s_ + i, 32 * q + 16, 1, 16, 128, 1) == 512 * s_ + 256 + 64 * q + 16 * i
-    # V element (page 2, head 1, slot 3, d 4), Hkv=2, S=4, Dv=5: ((2*2+1)*5+4)*4+3 = 119
-    assert paged.v_offset(2, 1, 3, 4, 2, 4, 5) == 119
-    assert paged.v_offset(0, 0, 1, 0, 2, 4, 5) == 1
+def test_append_writes_exactly_the_addressed_elements():
+    """Token 19 of a request whose second page-table entry is page 0 lands at page 0, slot 3, for every
+    kv head, in K and V; nothing else changes."""
+    H, S, D, P = 2, 16, 64, 3
+    kp = np.zeros((P, H, S, D), dtype=np.uint8)
+    vp = np.zeros((P, H, S, 16), dtype=np.uint8)
+    pt = np.array([[2, 0]], dtype=np.int32)
+    k_new = np.arange(1, 1 + H * D, dtype=np.uint8).reshape(1, H, D)
+    v_new = (100 + np.arange(H * 16) % 100).astype(np.uint8).reshape(1, H, 16)
+    paged.append(kp, vp, k_new, v_new, [0], [19], pt)
+    assert np.array_equal(kp[0, :, 3, :], k_new[0]) and np.array_equal(vp[0, :, 3, :], v_new[0])
+    assert kp.astype(np.int64).sum() == k_new.astype(np.int64).sum()
+    assert vp.astype(np.int64).sum() == v_new.astype(np.int64).sum()
+    got_k, got_v = paged.gather(kp, vp, pt, 0, 20)
+    assert np.array_equal(got_k[19], k_new[0]) and np.array_equal(got_v[19], v_new[0])
+    assert not got_k[:19].any()
 
 
-def test_latent_layout_offsets_by_hand():
-    """A latent pool (no V pool) is row-major: element (page 3, slot 5, d 7) of a 576-wide, 16-slot pool
-    sits (3*16 + 5)*576 + 7 = 30535 elements in; a page's tokens are consecutive 576-element rows."""
-    assert paged.c_offset(3, 0, 5, 7, 1, 16, 576) == 30535
-    assert paged.c_offset(0, 0, 0, 0, 1, 64, 576) == 0
-    assert paged.c_offset(2, 0, 63, 575, 1, 64, 576) == 3 * 64 * 576 - 1   # last element of page 2
-    slot, d = np.meshgrid(np.arange(64), np.arange(576), indexing="ij")
-    assert np.array_equal(paged.c_offset(1, 0, slot, d, 1, 64, 576).ravel(), 64 * 576 + np.arange(64 * 576))
-
-
-def test_latent_append_writes_contiguous_rows():
-    """Appending into a latent pool (v_pool None) writes each token's whole row at row-major offsets."""
+def test_latent_append_writes_whole_rows():
+    """Appending into a latent pool (v_pool None) writes each token's whole 576-wide row."""
     S, D, P = 16, 576, 4
-    cp = np.zeros(P * S * D, dtype=np.uint8)
+    cp = np.zeros((P, 1, S, D), dtype=np.uint8)
     pt = np.array([[3, 1]], dtype=np.int32)
     rows = (np.arange(2 * D) % 251 + 1).astype(np.uint8).reshape(2, 1, D)
-    paged.append(cp, None, rows, None, [0, 0], [2, 17], pt, 1, S)   # slot 2 of page 3, slot 1 of page 1
-    assert np.array_equal(cp[(3 * S + 2) * D:(3 * S + 3) * D], rows[0, 0])
-    assert np.array_equal(cp[(1 * S + 1) * D:(1 * S + 2) * D], rows[1, 0])
+    paged.append(cp, None, rows, None, [0, 0], [2, 17], pt)   # slot 2 of page 3, slot 1 of page 1
+    assert np.array_equal(cp[3, 0, 2], rows[0, 0]) and np.array_equal(cp[1, 0, 1], rows[1, 0])
     assert cp.astype(np.int64).sum() == rows.astype(np.int64).sum()
-    k, v = paged.gather(cp, None, pt, 0, 18, 1, S, D, 0)
+    k, v = paged.gather(cp, None, pt, 0, 18)
     assert v is None and np.array_equal(k[17, 0], rows[1, 0]) and np.array_equal(k[2, 0], rows[0, 0])
 
 
-@pytest.mark.parametrize("S,D,elt", [(16, 128, 1), (16, 128, 2), (64, 128, 1), (32, 576, 1), (16, 576, 2), (16, 64, 1)])
-def test_k_layout_is_a_bijection_per_block(S, D, elt):
-    slot, d = np.meshgrid(np.arange(S), np.arange(D), indexing="ij")
-    off = paged.k_offset(1, 1, slot, d, 2, S, D, elt)
-    base = (1 * 2 + 1) * S * D
-    assert np.array_equal(np.sort(off.ravel()), base + np.arange(S * D))
-
-
-def test_append_writes_exactly_the_addressed_elements():
-    H, S, D, P = 2, 16, 64, 3
-    kp = np.zeros(P * H * S * D, dtype=np.uint8)
-    vp = np.zeros(P * H * S * D, dtype=np.uint8)
-    pt = np.array([[2, 0]], dtype=np.int32)
-    k_new = np.arange(1, 1 + H * D, dtype=np.uint8).reshape(1, H, D)
-    v_new = (100 + np.arange(H * D) % 100).astype(np.uint8).reshape(1, H, D)
-    paged.append(kp, vp, k_new, v_new, [0], [19], pt, H, S)       # token 19 -> page pt[0][1] = 0, slot 3
-    for h in range(H):
-        for d in range(D):
-            assert kp[paged.k_offset(0, h, 3, d, H, S, D, 1)] == k_new[0, h, d]
-    vv = vp.reshape(P, H, D, S)
-    assert np.array_equal(vv[0, :, :, 3], v_new[0])
-    assert kp.astype(np.int64).sum() == k_new.astype(np.int64).sum()
-    assert vp.astype(np.int64).sum() == v_new.astype(np.int64).sum()
+def test_later_token_wins_on_one_slot():
+    kp = np.zeros((2, 1, 16, 4), dtype=np.uint16)
+    pt = np.array([[1]], dtype=np.int32)
+    rows = np.array([[[1, 1, 1, 1]], [[2, 2, 2, 2]]], dtype=np.uint16)
+    paged.append(kp, None, rows, None, [0, 0], [5, 5], pt)
+    assert kp[1, 0, 5].tolist() == [2, 2, 2, 2]
 
 
 def test_append_gather_roundtrip_and_untouched_bytes():
@@ -157,43 +124,42 @@ def test_append_gather_roundtrip_and_untouched_bytes():
     pt, _ = wl.page_table(w, lens)
     k, v = wl.all_kv(w, lens, threads=1)
     req, pos = wl.token_index(lens)
-    kp0 = wl.pool_bytes(w, "k", 1)
-    vp0 = wl.pool_bytes(w, "v", 1)
+    kp0 = wl.pool_init(w, "k", 1)
+    vp0 = wl.pool_init(w, "v", 1)
     kp, vp = kp0.copy(), vp0.copy()
     ks, vs = codec.calibrate_scale(k), codec.calibrate_scale(v)
-    paged.append_fp8(kp, vp, k, v, req, pos, pt, w.num_kv_heads, w.page_size, ks, vs)
+    paged.append_fp8(kp, vp, k, v, req, pos, pt, ks, vs)
     off = np.concatenate([[0], np.cumsum(lens)])
     for r in range(w.batch):
-        gk, gv = paged.gather(kp, vp, pt, r, int(lens[r]), w.num_kv_heads, w.page_size, w.head_dim, w.v_dim)
+        gk, gv = paged.gather(kp, vp, pt, r, int(lens[r]))
         assert np.array_equal(gk, codec.quantize_e4m3(k[off[r]:off[r + 1]], ks))
         assert np.array_equal(gv, codec.quantize_e4m3(v[off[r]:off[r + 1]], vs))
     # pages no request owns keep their random bytes
-    used = set(pt[pt >= 0].tolist())
-    blk = w.num_kv_heads * w.page_size * w.head_dim
-    for p in range(w.num_pages):
-        if p not in used:
-            assert np.array_equal(kp[p * blk:(p + 1) * blk], kp0[p * blk:(p + 1) * blk])
-            assert np.array_equal(vp[p * blk:(p + 1) * blk], vp0[p * blk:(p + 1) * blk])
+    unused = sorted(set(range(w.num_pages)) - set(pt[pt >= 0].tolist()))
+    assert np.array_equal(kp[unused], kp0[unused]) and np.array_equal(vp[unused], vp0[unused])
+    # slots past a request's last token keep their random bytes too
+    r = int(np.argmin(lens % w.page_size == 0))
+    p_last, s_last = pt[r, (lens[r] - 1) // w.page_size], (lens[r] - 1) % w.page_size
+    assert np.array_equal(kp[p_last, :, s_last + 1:], kp0[p_last, :, s_last + 1:])
 
 
 def test_append_skips_flagged_and_out_of_range():
     H, S, D, P = 1, 16, 32, 4
-    kp = np.zeros(P * H * S * D, dtype=np.uint16)
-    vp = np.zeros(P * H * S * D, dtype=np.uint16)
+    kp = np.zeros((P, H, S, D), dtype=np.uint16)
+    vp = np.zeros((P, H, S, D), dtype=np.uint16)
     pt = np.array([[0, 1], [2, -1], [3, 9]], dtype=np.int32)
     k_new = np.full((5, H, D), 7, dtype=np.uint16)
     req = [0, 1, 1, 2, 2]
     pos = [1, 0, 17, 2, 18]      # r1 pos17 -> entry -1 (skip); r2 pos18 -> page 9 (skip)
     flags = np.array([1, 0, 0], dtype=np.uint32)                 # r0 aborted
-    paged.append(kp, vp, k_new, k_new, req, pos, pt, H, S, flags=flags)
-    blk = H * S * D
-    assert kp[:2 * blk].sum() == 0
-    got = lambda page, slot: kp[paged.k_offset(page, 0, slot, np.arange(D), H, S, D, 2)]
-    assert (got(2, 0) == 7).all() and (got(3, 2) == 7).all()
+    paged.append(kp, vp, k_new, k_new, req, pos, pt, flags=flags)
+    assert kp[:2].sum() == 0
+    assert (kp[2, 0, 0] == 7).all() and (kp[3, 0, 2] == 7).all()
     assert kp.astype(np.int64).sum() == 7 * D * 2
+    assert np.array_equal(kp, vp)
     # positions beyond the page-table row are skipped too
     kp2 = np.zeros_like(kp)
-    paged.append(kp2, None, k_new[:1], None, [2], [32], pt, H, S)
+    paged.append(kp2, None, k_new[:1], None, [2], [32], pt)
     assert kp2.sum() == 0
 
 
