@@ -11,13 +11,13 @@ e4m3 pools as torch.uint8 (or torch.float8_e4m3fn).
 """
 from __future__ import annotations
 
-import math
 from typing import Optional
 
 import torch
 
 from . import _lib
-from ._lib import FLAG_BAD_PAGE, FLAG_TAG_MISMATCH, KVFP8_ERR_NOSPACE, LayerStack, PoolDesc  # noqa: F401
+from ._lib import (FLAG_BAD_PAGE, FLAG_TAG_MISMATCH, KVFP8_ERR_NOSPACE, READ_SINK_WORDS, LayerStack,  # noqa: F401
+                   PoolDesc)
 
 __all__ = ["KvFp8Error", "PoolDesc", "pool_desc", "kv_absmax_bf16", "kv_scale_from_absmax", "calibrate_scale",
            "kv_append_fp8", "kv_append_bf16", "kv_tag_check", "kv_tag_check_append_fp8",
@@ -26,7 +26,7 @@ __all__ = ["KvFp8Error", "PoolDesc", "pool_desc", "kv_absmax_bf16", "kv_scale_fr
            "paged_decode_attn_latent_auto_splits", "paged_decode_attn_latent_fp8",
            "paged_decode_attn_latent_bf16", "kv_gather_fp8", "kv_gather_bf16", "decode_step", "decode_step_layers", "PageAllocator",
            "w4_quantize_bf16", "w8_quantize_bf16", "wgemm_auto_splits", "wgemm_workspace_bytes", "w4a16_gemm",
-           "w8a16_gemm",
+           "w8a16_gemm", "kv_read_stream", "kv_read_blocks", "READ_SINK_WORDS",
            "lib"]
 
 
@@ -163,10 +163,12 @@ def paged_decode_attn_auto_splits(batch, num_kv_heads, max_ctx_len) -> int:
 
 def decode_step_layers(desc: PoolDesc, kv_dtype: str, k_pools, v_pools, page_table, ctx_lens, max_ctx_len: int,
                        q, k_new, v_new, out, *, page_tags=None, expected_tags=None, abort_flags=None,
-                       k_scales=None, v_scales=None, sm_scale: Optional[float] = None, num_splits: int = 0,
-                       workspace=None, stream=None):
+                       k_scales=None, v_scales=None, sm_scale: float = 0.0, num_splits: int = 0,
+                       workspace=None, stream=None, fused_check: bool = False):
     """One decode step over a stack of layers sharing the page table, tags and flags (kv_decode_step_*):
-    the tag check once, fused with layer 0's write, then each layer's write and attention in stream order.
+    the tag check once, as its own launch with layer 0's write (fused_check: inside layer 0's attention
+    launch instead), then each layer's write and attention in stream order.  sm_scale 0 lets the
+    library use 1/sqrt(score dim).
 
     k_pools/v_pools: [layers][pool elements] (v_pools None: the latent cache, v_new None too);
     q [layers][B][Hq][D]; k_new/v_new [layers][B][Hkv][D|Dv]; out [layers][B][Hq][Dv];
@@ -191,8 +193,6 @@ def decode_step_layers(desc: PoolDesc, kv_dtype: str, k_pools, v_pools, page_tab
     if k_pools.numel() != n_layers * slots * desc.head_dim or (
             not latent and v_pools.numel() != n_layers * slots * desc.v_dim):
         raise ValueError("each layer's pool must hold exactly the pool the descriptor describes")
-    if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(D)
     ks = vs = None
     if fp8:
         if k_scales is None or (not latent and v_scales is None):
@@ -204,7 +204,7 @@ def decode_step_layers(desc: PoolDesc, kv_dtype: str, k_pools, v_pools, page_tab
     stack = LayerStack(n_layers, _ptr(k_pools, pool_t, "k_pools"), _ptr(v_pools, pool_t, "v_pools", True),
                        _ptr(q, _BF16, "q"), _ptr(k_new, _BF16, "k_new"), _ptr(v_new, _BF16, "v_new", True),
                        None if ks is None else ks.ctypes.data, None if vs is None else vs.ctypes.data,
-                       _ptr(out, _BF16, "out"))
+                       _ptr(out, _BF16, "out"), _lib.STEP_FUSED_CHECK if fused_check else 0)
     ws, wsb = _ws(workspace)
     f = lib().kv_decode_step_fp8 if fp8 else lib().kv_decode_step_bf16
     _check(f(desc, stack, Hq, _ptr(page_table, _I32, "page_table"), page_table.shape[1],
@@ -222,11 +222,9 @@ def _ws(workspace):
 
 
 def paged_decode_attn_fp8(desc: PoolDesc, q, k_pool, v_pool, page_table, ctx_lens, max_ctx_len: int, out,
-                          abort_flags=None, *, k_scale: float, v_scale: float, sm_scale: Optional[float] = None,
+                          abort_flags=None, *, k_scale: float, v_scale: float, sm_scale: float = 0.0,
                           num_splits: int = 0, workspace=None, stream=None):
     B, Hq, D = q.shape
-    if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(D)
     ws, wsb = _ws(workspace)
     _check(lib().paged_decode_attn_fp8(
         desc, _ptr(q, _BF16, "q"), Hq, _ptr(k_pool, _U8, "k_pool"), _ptr(v_pool, _U8, "v_pool"),
@@ -237,11 +235,9 @@ def paged_decode_attn_fp8(desc: PoolDesc, q, k_pool, v_pool, page_table, ctx_len
 
 
 def paged_decode_attn_bf16(desc: PoolDesc, q, k_pool, v_pool, page_table, ctx_lens, max_ctx_len: int, out,
-                           abort_flags=None, *, sm_scale: Optional[float] = None, num_splits: int = 0,
+                           abort_flags=None, *, sm_scale: float = 0.0, num_splits: int = 0,
                            workspace=None, stream=None):
     B, Hq, D = q.shape
-    if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(D)
     ws, wsb = _ws(workspace)
     _check(lib().paged_decode_attn_bf16(
         desc, _ptr(q, _BF16, "q"), Hq, _ptr(k_pool, _BF16, "k_pool"), _ptr(v_pool, _BF16, "v_pool"),
@@ -255,11 +251,9 @@ def paged_decode_attn_latent_auto_splits(batch, num_q_heads, max_ctx_len) -> int
 
 
 def paged_decode_attn_latent_fp8(desc: PoolDesc, q, pool, page_table, ctx_lens, max_ctx_len: int, out,
-                                 abort_flags=None, *, scale: float, sm_scale: Optional[float] = None,
+                                 abort_flags=None, *, scale: float, sm_scale: float = 0.0,
                                  num_splits: int = 0, workspace=None, stream=None):
     B, Hq, D = q.shape
-    if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(D)
     ws, wsb = _ws(workspace)
     _check(lib().paged_decode_attn_latent_fp8(
         desc, _ptr(q, _BF16, "q"), Hq, _ptr(pool, _U8, "pool"), _ptr(page_table, _I32, "page_table"),
@@ -269,11 +263,9 @@ def paged_decode_attn_latent_fp8(desc: PoolDesc, q, pool, page_table, ctx_lens, 
 
 
 def paged_decode_attn_latent_bf16(desc: PoolDesc, q, pool, page_table, ctx_lens, max_ctx_len: int, out,
-                                  abort_flags=None, *, sm_scale: Optional[float] = None, num_splits: int = 0,
+                                  abort_flags=None, *, sm_scale: float = 0.0, num_splits: int = 0,
                                   workspace=None, stream=None):
     B, Hq, D = q.shape
-    if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(D)
     ws, wsb = _ws(workspace)
     _check(lib().paged_decode_attn_latent_bf16(
         desc, _ptr(q, _BF16, "q"), Hq, _ptr(pool, _BF16, "pool"), _ptr(page_table, _I32, "page_table"),
@@ -337,6 +329,25 @@ def w4a16_gemm(x, w_packed, scales, n, k, y, *, num_splits: int = 0, workspace=N
 def w8a16_gemm(x, w_packed, scales, n, k, y, *, num_splits: int = 0, workspace=None, stream=None):
     """y [M][N] (bf16) = x [M][K] (bf16) times the FP8 weights (packed by w8_quantize_bf16), transposed."""
     _wgemm(8, x, w_packed, scales, n, k, y, num_splits, workspace, stream)
+
+
+# ----------------------------------------------------------------------------- read-rate calibration
+
+def kv_read_stream(src, sink, nbytes=None, stream=None):
+    """Read nbytes (default: all) of a device tensor; sink: int32/uint32 [READ_SINK_WORDS] checksum words."""
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    _check(lib().kv_read_stream(src.data_ptr(), n, _ptr(sink, _U32, "sink"), _stream(stream)), "kv_read_stream")
+
+
+def kv_read_blocks(base, block_bytes, ids, sink, stream=None):
+    """Read the block_bytes-byte blocks ids[k] of a device tensor (ids int32 on the device)."""
+    if not base.is_cuda or not base.is_contiguous():
+        raise ValueError("base must be a contiguous device tensor")
+    nb = base.numel() * base.element_size() // int(block_bytes)
+    _check(lib().kv_read_blocks(base.data_ptr(), nb, int(block_bytes), _ptr(ids, _I32, "ids"), ids.numel(),
+                                _ptr(sink, _U32, "sink"), _stream(stream)), "kv_read_blocks")
 
 
 # ----------------------------------------------------------------------------- read back (tests)
@@ -406,8 +417,8 @@ class PageAllocator:
 
 def decode_step(desc: PoolDesc, kv_dtype: str, k_pool, v_pool, page_table, ctx_lens, max_ctx_len: int, q,
                 k_new, v_new, tok_req, tok_pos, out, *, page_tags=None, expected_tags=None, abort_flags=None,
-                k_scale: float = 1.0, v_scale: float = 1.0, sm_scale: Optional[float] = None, num_splits: int = 0,
-                workspace=None, stream=None):
+                k_scale: float = 1.0, v_scale: float = 1.0, sm_scale: float = 0.0, num_splits: int = 0,
+                workspace=None, stream=None, fused_check: bool = False):
     """One attention layer's decode step, in stream order: tag check -> append -> attention.
 
     With page_tags/expected_tags given, the batched check writes abort_flags
@@ -415,11 +426,11 @@ def decode_step(desc: PoolDesc, kv_dtype: str, k_pool, v_pool, page_table, ctx_l
     (the no-op tracker) no check runs and abort_flags is passed through
     (None = no flags).  tok_req/tok_pos None means one new token per
     request, at position ctx_lens[r] - 1: the step is then kv_decode_step_*
-    over this one layer, a single launch for the GQA cache (every block
-    checks its request's pages before reading any, the block holding
-    position L - 1 writes the token), a check + write launch and the
-    attention for the latent cache.  Otherwise three launches: kv_tag_check,
-    kv_append_*, the attention.
+    over this one layer: the check + write launch, then the attention (with
+    no tracker, one attention launch whose block holding position L - 1
+    writes the token); fused_check puts the check in the attention launch
+    (one launch for the GQA and FP8 latent caches).  Otherwise three
+    launches: kv_tag_check, kv_append_*, the attention.
     """
     if kv_dtype not in ("fp8", "bf16"):
         raise ValueError(f"kv_dtype {kv_dtype!r}")
@@ -436,7 +447,7 @@ def decode_step(desc: PoolDesc, kv_dtype: str, k_pool, v_pool, page_table, ctx_l
                            expected_tags=expected_tags, abort_flags=abort_flags,
                            k_scales=[k_scale] if fp8 else None,
                            v_scales=[v_scale] if fp8 and not latent else None, sm_scale=sm_scale,
-                           num_splits=num_splits, workspace=workspace, stream=stream)
+                           num_splits=num_splits, workspace=workspace, stream=stream, fused_check=fused_check)
         return
     if page_tags is not None:
         kv_tag_check(page_tags, page_table, expected_tags, ctx_lens, desc.page_size, abort_flags, stream=stream)

@@ -14,6 +14,7 @@ STATUS = {0: "KVFP8_OK", -1: "KVFP8_ERR_NULL", -2: "KVFP8_ERR_SHAPE", -3: "KVFP8
 KVFP8_ERR_NOSPACE = -8
 FLAG_TAG_MISMATCH = 1
 FLAG_BAD_PAGE = 2
+READ_SINK_WORDS = 2048
 
 
 class PoolDesc(C.Structure):
@@ -24,7 +25,8 @@ class PoolDesc(C.Structure):
 class LayerStack(C.Structure):
     _fields_ = [("num_layers", C.c_int32), ("k_pools", C.c_void_p), ("v_pools", C.c_void_p), ("q", C.c_void_p),
                 ("k_new", C.c_void_p), ("v_new", C.c_void_p), ("k_scales", C.c_void_p), ("v_scales", C.c_void_p),
-                ("out", C.c_void_p)]
+                ("out", C.c_void_p), ("options", C.c_uint32)]
+STEP_FUSED_CHECK = 1
 
 
 _p = C.c_void_p
@@ -75,6 +77,8 @@ PROTOTYPES = {
     "wgemm_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "w4a16_gemm": (C.c_int, [_p, _i32, _p, _p, _i32, _i32, _i32, _p, _sz, _p, _p]),
     "w8a16_gemm": (C.c_int, [_p, _i32, _p, _p, _i32, _i32, _i32, _p, _sz, _p, _p]),
+    "kv_read_stream": (C.c_int, [_p, _sz, _p, _p]),
+    "kv_read_blocks": (C.c_int, [_p, _i64, _i64, _p, _i64, _p, _p]),
     "kv_gather_fp8": (C.c_int, [_desc, _p, _p, _p, _p, _i32, _p, _i32, _i32, _p, _p, _p]),
     "kv_gather_bf16": (C.c_int, [_desc, _p, _p, _p, _p, _i32, _p, _i32, _i32, _p, _p, _p]),
 }

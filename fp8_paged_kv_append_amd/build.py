@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvfp8.so")
 
 SOURCES = ["api.hip", "kv_small.hip", "attn_gqa.hip", "attn_latent.hip", "attn_latent_pairs.hip", "page_alloc.hip",
-           "wgemm.hip"]
+           "wgemm.hip", "read_stream.hip"]
 ARCH = os.environ.get("KVFP8_ARCH", "gfx950")
 
 

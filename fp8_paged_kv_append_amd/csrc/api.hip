@@ -16,6 +16,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool good_scale(float s) { return isfinite(s) && s > 0.f; }
+// The softmax scale a caller passes, with 0 standing for the usual 1/sqrt(score dim).
+inline float softmax_scale(float sm_scale, int32_t score_dim) {
+  return sm_scale == 0.f ? 1.0f / sqrtf((float)score_dim) : sm_scale;
+}
 
 int check_pool(const kvfp8_pool_desc* d, bool need_v_dim_eq, int elt_bytes) {
   if (d == nullptr) return KVFP8_ERR_NULL;
@@ -131,6 +135,7 @@ int attn_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_he
   if ((int64_t)pt_stride * desc->page_size < max_ctx_len) return KVFP8_ERR_SHAPE;
   if (batch > 65535 || desc->num_kv_heads > 65535) return KVFP8_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return KVFP8_ERR_ALIGN;
+  sm_scale = softmax_scale(sm_scale, desc->head_dim);
   if (!good_scale(k_scale) || !good_scale(v_scale) || !good_scale(sm_scale)) return KVFP8_ERR_VALUE;
   const int32_t tiles = n_tiles_of(max_ctx_len);
   int32_t splits = num_splits == 0 ? auto_splits(batch, desc->num_kv_heads, max_ctx_len) : num_splits;
@@ -187,7 +192,7 @@ int check_append_common(const kvfp8_pool_desc* desc, void* k_pool, void* v_pool,
                         const uint16_t* v_new, const int32_t* page_table, int32_t pt_stride,
                         const int32_t* ctx_lens, int32_t batch, const uint32_t* page_tags,
                         const uint32_t* expected_tags, uint32_t* abort_flags, bool fp8, float k_scale,
-                        float v_scale, hipStream_t stream, bool launch = true) {
+                        float v_scale, hipStream_t stream, bool launch = true, int32_t max_ctx = 0) {
   // page_tags null: no check, abort_flags (may be null) only read -- see check_append_kernel
   int st = check_pool(desc, false, fp8 ? 1 : 2);
   if (st) return st;
@@ -212,6 +217,7 @@ int check_append_common(const kvfp8_pool_desc* desc, void* k_pool, void* v_pool,
   c.pt_stride = pt_stride;
   c.batch = batch;
   c.page_size = desc->page_size;
+  c.max_ctx = max_ctx;
   AppendArgs a;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
@@ -286,6 +292,7 @@ int latent_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_
   if (max_ctx_len < 1) return KVFP8_ERR_SHAPE;
   if ((int64_t)pt_stride * desc->page_size < max_ctx_len) return KVFP8_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(pool) || !aligned16(out)) return KVFP8_ERR_ALIGN;
+  sm_scale = softmax_scale(sm_scale, desc->head_dim);
   if (!good_scale(scale) || !good_scale(sm_scale)) return KVFP8_ERR_VALUE;
   const int32_t tiles = (int32_t)(((int64_t)max_ctx_len + kLatentTileTokens - 1) / kLatentTileTokens);
   // FP8: the wave-pair kernel while its splits stay short (latent_use_pairs), else the 128-head
@@ -343,12 +350,16 @@ int latent_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_
 }
 
 // One decode step over a layer stack: every argument of every layer is checked (a dry pass of the
-// per-layer checks) before the first launch, so an error launches nothing.  GQA cache: one attention
-// launch per layer (plus the merge when split) that also writes the layer's token -- the block whose
-// split holds position L - 1 writes it and adds it to its softmax from registers -- and, in layer 0
-// with page_tags given, runs the tag check first in every block and stores the flags that the later
-// layers read.  Latent cache: per layer a check + write launch (the check in layer 0 only), then the
-// attention.  Stream order carries the layer-to-layer dependency.
+// per-layer checks) before the first launch, so an error launches nothing.  With page_tags given, the
+// tag check is its own batched launch before anything reads the cache (the agentlenshq summary,
+// section "KV Cache 完整性检查", and the xujun.org note, section "一个不能出错的共享缓存", keep it out
+// of the attention kernel): layer 0's check + write launch, then layer 0's attention reading the
+// flags it left.  Every later layer (and layer 0 without the tracker) is one attention launch (plus
+// the merge when split) that also writes the layer's token: GQA, the block whose split holds position
+// L - 1 writes it and adds it to its softmax from registers; latent, the block(s) holding it store it
+// before copying any tile and read it back.  With KVFP8_STEP_FUSED_CHECK layer 0's check runs inside
+// its attention launch instead (GQA and FP8 latent: in every block, before it reads any page; BF16
+// latent keeps its check + write launch).  Stream order carries the layer-to-layer dependency.
 int decode_step_common(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* layers, int32_t num_q_heads,
                        const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens, int32_t batch,
                        int32_t max_ctx_len, const uint32_t* page_tags, const uint32_t* expected_tags,
@@ -357,6 +368,8 @@ int decode_step_common(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* lay
   if (desc == nullptr || layers == nullptr) return KVFP8_ERR_NULL;
   const kvfp8_layer_stack& ls = *layers;
   if (ls.num_layers < 1 || batch < 0 || num_q_heads < 1) return KVFP8_ERR_SHAPE;
+  if ((ls.options & ~KVFP8_STEP_FUSED_CHECK) != 0u) return KVFP8_ERR_VALUE;
+  const bool fused = (ls.options & KVFP8_STEP_FUSED_CHECK) != 0u;
   if (!ls.k_pools || !ls.q || !ls.k_new || !ls.out) return KVFP8_ERR_NULL;
   const bool latent = ls.v_pools == nullptr;
   if (latent != (ls.v_new == nullptr)) return KVFP8_ERR_NULL;
@@ -382,20 +395,16 @@ int decode_step_common(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* lay
       uint16_t* out = ls.out + l * out_n;
       const float ks = fp8 ? ls.k_scales[l] : 1.f;
       const float vs = fp8 && !latent ? ls.v_scales[l] : 1.f;
-      // Every layer is one attention launch (plus the merge when split) that also writes the layer's
-      // token and, in layer 0 with page_tags given, runs the tag check in every block first.  GQA: the
-      // block holding position L - 1 adds the token to its softmax from registers; latent: the
-      // block(s) holding it store it before copying any tile and read it back with the rest.  The
-      // BF16 latent cache checks and writes layer 0 in a launch of its own instead: measured faster
-      // at 64 x 4096 (132.5-132.9 us per single-layer step against 135.0-136.1 with the check in its
-      // attention blocks), where the FP8 cache gains from the one launch (130.1-130.9 against
-      // 133.3-133.4 us)
-      const bool own_write = latent && !fp8 && l == 0;
       const uint32_t* tags = l == 0 ? page_tags : nullptr;
+      // layer 0 with the tracker: the check (and the layer's write) as a launch of its own, unless the
+      // caller asks for the fused form -- which the BF16 latent cache does not take (measured slower
+      // at 64 x 4096: 135.0-136.1 us per single-layer step with the check in its 128-head blocks
+      // against 132.5-132.9 with the separate launch)
+      const bool own_write = tags != nullptr && (!fused || (latent && !fp8));
       int st = KVFP8_OK;
       if (!launch || own_write)  // the dry pass checks the write's arguments for every layer
         st = check_append_common(desc, kp, vp, kn, vn, page_table, pt_stride, ctx_lens, batch, tags, expected_tags,
-                                 abort_flags, fp8, ks, vs, stream, launch);
+                                 abort_flags, fp8, ks, vs, stream, launch, max_ctx_len);
       if (st) return st;
       if (own_write) tags = nullptr;
       st = latent ? latent_common(desc, q, num_q_heads, kp, page_table, pt_stride, ctx_lens, batch, max_ctx_len,
@@ -404,8 +413,8 @@ int decode_step_common(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* lay
                                   expected_tags, tags ? abort_flags : nullptr)
                   : attn_common(desc, q, num_q_heads, kp, vp, page_table, pt_stride, ctx_lens, batch, max_ctx_len,
                                 tags ? nullptr : abort_flags, fp8, ks, vs, sm_scale, num_splits, workspace,
-                                workspace_bytes, out, stream, launch, kn, vn, tags, expected_tags,
-                                tags ? abort_flags : nullptr);
+                                workspace_bytes, out, stream, launch, own_write ? nullptr : kn,
+                                own_write ? nullptr : vn, tags, expected_tags, tags ? abort_flags : nullptr);
       if (st) return st;
     }
   }
@@ -480,6 +489,7 @@ int kv_tag_check(const uint32_t* page_tags, int32_t num_pages, const int32_t* pa
   a.pt_stride = pt_stride;
   a.batch = batch;
   a.page_size = page_size;
+  a.max_ctx = 0;
   return launch_tag_check(a, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
 }
 
@@ -575,6 +585,31 @@ int paged_decode_attn_latent_bf16(const kvfp8_pool_desc* desc, const uint16_t* q
                                   size_t workspace_bytes, uint16_t* out, hipStream_t stream) {
   return latent_common(desc, q, num_q_heads, pool, page_table, pt_stride, ctx_lens, batch, max_ctx_len, abort_flags,
                        false, 1.f, sm_scale, num_splits, workspace, workspace_bytes, out, stream);
+}
+
+int kv_read_stream(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (bytes == 0) return KVFP8_OK;
+  if (!src || !sink) return KVFP8_ERR_NULL;
+  if (bytes % 4 != 0) return KVFP8_ERR_SHAPE;
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return KVFP8_ERR_ALIGN;
+  const uint64_t want = (bytes / 16 + 255) / 256;  // one 16-byte load per thread at least
+  const int blocks = (int)(want < KVFP8_READ_SINK_WORDS ? (want < 1 ? 1 : want) : KVFP8_READ_SINK_WORDS);
+  return launch_read_stream(src, bytes, sink, blocks, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
+}
+
+int kv_read_blocks(const void* base, int64_t num_blocks, int64_t block_bytes, const int32_t* ids, int64_t n_ids,
+                   uint32_t* sink, hipStream_t stream) {
+  if (n_ids < 0 || num_blocks < 0 || block_bytes <= 0 || block_bytes % 16 != 0) return KVFP8_ERR_SHAPE;
+  if (n_ids == 0) return KVFP8_OK;
+  if (!base || !ids || !sink) return KVFP8_ERR_NULL;
+  if (!aligned16(base) || (reinterpret_cast<uintptr_t>(ids) & 3u) || (reinterpret_cast<uintptr_t>(sink) & 3u))
+    return KVFP8_ERR_ALIGN;
+  const int64_t steps = (block_bytes / 16 + 63) / 64;  // 1 KiB steps a wave takes per block
+  const int64_t want = (n_ids * steps + 3) / 4;          // four waves per thread block
+  const int blocks = (int)(want < KVFP8_READ_SINK_WORDS ? want : KVFP8_READ_SINK_WORDS);
+  return launch_read_blocks(base, num_blocks, ids, n_ids, block_bytes, sink, blocks, stream) == hipSuccess
+             ? KVFP8_OK
+             : KVFP8_ERR_HIP;
 }
 
 int kv_gather_fp8(const kvfp8_pool_desc* desc, const uint8_t* k_pool, const uint8_t* v_pool, const int32_t* tok_req,

@@ -125,11 +125,16 @@ hipError_t launch_append(const AppendArgs& a, bool fp8, hipStream_t stream) {
 // ------------------------------------------------------------------ check + write in one launch
 // The decode step's first two passes fused per request: block r ORs the flags of request r's used
 // pages exactly as tag_check_kernel does, and only when they are clear writes r's new token
-// (position ctx_lens[r] - 1) exactly as append_kernel would.  The new rows are loaded before the
-// check so their latency overlaps it.  Check before write is preserved inside the block.
+// (position ctx_lens[r] - 1) exactly as append_kernel would.  The new rows and the first
+// kCaBatch * 256 page-table and expected-tag words of the row are loaded together with the context
+// length (every row holds pt_stride words, so these loads stay inside the tables whatever the
+// length turns out to be), so the check's first tag gathers follow one memory round trip after the
+// launch.  Check before write is preserved inside the block.
 // With c.page_tags null there is no check: the flags (when given) were set by an earlier launch and
 // are only read -- the later layers of a step that shares one check -- and the page id of the
 // written slot is validated here instead.
+constexpr int kCaBatch = 2;  // page-table words per thread loaded with the length (512 cover 8192 tokens at S = 16)
+
 template <bool FP8>
 __global__ __launch_bounds__(256) void check_append_kernel(TagArgs c, AppendArgs a) {
   __shared__ uint32_t s_or[4];
@@ -146,8 +151,20 @@ __global__ __launch_bounds__(256) void check_append_kernel(TagArgs c, AppendArgs
     kw[i] = e < nk ? ksrc[e] : 0u;
     vw[i] = e < nv ? vsrc[e] : 0u;
   }
+  const bool check = c.page_tags != nullptr;
+  const int32_t* pt = c.page_table + (int64_t)r * c.pt_stride;
+  const uint32_t* ex = check ? c.expected + (int64_t)r * c.pt_stride : nullptr;
+  int32_t sp[kCaBatch];
+  uint32_t se[kCaBatch];
+#pragma unroll
+  for (int j = 0; j < kCaBatch; ++j) {
+    const int64_t i = threadIdx.x + 256 * j;
+    const bool in = check && i < c.pt_stride;
+    sp[j] = in ? pt[i] : -1;
+    se[j] = in ? ex[i] : 0u;
+  }
   const int64_t L = c.ctx_lens[r];
-  if (c.page_tags == nullptr) {
+  if (!check) {
     // ---- no check: honour the flags an earlier launch wrote
     if (L <= 0 || (c.flags != nullptr && c.flags[r] != 0u)) return;
     if ((L - 1) / a.page_size >= a.pt_stride) return;
@@ -161,9 +178,24 @@ __global__ __launch_bounds__(256) void check_append_kernel(TagArgs c, AppendArgs
         f |= 2u;
         n = c.pt_stride;
       }
-      const int32_t* pt = c.page_table + (int64_t)r * c.pt_stride;
-      const uint32_t* ex = c.expected + (int64_t)r * c.pt_stride;
-      for (int64_t i = threadIdx.x; i < n; i += 256) {
+      uint32_t tv[kCaBatch];
+#pragma unroll
+      for (int j = 0; j < kCaBatch; ++j) {
+        const int64_t i = threadIdx.x + 256 * j;
+        const bool ok = sp[j] >= 0 && sp[j] < c.num_pages;
+        tv[j] = (i < n && ok) ? c.page_tags[sp[j]] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kCaBatch; ++j) {
+        const int64_t i = threadIdx.x + 256 * j;
+        if (i < n) {
+          if (sp[j] < 0 || sp[j] >= c.num_pages)
+            f |= 2u;
+          else if (tv[j] != se[j])
+            f |= 1u;
+        }
+      }
+      for (int64_t i = threadIdx.x + 256 * kCaBatch; i < n; i += 256) {
         const int32_t p = pt[i];
         if (p < 0 || p >= c.num_pages)
           f |= 2u;
@@ -179,6 +211,7 @@ __global__ __launch_bounds__(256) void check_append_kernel(TagArgs c, AppendArgs
     if (threadIdx.x == 0) c.flags[r] = flag;
     if (flag != 0u || L <= 0) return;
   }
+  if (c.max_ctx > 0 && L > c.max_ctx) return;  // beyond the step's grid: flagged as usual, not written
   // ---- the write, for a request whose pages all check out
   const int pos = (int)(L - 1);
   const int page = a.page_table[(int64_t)r * a.pt_stride + pos / S];  // in range: checked above

@@ -79,6 +79,9 @@ struct TagArgs {
   const int32_t* ctx_lens;
   uint32_t* flags;
   int32_t num_pages, pt_stride, batch, page_size;
+  // check + write launch only: a request longer than this (the attention grid's bound) keeps its flag
+  // but its token is not written, as the attention launches of a decode step treat it (0: no bound)
+  int32_t max_ctx;
 };
 
 struct LatentArgs {
@@ -125,5 +128,8 @@ hipError_t launch_tag_check(const TagArgs& a, hipStream_t stream);
 hipError_t launch_check_append(const TagArgs& c, const AppendArgs& a, bool fp8, hipStream_t stream);
 constexpr int kCheckAppendMaxPairs = 8 * 256;  // (Hkv*D)/2 and (Hkv*Dv)/2 limit of the fused kernel
 hipError_t launch_absmax(const uint16_t* x, int64_t n, uint32_t* out, hipStream_t stream);
+hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
+hipError_t launch_read_blocks(const void* base, int64_t num_blocks, const int32_t* ids, int64_t n_ids,
+                              int64_t block_bytes, uint32_t* sink, int blocks, hipStream_t stream);
 
 }  // namespace kvfp8

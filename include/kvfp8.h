@@ -61,7 +61,7 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;
 
-#define KVFP8_ABI_VERSION 1
+#define KVFP8_ABI_VERSION 2
 
 #define KVFP8_OK 0
 #define KVFP8_ERR_NULL (-1)        /* a required pointer is NULL                       */
@@ -176,7 +176,8 @@ int kv_tag_check_append_bf16(const kvfp8_pool_desc* desc, uint16_t* k_pool, uint
  *   ceil(max_ctx_len/64).  workspace: fp32 partials, at least
  *   paged_decode_attn_workspace_bytes(...) bytes for the split count used
  *   (0 when it is 1; then workspace may be NULL).
- *   sm_scale: usually 1/sqrt(D).  Scales must be finite and > 0. */
+ *   sm_scale: the softmax scale; 0 selects 1/sqrt(D) (the pages give none).
+ *   k_scale, v_scale and a non-zero sm_scale must be finite and > 0. */
 size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t v_dim,
                                          int32_t num_splits);
 /* The split count that num_splits = 0 selects for this shape (host only). */
@@ -211,7 +212,7 @@ int paged_decode_attn_bf16(const kvfp8_pool_desc* desc, const uint16_t* q, int32
  *   num_splits = 0 each cache type picks its own count (the FP8 kernel works
  *   on 64 heads per block, the BF16 one on 128);
  *   paged_decode_attn_latent_auto_splits returns the larger of the two, so a
- *   workspace sized with it fits either. */
+ *   workspace sized with it fits either.  sm_scale 0 selects 1/sqrt(576). */
 int32_t paged_decode_attn_latent_auto_splits(int32_t batch, int32_t num_q_heads, int32_t max_ctx_len);
 int paged_decode_attn_latent_fp8(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads,
                                  const uint8_t* pool, const int32_t* page_table, int32_t pt_stride,
@@ -236,33 +237,35 @@ int paged_decode_attn_latent_bf16(const kvfp8_pool_desc* desc, const uint16_t* q
  *   k_scales, v_scales (host) float [layers]: per-tensor scales of each
  *   layer's FP8 cache (the latent cache uses k_scales; both ignored, may be
  *   NULL, for BF16).
- * Launch order on `stream`: layer 0's check + write (kv_tag_check_append_*
- * semantics; with page_tags NULL, the write only), layer 0's attention, then
- * for each later layer its write, honouring the flags layer 0 left (read,
- * not rewritten: the pages' tag check runs once per step, before any read),
- * and its attention.  Each write puts request r's token at ctx_lens[r] - 1.
- * For the GQA cache every layer is ONE attention launch (plus the merge
- * launch when split): in layer 0 with page_tags given, every block first
- * checks all pages of its request (kv_tag_check semantics, before it reads
- * any page) and block (split 0, head 0) stores the request's flag; the
+ * Each layer writes request r's token at position ctx_lens[r] - 1 and
+ * attends.  With page_tags given, the tag check runs ONCE per step, as its
+ * own batched launch before anything reads the cache [T]: layer 0's
+ * kv_tag_check_append_* launch (check, then layer 0's write of every clean
+ * request), then layer 0's attention reading the flags it left.  Every later
+ * layer honours those flags (read, not rewritten) and is one attention launch
+ * (plus the merge when split) that also writes the layer's token: GQA, the
  * block whose split holds position ctx_lens[r] - 1 quantises the token as
- * kv_append_fp8 does, stores it, and adds it to its softmax from the values
- * it holds.  For the latent cache every layer is likewise one attention
- * launch (plus the merge) in which the block(s) whose split holds position
- * ctx_lens[r] - 1 quantise and store the token before copying any tile of
- * it, then read it back with the rest; FP8 layer 0 with page_tags given runs
- * the check in every block first, BF16 layer 0 keeps a check + write launch
- * before its attention.
- * Flags, pools and outputs are those of the launch order above.
- * A request with ctx_lens[r] > max_ctx_len is a caller error: its rows are
- * zero and the GQA layers and later latent layers do not write its token.
- * page_tags NULL = no-op tracker: no check; abort_flags, when given, are
- * only read.  Every layer's arguments are checked before the first launch,
- * so an error status means nothing was enqueued.  The workspace is shared by
- * the layers (stream order); size it as for one layer's attention.  Other
- * shapes, limits and outputs as for the per-layer calls above.  In a model
- * the layers' q and new rows come from the layer below; here they are given
- * up front (the projections between layers are not this library's). */
+ * kv_append_fp8 does, stores it and adds it to its softmax from the values it
+ * holds; latent, the block(s) holding it store it before copying any tile and
+ * read it back with the rest.  With page_tags NULL (no-op tracker) there is
+ * no check and layer 0 is such a launch too; abort_flags, when given, are
+ * only read.
+ * options (in the struct): KVFP8_STEP_FUSED_CHECK moves layer 0's check into
+ * its attention launch (GQA and FP8 latent: every block checks all pages of
+ * its request before it reads any, block (split 0, first head group) stores
+ * the flag; the BF16 latent cache keeps the separate launch).  Same flags,
+ * pools and outputs; one launch fewer.  Other bits: KVFP8_ERR_VALUE.
+ * A request with ctx_lens[r] > max_ctx_len is a caller error: its flag is
+ * computed as usual, its rows are zero and no layer writes its token.
+ * Every layer's arguments are checked before the first launch, so an error
+ * status means nothing was enqueued.  The workspace is shared by the layers
+ * (stream order); size it as for one layer's attention.  sm_scale 0 selects
+ * 1/sqrt(score dim).  Other shapes, limits and outputs as for the per-layer
+ * calls above.  In a model the layers' q and new rows come from the layer
+ * below; here they are given up front (the projections between layers are
+ * not this library's). */
+#define KVFP8_STEP_FUSED_CHECK 1u
+
 typedef struct kvfp8_layer_stack {
   int32_t num_layers;
   void* k_pools;
@@ -273,6 +276,7 @@ typedef struct kvfp8_layer_stack {
   const float* k_scales; /* host */
   const float* v_scales; /* host */
   uint16_t* out;
+  uint32_t options;      /* 0, or KVFP8_STEP_FUSED_CHECK */
 } kvfp8_layer_stack;
 
 int kv_decode_step_fp8(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* layers, int32_t num_q_heads,
@@ -311,6 +315,28 @@ int32_t kv_page_alloc_free_count(const void* state);
 int kv_page_alloc(void* state, int32_t n, int32_t* pages, uint32_t* tags);
 int kv_page_free(void* state, const int32_t* pages, int32_t n);
 int kv_page_alloc_tags(const void* state, uint32_t* tags);
+
+/* ---------------------------------------------------------------- read-rate calibration
+ * Read-only kernels that measure the HBM read rate attainable on the device,
+ * against which the attention kernels' KV-read rates are also reported (no
+ * page describes them; they compute nothing of the method).  Both read every
+ * byte once with 16-byte non-temporal loads and fold the 32-bit words read
+ * into XOR checksums: sink (device, at least KVFP8_READ_SINK_WORDS uint32
+ * words, 4-byte aligned) receives one word per thread block of the launch, and
+ * the XOR of all KVFP8_READ_SINK_WORDS words -- after the caller zeroes them --
+ * equals the XOR of every 32-bit word read.
+ *   kv_read_stream: bytes consecutive bytes at src (16-byte aligned; bytes a
+ *     multiple of 4).
+ *   kv_read_blocks: for k < n_ids, the block_bytes bytes at
+ *     base + ids[k] * block_bytes (ids int32 on the device; an id outside
+ *     [0, num_blocks) is skipped); block_bytes a multiple of 16, base 16-byte
+ *     aligned.  With ids listing the (page, kv head) blocks a decode step
+ *     reads, in the order of its page table, this is the attention's access
+ *     pattern without its arithmetic. */
+#define KVFP8_READ_SINK_WORDS 2048
+int kv_read_stream(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+int kv_read_blocks(const void* base, int64_t num_blocks, int64_t block_bytes, const int32_t* ids, int64_t n_ids,
+                   uint32_t* sink, hipStream_t stream);
 
 /* ---------------------------------------------------------------- test export
  * Read back tokens through the page table: k_out [N][Hkv][D], v_out

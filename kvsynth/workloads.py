@@ -263,3 +263,15 @@ def pool_init(w: Workload, which: str, elt_bytes: int, num_pages: Optional[int] 
     d = w.head_dim if which == "k" else w.v_dim
     flat = pool_bytes(w, which, elt_bytes, p)
     return flat.view(np.uint8 if elt_bytes == 1 else np.uint16).reshape(p, w.num_kv_heads, w.page_size, d)
+
+
+def rotation_tables(w: Workload, lens: np.ndarray, copies: int):
+    """`copies` page tables over disjoint page sets of one pool, for timing loops that rotate through
+    them so that consecutive steps read different memory.  The pool has max(w.num_pages, copies x the
+    pages one batch needs) pages; its pages are drawn without replacement across all copies.  Returns
+    (tables int32 [copies][B][stride], num_pages)."""
+    need = int(pages_needed(lens, w.page_size).sum())
+    P = max(w.num_pages, copies * need)
+    wb = w.with_(batch=w.batch * copies, num_pages=P)
+    pt, stride = page_table(wb, np.tile(np.asarray(lens, dtype=np.int32), copies))
+    return pt.reshape(copies, w.batch, stride), P

@@ -39,13 +39,16 @@ def host(t: torch.Tensor, dtype) -> np.ndarray:
 class Case:
     """One workload, filled into an oracle cache (numpy) and a device cache (HIP), plus a decode step's inputs."""
 
-    def __init__(self, w: wl.Workload, kv_dtype: str, lens=None, stride=None, oracle_fill=True, stale=None):
+    def __init__(self, w: wl.Workload, kv_dtype: str, lens=None, stride=None, oracle_fill=True, stale=None,
+                 calib_outliers=False):
+        """calib_outliers: with K outliers in the workload, take the K scale over K as drawn (outliers
+        included, nothing saturates) instead of over the outlier-free draw (outliers saturate)."""
         self.w, self.kv_dtype = w, kv_dtype
         self.lens = wl.ctx_lens(w) if lens is None else np.asarray(lens, dtype=np.int32)
         self.pt, self.stride = wl.page_table(w, self.lens, stride)
         self.k, self.v = wl.all_kv(w, self.lens)
         self.k_calib = self.k
-        if w.outlier_frac > 0:
+        if w.outlier_frac > 0 and not calib_outliers:
             self.k_calib, _ = wl.all_kv(w, self.lens, outliers=False)
         self.req, self.pos = wl.token_index(self.lens)
         self.tags = wl.page_tags(w)
@@ -98,11 +101,11 @@ class Case:
         self.dreq, self.dpos = dev(self.req), dev(self.pos)
         self.dtags, self.dexp = dev(self.tags), dev(self.exp)
         if kv_dtype == "fp8":
-            dkc = self.dk if w.outlier_frac == 0 else dev(self.k_calib)
+            separate = w.outlier_frac > 0 and not calib_outliers
+            dkc = dev(self.k_calib) if separate else self.dk
             self.d_k_scale = kv.calibrate_scale(dkc)
             self.d_v_scale = self.d_k_scale if w.latent else kv.calibrate_scale(self.dv)
-            if w.outlier_frac:
-                del dkc
+            del dkc
         else:
             self.d_k_scale = self.d_v_scale = 1.0
 

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvfp8_abi_version() == 1
+    assert lib.kvfp8_abi_version() == 2
     for s in range(-8, 1):
         assert lib.kvfp8_status_string(s).decode() not in ("", "unknown status")
     assert lib.kvfp8_status_string(5) == b"unknown status"
@@ -99,6 +99,8 @@ def test_host_validation_codes(lib):
     assert f(d, A, 8, A, A, A, 15, A, 1, 256, None, 1., 1., 1., 0, None, 0, A, None) == -2     # 15*16 < 256
     assert f(d, A, 32, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 0, None, 0, A, None) == -3    # group 32 > 16
     assert f(d, A, 8, A, A, A, 16, A, 1, 256, None, 1., -1., 1., 0, None, 0, A, None) == -7
+    assert f(d, A, 8, A, A, A, 16, A, 1, 256, None, 1., 1., -1., 0, None, 0, A, None) == -7     # sm_scale < 0
+    assert f(d, A, 8, A, A, A, 16, A, 1, 256, None, 1., 1., float("inf"), 0, None, 0, A, None) == -7
     assert f(d, A, 8, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 5, None, 0, A, None) == -2     # 5 splits > 4 tiles
     assert f(d, A, 8, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 2, None, 0, A, None) == -1     # no workspace
     assert f(d, A, 8, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 2, A, 64, A, None) == -4       # too small
@@ -111,6 +113,8 @@ def test_host_validation_codes(lib):
     Ls = _lib.LayerStack(3, A, A, A, A, A, C.cast(sc, C.c_void_p), C.cast(sc, C.c_void_p), A)
     args = (8, A, 16, A, 1, 256, A, A, A, 1., 0, A, 1 << 20, None)
     assert step(d, None, *args) == -1
+    assert step(d, _lib.LayerStack(3, A, A, A, A, A, C.cast(sc, C.c_void_p), C.cast(sc, C.c_void_p), A, 2),
+                *args) == -7                                        # an option bit the library does not know
     assert step(d, _lib.LayerStack(0, A, A, A, A, A, C.cast(sc, C.c_void_p), C.cast(sc, C.c_void_p), A), *args) == -2
     assert step(d, _lib.LayerStack(3, A, A, A, A, A, None, None, A), *args) == -1     # FP8 needs the scales
     assert step(d, _lib.LayerStack(3, A, A, A, A, A, C.cast(bad, C.c_void_p), C.cast(sc, C.c_void_p), A),
@@ -144,5 +148,14 @@ def test_host_validation_codes(lib):
     assert lib.wgemm_workspace_bytes(4, 64, 512, 1) == 0
     assert lib.wgemm_workspace_bytes(4, 64, 512, 2) == 2 * 4 * 64 * 4
     assert 1 <= lib.wgemm_auto_splits(1, 8192, 8192) <= 32
+    # read-rate calibration
+    assert lib.kv_read_stream(A, 0, A, None) == 0
+    assert lib.kv_read_stream(None, 64, A, None) == -1
+    assert lib.kv_read_stream(A, 62, A, None) == -2                           # not a multiple of 4 bytes
+    assert lib.kv_read_stream(A + 4, 64, A, None) == -5
+    assert lib.kv_read_blocks(A, 16, 2048, A, 0, A, None) == 0
+    assert lib.kv_read_blocks(A, 16, 2008, A, 4, A, None) == -2              # block not a multiple of 16 bytes
+    assert lib.kv_read_blocks(A, 16, 2048, None, 4, A, None) == -1
+    assert lib.kv_read_blocks(A + 8, 16, 2048, A, 4, A, None) == -5
     assert lib.paged_decode_attn_workspace_bytes(64, 64, 128, 1) == 0
     assert lib.paged_decode_attn_workspace_bytes(64, 64, 128, 2) == 64 * 64 * 2 * 129 * 4

@@ -184,3 +184,19 @@ def test_group_sizes(kv_dtype):
         c = Case(w, kv_dtype)
         c.fill_device()
         _check(c, c.attend())
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_default_softmax_scale_is_inverse_sqrt_dim(kv_dtype):
+    """sm_scale 0 asks the library for 1/sqrt(D): the output equals, bit for bit, the one with the scale
+    given explicitly as fl32(1/sqrt(128)), and a different scale changes it."""
+    note(f"default softmax scale {kv_dtype}")
+    c = Case(wl.WORKLOADS["tiny"], kv_dtype)
+    c.fill_device()
+    c.sm_scale = float(np.float32(1.0) / np.sqrt(np.float32(128.0)))
+    explicit = c.attend(num_splits=2)
+    c.sm_scale = 0.0
+    default = c.attend(num_splits=2)
+    assert np.array_equal(explicit, default)
+    c.sm_scale = 0.05
+    assert not np.array_equal(c.attend(num_splits=2), default)

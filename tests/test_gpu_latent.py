@@ -79,16 +79,17 @@ def test_latent_page16_and_abort(kv_dtype):
     assert not got[2].any() and got[0].any()
 
 
-@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
-def test_latent_full_size_sampled(kv_dtype):
-    """64 requests x 4096 tokens, 128 heads, page 64, 8192-page pool, in the library's default split."""
-    w = wl.WORKLOADS["latent"]
-    note(f"latent full size {kv_dtype}")
+@pytest.mark.parametrize("batch,kv_dtype", [(64, "fp8"), (64, "bf16"), (16, "fp8"), (16, "bf16")])
+def test_latent_full_size_sampled(batch, kv_dtype):
+    """B requests x 4096 tokens, 128 heads, page 64, 8192-page pool, in the library's default split: at
+    64 requests the 128-head kernel, at 16 the FP8 cache's wave-pair kernel (8 splits of 512 tokens)."""
+    w = wl.WORKLOADS["latent"].with_(batch=batch)
+    note(f"latent full size B={batch} {kv_dtype}")
     c = Case(w, kv_dtype, oracle_fill=False)
     assert c.d_k_scale == float(c.o_k_scale)
     c.fill_device()
     got = _latent_attend(c)
-    for r in (0, 31, 63):
+    for r in sorted({0, batch // 2 - 1, batch - 1}):
         ref = c.oracle_request(r)
         err = float(np.max(attention.row_rel_error(codec.f64_from_bf16(got[r]), ref)))
         note(f"  request {r}: row error {err:.3e}")

@@ -98,6 +98,16 @@ class Stack:
         self.dv_new = None if latent else dev(np.stack(self.v_new))
         self.max_ctx = int(lens.max())
         self.latent, self.elt = latent, elt
+        B, Hq = w.batch, w.num_q_heads
+        self.splits = splits
+        if splits == 0 and latent:
+            splits = kv.paged_decode_attn_latent_auto_splits(B, Hq, self.max_ctx)
+        elif splits == 0:
+            splits = kv.paged_decode_attn_auto_splits(B, w.num_kv_heads, self.max_ctx)
+        n = kv.paged_decode_attn_workspace_bytes(B, Hq, w.v_dim, splits)
+        self.ws = torch.empty(max(n, 16) // 4 + 4, dtype=torch.float32, device="cuda")
+        self.out = torch.empty((LAYERS, B, Hq, w.v_dim), dtype=torch.int16, device="cuda")
+        self.flags = torch.full((B,), -1, dtype=torch.int32, device="cuda")
 
     def layer_pools_match(self, l):
         """Layer l's device pools, mapped to logical order, equal the oracle's element by element."""
@@ -110,25 +120,15 @@ class Stack:
             return True
         v = layout.from_device(host(self.dvp[l], self.et), "v", st["v_pool"].shape, self.elt)
         return np.array_equal(v, st["v_pool"])
-        B, Hq = w.batch, w.num_q_heads
-        self.splits = splits
-        if splits == 0 and latent:
-            splits = kv.paged_decode_attn_latent_auto_splits(B, Hq, self.max_ctx)
-        elif splits == 0:
-            splits = kv.paged_decode_attn_auto_splits(B, w.num_kv_heads, self.max_ctx)
-        n = kv.paged_decode_attn_workspace_bytes(B, Hq, w.v_dim, splits)
-        self.ws = torch.empty(max(n, 16) // 4 + 4, dtype=torch.float32, device="cuda")
-        self.out = torch.empty((LAYERS, B, Hq, w.v_dim), dtype=torch.int16, device="cuda")
-        self.flags = torch.full((B,), -1, dtype=torch.int32, device="cuda")
 
-    def run(self, tracker=True):
+    def run(self, tracker=True, fused=False):
         kv.decode_step_layers(self.desc, self.kv_dtype, self.dkp, self.dvp, self.dpt, self.dlens, self.max_ctx,
                               self.dq, self.dk_new, self.dv_new, self.out,
                               page_tags=self.dtags if tracker else None, expected_tags=self.dexp if tracker else None,
                               abort_flags=self.flags if tracker else None,
                               k_scales=self.ks if self.kv_dtype == "fp8" else None,
                               v_scales=self.vs if self.kv_dtype == "fp8" and not self.latent else None,
-                              sm_scale=self.sm_scale, num_splits=self.splits, workspace=self.ws)
+                              sm_scale=self.sm_scale, num_splits=self.splits, workspace=self.ws, fused_check=fused)
 
     def oracle(self, tracker=True):
         B = self.w.batch
@@ -136,12 +136,15 @@ class Stack:
                                        (self.lens - 1).astype(np.int32), tracker=tracker)
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("latent", [False, True])
 @pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
-def test_layer_stack_step_matches_oracle(kv_dtype, latent):
-    note(f"layer stack {kv_dtype} latent={latent}")
+def test_layer_stack_step_matches_oracle(kv_dtype, latent, fused):
+    """The step over a layer stack with the tag check as its own launch (default) or inside layer 0's
+    attention launch (fused): flags, every layer's pools and rows against the oracle's multi-layer step."""
+    note(f"layer stack {kv_dtype} latent={latent} fused={fused}")
     s = Stack(kv_dtype, latent)
-    s.run()
+    s.run(fused=fused)
     torch.cuda.synchronize()
     o_flags, o_outs = s.oracle()
     g_flags = host(s.flags, np.uint32)
@@ -199,21 +202,22 @@ def test_layer_stack_no_op_tracker(kv_dtype, latent):
         assert g_out[l, 1].any() and g_out[l, 6].any()
 
 
-@pytest.mark.parametrize("kv_dtype,latent", [("fp8", False), ("bf16", False), ("fp8", True)])
-def test_layer_stack_graph_replays_match_eager(kv_dtype, latent):
-    note(f"layer stack graph {kv_dtype} latent={latent}")
+@pytest.mark.parametrize("kv_dtype,latent,fused", [("fp8", False, False), ("bf16", False, False),
+                                                   ("fp8", True, False), ("fp8", False, True)])
+def test_layer_stack_graph_replays_match_eager(kv_dtype, latent, fused):
+    note(f"layer stack graph {kv_dtype} latent={latent} fused={fused}")
     s = Stack(kv_dtype, latent)
-    s.run()
+    s.run(fused=fused)
     torch.cuda.synchronize()
     want_out, want_flags, want_k = s.out.clone(), s.flags.clone(), s.dkp.clone()
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        s.run()
+        s.run(fused=fused)
     torch.cuda.current_stream().wait_stream(side)
     with torch.cuda.graph(g):
-        s.run()
+        s.run(fused=fused)
     junk = torch.empty(1 << 20, dtype=torch.float32, device="cuda")
     for i in range(4):
         s.out.fill_(0x5555)
