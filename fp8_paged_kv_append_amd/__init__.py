@@ -22,7 +22,7 @@ from ._lib import (FLAG_BAD_PAGE, FLAG_TAG_MISMATCH, KVFP8_ERR_NOSPACE, READ_SIN
 __all__ = ["KvFp8Error", "PoolDesc", "pool_desc", "kv_absmax_bf16", "kv_scale_from_absmax", "calibrate_scale",
            "kv_append_fp8", "kv_append_bf16", "kv_tag_check", "kv_tag_check_append_fp8",
            "kv_tag_check_append_bf16", "paged_decode_attn_workspace_bytes",
-           "paged_decode_attn_auto_splits", "paged_decode_attn_fp8", "paged_decode_attn_bf16",
+           "paged_decode_attn_auto_splits", "paged_decode_attn_fp8", "paged_decode_attn_bf16", "paged_decode_attn_fp8_noalloc",
            "paged_decode_attn_latent_auto_splits", "paged_decode_attn_latent_fp8",
            "paged_decode_attn_latent_bf16", "kv_gather_fp8", "kv_gather_bf16", "decode_step", "decode_step_layers", "PageAllocator",
            "w4_quantize_bf16", "w8_quantize_bf16", "wgemm_auto_splits", "wgemm_workspace_bytes", "w4a16_gemm",
@@ -232,6 +232,19 @@ def paged_decode_attn_fp8(desc: PoolDesc, q, k_pool, v_pool, page_table, ctx_len
         int(max_ctx_len), _ptr(abort_flags, _U32, "abort_flags", True), float(k_scale), float(v_scale),
         float(sm_scale), int(num_splits), ws, wsb, _ptr(out, _BF16, "out"), _stream(stream)),
         "paged_decode_attn_fp8")
+
+
+def paged_decode_attn_fp8_noalloc(desc: PoolDesc, q, k_pool, v_pool, page_table, ctx_lens, max_ctx_len: int, out,
+                                  abort_flags=None, *, k_scale: float, v_scale: float, sm_scale: float = 0.0,
+                                  num_splits: int = 0, stream=None):
+    """paged_decode_attn_fp8 with the split partials in the library's own device scratch (no workspace)."""
+    B, Hq, D = q.shape
+    _check(lib().paged_decode_attn_fp8_noalloc(
+        desc, _ptr(q, _BF16, "q"), Hq, _ptr(k_pool, _U8, "k_pool"), _ptr(v_pool, _U8, "v_pool"),
+        _ptr(page_table, _I32, "page_table"), page_table.shape[1], _ptr(ctx_lens, _I32, "ctx_lens"), B,
+        int(max_ctx_len), _ptr(abort_flags, _U32, "abort_flags", True), float(k_scale), float(v_scale),
+        float(sm_scale), int(num_splits), _ptr(out, _BF16, "out"), _stream(stream)),
+        "paged_decode_attn_fp8_noalloc")
 
 
 def paged_decode_attn_bf16(desc: PoolDesc, q, k_pool, v_pool, page_table, ctx_lens, max_ctx_len: int, out,

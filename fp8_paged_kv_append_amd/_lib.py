@@ -15,6 +15,7 @@ KVFP8_ERR_NOSPACE = -8
 FLAG_TAG_MISMATCH = 1
 FLAG_BAD_PAGE = 2
 READ_SINK_WORDS = 2048
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class PoolDesc(C.Structure):
@@ -57,6 +58,8 @@ PROTOTYPES = {
                                         _f32, _i32, _p, _sz, _p, _p]),
     "paged_decode_attn_bf16": (C.c_int, [_desc, _p, _i32, _p, _p, _p, _i32, _p, _i32, _i32, _p, _f32, _i32,
                                          _p, _sz, _p, _p]),
+    "paged_decode_attn_fp8_noalloc": (C.c_int, [_desc, _p, _i32, _p, _p, _p, _i32, _p, _i32, _i32, _p, _f32, _f32,
+                                                _f32, _i32, _p, _p]),
     "paged_decode_attn_latent_auto_splits": (_i32, [_i32, _i32, _i32]),
     "paged_decode_attn_latent_fp8": (C.c_int, [_desc, _p, _i32, _p, _p, _i32, _p, _i32, _i32, _p, _f32, _f32, _i32,
                                                _p, _sz, _p, _p]),

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/kvfp8.h"
 #include "kvfp8_internal.h"
 
@@ -421,6 +423,34 @@ int decode_step_common(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* lay
   return KVFP8_OK;
 }
 
+// ---- the attention scratch of the allocation-free entry point
+// Split partials (fp32 o and lse) of paged_decode_attn_fp8_noalloc live in this file-scope array
+// instead of a caller's workspace.  Host code never uses its name as an address: each device's copy is
+// found once with hipGetSymbolAddress (that device current) and that pointer is what the kernels get.
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+
+}  // namespace
+
+static __device__ __align__(256) float scratch[KVFP8_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KVFP8_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return KVFP8_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return KVFP8_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVFP8_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -559,6 +589,26 @@ int paged_decode_attn_bf16(const kvfp8_pool_desc* desc, const uint16_t* q, int32
                            size_t workspace_bytes, uint16_t* out, hipStream_t stream) {
   return attn_common(desc, q, num_q_heads, k_pool, v_pool, page_table, pt_stride, ctx_lens, batch, max_ctx_len,
                      abort_flags, false, 1.f, 1.f, sm_scale, num_splits, workspace, workspace_bytes, out, stream);
+}
+
+int paged_decode_attn_fp8_noalloc(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads,
+                                  const uint8_t* k_pool, const uint8_t* v_pool, const int32_t* page_table,
+                                  int32_t pt_stride, const int32_t* ctx_lens, int32_t batch, int32_t max_ctx_len,
+                                  const uint32_t* abort_flags, float k_scale, float v_scale, float sm_scale,
+                                  int32_t num_splits, uint16_t* out, hipStream_t stream) {
+  // every argument checked (with the scratch as the workspace: a split count whose partials exceed it
+  // fails with KVFP8_ERR_WORKSPACE) before the scratch address is looked up or anything launched
+  static char probe alignas(256);
+  int st = attn_common(desc, q, num_q_heads, k_pool, v_pool, page_table, pt_stride, ctx_lens, batch, max_ctx_len,
+                       abort_flags, true, k_scale, v_scale, sm_scale, num_splits, &probe,
+                       KVFP8_NOALLOC_SCRATCH_BYTES, out, stream, false);
+  if (st || batch == 0) return st;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st) return st;
+  return attn_common(desc, q, num_q_heads, k_pool, v_pool, page_table, pt_stride, ctx_lens, batch, max_ctx_len,
+                     abort_flags, true, k_scale, v_scale, sm_scale, num_splits, ws, KVFP8_NOALLOC_SCRATCH_BYTES, out,
+                     stream);
 }
 
 int32_t paged_decode_attn_latent_auto_splits(int32_t batch, int32_t num_q_heads, int32_t max_ctx_len) {

@@ -196,6 +196,28 @@ int paged_decode_attn_bf16(const kvfp8_pool_desc* desc, const uint16_t* q, int32
                            float sm_scale, int32_t num_splits, void* workspace,
                            size_t workspace_bytes, uint16_t* out, hipStream_t stream);
 
+/* ---------------------------------------------------------------- attention with no workspace
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation, arguments, kernels and results as paged_decode_attn_fp8, with
+ * the split partials kept in a scratch array of KVFP8_NOALLOC_SCRATCH_BYTES
+ * that the library holds in device memory (one per GPU it runs on, for the
+ * life of the process) instead of a caller's workspace.  The call allocates
+ * nothing.  The current device must be the one `stream` belongs to; the first
+ * call on a device looks the array up there (hipGetSymbolAddress).  A split
+ * count whose partials would exceed the array
+ * (paged_decode_attn_workspace_bytes(B, Hq, 128, splits) bytes) is rejected
+ * with KVFP8_ERR_WORKSPACE before anything is enqueued.  Every call on a
+ * device shares that device's array: calls that overlap on one GPU (other
+ * streams, other threads) race on it; calls in one stream's order do not.
+ * Nothing in the array needs clearing between calls. */
+#define KVFP8_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int paged_decode_attn_fp8_noalloc(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads,
+                                  const uint8_t* k_pool, const uint8_t* v_pool, const int32_t* page_table,
+                                  int32_t pt_stride, const int32_t* ctx_lens, int32_t batch, int32_t max_ctx_len,
+                                  const uint32_t* abort_flags, float k_scale, float v_scale, float sm_scale,
+                                  int32_t num_splits, uint16_t* out, hipStream_t stream);
+
 /* ---------------------------------------------------------------- latent (MLA-style) cache  [Q]
  * One cached vector c_t of width Dl = 576 per token, shared by every query
  * head (the pool: latent layout, num_kv_heads = 1, head_dim = 576,

@@ -104,6 +104,14 @@ def test_host_validation_codes(lib):
     assert f(d, A, 8, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 5, None, 0, A, None) == -2     # 5 splits > 4 tiles
     assert f(d, A, 8, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 2, None, 0, A, None) == -1     # no workspace
     assert f(d, A, 8, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 2, A, 64, A, None) == -4       # too small
+    # the allocation-free form: partials beyond its scratch are refused before anything else happens
+    na = lib.paged_decode_attn_fp8_noalloc
+    d8 = _lib.PoolDesc(16, 16, 8, 128, 128)
+    assert 64 * 64 * 4 * 129 * 4 > _lib.NOALLOC_SCRATCH_BYTES >= 64 * 64 * 2 * 129 * 4
+    assert na(d8, A, 64, A, A, A, 16, A, 64, 256, None, 1., 1., 1., 4, A, None) == -4
+    assert na(d8, A, 64, A, A, A, 16, A, 64, 256, None, 1., 1., 1., 5, A, None) == -2       # 5 splits > 4 tiles
+    assert na(d8, A, 64, A, A, A, 16, A, 0, 256, None, 1., 1., 1., 0, A, None) == 0        # empty batch
+    assert na(d8, None, 64, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 0, A, None) == -1
     d64 = _lib.PoolDesc(16, 16, 1, 64, 64)
     assert f(d64, A, 8, A, A, A, 16, A, 1, 256, None, 1., 1., 1., 0, None, 0, A, None) == -3
     # one step over a layer stack: every layer checked before anything is enqueued
