@@ -188,7 +188,7 @@ class Cache:
         # the public bound, which covers both
         self.req_splits = ws.splits
         nb = kv.paged_decode_attn_workspace_bytes(w.batch, w.num_q_heads, w.v_dim, self.splits)
-        self.wsp = torch.empty(max(nb // 4, 4), dtype=torch.float32, device="cuda")
+        self.wsp = torch.zeros(max(nb // 4, 4), dtype=torch.float32, device="cuda")  # zeroed once
         torch.cuda.synchronize()
 
     def _c(self, i):
@@ -262,6 +262,16 @@ class Timer:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
+    def warm(self, fn, seconds=1.0):
+        """Run fn back to back for about `seconds`, so that clocks have left their idle states."""
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(50):
+                fn(i)
+                i += 1
+            self.torch.cuda.synchronize()
+
     def per_call(self, fn):
         """ms of each of `steps` calls (an event before and after every call)."""
         torch = self.torch
@@ -326,7 +336,8 @@ def attainable(torch, kv, ws, cache, timer):
     nbytes = ws.kv_elems * (1 if cache.fp8 else 2)
     sink = torch.zeros(kv.READ_SINK_WORDS, dtype=torch.int32, device="cuda")
     bufs = [torch.empty(nbytes // 4 + 4, dtype=torch.int32, device="cuda").fill_(i + 1) for i in range(2)]
-    t_stream = timer.back_to_back(lambda i: kv.kv_read_stream(bufs[i % 2], sink, nbytes=nbytes))
+    t_stream = min(timer.back_to_back(lambda i: kv.kv_read_stream(bufs[i % 2], sink, nbytes=nbytes))
+                   for _ in range(3))
     del bufs
     blk = w.page_size * w.head_dim * (1 if cache.fp8 else 2)
 
@@ -337,12 +348,13 @@ def attainable(torch, kv, ws, cache, timer):
         if vp is not None:
             kv.kv_read_blocks(vp, blk, ids, sink)
 
-    t_blocks = timer.back_to_back(blocks)
+    t_blocks = min(timer.back_to_back(blocks) for _ in range(3))
     return {"stream_gbs": round(nbytes / (t_stream * 1e-3) / 1e9, 1),
             "page_blocks_gbs": round(nbytes / (t_blocks * 1e-3) / 1e9, 1),
             "bytes": nbytes, "block_bytes": blk,
             "note": "kv_read_stream over the step's KV byte count (contiguous), and kv_read_blocks over the "
-                    "same (page, kv head) blocks of K and V the attention reads (two launches per step)"}
+                    "same (page, kv head) blocks of K and V the attention reads (two launches per step); "
+                    "the best of three back-to-back runs of each"}
 
 
 def capacity_admission(kv, w, kvd, budget_bytes, seed=0):
@@ -482,6 +494,7 @@ def main():
         c = Cache(ws, kvd, torch, kv)
         elt = 1 if kvd == "fp8" else 2
         r = {"kv_bytes": ws.kv_elems * elt, "splits": c.splits, "page_sets": c.n}
+        timer.warm(lambda i: c.step(i, args.mode))
         r["step_ms"] = timer.back_to_back(lambda i: c.step(i, args.mode))
         per = timer.per_call(lambda i: c.step(i, args.mode))
         r["step_ms_median_events"] = float(np.median(per))

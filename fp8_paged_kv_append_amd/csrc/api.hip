@@ -11,6 +11,8 @@
 
 using namespace kvfp8;
 
+static_assert(KVFP8_READ_SINK_WORDS == kReadSinkWords, "checksum words of the read-rate kernels");
+
 namespace {
 
 constexpr int kHeadDim = 128;
@@ -152,8 +154,9 @@ int attn_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_he
     if (workspace == nullptr) return KVFP8_ERR_NULL;
     if (workspace_bytes < need) return KVFP8_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KVFP8_ERR_ALIGN;
+    const size_t rows = (size_t)batch * num_q_heads * splits;
     a.o_part = reinterpret_cast<float*>(workspace);
-    a.lse_part = a.o_part + (size_t)batch * num_q_heads * splits * kHeadDim;
+    a.lse_part = a.o_part + rows * kHeadDim;
   }
   a.q = q;
   a.k_pool = k_pool;
@@ -564,6 +567,7 @@ int kv_decode_step_bf16(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* la
 size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t v_dim, int32_t num_splits) {
   if (batch <= 0 || num_q_heads <= 0 || v_dim <= 0 || num_splits <= 1) return 0;
   const size_t rows = (size_t)batch * num_q_heads * num_splits;
+  // fp32 partials and lse of every (request, head, split)
   return rows * (size_t)v_dim * sizeof(float) + rows * sizeof(float);
 }
 
@@ -642,9 +646,8 @@ int kv_read_stream(const void* src, size_t bytes, uint32_t* sink, hipStream_t st
   if (!src || !sink) return KVFP8_ERR_NULL;
   if (bytes % 4 != 0) return KVFP8_ERR_SHAPE;
   if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return KVFP8_ERR_ALIGN;
-  const uint64_t want = (bytes / 16 + 255) / 256;  // one 16-byte load per thread at least
-  const int blocks = (int)(want < KVFP8_READ_SINK_WORDS ? (want < 1 ? 1 : want) : KVFP8_READ_SINK_WORDS);
-  return launch_read_stream(src, bytes, sink, blocks, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
+  if (bytes / 16 > ((uint64_t)1 << 40)) return KVFP8_ERR_SHAPE;  // the grid's block count stays below 2^31
+  return launch_read_stream(src, bytes, sink, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
 }
 
 int kv_read_blocks(const void* base, int64_t num_blocks, int64_t block_bytes, const int32_t* ids, int64_t n_ids,
@@ -654,12 +657,10 @@ int kv_read_blocks(const void* base, int64_t num_blocks, int64_t block_bytes, co
   if (!base || !ids || !sink) return KVFP8_ERR_NULL;
   if (!aligned16(base) || (reinterpret_cast<uintptr_t>(ids) & 3u) || (reinterpret_cast<uintptr_t>(sink) & 3u))
     return KVFP8_ERR_ALIGN;
-  const int64_t steps = (block_bytes / 16 + 63) / 64;  // 1 KiB steps a wave takes per block
-  const int64_t want = (n_ids * steps + 3) / 4;          // four waves per thread block
-  const int blocks = (int)(want < KVFP8_READ_SINK_WORDS ? want : KVFP8_READ_SINK_WORDS);
-  return launch_read_blocks(base, num_blocks, ids, n_ids, block_bytes, sink, blocks, stream) == hipSuccess
-             ? KVFP8_OK
-             : KVFP8_ERR_HIP;
+  const int64_t pieces = (block_bytes / 16 + 63) / 64;  // 1 KiB pieces per block
+  if (n_ids > ((int64_t)1 << 40) / pieces) return KVFP8_ERR_SHAPE;  // the grid's block count stays below 2^31
+  return launch_read_blocks(base, num_blocks, ids, n_ids, block_bytes, sink, stream) == hipSuccess ? KVFP8_OK
+                                                                                                    : KVFP8_ERR_HIP;
 }
 
 int kv_gather_fp8(const kvfp8_pool_desc* desc, const uint8_t* k_pool, const uint8_t* v_pool, const int32_t* tok_req,

@@ -128,8 +128,9 @@ hipError_t launch_tag_check(const TagArgs& a, hipStream_t stream);
 hipError_t launch_check_append(const TagArgs& c, const AppendArgs& a, bool fp8, hipStream_t stream);
 constexpr int kCheckAppendMaxPairs = 8 * 256;  // (Hkv*D)/2 and (Hkv*Dv)/2 limit of the fused kernel
 hipError_t launch_absmax(const uint16_t* x, int64_t n, uint32_t* out, hipStream_t stream);
-hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
+constexpr int kReadSinkWords = 2048;  // checksum words of the read-rate kernels
+hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_read_blocks(const void* base, int64_t num_blocks, const int32_t* ids, int64_t n_ids,
-                              int64_t block_bytes, uint32_t* sink, int blocks, hipStream_t stream);
+                              int64_t block_bytes, uint32_t* sink, hipStream_t stream);
 
 }  // namespace kvfp8

@@ -173,9 +173,10 @@ int kv_tag_check_append_bf16(const kvfp8_pool_desc* desc, uint16_t* k_pool, uint
  *   pages and gets zero rows [T].  A page id outside [0,P) met while reading
  *   also zeroes the request's rows (memory safety when the tracker is off).
  *   num_splits: 0 = chosen by the library; otherwise at most
- *   ceil(max_ctx_len/64).  workspace: fp32 partials, at least
+ *   ceil(max_ctx_len/64).  workspace: at least
  *   paged_decode_attn_workspace_bytes(...) bytes for the split count used
- *   (0 when it is 1; then workspace may be NULL).
+ *   (0 when it is 1; then workspace may be NULL).  Calls that share a
+ *   workspace must be ordered (one stream).
  *   sm_scale: the softmax scale; 0 selects 1/sqrt(D) (the pages give none).
  *   k_scale, v_scale and a non-zero sm_scale must be finite and > 0. */
 size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t v_dim,
@@ -343,9 +344,9 @@ int kv_page_alloc_tags(const void* state, uint32_t* tags);
  * against which the attention kernels' KV-read rates are also reported (no
  * page describes them; they compute nothing of the method).  Both read every
  * byte once with 16-byte non-temporal loads and fold the 32-bit words read
- * into XOR checksums: sink (device, at least KVFP8_READ_SINK_WORDS uint32
- * words, 4-byte aligned) receives one word per thread block of the launch, and
- * the XOR of all KVFP8_READ_SINK_WORDS words -- after the caller zeroes them --
+ * into XOR checksums: every thread block of the launch XORs its fold into one
+ * of the KVFP8_READ_SINK_WORDS uint32 words of sink (device, 4-byte aligned),
+ * so that, with the words zeroed by the caller beforehand, the XOR of them all
  * equals the XOR of every 32-bit word read.
  *   kv_read_stream: bytes consecutive bytes at src (16-byte aligned; bytes a
  *     multiple of 4).

@@ -143,7 +143,7 @@ class Case:
 
     def workspace(self, splits):
         n = kv.paged_decode_attn_workspace_bytes(self.w.batch, self.w.num_q_heads, self.w.v_dim, splits)
-        return torch.empty(max(n, 16) // 4 + 4, dtype=torch.float32, device="cuda")
+        return torch.zeros(max(n, 16) // 4 + 4, dtype=torch.float32, device="cuda")   # zeroed once, as the library asks
 
     def attend(self, flags=None, num_splits=0, max_ctx=None):
         out = self.out_tensor()

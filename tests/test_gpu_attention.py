@@ -200,3 +200,38 @@ def test_default_softmax_scale_is_inverse_sqrt_dim(kv_dtype):
     assert np.array_equal(explicit, default)
     c.sm_scale = 0.05
     assert not np.array_equal(c.attend(num_splits=2), default)
+
+
+@pytest.mark.parametrize("kv_dtype,splits", [("fp8", 16), ("bf16", 16), ("fp8", 62), ("fp8", 3), ("fp8", 0)])
+def test_workspace_reuse_never_mixes_launches(kv_dtype, splits):
+    """Launches alternating between two query sets share one workspace (partials, and with the library's
+    split choice the per-request split counts): every result equals, bit for bit, the one computed with a
+    fresh workspace, so no merge reads what another launch left."""
+    w = wl.WORKLOADS["gqa_batch"].with_(batch=3, num_pages=1600, ctx_lo=1, ctx_hi=4000)
+    lens = np.array([4000, 2500, 300], dtype=np.int32)
+    note(f"workspace reuse, alternating queries {kv_dtype} splits={splits}")
+    c = Case(w, kv_dtype, lens=lens)
+    c.fill_device()
+    q1 = c.dq
+    q2 = dev(wl.queries(w.with_(seed=w.seed + 101)))
+    refs = []
+    for q in (q1, q2):
+        c.dq = q
+        refs.append(c.attend(num_splits=splits))
+    assert not np.array_equal(refs[0], refs[1])
+    c.dq = q1
+    _check(c, refs[0])
+    n = splits or kv.paged_decode_attn_auto_splits(w.batch, w.num_kv_heads, c.max_ctx)
+    ws = c.workspace(n)
+    out = c.out_tensor()
+    for i in range(40):
+        q = (q1, q2)[i % 2]
+        if kv_dtype == "fp8":
+            kv.paged_decode_attn_fp8(c.desc, q, c.dkp, c.dvp, c.dpt, c.dlens, c.max_ctx, out, k_scale=c.d_k_scale,
+                                     v_scale=c.d_v_scale, sm_scale=c.sm_scale, num_splits=splits, workspace=ws)
+        else:
+            kv.paged_decode_attn_bf16(c.desc, q, c.dkp, c.dvp, c.dpt, c.dlens, c.max_ctx, out,
+                                      sm_scale=c.sm_scale, num_splits=splits, workspace=ws)
+        if i % 5 == 4 or i < 4:
+            torch.cuda.synchronize()
+            assert np.array_equal(host(out, np.uint16), refs[i % 2]), i

@@ -105,7 +105,7 @@ class Stack:
         elif splits == 0:
             splits = kv.paged_decode_attn_auto_splits(B, w.num_kv_heads, self.max_ctx)
         n = kv.paged_decode_attn_workspace_bytes(B, Hq, w.v_dim, splits)
-        self.ws = torch.empty(max(n, 16) // 4 + 4, dtype=torch.float32, device="cuda")
+        self.ws = torch.zeros(max(n, 16) // 4 + 4, dtype=torch.float32, device="cuda")
         self.out = torch.empty((LAYERS, B, Hq, w.v_dim), dtype=torch.int16, device="cuda")
         self.flags = torch.full((B,), -1, dtype=torch.int32, device="cuda")
 
