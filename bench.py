@@ -78,6 +78,8 @@ def parse():
                    help="time only the FP8 headline (profiling runs: the step, then attention and check alone)")
     p.add_argument("--mode", choices=("separate", "fused"), default="separate",
                    help="step form of the headline (separate: the library's default)")
+    p.add_argument("--warm-seconds", type=float, default=1.0,
+                   help="back-to-back steps before the headline is timed, so that clocks leave their idle states")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after timing, copy a MIB-MiB buffer 3 times (a known-size kernel for HBM counters)")
     return p.parse_args()
@@ -156,8 +158,11 @@ class Cache:
         P = ws.num_pages
         nk = P * w.num_kv_heads * w.page_size * w.head_dim
         nv = P * w.num_kv_heads * w.page_size * w.v_dim
-        kp = torch.zeros(nk, dtype=tdt, device="cuda")
-        vp = None if w.latent else torch.zeros(nv, dtype=tdt, device="cuda")
+        # K and V pools in one allocation (V right after K), so that one read-rate launch covers both
+        kvmem = torch.zeros(nk + (0 if w.latent else nv), dtype=tdt, device="cuda")
+        kp = kvmem[:nk]
+        vp = None if w.latent else kvmem[nk:]
+        self.kvmem = kvmem
         self.desc = kv.pool_desc(P, w.page_size, w.num_kv_heads, w.head_dim, w.v_dim)
         dv = None if w.latent else ws.dv
         if self.fp8:
@@ -173,8 +178,9 @@ class Cache:
                 kv.kv_append_bf16(self.desc, kp, vp, ws.dk, dv, ws.dreq, ws.dpos, ws.dpt[c])
         self.kps, self.vps = [kp], [vp]
         for _ in range(pool_clones - 1):
-            self.kps.append(kp.clone())
-            self.vps.append(None if vp is None else vp.clone())
+            mem = kvmem.clone()
+            self.kps.append(mem[:nk])
+            self.vps.append(None if vp is None else mem[nk:])
         self.n = max(ws.copies, pool_clones)
         self.flags = torch.zeros((self.n, w.batch), dtype=torch.int32, device="cuda")
         self.out = torch.empty((w.batch, w.num_q_heads, w.v_dim), dtype=torch.int16, device="cuda")
@@ -340,21 +346,20 @@ def attainable(torch, kv, ws, cache, timer):
                    for _ in range(3))
     del bufs
     blk = w.page_size * w.head_dim * (1 if cache.fp8 else 2)
+    # the K blocks' ids, then the V blocks' (the V pool follows the K pool in memory): one launch
+    v_off = cache.kps[0].numel() * cache.kps[0].element_size() // blk
+    ids_kv = [torch.cat([ids, ids + v_off]) if cache.vps[0] is not None else ids for ids in ws.block_ids]
 
     def blocks(i):
-        kp, vp, _, _, _ = cache._c(i)
-        ids = ws.block_ids[i % ws.copies]
-        kv.kv_read_blocks(kp, blk, ids, sink)
-        if vp is not None:
-            kv.kv_read_blocks(vp, blk, ids, sink)
+        kv.kv_read_blocks(cache.kvmem, blk, ids_kv[i % ws.copies], sink)
 
     t_blocks = min(timer.back_to_back(blocks) for _ in range(3))
     return {"stream_gbs": round(nbytes / (t_stream * 1e-3) / 1e9, 1),
             "page_blocks_gbs": round(nbytes / (t_blocks * 1e-3) / 1e9, 1),
             "bytes": nbytes, "block_bytes": blk,
             "note": "kv_read_stream over the step's KV byte count (contiguous), and kv_read_blocks over the "
-                    "same (page, kv head) blocks of K and V the attention reads (two launches per step); "
-                    "the best of three back-to-back runs of each"}
+                    "same (page, kv head) blocks of K and V the attention reads, in one launch; the best of "
+                    "three back-to-back runs of each"}
 
 
 def capacity_admission(kv, w, kvd, budget_bytes, seed=0):
@@ -403,6 +408,19 @@ def stored_traffic(workload, mode):
     if h.hexdigest() != d["kernel_sources_sha256"] or d["workload"] != workload or d.get("mode") != mode:
         return None
     return d
+
+
+def copy_calibration(torch, mib):
+    """Three device copies of mib MiB: a kernel of known traffic that scales the HBM counters."""
+    if not mib:
+        return 0
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return n
 
 
 def cpu_model():
@@ -494,13 +512,15 @@ def main():
         c = Cache(ws, kvd, torch, kv)
         elt = 1 if kvd == "fp8" else 2
         r = {"kv_bytes": ws.kv_elems * elt, "splits": c.splits, "page_sets": c.n}
-        timer.warm(lambda i: c.step(i, args.mode))
+        timer.warm(lambda i: c.step(i, args.mode), args.warm_seconds)
         r["step_ms"] = timer.back_to_back(lambda i: c.step(i, args.mode))
+        # the attention launch alone (reading the flags the steps left): the best of three back-to-back
+        # blocks, a kernel time inside the step's
+        r["attn_ms"] = min(timer.back_to_back(lambda i: c.attend(i)) for _ in range(3))
+        r["check_append_ms"] = min(timer.back_to_back(c.check_append) for _ in range(3))
         per = timer.per_call(lambda i: c.step(i, args.mode))
         r["step_ms_median_events"] = float(np.median(per))
         r["step_ms_p95_events"] = float(np.percentile(per, 95))
-        r["attn_ms"] = timer.back_to_back(lambda i: c.attend(i))
-        r["check_append_ms"] = timer.back_to_back(c.check_append)
         c.flags_ok()
         if full:
             other = "fused" if args.mode == "separate" else "separate"
@@ -679,6 +699,7 @@ def main():
         torch.cuda.empty_cache()
         if args.fp8_only_steps:
             f8 = results["fp8"]
+            copy_calibration(torch, args.copy_calibration)
             print(json.dumps({"metric": METRIC, "mode": args.mode, "steps": args.steps,
                               "ms_per_step": round(f8["step_ms"], 5), "attn_ms": round(f8["attn_ms"], 5),
                               "check_append_ms": round(f8["check_append_ms"], 5),
@@ -844,7 +865,7 @@ def main():
                      "kernel": "attn_gqa_split_kernel<fp8> (paged_decode_attn_fp8 reading the check's flags)",
                      "attn_ms": round(f8["attn_ms"], 5),
                      "timing": "back-to-back attention launches between two events on the launch stream, rotating "
-                               "page sets (a kernel time within the step's)",
+                               "page sets, the best of three blocks (a kernel time within the step's)",
                      "pct_attainable": round(100 * attn_gbs / att["page_blocks_gbs"], 2)},
         "attainable_read": att,
         "step_breakdown_ms": {"check_append": round(f8["check_append_ms"], 5), "attention": round(f8["attn_ms"], 5),
@@ -883,13 +904,7 @@ def main():
     if extra:
         line["other_workloads"] = extra
     if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        line["copy_calibration_bytes"] = n
+        line["copy_calibration_bytes"] = copy_calibration(torch, args.copy_calibration)
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_sample} requests")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
