@@ -5,7 +5,8 @@ import ctypes as C
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvfp8.so")
+# KVFP8_LIB names another build of the library (the host-sanitizer test loads one that way)
+LIB_PATH = os.environ.get("KVFP8_LIB") or os.path.join(_HERE, "libkvfp8.so")
 
 KVFP8_OK = 0
 STATUS = {0: "KVFP8_OK", -1: "KVFP8_ERR_NULL", -2: "KVFP8_ERR_SHAPE", -3: "KVFP8_ERR_UNSUPPORTED",

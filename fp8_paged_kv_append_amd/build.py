@@ -36,9 +36,11 @@ def flags() -> list:
     ]
 
 
-def build(verbose: bool = False, extra: list | None = None) -> str:
+def build(verbose: bool = False, extra: list | None = None, out: str | None = None) -> str:
+    """Compile every source into libkvfp8.so (or `out`), with `extra` hipcc flags appended."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+    target = out or LIB
+    tmp = target + ".tmp"
     cmd = [hipcc()] + flags() + (extra or []) + srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -47,8 +49,14 @@ def build(verbose: bool = False, extra: list | None = None) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
     if verbose and r.stderr.strip():
         print(r.stderr, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, target)
+    return target
+
+
+# Host-code sanitizers (AddressSanitizer, UndefinedBehaviorSanitizer) on the CPU side only: the device code
+# is compiled as usual.  The result needs the clang ASan runtime preloaded into the process that loads it.
+HOST_SANITIZER_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                        "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-shared-libsan", "-g"]
 
 
 if __name__ == "__main__":
