@@ -354,12 +354,15 @@ def attainable(torch, kv, ws, cache, timer):
         kv.kv_read_blocks(cache.kvmem, blk, ids_kv[i % ws.copies], sink)
 
     t_blocks = min(timer.back_to_back(blocks) for _ in range(3))
-    return {"stream_gbs": round(nbytes / (t_stream * 1e-3) / 1e9, 1),
-            "page_blocks_gbs": round(nbytes / (t_blocks * 1e-3) / 1e9, 1),
+    stream_gbs = nbytes / (t_stream * 1e-3) / 1e9
+    blocks_gbs = nbytes / (t_blocks * 1e-3) / 1e9
+    return {"stream_gbs": round(stream_gbs, 1), "page_blocks_gbs": round(blocks_gbs, 1),
+            "attainable_gbs": round(max(stream_gbs, blocks_gbs), 1),
             "bytes": nbytes, "block_bytes": blk,
             "note": "kv_read_stream over the step's KV byte count (contiguous), and kv_read_blocks over the "
                     "same (page, kv head) blocks of K and V the attention reads, in one launch; the best of "
-                    "three back-to-back runs of each"}
+                    "three back-to-back runs of each; attainable_gbs = the faster of the two, the read rate "
+                    "pct_attainable is taken against"}
 
 
 def capacity_admission(kv, w, kvd, budget_bytes, seed=0):
@@ -837,7 +840,7 @@ def main():
         "ms_per_step": round(f8["step_ms"], 5),
         "steps_per_s": round(1e3 / f8["step_ms"], 1),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "pct_attainable": round(100 * gbs / att["page_blocks_gbs"], 2),
+        "pct_attainable": round(100 * gbs / att["attainable_gbs"], 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -866,7 +869,7 @@ def main():
                      "attn_ms": round(f8["attn_ms"], 5),
                      "timing": "back-to-back attention launches between two events on the launch stream, rotating "
                                "page sets, the best of three blocks (a kernel time within the step's)",
-                     "pct_attainable": round(100 * attn_gbs / att["page_blocks_gbs"], 2)},
+                     "pct_attainable": round(100 * attn_gbs / att["attainable_gbs"], 2)},
         "attainable_read": att,
         "step_breakdown_ms": {"check_append": round(f8["check_append_ms"], 5), "attention": round(f8["attn_ms"], 5),
                               "step": round(f8["step_ms"], 5),

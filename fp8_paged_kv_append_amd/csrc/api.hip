@@ -646,7 +646,8 @@ int kv_read_stream(const void* src, size_t bytes, uint32_t* sink, hipStream_t st
   if (!src || !sink) return KVFP8_ERR_NULL;
   if (bytes % 4 != 0) return KVFP8_ERR_SHAPE;
   if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return KVFP8_ERR_ALIGN;
-  if (bytes / 16 > ((uint64_t)1 << 40)) return KVFP8_ERR_SHAPE;  // the grid's block count stays below 2^31
+  // at most 2^40 16-byte vectors, 2^29 thread blocks of 2048 vectors: inside the grid's 2^31 - 1
+  if (bytes / 16 > ((uint64_t)1 << 40)) return KVFP8_ERR_SHAPE;
   return launch_read_stream(src, bytes, sink, stream) == hipSuccess ? KVFP8_OK : KVFP8_ERR_HIP;
 }
 
@@ -658,7 +659,8 @@ int kv_read_blocks(const void* base, int64_t num_blocks, int64_t block_bytes, co
   if (!aligned16(base) || (reinterpret_cast<uintptr_t>(ids) & 3u) || (reinterpret_cast<uintptr_t>(sink) & 3u))
     return KVFP8_ERR_ALIGN;
   const int64_t pieces = (block_bytes / 16 + 63) / 64;  // 1 KiB pieces per block
-  if (n_ids > ((int64_t)1 << 40) / pieces) return KVFP8_ERR_SHAPE;  // the grid's block count stays below 2^31
+  // at most 2^35 pieces, 2^30 thread blocks of 32 pieces: inside the grid's 2^31 - 1
+  if (n_ids > ((int64_t)1 << 35) / pieces) return KVFP8_ERR_SHAPE;
   return launch_read_blocks(base, num_blocks, ids, n_ids, block_bytes, sink, stream) == hipSuccess ? KVFP8_OK
                                                                                                     : KVFP8_ERR_HIP;
 }

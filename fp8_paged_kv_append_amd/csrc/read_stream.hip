@@ -6,10 +6,11 @@
 //
 // Both are one pass with no loop: every thread issues a fixed number of 16-byte non-temporal loads
 // (all in flight together) and the grid covers the input, so the hardware's dispatcher keeps every CU
-// full.  Measured on MI355X over 1 GiB, this shape streams at ~7.0 TB/s where a grid-stride loop over a
-// fixed 2048 blocks reached ~5.5 TB/s.  Each thread XORs the 32-bit words it reads into one
-// accumulator; a block folds its threads' accumulators with wave shuffles and LDS and XORs the result
-// into sink[blockIdx.x % kSinkWords] (one atomic per block).  Every word of the input is read by
+// full.  Measured on MI355X over the 1.06 GB of a 64 x 8192 decode step, eight loads per thread stream at
+// 6.9 TB/s and read the step's 2 KiB page blocks at 6.35 TB/s (four loads: 6.7 and 6.0; sixteen: 6.8 and
+// 5.9), where a grid-stride loop over a fixed 2048 blocks reached ~5.5 TB/s.  Each thread XORs the
+// 32-bit words it reads into one accumulator; a block folds its threads' accumulators with wave
+// shuffles and LDS and XORs the result into sink[blockIdx.x % kSinkWords] (one atomic per block).  Every word of the input is read by
 // exactly one thread, so the XOR of all sink words equals the XOR of all words read.
 #include "kvfp8_device.h"
 #include "kvfp8_internal.h"
@@ -17,7 +18,7 @@
 namespace kvfp8 {
 
 constexpr int kStreamThreads = 256;
-constexpr int kStreamVecs = 4;  // 16-byte loads per thread
+constexpr int kStreamVecs = 8;  // 16-byte loads per thread
 
 __device__ __forceinline__ u32x4_t ld_nt(const u32x4_t* p) { return __builtin_nontemporal_load(p); }
 
@@ -35,8 +36,8 @@ __device__ __forceinline__ void block_fold_xor(uint32_t acc, uint32_t* sink) {
   }
 }
 
-// Vectors [b * 1024, (b + 1) * 1024) of the n16 16-byte vectors for block b, thread t reading
-// b * 1024 + u * 256 + t; block 0 also reads the tail_words trailing 32-bit words.
+// Vectors [b * 2048, (b + 1) * 2048) of the n16 16-byte vectors for block b, thread t reading
+// b * 2048 + u * 256 + t; block 0 also reads the tail_words trailing 32-bit words.
 __global__ __launch_bounds__(kStreamThreads) void read_stream_kernel(const u32x4_t* src, int64_t n16,
                                                                      const uint32_t* tail, int tail_words,
                                                                      uint32_t* sink) {

@@ -355,7 +355,9 @@ int kv_page_alloc_tags(const void* state, uint32_t* tags);
  *     [0, num_blocks) is skipped); block_bytes a multiple of 16, base 16-byte
  *     aligned.  With ids listing the (page, kv head) blocks a decode step
  *     reads, in the order of its page table, this is the attention's access
- *     pattern without its arithmetic. */
+ *     pattern without its arithmetic.
+ * Sizes beyond 2^44 bytes (kv_read_stream) or 2^35 KiB-pieces of blocks
+ * (kv_read_blocks) return KVFP8_ERR_SHAPE. */
 #define KVFP8_READ_SINK_WORDS 2048
 int kv_read_stream(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 int kv_read_blocks(const void* base, int64_t num_blocks, int64_t block_bytes, const int32_t* ids, int64_t n_ids,
