@@ -335,7 +335,8 @@ def _wgemm(bits, x, w_packed, scales, n, k, y, num_splits, workspace, stream):
 
 
 def w4a16_gemm(x, w_packed, scales, n, k, y, *, num_splits: int = 0, workspace=None, stream=None):
-    """y [M][N] (bf16) = x [M][K] (bf16) times the INT4 weights (packed by w4_quantize_bf16), transposed."""
+    """y [M][N] (bf16) = x [M][K] (bf16) times the INT4 weights (packed by w4_quantize_bf16), transposed.
+    With several splits, `workspace` (wgemm_workspace_bytes) must have been zeroed once before its first use."""
     _wgemm(4, x, w_packed, scales, n, k, y, num_splits, workspace, stream)
 
 

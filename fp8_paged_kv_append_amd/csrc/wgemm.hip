@@ -51,6 +51,7 @@ struct WgemmArgs {
   const uint8_t* w;         // packed codes
   const uint16_t* s;        // bf16 scales [N/16][K/128][16]
   float* part;              // fp32 [splits][M][N] (splits > 1)
+  uint32_t* count;          // finished splits per column group (splits > 1): zero before a launch and after it
   uint16_t* y;              // bf16 [M][N]
   int32_t M, N, K, splits, groups_per_split;
 };
@@ -158,17 +159,15 @@ __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                  c, 0, 0, 0);
 }
 
-// acc += s * (group sum - 136 * sum of the group's activations) for INT4 (the expansion's bias),
-// acc += s * group sum for FP8.
-template <bool W4>
-__device__ __forceinline__ void add_group(f32x4_t& acc, const f32x4_t& accg, float sc, const f32x4_t& xs) {
+// acc += s * group sum.  For INT4 the group's MFMAs start from -136 * (sum of the group's activations)
+// instead of zero, which removes the expansion's bias from the sum they accumulate.
+__device__ __forceinline__ void add_group(f32x4_t& acc, const f32x4_t& accg, float sc) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-    acc[r] = W4 ? fmaf(sc, fmaf(-kW4Bias, xs[r], accg[r]), acc[r]) : fmaf(sc, accg[r], acc[r]);
+  for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc, accg[r], acc[r]);
 }
 
 template <int MT>
-__device__ __forceinline__ void store_out(const WgemmArgs& a, const f32x4_t (&acc)[MT], int tile, int nn, int qq) {
+__device__ __forceinline__ void store_y(const WgemmArgs& a, const f32x4_t (&acc)[MT], int tile, int nn, int qq) {
   if (tile * 16 >= a.N) return;
   const int n = tile * 16 + nn;
 #pragma unroll
@@ -176,26 +175,72 @@ __device__ __forceinline__ void store_out(const WgemmArgs& a, const f32x4_t (&ac
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 16 * mt + 4 * qq + r;
-      if (m >= a.M) continue;
-      if (a.splits == 1)
-        a.y[(int64_t)m * a.N + n] = (uint16_t)(pack_bf16x2(acc[mt][r], 0.f) & 0xFFFFu);
-      else
-        a.part[((int64_t)blockIdx.y * a.M + m) * a.N + n] = acc[mt][r];
+      if (m < a.M) a.y[(int64_t)m * a.N + n] = (uint16_t)(pack_bf16x2(acc[mt][r], 0.f) & 0xFFFFu);
     }
   }
 }
 
-// y = bf16(sum over splits of the partials), splits added in order.
-__global__ __launch_bounds__(256) void wgemm_reduce_kernel(const float* part, int32_t splits, int64_t mn,
-                                                           uint16_t* y) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= mn) return;
-  f32x4_t s = *reinterpret_cast<const f32x4_t*>(part + i);
-  for (int sp = 1; sp < splits; ++sp) s += *reinterpret_cast<const f32x4_t*>(part + (int64_t)sp * mn + i);
-  u32x2_t o;
-  o[0] = pack_bf16x2(s[0], s[1]);
-  o[1] = pack_bf16x2(s[2], s[3]);
-  *reinterpret_cast<u32x2_t*>(y + i) = o;
+// The block's results, called by every thread of the block.  One split: y directly.  Several: each block
+// stores its fp32 partials, 16 bytes per lane and row tile, with device-coherent stores (sc1: they reach
+// the point every XCD reads from, and no L2 writeback is needed), waits for them, and counts itself
+// finished for its column group; the block that finishes last reads the other splits' partials with
+// device-coherent loads, all issued before any is used, adds them in split order (the order a separate
+// reduction would take), writes y and sets the count back to zero.  Partials sit at
+// [split][column group][wave][row tile][lane] in 16-byte units.
+constexpr int kCohAux = 16;   // cache-policy operand of a buffer access: sc1
+constexpr int kFinishBatch = 4;
+
+template <int MT>
+__device__ __forceinline__ void store_out(const WgemmArgs& a, const f32x4_t (&acc)[MT], int tile, int nn, int qq) {
+  if (a.splits == 1) {
+    store_y<MT>(a, acc, tile, nn, qq);
+    return;
+  }
+  __shared__ uint32_t s_last;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const __amdgpu_buffer_rsrc_t pr =
+      make_rsrc(a.part, (uint32_t)((int64_t)a.splits * gridDim.x * nw * MT * 64 * 16));
+  auto off = [&](int sp, int mt) {
+    return (uint32_t)(((((int64_t)sp * gridDim.x + blockIdx.x) * nw + wave) * MT + mt) * 64 + lane) * 16;
+  };
+  const bool live = tile * 16 < a.N;
+  if (live) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[mt]), pr, off(blockIdx.y, mt), 0, kCohAux);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partials are stored before the block counts itself done
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(a.count + blockIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = done == (uint32_t)(a.splits - 1);
+    if (last) __hip_atomic_store(a.count + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last ? 1u : 0u;
+  }
+  __syncthreads();
+  if (s_last == 0u || !live) return;
+  f32x4_t sum[MT];
+  for (int sp0 = 0; sp0 < a.splits; sp0 += kFinishBatch) {
+    u32x4_t v[kFinishBatch][MT];
+#pragma unroll
+    for (int b = 0; b < kFinishBatch; ++b)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int sp = sp0 + b;
+        v[b][mt] = (sp < a.splits && sp != (int)blockIdx.y)
+                       ? __builtin_amdgcn_raw_buffer_load_b128(pr, off(sp, mt), 0, kCohAux)
+                       : __builtin_bit_cast(u32x4_t, acc[mt]);
+      }
+#pragma unroll
+    for (int b = 0; b < kFinishBatch; ++b)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const f32x4_t x = __builtin_bit_cast(f32x4_t, v[b][mt]);
+        if (sp0 + b == 0) sum[mt] = x;
+        else if (sp0 + b < a.splits) sum[mt] += x;
+      }
+  }
+  store_y<MT>(a, sum, tile, nn, qq);
 }
 
 // ---- M <= 16: the block's whole K range of the activations stays in LDS (rows 0..M-1, then the
@@ -210,7 +255,10 @@ __global__ __launch_bounds__(WK ? 256 : 64 * WB) void wgemm_small_kernel(WgemmAr
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int kTiles = WK ? 1 : WB;
   constexpr int kThr = WK ? 256 : 64 * WB;
-  constexpr int kRingS = kRing;   // measured on 8192 x 8192: 4 and 8 alike, 12 and 16 slower
+  // groups in flight per wave, measured on 8192 x 8192: with the K range cut among the waves (M <= 4) 4
+  // beats 8 (INT4 M=1 11.7 against 12.4 us, FP8 14.9 against 15.2) and 16 is slower (14.5, 17.0); split over
+  // blocks, 4 and 8 are alike and 12 and 16 slower
+  constexpr int kRingS = WK ? 4 : kRing;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nn = lane & 15, qq = lane >> 4;
   const int KG = a.K / kGroup;
@@ -246,13 +294,12 @@ __global__ __launch_bounds__(WK ? 256 : 64 * WB) void wgemm_small_kernel(WgemmAr
   };
   auto x_put = [&](int i, const u32x4_t& v) {
     if (i < total) *reinterpret_cast<u32x4_t*>(smem + (i / per_row) * row_bytes + 16 * (i % per_row)) = v;
-    // INT4: group sums on the way (the code bias is removed with them; FP8 codes carry none): a group
-    // of a row is 16 consecutive columns, i.e. 16 aligned lanes (per_row and the thread count are
-    // multiples of 16);
-    // out-of-range lanes loaded zeros
+    // INT4: -136 * group sum on the way, the starting value of the group's MFMAs (it removes the code
+    // bias; FP8 codes carry none): a group of a row is 16 consecutive columns, i.e. 16 aligned lanes
+    // (per_row and the thread count are multiples of 16); out-of-range lanes loaded zeros
     if constexpr (W4) {
       const float sum = row_sum16(sum8_bf16(v));
-      if (i < total && (threadIdx.x & 15) == 0) xs[((i % per_row) >> 4) * 16 + i / per_row] = sum;
+      if (i < total && (threadIdx.x & 15) == 0) xs[((i % per_row) >> 4) * 16 + i / per_row] = -kW4Bias * sum;
     }
   };
   constexpr int kXB = 4096 / kThr;                       // activation loads per thread and batch
@@ -289,12 +336,13 @@ __global__ __launch_bounds__(WK ? 256 : 64 * WB) void wgemm_small_kernel(WgemmAr
       u32x4_t av[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const u32x4_t*>(xa + (gc * kGroup + 32 * j) * 2);
-      const f32x4_t x4 = *reinterpret_cast<const f32x4_t*>(&xs[gc * 16 + 4 * qq]);
       const float sc = bf16_bits_to_f32(s_sc[(st * gcap + gc) * 16 + nn]);
+      // rows >= M start from whatever their unused entries hold: their results are never stored
       f32x4_t accg = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (W4) accg = *reinterpret_cast<const f32x4_t*>(&xs[gc * 16 + 4 * qq]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) accg = mfma_bf16(av[j], expand<W4>(wr[u], j), accg);
-      add_group<W4>(acc, accg, base + u < ngw ? sc : 0.f, x4);
+      add_group(acc, accg, base + u < ngw ? sc : 0.f);
       // refill this slot now: without the fence the scheduler sinks all refills of the unrolled loop
       // to its end, and every pass then waits a full memory latency for loads it has just issued
       ws.load(wr[u], base + u + kRingS);
@@ -360,7 +408,7 @@ __global__ __launch_bounds__(64 * WB, 8 / WB) void wgemm_kernel(WgemmArgs a) {
       // INT4 only: the 16 lanes of one (row, group) are lanes 16h..16h+15 of this wave
       if constexpr (W4) {
         const float sum = row_sum16(sum8_bf16(xr[set][p]));
-        if ((xr_col & 15) == 0) s_xs[buf][xr_col >> 4][row] = sum;
+        if ((xr_col & 15) == 0) s_xs[buf][xr_col >> 4][row] = -kW4Bias * sum;
       }
     }
   };
@@ -392,7 +440,8 @@ __global__ __launch_bounds__(64 * WB, 8 / WB) void wgemm_kernel(WgemmArgs a) {
       if (gl == 0) x_load(buf, (base + u) / 2 + 2);
       f32x4_t accg[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) accg[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < MT; ++mt)
+        accg[mt] = W4 ? *reinterpret_cast<const f32x4_t*>(&s_xs[buf][gl][16 * mt + 4 * qq]) : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x4_t b = expand<W4>(wr[u], j);
@@ -404,9 +453,7 @@ __global__ __launch_bounds__(64 * WB, 8 / WB) void wgemm_kernel(WgemmArgs a) {
       }
       const float sc = bf16_bits_to_f32(s_sc[(wave * kMaxGroupsChunked + min(base + u, kMaxGroupsChunked - 1)) * 16 + nn]);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        add_group<W4>(acc[mt], accg[mt], base + u < ng ? sc : 0.f,
-                      *reinterpret_cast<const f32x4_t*>(&s_xs[buf][gl][16 * mt + 4 * qq]));
+      for (int mt = 0; mt < MT; ++mt) add_group(acc[mt], accg[mt], base + u < ng ? sc : 0.f);
       ws.load(wr[u], base + u + kR);
       __builtin_amdgcn_sched_barrier(0);
       if (gl == 1) {
@@ -464,6 +511,10 @@ __global__ __launch_bounds__(256) void wquant_kernel(const uint16_t* w, int32_t 
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The split-K workspace opens with one uint32 count per possible column group (one per 16 output
+// channels, whatever the launch's group width), padded to 256 bytes; the fp32 partials follow.
+inline size_t count_bytes(int32_t n) { return (((size_t)(n + 15) / 16) * 4 + 255) / 256 * 256; }
 
 int check_shape(int32_t n, int32_t k) {
   if (n < 16 || k < kChunk || n % 16 != 0 || k % kChunk != 0) return KVFP8_ERR_SHAPE;
@@ -557,6 +608,7 @@ int gemm_common(const uint16_t* x, int32_t m, const uint8_t* w, const uint16_t* 
   a.s = scales;
   a.y = y;
   a.part = nullptr;
+  a.count = nullptr;
   a.M = m;
   a.N = n;
   a.K = k;
@@ -567,7 +619,8 @@ int gemm_common(const uint16_t* x, int32_t m, const uint8_t* w, const uint16_t* 
     if (!workspace) return KVFP8_ERR_NULL;
     if (workspace_bytes < need) return KVFP8_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KVFP8_ERR_ALIGN;
-    a.part = reinterpret_cast<float*>(workspace);
+    a.count = reinterpret_cast<uint32_t*>(workspace);
+    a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + count_bytes(n));
   }
   const size_t lds = small_lds_bytes(m, a.groups_per_split);
   const bool wk = splits == 1 && m <= 16 && small_lds_bytes(m, a.groups_per_split, true) <= kSmallLdsMax;
@@ -602,12 +655,6 @@ int gemm_common(const uint16_t* x, int32_t m, const uint8_t* w, const uint16_t* 
     }
   }
   if (hipGetLastError() != hipSuccess) return KVFP8_ERR_HIP;
-  if (splits > 1) {
-    const int64_t mn = (int64_t)m * n;                 // a multiple of 16
-    hipLaunchKernelGGL(wgemm_reduce_kernel, dim3((uint32_t)((mn / 4 + 255) / 256)), dim3(256), 0, stream,
-                       a.part, splits, mn, y);
-    if (hipGetLastError() != hipSuccess) return KVFP8_ERR_HIP;
-  }
   return KVFP8_OK;
 }
 
@@ -644,7 +691,10 @@ int32_t wgemm_auto_splits(int32_t m, int32_t n, int32_t k) { return auto_splits(
 
 size_t wgemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t num_splits) {
   if (m < 1 || n < 1 || k < 1 || num_splits <= 1) return 0;
-  return (size_t)num_splits * m * n * sizeof(float);
+  // partials: 16 bytes per lane, row tile and 16-channel wave tile, over the column groups' whole tiles
+  // (the widest group, eight tiles, rounds N up the most)
+  const size_t tiles = ((size_t)(n + 127) / 128) * 8, row_tiles = ((size_t)m + 15) / 16;
+  return count_bytes(n) + (size_t)num_splits * tiles * row_tiles * 64 * 16;
 }
 
 int w4a16_gemm(const uint16_t* x, int32_t m, const uint8_t* w_packed, const uint16_t* scales, int32_t n, int32_t k,

@@ -69,9 +69,15 @@ int w8_quantize_bf16(const uint16_t* w, int32_t n, int32_t k, uint8_t* packed, u
  * num_splits: 0 = chosen by the library, else at most K/256; the K range is
  * cut into that many slices (for M > 16 with more than 16 activation rows'
  * worth of LDS, at most 8192 input channels per slice: KVFP8_ERR_UNSUPPORTED
- * otherwise) whose fp32 partials go to `workspace` (at least
+ * otherwise).  One launch either way: with several slices their fp32 partials
+ * go to `workspace` (device, 16-byte aligned, at least
  * wgemm_workspace_bytes(M, N, K, splits) bytes; 0 and NULL allowed for one
- * split) and are added in split order by a second launch. */
+ * split), and the last block of each column group to finish adds them in
+ * split order.  The workspace opens with ceil(N/16) uint32 counters (padded
+ * to 256 bytes) that must be zero before the first call that uses it (e.g.
+ * allocate it zeroed once); every call leaves them zero, so one workspace
+ * serves any sequence of calls on one stream.  Calls that overlap in time
+ * must not share a workspace. */
 int32_t wgemm_auto_splits(int32_t m, int32_t n, int32_t k);
 size_t wgemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t num_splits);
 int w4a16_gemm(const uint16_t* x, int32_t m, const uint8_t* w_packed, const uint16_t* scales, int32_t n,

@@ -154,7 +154,11 @@ def test_host_validation_codes(lib):
     assert 2 <= lib.wgemm_auto_splits(32, 64, 16384)                           # the library's own choice fits
     assert lib.w4_packed_bytes(65536, 65536) == 65536 * 65536 // 2
     assert lib.wgemm_workspace_bytes(4, 64, 512, 1) == 0
-    assert lib.wgemm_workspace_bytes(4, 64, 512, 2) == 2 * 4 * 64 * 4
+    # counters (padded to 256 B), then 1 KiB of partials per split, 16-channel tile (N rounded up to 128) and
+    # 16-row tile
+    assert lib.wgemm_workspace_bytes(4, 64, 512, 2) == 256 + 2 * 8 * 1024
+    assert lib.wgemm_workspace_bytes(1, 8192, 8192, 4) == 2048 + 4 * 512 * 1024
+    assert lib.wgemm_workspace_bytes(33, 8192, 8192, 4) == 2048 + 4 * 512 * 3 * 1024
     assert 1 <= lib.wgemm_auto_splits(1, 8192, 8192) <= 32
     # read-rate calibration
     assert lib.kv_read_stream(A, 0, A, None) == 0
