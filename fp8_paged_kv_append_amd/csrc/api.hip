@@ -19,6 +19,18 @@ constexpr int kHeadDim = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// An attention workspace opens with one uint32 count per (request, query head) -- the GQA kernel uses one
+// per (request, KV head) -- padded to 256 bytes; the split partials follow.
+// GQA split counts up to this are merged inside the attention launch (by the last split block of each
+// (request, KV head)); more are merged by a launch of their own.  Measured on MI355X: one request of 8192
+// tokens in a 61-layer step, 16 splits, 14.2 against 15.3 us per layer; 8 requests, 4 splits, 30.3 against
+// 30.7; 4 x 131072 tokens at 32 splits 167.0 us with the separate merge, 182.5 with the merge inside.
+constexpr int32_t kMergeInLaunchMaxSplits = 16;
+
+inline size_t attn_count_bytes(int32_t batch, int32_t num_q_heads) {
+  return ((size_t)batch * num_q_heads * 4 + 255) / 256 * 256;
+}
 inline bool good_scale(float s) { return isfinite(s) && s > 0.f; }
 // The softmax scale a caller passes, with 0 standing for the usual 1/sqrt(score dim).
 inline float softmax_scale(float sm_scale, int32_t score_dim) {
@@ -149,13 +161,19 @@ int attn_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_he
   AttnArgs a;
   a.o_part = nullptr;
   a.lse_part = nullptr;
+  a.count = nullptr;
+  a.merge_here = 0;
   if (splits > 1) {
     const size_t need = paged_decode_attn_workspace_bytes(batch, num_q_heads, kHeadDim, splits);
     if (workspace == nullptr) return KVFP8_ERR_NULL;
     if (workspace_bytes < need) return KVFP8_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KVFP8_ERR_ALIGN;
+    // the merge's rows are addressed with 32-bit buffer offsets: at most 2^31 bytes per (request, KV head)
+    if ((int64_t)group * splits * kHeadDim * 4 >= ((int64_t)1 << 31)) return KVFP8_ERR_UNSUPPORTED;
     const size_t rows = (size_t)batch * num_q_heads * splits;
-    a.o_part = reinterpret_cast<float*>(workspace);
+    a.count = reinterpret_cast<uint32_t*>(workspace);
+    a.merge_here = splits <= kMergeInLaunchMaxSplits ? 1 : 0;
+    a.o_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + attn_count_bytes(batch, num_q_heads));
     a.lse_part = a.o_part + rows * kHeadDim;
   }
   a.q = q;
@@ -319,7 +337,7 @@ int latent_common(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_
     if (workspace == nullptr) return KVFP8_ERR_NULL;
     if (workspace_bytes < need) return KVFP8_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KVFP8_ERR_ALIGN;
-    a.o_part = reinterpret_cast<float*>(workspace);
+    a.o_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + attn_count_bytes(batch, num_q_heads));
     a.lse_part = a.o_part + (size_t)batch * num_q_heads * splits * kLatentVDim;
   }
   a.q = q;
@@ -567,8 +585,8 @@ int kv_decode_step_bf16(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* la
 size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t v_dim, int32_t num_splits) {
   if (batch <= 0 || num_q_heads <= 0 || v_dim <= 0 || num_splits <= 1) return 0;
   const size_t rows = (size_t)batch * num_q_heads * num_splits;
-  // fp32 partials and lse of every (request, head, split)
-  return rows * (size_t)v_dim * sizeof(float) + rows * sizeof(float);
+  // the split counters, then the fp32 partials and lse of every (request, head, split)
+  return attn_count_bytes(batch, num_q_heads) + rows * (size_t)v_dim * sizeof(float) + rows * sizeof(float);
 }
 
 int32_t paged_decode_attn_auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_ctx_len) {

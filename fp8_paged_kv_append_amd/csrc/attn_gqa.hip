@@ -234,8 +234,7 @@ __device__ __forceinline__ void compute_tile(TileRegs<FP8>& T, const u32x4_t (&q
       x[pos] = v;
       tmax = fmaxf(tmax, v);
     }
-  tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+  tmax = max_x32(max_x16(tmax));
   // The accumulators stay referenced to st.m until a tile's max exceeds it by more than kLazy
   // (log2 units): p <= 2^kLazy meanwhile (exact up to rounding) and the rescale of the
   // AGPR-resident accumulators runs only when some head's max really grows.
@@ -267,6 +266,77 @@ __device__ __forceinline__ void compute_tile(TileRegs<FP8>& T, const u32x4_t (&q
     for (int kb = 0; kb < 2; ++kb) st.acc[j] = mfma_pv<FP8>(T.v[j], kb, pp[kb], st.acc[j]);
 }
 
+// ---- split-K: the merge inside the attention launch -------------------------------------------
+//
+// With several splits every block stores its G rows' partials (fp32 o, lse) with device-coherent stores
+// (sc1: they reach the point every XCD reads from, with no L2 writeback), waits for them and counts itself
+// finished for its (request, KV head); the block that finishes last merges all splits' partials into the
+// bf16 output, reading them with device-coherent loads, and sets the count back to zero.  The counts sit
+// at the head of the workspace: zero before a launch, zero after it.
+constexpr int kCohAux = 16;       // cache-policy operand of a buffer access: sc1
+constexpr int kMergeGroup = 16;   // splits whose lse and partials are loaded together
+constexpr uint32_t kOffOOB = 0x80000000u;  // a buffer offset past the buffer: the load returns 0
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// The LSE merge of rows row0 .. row0 + G - 1 over the splits, as the separate merge kernel computes it:
+// splits in groups of kMergeGroup, all of a group's loads issued before any is used, later groups
+// rescaling the running sums to the new maximum; a split that saw a bad page (lse NaN) zeroes the row.
+__device__ __forceinline__ void merge_rows_in_launch(const AttnArgs& a, int r, int g, int L, bool zero_rows) {
+  const int G = a.group, S = a.num_splits;
+  const int64_t row0 = (int64_t)r * a.num_q_heads + (int64_t)g * G;
+  const __amdgpu_buffer_rsrc_t orc = coh_rsrc(a.o_part + row0 * S * kD, (int64_t)G * S * kD * 4);
+  const __amdgpu_buffer_rsrc_t lrc = coh_rsrc(a.lse_part + row0 * S, (int64_t)G * S * 4);
+  const int chunk = a.chunk_tiles * kTile;
+  const int nvalid = zero_rows ? 0 : min(S, (L + chunk - 1) / chunk);
+  for (int t = threadIdx.x; t < G * (kD / 4); t += kThreads) {
+    const int hn = t / (kD / 4), d = 4 * (t % (kD / 4));
+    float M = -INFINITY, s = 0.f;
+    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+    bool nan = false;
+    for (int c0 = 0; c0 < nvalid; c0 += kMergeGroup) {
+      float x[kMergeGroup];
+      f32x4_t pv[kMergeGroup];
+#pragma unroll
+      for (int j = 0; j < kMergeGroup; ++j) {
+        const int c = c0 + j;
+        const bool in = c < nvalid;
+        const uint32_t lo = in ? (uint32_t)(hn * S + c) * 4u : kOffOOB;
+        const uint32_t po = in ? (uint32_t)(((int64_t)(hn * S + c) * kD + d) * 4) : kOffOOB;
+        const uint32_t xl = __builtin_amdgcn_raw_buffer_load_b32(lrc, lo, 0, kCohAux);
+        pv[j] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(orc, po, 0, kCohAux));
+        x[j] = in ? __uint_as_float(xl) : -INFINITY;
+      }
+      float gm = M;
+#pragma unroll
+      for (int j = 0; j < kMergeGroup; ++j) {
+        nan |= x[j] != x[j];
+        gm = fmaxf(gm, x[j]);
+      }
+      if (gm == -INFINITY) continue;  // nothing but empty splits so far
+      const float rs = exp2f(M - gm);  // 0 while M is still -inf
+      s *= rs;
+      o *= rs;
+#pragma unroll
+      for (int j = 0; j < kMergeGroup; ++j) {
+        const float f = exp2f(x[j] - gm);
+        s += f;
+        o += f * pv[j];
+      }
+      M = gm;
+    }
+    if (nan || zero_rows) {
+      s = 0.f;
+      o = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const float inv = s > 0.f ? 1.f / s : 0.f;
+    *reinterpret_cast<u32x2_t*>(a.out + (row0 + hn) * kD + d) =
+        u32x2_t{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+  }
+}
+
 template <bool FP8>
 // At least two waves per SIMD (eight per CU, two blocks): the register budget the tile pipeline is
 // written for.
@@ -287,6 +357,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
   __shared__ uint16_t s_kcode[kD], s_vcode[kD];
   __shared__ int s_newpage;
   __shared__ uint32_t s_flag[kWaves];
+  __shared__ uint32_t s_last;
 
   const int chunk = a.chunk_tiles * kTile;
   const int c0 = split * chunk;
@@ -422,14 +493,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
   }
   const bool aborted = checked != 0u || (a.flags != nullptr && a.flags[r] != 0u);
   const bool bad_len = L <= 0 || L > a.max_ctx || L > a.pt_stride * S;
+  // several splits: count this block finished (its partials, if any, stored); the last one merges
+  auto finish = [&](bool zero_rows) {
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete before the block counts
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t* cnt = a.count + (int64_t)r * a.num_kv_heads + g;
+      const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = done == (uint32_t)(a.num_splits - 1);
+      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last ? 1u : 0u;
+    }
+    __syncthreads();
+    if (s_last != 0u) merge_rows_in_launch(a, r, g, L, zero_rows);
+  };
   if (aborted || bad_len) {
     if (a.num_splits == 1) {  // rows of this group are zero
       for (int e = threadIdx.x; e < G * kD; e += kThreads)
         a.out[((int64_t)r * a.num_q_heads + g * G + e / kD) * kD + e % kD] = 0;
+    } else if (a.merge_here) {
+      finish(true);  // the last split block zeroes the rows
     }
-    return;  // the merge kernel zeroes the rows itself
+    return;  // (else the merge launch zeroes them)
   }
-  if (c0 >= L) return;  // past this request's context: the merge does not read this split
+  if (c0 >= L) {  // past this request's context: no partials, and the merge does not read this split
+    if (a.merge_here) finish(false);
+    return;
+  }
 
   const uint8_t* kpool = reinterpret_cast<const uint8_t*>(a.k_pool);
   const uint8_t* vpool = reinterpret_cast<const uint8_t*>(a.v_pool);
@@ -503,8 +593,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
 
   // ---- merge the four waves
   float l_run = st.l;
-  l_run += shfl_xor(l_run, 16);
-  l_run += shfl_xor(l_run, 32);
+  l_run = sum_x32(sum_x16(l_run));
   if (threadIdx.x == 0) s_bad = 0;
   __syncthreads();
   if (owner) {
@@ -535,8 +624,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
         const int d = 32 * q4 + 8 * kk + 2 * e;
         dot += __uint_as_float(w << 16) * s_knew[d] + __uint_as_float(w & 0xFFFF0000u) * s_knew[d + 1];
       }
-    dot += shfl_xor(dot, 16);
-    dot += shfl_xor(dot, 32);
+    dot = sum_x32(sum_x16(dot));
     if (q4 == 0 && n < G) s_snew[n] = dot * c_log2;
   }
   if (q4 == 0) {
@@ -551,6 +639,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
   const bool any_bad = s_bad != 0;
 
   const int Hq = a.num_q_heads;
+  const int64_t row0 = (int64_t)r * Hq + (int64_t)g * G;
+  const __amdgpu_buffer_rsrc_t orc =
+      coh_rsrc(a.o_part + row0 * a.num_splits * kD, (int64_t)G * a.num_splits * kD * 4);
+  const __amdgpu_buffer_rsrc_t lrc = coh_rsrc(a.lse_part + row0 * a.num_splits, (int64_t)G * a.num_splits * 4);
   for (int e = threadIdx.x; e < G * kD; e += kThreads) {
     const int hn = e / kD, d = e % kD;
     float M = -INFINITY;
@@ -576,11 +668,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
       const float val = (any_bad || lsum == 0.f) ? 0.f : o * (a.v_scale / lsum);
       a.out[row * kD + d] = (uint16_t)(pack_bf16x2(val, 0.f) & 0xFFFFu);
     } else {
-      const int64_t slot = row * a.num_splits + split;
-      a.o_part[slot * kD + d] = lsum == 0.f ? 0.f : o * (a.v_scale / lsum);
-      if (d == 0) a.lse_part[slot] = any_bad ? NAN : (lsum == 0.f ? -INFINITY : M + __log2f(lsum));
+      const uint32_t slot = (uint32_t)(hn * a.num_splits + split);   // inside the block's rows
+      const float ov = lsum == 0.f ? 0.f : o * (a.v_scale / lsum);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), orc, (slot * kD + d) * 4u, 0, kCohAux);
+      if (d == 0) {
+        const float lv = any_bad ? NAN : (lsum == 0.f ? -INFINITY : M + __log2f(lsum));
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lv), lrc, slot * 4u, 0, kCohAux);
+      }
     }
   }
+  if (a.merge_here) finish(false);
 }
 
 // --- merge of the split partials ----------------------------------------------------------------
@@ -661,7 +758,7 @@ hipError_t launch_attn_gqa(const AttnArgs& a, bool fp8, int batch, hipStream_t s
   else
     hipLaunchKernelGGL(attn_gqa_split_kernel<false>, grid, dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.num_splits == 1) return e;
+  if (e != hipSuccess || a.num_splits == 1 || a.merge_here) return e;
   MergeArgs m;
   m.o_part = a.o_part;
   m.lse_part = a.lse_part;

@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
       float tmax = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, x[j]);
-      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+      tmax = max_x32(tmax);
       const bool grow = tmax > m_run + kLazy;  // m_run = -inf: any finite tile max grows it
       if (__any(grow)) {
         const float m_new = grow ? tmax : m_run;
@@ -427,8 +427,7 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
       u32x4_t qb[QD + 1][2];
 #pragma unroll
       for (int p = 0; p < QD; ++p) qk_read(tile_n, p, qb[p]);
-      f32x16_t sn = f32x16_t{};
-      asm volatile("" : "+v"(sn));
+      f32x16_t sn = f32x16_t{};  // the first MFMA starts from an inline zero
       if constexpr (FP8) {
         // 9 k-steps of 64 dims, each two FP8 MFMAs (q hi and lo terms) over the raw cached bytes
 #pragma unroll
@@ -438,6 +437,9 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
             x[2 * p] = __builtin_amdgcn_exp2f(x[2 * p] - m_use);  // v_exp_f32: weights below 2^-126 flush to 0
             x[2 * p + 1] = __builtin_amdgcn_exp2f(x[2 * p + 1] - m_use);
             psum += x[2 * p] + x[2 * p + 1];
+            // kept here, between the QK MFMAs: otherwise the compiler moves the exponentials into the PV
+            // section, where their only uses are
+            asm volatile("" : "+v"(x[2 * p]), "+v"(x[2 * p + 1]), "+v"(psum));
           }
           __builtin_amdgcn_sched_barrier(0);
           const u32x4_t(&kr)[2] = qb[p % (QD + 1)];
@@ -455,6 +457,7 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
           if (p < 16) {
             x[p] = __builtin_amdgcn_exp2f(x[p] - m_use);  // v_exp_f32: weights below 2^-126 flush to 0
             psum += x[p];
+            asm volatile("" : "+v"(x[p]), "+v"(psum));
           }
           __builtin_amdgcn_sched_barrier(0);
           const u32x4_t(&raw)[2] = qb[p % (QD + 1)];
@@ -509,7 +512,7 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   __syncthreads();
   const bool any_bad = s_bad != 0;
   if (!active) return;
-  l_run += shfl_xor(l_run, 32);
+  l_run = sum_x32(l_run);
   const int h = h0 + n;
   if (h >= Hq) return;
   const int64_t row = (int64_t)r * Hq + h;

@@ -87,24 +87,6 @@ __device__ __forceinline__ int pv_token(int q4, int j) { return j < 4 ? 4 * q4 +
 __device__ __forceinline__ int lrow(int t) { return t < 16 ? t : 16 + ((t - 8) & 15); }
 __device__ __forceinline__ int ltok(int row) { return row < 16 ? row : 16 + ((row - 8) & 15); }
 
-// xor-16 / xor-32 lane reductions on the VALU (lane swaps), no LDS round trip
-__device__ __forceinline__ float max_x16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_x32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_x16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_x32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // four floats as two e4m3 terms: {hi, lo} with lo = e4m3(f - hi)
 __device__ __forceinline__ i32x2p_t to_hilo(float f0, float f1, float f2, float f3) {
   int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);

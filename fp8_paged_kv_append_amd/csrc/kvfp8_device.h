@@ -107,6 +107,26 @@ __device__ __forceinline__ T shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }
 
+// xor-16 / xor-32 lane reductions on the VALU (gfx950 lane swaps: a row of 16 lanes with its neighbour,
+// or the wave's two halves), with no LDS round trip.  Each lane ends with the same pair of operands as
+// its partner, so both compute the same result.
+__device__ __forceinline__ float max_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // The step's new row of request r (DIM elements, bf16 bits at a.c_new + r * DIM) quantised as the
 // append does and stored at position L - 1 of a row-major latent pool [page][slot][DIM].  Only the
 // stores are issued here: the caller waits for them (vmcnt, which counts stores on this GPU family)

@@ -15,6 +15,8 @@ struct AttnArgs {
   const uint32_t* flags;      // [B] or null
   float* o_part;              // [B][Hq][num_splits][Dv] (num_splits > 1)
   float* lse_part;            // [B][Hq][num_splits]
+  uint32_t* count;            // [B][Hkv] finished split blocks (merge_here): zero before and after a launch
+  int32_t merge_here;         // several splits merged by the launch itself (else by a merge launch after it)
   uint16_t* out;              // bf16 [B][Hq][Dv]
   int32_t num_pages, page_size, num_kv_heads, group, num_q_heads, pt_stride;
   int32_t chunk_tiles;        // 64-token tiles per split

@@ -173,10 +173,17 @@ int kv_tag_check_append_bf16(const kvfp8_pool_desc* desc, uint16_t* k_pool, uint
  *   pages and gets zero rows [T].  A page id outside [0,P) met while reading
  *   also zeroes the request's rows (memory safety when the tracker is off).
  *   num_splits: 0 = chosen by the library; otherwise at most
- *   ceil(max_ctx_len/64).  workspace: at least
+ *   ceil(max_ctx_len/64).  workspace (device, 16-byte aligned): at least
  *   paged_decode_attn_workspace_bytes(...) bytes for the split count used
- *   (0 when it is 1; then workspace may be NULL).  Calls that share a
- *   workspace must be ordered (one stream).
+ *   (0 when it is 1; then workspace may be NULL).  It opens with
+ *   B*Hq uint32 counters (padded to 256 bytes) that must be zero before the
+ *   first call that uses the workspace (allocate it zeroed once); every call
+ *   leaves them zero, so a workspace serves any sequence of ordered calls,
+ *   GQA or latent, of any shape it is large enough for.  With 2..16 splits
+ *   the GQA launch merges them itself (the last split block of each
+ *   (request, KV head) does the log-sum-exp merge); more splits, and the
+ *   latent cache, add a merge launch.  Calls that share a workspace must be
+ *   ordered (one stream).
  *   sm_scale: the softmax scale; 0 selects 1/sqrt(D) (the pages give none).
  *   k_scale, v_scale and a non-zero sm_scale must be finite and > 0. */
 size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t v_dim,
@@ -211,7 +218,9 @@ int paged_decode_attn_bf16(const kvfp8_pool_desc* desc, const uint16_t* q, int32
  * with KVFP8_ERR_WORKSPACE before anything is enqueued.  Every call on a
  * device shares that device's array: calls that overlap on one GPU (other
  * streams, other threads) race on it; calls in one stream's order do not.
- * Nothing in the array needs clearing between calls. */
+ * The array's split counters start at zero (it is zero-initialised when the
+ * library loads) and every call leaves them zero, so nothing in it needs
+ * clearing between calls. */
 #define KVFP8_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
 int paged_decode_attn_fp8_noalloc(const kvfp8_pool_desc* desc, const uint16_t* q, int32_t num_q_heads,
                                   const uint8_t* k_pool, const uint8_t* v_pool, const int32_t* page_table,
@@ -282,7 +291,7 @@ int paged_decode_attn_latent_bf16(const kvfp8_pool_desc* desc, const uint16_t* q
  * computed as usual, its rows are zero and no layer writes its token.
  * Every layer's arguments are checked before the first launch, so an error
  * status means nothing was enqueued.  The workspace is shared by the layers
- * (stream order); size it as for one layer's attention.  sm_scale 0 selects
+ * (stream order); size it, and zero it once, as for one layer's attention.  sm_scale 0 selects
  * 1/sqrt(score dim).  Other shapes, limits and outputs as for the per-layer
  * calls above.  In a model the layers' q and new rows come from the layer
  * below; here they are given up front (the projections between layers are
