@@ -41,7 +41,8 @@ int check_pool(const kvfp8_pool_desc* d, bool need_v_dim_eq, int elt_bytes) {
   if (d == nullptr) return KVFP8_ERR_NULL;
   if (d->num_pages < 1 || d->page_size < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->v_dim < 0)
     return KVFP8_ERR_SHAPE;
-  if (d->page_size % 16 != 0 || d->page_size > 256) return KVFP8_ERR_UNSUPPORTED;
+  // a power of two from 16 to 256: the kernels find a token's page and slot by shift and mask
+  if (d->page_size < 16 || d->page_size > 256 || (d->page_size & (d->page_size - 1)) != 0) return KVFP8_ERR_UNSUPPORTED;
   // K rows are cut into 64-byte slices (the chunk-reordered K layout)
   if ((d->head_dim * elt_bytes) % 64 != 0 || d->v_dim % 16 != 0) return KVFP8_ERR_UNSUPPORTED;
   if (need_v_dim_eq && (d->head_dim != kHeadDim || d->v_dim != kHeadDim)) return KVFP8_ERR_UNSUPPORTED;

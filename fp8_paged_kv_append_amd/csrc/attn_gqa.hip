@@ -176,12 +176,13 @@ struct TileRegs {
 template <bool FP8>
 __device__ __forceinline__ void issue_tile(TileRegs<FP8>& T, int tb, int w1, int e0, int ne, const int* s_pid,
                                            const uint8_t* kpool, const uint8_t* vpool, int64_t blk, int S,
-                                           int Hkv, int g, int q4, int n) {
+                                           int lgS, int Hkv, int g, int q4, int n) {
   constexpr int ELT = FP8 ? 1 : 2;
   const int tok_k = tb + 16 * (n >> 2);
   const int tok_v = tb + 16 * q4;
   // LDS index clamped into the staged range, the result discarded past w1: no branch
-  const int ik = min(tok_k / S - e0, ne - 1), iv = min(tok_v / S - e0, ne - 1);
+  // (S a power of two: page and slot by shift and mask)
+  const int ik = min((tok_k >> lgS) - e0, ne - 1), iv = min((tok_v >> lgS) - e0, ne - 1);
   const int sk = s_pid[ik], sv = s_pid[iv];
   const int pid_k = tok_k < w1 ? sk : -1;
   const int pid_v = tok_v < w1 ? sv : -1;
@@ -189,9 +190,9 @@ __device__ __forceinline__ void issue_tile(TileRegs<FP8>& T, int tb, int w1, int
   // masked afterwards, so every tile issues the same loads with no branch around them.
   // offsets computed for max(pid, 0) and zeroed by a mask: arithmetic, not a branch
   // K: sub-page block base + lane (q4, i = n&3)'s first chunk of token 4s+i (byte offsets)
-  const int64_t ko = ((((int64_t)max(pid_k, 0) * Hkv + g) * blk + (int64_t)(tok_k % S) * kD) * ELT + 64 * q4 +
+  const int64_t ko = ((((int64_t)max(pid_k, 0) * Hkv + g) * blk + (int64_t)(tok_k & (S - 1)) * kD) * ELT + 64 * q4 +
                       16 * (n & 3)) & -(int64_t)(pid_k >= 0);
-  const int64_t vo = ((((int64_t)max(pid_v, 0) * Hkv + g) * blk + (int64_t)n * S + tok_v % S) * ELT) &
+  const int64_t vo = ((((int64_t)max(pid_v, 0) * Hkv + g) * blk + (int64_t)n * S + (tok_v & (S - 1))) * ELT) &
                      -(int64_t)(pid_v >= 0);
   const uint8_t* kb = kpool + ko;
   const uint8_t* vb = vpool + vo;
@@ -347,6 +348,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
   const int q4 = lane >> 4, n = lane & 15;
   const int G = a.group;
   const int S = a.page_size;
+  const int lgS = __builtin_ctz(S);   // S is a power of two (checked on the host)
 
   __shared__ int s_pid[kPidWin];
   __shared__ float s_m[kWaves][16];
@@ -559,7 +561,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
     const int ntile = (w1 - w0 + kTile - 1) / kTile;
     int t = wave;
 #define KVFP8_ISSUE(T_, t_) \
-  issue_tile<FP8>(T_, w0 + (t_) * kTile, w1, e0, ne, s_pid, kpool, vpool, blk, S, a.num_kv_heads, g, q4, n)
+  issue_tile<FP8>(T_, w0 + (t_) * kTile, w1, e0, ne, s_pid, kpool, vpool, blk, S, lgS, a.num_kv_heads, g, q4, n)
     if (FP8) {
       // Two tiles in flight per wave.  Tiles past the end issue loads of the pool's first
       // line (masked), so the body is straight-line and both loop edges leave the same

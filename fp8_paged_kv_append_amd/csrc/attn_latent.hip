@@ -131,6 +131,7 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 31, hh = lane >> 5;
   const int S = a.page_size;
+  const int lgS = __builtin_ctz(S);   // S is a power of two (checked on the host)
   const int Hq = a.num_q_heads;
   const int hb0 = hg * kLatentHeadsPerBlock, hb1 = min(Hq, hb0 + kLatentHeadsPerBlock);
   const int h0 = hb0 + wave * kLHW;     // this wave's first head
@@ -304,10 +305,15 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
       const int tb_c = live ? tb : w0;
       // the two 16-token halves of a tile each lie inside one page (tile starts are 32-aligned, S % 16 == 0)
       // wave-uniform: kept in SGPRs, so the copy state costs no VGPRs across QK and PV
-      const int pid0 = __builtin_amdgcn_readfirstlane(s_pid[tb_c / S - e0]);
-      const int pid1 = ct.nv > 16 ? __builtin_amdgcn_readfirstlane(s_pid[(tb_c + 16) / S - e0]) : pid0;
-      ct.base0 = pool + (pid0 >= 0 ? ((int64_t)pid0 * S + tb_c % S) * C::ROWB : 0);
-      ct.base1 = ct.nv > 16 ? pool + (pid1 >= 0 ? ((int64_t)pid1 * S + (tb_c + 16) % S) * C::ROWB : 0) : ct.base0;
+      // (S a power of two: page and slot by shift and mask; both page ids read from LDS together, the
+      // second clamped into the window's staged entries when the tile has no second half)
+      const int s0 = __builtin_amdgcn_readfirstlane(s_pid[(tb_c >> lgS) - e0]);
+      const int s1 = __builtin_amdgcn_readfirstlane(s_pid[min(((tb_c + 16) >> lgS) - e0, ne - 1)]);
+      const int pid0 = s0;
+      const int pid1 = ct.nv > 16 ? s1 : pid0;
+      ct.base0 = pool + (pid0 >= 0 ? (((int64_t)pid0 << lgS) + (tb_c & (S - 1))) * C::ROWB : 0);
+      ct.base1 = ct.nv > 16 ? pool + (pid1 >= 0 ? (((int64_t)pid1 << lgS) + ((tb_c + 16) & (S - 1))) * C::ROWB : 0)
+                            : ct.base0;
       ct.dst = (uint32_t)(uintptr_t)((lds_u8*)(s_tile + bi * C::BUF) + 1024 * wave * C::NPW);
       return ct;
     };

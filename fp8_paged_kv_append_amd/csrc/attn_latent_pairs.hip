@@ -119,6 +119,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_latent_pair_kernel(LatentAr
   const int n = lane & 15, q4 = lane >> 4;
   const int x = wave >> 2;                       // half of the dims
   const int S = a.page_size;
+  const int lgS = __builtin_ctz(S);   // S is a power of two (checked on the host)
   const int Hq = a.num_q_heads;
   const int hb0 = hg * kPHB, hb1 = min(Hq, hb0 + kPHB);
   const int h0 = hb0 + 16 * (wave & 3);          // this pair's first head
@@ -251,10 +252,14 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_latent_pair_kernel(LatentAr
       const bool live = t < ntile;
       const int nv = live ? w1 - tb : 0;
       const int tb_c = live ? tb : w0;
-      const int pid0 = __builtin_amdgcn_readfirstlane(s_pid[tb_c / S - e0]);
-      const int pid1 = nv > 16 ? __builtin_amdgcn_readfirstlane(s_pid[(tb_c + 16) / S - e0]) : pid0;
-      const uint8_t* base0 = pool + (pid0 >= 0 ? ((int64_t)pid0 * S + tb_c % S) * kRowB : 0);
-      const uint8_t* base1 = nv > 16 ? pool + (pid1 >= 0 ? ((int64_t)pid1 * S + (tb_c + 16) % S) * kRowB : 0) : base0;
+      // (S a power of two: page and slot by shift and mask; both page ids read from LDS together)
+      const int s0 = __builtin_amdgcn_readfirstlane(s_pid[(tb_c >> lgS) - e0]);
+      const int s1 = __builtin_amdgcn_readfirstlane(s_pid[min(((tb_c + 16) >> lgS) - e0, ne - 1)]);
+      const int pid0 = s0;
+      const int pid1 = nv > 16 ? s1 : pid0;
+      const uint8_t* base0 = pool + (pid0 >= 0 ? (((int64_t)pid0 << lgS) + (tb_c & (S - 1))) * kRowB : 0);
+      const uint8_t* base1 =
+          nv > 16 ? pool + (pid1 >= 0 ? (((int64_t)pid1 << lgS) + ((tb_c + 16) & (S - 1))) * kRowB : 0) : base0;
       const uint32_t dst = (uint32_t)(uintptr_t)((lds_b*)(s_tile + bi * kBuf) + 1024 * wave * kNPW);
 #pragma unroll
       for (int k = 0; k < kNPW; ++k) {

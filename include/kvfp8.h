@@ -80,7 +80,7 @@ typedef struct ihipStream_t* hipStream_t;
 /* Shape of a page pool (host struct). */
 typedef struct kvfp8_pool_desc {
   int32_t num_pages;    /* P                                                   */
-  int32_t page_size;    /* S tokens per page; a multiple of 16, at most 256    */
+  int32_t page_size;    /* S tokens per page: 16, 32, 64, 128 or 256          */
   int32_t num_kv_heads; /* Hkv (1 for the latent cache)                        */
   int32_t head_dim;     /* D: K width (the latent width Dl for the latent cache) */
   int32_t v_dim;        /* Dv: V width (for the latent cache: the value part)  */
