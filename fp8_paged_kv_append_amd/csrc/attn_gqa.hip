@@ -688,7 +688,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
 // partial; the rows of one block are consecutive, so a block reads contiguous partials.
 constexpr int kMergeThreads = 128;
 
-template <int kGroup>
+template <int kGroup, bool F16>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(MergeArgs a) {
   const int tpr = a.v_dim / 4;  // threads per row
   const int64_t row = (int64_t)blockIdx.x * (kMergeThreads / tpr) + threadIdx.x / tpr;  // r * Hq + h
@@ -705,7 +705,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(MergeArgs a) 
   const int nvalid = min(a.num_splits, (L + a.chunk_tokens - 1) / a.chunk_tokens);
   const float* lse = a.lse_part + row * a.num_splits;
   const f32x4_t* part = reinterpret_cast<const f32x4_t*>(a.o_part + row * a.num_splits * a.v_dim + d);
-  const int stride = a.v_dim / 4;  // f32x4 per split row
+  const u32x2_t* parth =
+      reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint16_t*>(a.o_part) + row * a.num_splits * a.v_dim + d);
+  const int stride = a.v_dim / 4;  // 4-element vectors per split row
   // Splits in groups of kGroup (4, 8 or 16: the split count rounded up, at most 16) whose lse values
   // and partials are all loaded before any is used: one memory round trip per group (with few rows,
   // one request and many splits, the loads each thread has in flight are all the memory-level
@@ -721,7 +723,15 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(MergeArgs a) 
     for (int j = 0; j < kGroup; ++j) {
       if (c0 + j < nvalid) {
         x[j] = lse[c0 + j];
-        p[j] = part[(int64_t)(c0 + j) * stride];
+        if constexpr (F16) {
+          const u32x2_t h = parth[(int64_t)(c0 + j) * stride];
+          p[j] = f32x4_t{(float)__builtin_bit_cast(_Float16, (uint16_t)(h[0] & 0xFFFFu)),
+                         (float)__builtin_bit_cast(_Float16, (uint16_t)(h[0] >> 16)),
+                         (float)__builtin_bit_cast(_Float16, (uint16_t)(h[1] & 0xFFFFu)),
+                         (float)__builtin_bit_cast(_Float16, (uint16_t)(h[1] >> 16))};
+        } else {
+          p[j] = part[(int64_t)(c0 + j) * stride];
+        }
       } else {
         x[j] = -INFINITY;
         p[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -749,7 +759,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(MergeArgs a) 
     s = 0.f;
     o = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  const float inv = s > 0.f ? 1.f / s : 0.f;
+  const float inv = s > 0.f ? a.out_scale / s : 0.f;
   *out = u32x2_t{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
 }
 
@@ -774,6 +784,8 @@ hipError_t launch_attn_gqa(const AttnArgs& a, bool fp8, int batch, hipStream_t s
   m.max_ctx = a.max_ctx;
   m.pt_stride = a.pt_stride;
   m.page_size = a.page_size;
+  m.part_f16 = 0;
+  m.out_scale = 1.f;
   return launch_merge(m, batch, stream);
 }
 
@@ -783,12 +795,16 @@ hipError_t launch_merge(const MergeArgs& m_in, int batch, hipStream_t stream) {
   const int tpr = m.v_dim / 4;  // v_dim is 128 or 512: a power of two dividing 4 * kMergeThreads
   const int64_t rows_per_block = kMergeThreads / tpr;
   const int64_t blocks = (m.rows + rows_per_block - 1) / rows_per_block;
-  if (m.num_splits <= 4)
-    hipLaunchKernelGGL(attn_merge_kernel<4>, dim3((uint32_t)blocks), dim3(kMergeThreads), 0, stream, m);
-  else if (m.num_splits <= 8)
-    hipLaunchKernelGGL(attn_merge_kernel<8>, dim3((uint32_t)blocks), dim3(kMergeThreads), 0, stream, m);
-  else
-    hipLaunchKernelGGL(attn_merge_kernel<16>, dim3((uint32_t)blocks), dim3(kMergeThreads), 0, stream, m);
+  const dim3 g((uint32_t)blocks), t(kMergeThreads);
+  if (m.part_f16) {
+    if (m.num_splits <= 4) hipLaunchKernelGGL((attn_merge_kernel<4, true>), g, t, 0, stream, m);
+    else if (m.num_splits <= 8) hipLaunchKernelGGL((attn_merge_kernel<8, true>), g, t, 0, stream, m);
+    else hipLaunchKernelGGL((attn_merge_kernel<16, true>), g, t, 0, stream, m);
+  } else {
+    if (m.num_splits <= 4) hipLaunchKernelGGL((attn_merge_kernel<4, false>), g, t, 0, stream, m);
+    else if (m.num_splits <= 8) hipLaunchKernelGGL((attn_merge_kernel<8, false>), g, t, 0, stream, m);
+    else hipLaunchKernelGGL((attn_merge_kernel<16, false>), g, t, 0, stream, m);
+  }
   return hipGetLastError();
 }
 

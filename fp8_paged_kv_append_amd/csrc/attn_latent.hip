@@ -535,6 +535,23 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
         const u32x2_t v2 = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
         *reinterpret_cast<u32x2_t*>(&a.out[row * kLV + d0]) = v2;
       }
+  } else if constexpr (FP8) {
+    // fp16 partials of acc / l: convex combinations of e4m3 values (|x| <= 448, so no overflow and an
+    // 11-bit significand); the merge applies the tensor scale.  Half the bytes of fp32 partials, written
+    // here and read by the merge.
+    const int64_t slot = row * a.num_splits + split;
+    const float il = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* oh = reinterpret_cast<uint16_t*>(a.o_part);
+#pragma unroll
+    for (int db = 0; db < 16; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d0 = 32 * db + 8 * jg + 4 * hh;
+        const u32x2_t v2 = {pack_f16x2(acc[db][4 * jg] * il, acc[db][4 * jg + 1] * il),
+                            pack_f16x2(acc[db][4 * jg + 2] * il, acc[db][4 * jg + 3] * il)};
+        *reinterpret_cast<u32x2_t*>(&oh[slot * kLV + d0]) = v2;
+      }
+    if (hh == 0) a.lse_part[slot] = any_bad ? NAN : (l_run == 0.f ? -INFINITY : m_run + __log2f(l_run));
   } else {
     const int64_t slot = row * a.num_splits + split;
 #pragma unroll
@@ -577,6 +594,10 @@ hipError_t launch_attn_latent(const LatentArgs& a, bool fp8, bool pairs, hipStre
   m.flags = a.page_tags != nullptr ? a.flags_out : a.flags;
   m.num_q_heads = a.num_q_heads;
   m.v_dim = kLV;
+  // The FP8 kernel over all 128 heads stores fp16 partials of acc / l (the merge applies the tensor
+  // scale); the head-pair kernel keeps fp32 partials, which merged faster at one request x 32 splits.
+  m.part_f16 = fp8 && !pairs ? 1 : 0;
+  m.out_scale = fp8 && !pairs ? a.v_scale : 1.f;
   m.num_splits = a.num_splits;
   m.chunk_tokens = a.chunk_tiles * kLT;
   m.max_ctx = a.max_ctx;

@@ -45,6 +45,11 @@ struct MergeArgs {
   const int32_t* ctx_lens;
   const uint32_t* flags;
   int32_t num_q_heads, v_dim, num_splits, chunk_tokens, max_ctx, pt_stride, page_size;
+  // part_f16: the partials are fp16 (in o_part's first half, same indices) and the merged row is multiplied
+  // by out_scale (the FP8 latent cache: its partials are convex combinations of e4m3 values, |x| <= 448,
+  // stored before the tensor scale); otherwise fp32 partials and out_scale 1
+  int32_t part_f16;
+  float out_scale;
   int64_t rows;  // batch * num_q_heads (set by launch_merge)
 };
 
