@@ -684,57 +684,63 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
 
 // --- merge of the split partials ----------------------------------------------------------------
 
-// One thread per 4 consecutive value dims of a (request, head) row, 16-byte loads of each split's
-// partial; the rows of one block are consecutive, so a block reads contiguous partials.
+// One thread per VEC consecutive value dims of a (request, head) row (4 for fp32 partials, 8 for fp16
+// partials: one 16-byte load of each split's partial either way); the rows of one block are consecutive,
+// so a block reads contiguous partials.
 constexpr int kMergeThreads = 128;
 
 template <int kGroup, bool F16>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(MergeArgs a) {
-  const int tpr = a.v_dim / 4;  // threads per row
+  constexpr int VEC = F16 ? 8 : 4;
+  const int tpr = a.v_dim / VEC;  // threads per row
   const int64_t row = (int64_t)blockIdx.x * (kMergeThreads / tpr) + threadIdx.x / tpr;  // r * Hq + h
   if (row >= a.rows) return;
-  const int d = 4 * (threadIdx.x % tpr);
+  const int d = VEC * (threadIdx.x % tpr);
   const int r = (int)(row / a.num_q_heads);
   const int L = a.ctx_lens[r];
   const bool aborted = a.flags != nullptr && a.flags[r] != 0u;
-  u32x2_t* out = reinterpret_cast<u32x2_t*>(a.out + row * a.v_dim + d);
+  uint16_t* out = a.out + row * a.v_dim + d;
+  float o[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) o[e] = 0.f;
+  auto store_out = [&](float scale) {
+    uint32_t w[VEC / 2];
+#pragma unroll
+    for (int e = 0; e < VEC / 2; ++e) w[e] = pack_bf16x2(o[2 * e] * scale, o[2 * e + 1] * scale);
+    if constexpr (F16)
+      *reinterpret_cast<u32x4_t*>(out) = u32x4_t{w[0], w[1], w[2], w[3]};
+    else
+      *reinterpret_cast<u32x2_t*>(out) = u32x2_t{w[0], w[1]};
+  };
   if (aborted || L <= 0 || L > a.max_ctx || L > a.pt_stride * a.page_size) {
-    *out = u32x2_t{0u, 0u};
+    store_out(0.f);
     return;
   }
   const int nvalid = min(a.num_splits, (L + a.chunk_tokens - 1) / a.chunk_tokens);
   const float* lse = a.lse_part + row * a.num_splits;
-  const f32x4_t* part = reinterpret_cast<const f32x4_t*>(a.o_part + row * a.num_splits * a.v_dim + d);
-  const u32x2_t* parth =
-      reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint16_t*>(a.o_part) + row * a.num_splits * a.v_dim + d);
-  const int stride = a.v_dim / 4;  // 4-element vectors per split row
+  // split c's 16 bytes: at element (row * num_splits + c) * v_dim + d of the fp32 or fp16 partials
+  const int64_t e0 = row * a.num_splits * a.v_dim + d;
+  const u32x4_t* part = F16 ? reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.o_part) + e0)
+                            : reinterpret_cast<const u32x4_t*>(a.o_part + e0);
+  const int stride = a.v_dim / VEC;  // 16-byte vectors per split row
   // Splits in groups of kGroup (4, 8 or 16: the split count rounded up, at most 16) whose lse values
   // and partials are all loaded before any is used: one memory round trip per group (with few rows,
   // one request and many splits, the loads each thread has in flight are all the memory-level
   // parallelism there is; with few splits a small group keeps registers and ALU work down).  Groups
   // after the first rescale the running sums to the new maximum, as the online softmax does.
   float M = -INFINITY, s = 0.f;
-  f32x4_t o = {0.f, 0.f, 0.f, 0.f};
   bool nan = false;
   for (int c0 = 0; c0 < nvalid; c0 += kGroup) {
     float x[kGroup];
-    f32x4_t p[kGroup];
+    u32x4_t p[kGroup];
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
       if (c0 + j < nvalid) {
         x[j] = lse[c0 + j];
-        if constexpr (F16) {
-          const u32x2_t h = parth[(int64_t)(c0 + j) * stride];
-          p[j] = f32x4_t{(float)__builtin_bit_cast(_Float16, (uint16_t)(h[0] & 0xFFFFu)),
-                         (float)__builtin_bit_cast(_Float16, (uint16_t)(h[0] >> 16)),
-                         (float)__builtin_bit_cast(_Float16, (uint16_t)(h[1] & 0xFFFFu)),
-                         (float)__builtin_bit_cast(_Float16, (uint16_t)(h[1] >> 16))};
-        } else {
-          p[j] = part[(int64_t)(c0 + j) * stride];
-        }
+        p[j] = part[(int64_t)(c0 + j) * stride];
       } else {
         x[j] = -INFINITY;
-        p[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        p[j] = u32x4_t{0u, 0u, 0u, 0u};
       }
     }
     float gm = M;
@@ -746,21 +752,32 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(MergeArgs a) 
     if (gm == -INFINITY) continue;  // nothing but empty splits so far
     const float rs = exp2f(M - gm);  // 0 while M is still -inf
     s *= rs;
-    o *= rs;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[e] *= rs;
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
       const float f = exp2f(x[j] - gm);
       s += f;
-      o += f * p[j];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        // the element is copied out first: a bit cast of a vector element expression read element 0 here
+        const uint32_t u = p[j][F16 ? e >> 1 : e];
+        float v;
+        if constexpr (F16)
+          v = (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> (16 * (e & 1))));
+        else
+          v = __builtin_bit_cast(float, u);
+        o[e] += f * v;
+      }
     }
     M = gm;
   }
   if (nan) {  // a bad page seen by some split: the row is zero
     s = 0.f;
-    o = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[e] = 0.f;
   }
-  const float inv = s > 0.f ? a.out_scale / s : 0.f;
-  *out = u32x2_t{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+  store_out(s > 0.f ? a.out_scale / s : 0.f);
 }
 
 hipError_t launch_attn_gqa(const AttnArgs& a, bool fp8, int batch, hipStream_t stream) {
@@ -792,7 +809,7 @@ hipError_t launch_attn_gqa(const AttnArgs& a, bool fp8, int batch, hipStream_t s
 hipError_t launch_merge(const MergeArgs& m_in, int batch, hipStream_t stream) {
   MergeArgs m = m_in;
   m.rows = (int64_t)batch * m.num_q_heads;
-  const int tpr = m.v_dim / 4;  // v_dim is 128 or 512: a power of two dividing 4 * kMergeThreads
+  const int tpr = m.v_dim / (m.part_f16 ? 8 : 4);  // v_dim 128 or 512: tpr a power of two dividing kMergeThreads
   const int64_t rows_per_block = kMergeThreads / tpr;
   const int64_t blocks = (m.rows + rows_per_block - 1) / rows_per_block;
   const dim3 g((uint32_t)blocks), t(kMergeThreads);

@@ -50,6 +50,7 @@ constexpr int kLThreads = kLWaves * kWave;
 constexpr int kLHW = 32;                  // heads per wave
 constexpr int kLPidWin = 1024;
 constexpr float kLazy = 8.f;              // log2-domain slack before the accumulators are rescaled
+static_assert(kLPidWin % kLThreads == 0, "a window's page ids are loaded as kLPidWin / kLThreads per thread");
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -165,44 +166,24 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   // of qhi[ks] / qlo[ks].
   u32x4_t qv[36];
   v8i_t qhi[9], qlo[9];
-  float q_unscale = 1.f;
   const bool q_live = h0 + n < Hq;
   if constexpr (FP8) {
+    // the raw bf16 q (dims 64ks + 32hh .. +32 of this lane's head: 16 words per k-step, the first 8 in
+    // qhi[ks], the rest in qlo[ks]) is loaded here and turned into its two e4m3 terms in place once the
+    // first tiles' copies are in flight (below), so that its load overlaps the page-id loads and its
+    // conversion the copies
     const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(a.q + ((int64_t)r * Hq + h0 + n) * kLD + 32 * hh);
-    float amax = 0.f;
-    if (q_live) {
-#pragma unroll
-      for (int ks = 0; ks < 9; ++ks)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4_t w = qp[8 * ks + i];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w[e] & 0xFFFFu)), fabsf(bf16_bits_to_f32(w[e] >> 16))));
-        }
-    }
-    amax = fmaxf(amax, shfl_xor(amax, 32));
-    int ex;
-    frexpf(amax, &ex);  // amax < 2^ex
-    const float qs = ldexpf(1.f, 8 - ex);
-    q_unscale = ldexpf(1.f, ex - 8);
 #pragma unroll
     for (int ks = 0; ks < 9; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const u32x4_t w = q_live ? qp[8 * ks + i] : u32x4_t{0, 0, 0, 0};  // dims 64ks + 32hh + 8i .. +8
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const float f0 = bf16_bits_to_f32(w[2 * h2] & 0xFFFFu) * qs, f1 = bf16_bits_to_f32(w[2 * h2] >> 16) * qs;
-          const float f2 = bf16_bits_to_f32(w[2 * h2 + 1] & 0xFFFFu) * qs;
-          const float f3 = bf16_bits_to_f32(w[2 * h2 + 1] >> 16) * qs;
-          int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
-          hi = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, hi, true);
-          const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false), b1 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-          int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f0 - b0[0], f1 - b0[1], 0, false);
-          lo = __builtin_amdgcn_cvt_pk_fp8_f32(f2 - b1[0], f3 - b1[1], lo, true);
-          qhi[ks][2 * i + h2] = hi;
-          qlo[ks][2 * i + h2] = lo;
+        for (int e = 0; e < 4; ++e) {
+          if (i < 2)
+            qhi[ks][4 * i + e] = (int)w[e];
+          else
+            qlo[ks][4 * (i - 2) + e] = (int)w[e];
         }
       }
   } else {
@@ -218,6 +199,55 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
       for (int k = 0; k < 36; ++k) qv[k] = u32x4_t{0, 0, 0, 0};
     }
   }
+  // FP8: q*s, with s a power of two per head that puts max|q*s| in [128, 256), as two e4m3 terms hi + lo,
+  // lo = e4m3(q*s - hi) (exact for every element within 2^9 of the head's max |q|); 1/s joins the score
+  // scale.  Lane (hh, n) then holds dims 64ks + 32hh + b (b = 0..31) of k-step ks as byte b of qhi[ks] /
+  // qlo[ks].
+  float q_unscale = 1.f;
+  auto q_to_fp8 = [&]() {
+    float amax = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t w0 = (uint32_t)qhi[ks][j], w1 = (uint32_t)qlo[ks][j];
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w0 & 0xFFFFu)), fabsf(bf16_bits_to_f32(w0 >> 16))));
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w1 & 0xFFFFu)), fabsf(bf16_bits_to_f32(w1 >> 16))));
+      }
+    amax = fmaxf(amax, shfl_xor(amax, 32));
+    int ex;
+    frexpf(amax, &ex);  // amax < 2^ex
+    const float qs = ldexpf(1.f, 8 - ex);
+    q_unscale = ldexpf(1.f, ex - 8);
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks) {
+      // one k-step at a time, its words taken as new values: otherwise the compiler keeps the max pass's
+      // unpacked floats of all of q live for this pass and runs out of registers
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" : "+v"(qhi[ks]), "+v"(qlo[ks]));
+      uint32_t w[16];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        w[j] = (uint32_t)qhi[ks][j];
+        w[8 + j] = (uint32_t)qlo[ks][j];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const uint32_t wa = w[4 * i + 2 * h2], wb = w[4 * i + 2 * h2 + 1];
+          const float f0 = bf16_bits_to_f32(wa & 0xFFFFu) * qs, f1 = bf16_bits_to_f32(wa >> 16) * qs;
+          const float f2 = bf16_bits_to_f32(wb & 0xFFFFu) * qs, f3 = bf16_bits_to_f32(wb >> 16) * qs;
+          int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+          hi = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, hi, true);
+          const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false), b1 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+          int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f0 - b0[0], f1 - b0[1], 0, false);
+          lo = __builtin_amdgcn_cvt_pk_fp8_f32(f2 - b1[0], f3 - b1[1], lo, true);
+          qhi[ks][2 * i + h2] = hi;
+          qlo[ks][2 * i + h2] = lo;
+        }
+    }
+  };
 
   // The step's token (later layers of a decode step), stored before any tile copy by the block(s)
   // whose chunk holds position L - 1 (all head groups of that chunk store the same bytes); the wait
@@ -225,10 +255,6 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   // every wave's copies, which then read the token back like any other row.
   const bool tok_bad = a.c_new != nullptr && c0 <= L - 1 && L - 1 < c0 + chunk &&
                        !store_latent_row<FP8, kLD>(a, r, L, kLThreads);
-
-  // q has landed (and the token's stores are done) before any tile copy is in flight: the loop
-  // below then carries no waits for them
-  vm_wait<0>();
 
   // LDS byte offsets this lane reads, relative to a tile buffer
   // QK row reads: FP8 32 bytes at lat_row(n)*RS + 32hh + 64*ks; BF16 32 bytes at lat_row(n)*RS + 32hh + 64*p
@@ -262,107 +288,130 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
 
   const int32_t* pt = a.page_table + (int64_t)r * a.pt_stride;
   const uint8_t* pool = reinterpret_cast<const uint8_t*>(a.pool);
-  const float c_qk = a.qk_scale_log2 * q_unscale;  // log2-domain score scale (FP8: also undoes q's s)
+  float c_qk = a.qk_scale_log2;  // log2-domain score scale (FP8: times 1/s, once q is converted)
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t acc[16];
 #pragma unroll
   for (int db = 0; db < 16; ++db) acc[db] = f32x16_t{};
   bool bad = tok_bad;
 
-  // at most kLPidWin - 1 pages of tokens per window: a window starting mid-page still fits kLPidWin ids
+  // Tokens [c0, c1) in windows of at most kLPidWin - 1 pages (a window starting mid-page still fits
+  // kLPidWin ids), whose page ids are staged in LDS.
   const int win = ((kLPidWin - 1) * S / kLT) * kLT;
-  for (int w0 = c0; w0 < c1; w0 += win) {
-    const int w1 = min(c1, w0 + win);
-    const int e0 = w0 / S;
-    const int ne = (w1 - 1) / S - e0 + 1;
+  int w0 = c0, w1 = 0, e0 = 0, ne = 0, ntile = 0;
+  auto window_setup = [&]() {
+    w1 = min(c1, w0 + win);
+    e0 = w0 / S;
+    ne = (w1 - 1) / S - e0 + 1;
+    // the window's page ids (at most kLPidWin: kLPidWin / kLThreads per thread), loaded before the
+    // barrier; in the first window they are in flight with q's loads and the token's stores, all of
+    // which have landed before any tile copy is issued (the tile loop then carries no waits for them)
+    int pre[kLPidWin / kLThreads];
+#pragma unroll
+    for (int k = 0; k < kLPidWin / kLThreads; ++k) {
+      const int i = threadIdx.x + k * kLThreads;
+      pre[k] = i < ne ? pt[e0 + i] : 0;
+    }
+    vm_wait<0>();
     __syncthreads();  // the previous window's ids and tiles are no longer read
-    for (int i = threadIdx.x; i < ne; i += kLThreads) {
-      int p = pt[e0 + i];
-      if (p < 0 || p >= a.num_pages) {
-        bad = true;
-        p = -1;
+#pragma unroll
+    for (int k = 0; k < kLPidWin / kLThreads; ++k) {
+      const int i = threadIdx.x + k * kLThreads;
+      if (i < ne) {
+        int p = pre[k];
+        if (p < 0 || p >= a.num_pages) {
+          bad = true;
+          p = -1;
+        }
+        s_pid[i] = p;
       }
-      s_pid[i] = p;
     }
     __syncthreads();
-    const int ntile = (w1 - w0 + kLT - 1) / kLT;
+    ntile = (w1 - w0 + kLT - 1) / kLT;
+  };
 
-    // Copy tile t of the window into buffer bi: NPW 16-byte global->LDS loads per lane.  Every
-    // lane of every copy loads from inside the pool: tokens past the window end re-read the tile's
-    // first row (finite data, weight 0), padding slots and tiles past the end read the first
-    // row too, and a page id outside the pool reads the pool's first page (the request is zeroed).
-    struct CopyTile {
-      const uint8_t* base0;
-      const uint8_t* base1;
-      uint32_t dst;
-      int nv;
-    };
-    auto copy_prep = [&](int t, int bi) {
-      CopyTile ct;
-      const int tb = w0 + t * kLT;
-      const bool live = t < ntile;
-      ct.nv = live ? w1 - tb : 0;
-      const int tb_c = live ? tb : w0;
-      // the two 16-token halves of a tile each lie inside one page (tile starts are 32-aligned, S % 16 == 0)
-      // wave-uniform: kept in SGPRs, so the copy state costs no VGPRs across QK and PV
-      // (S a power of two: page and slot by shift and mask; both page ids read from LDS together, the
-      // second clamped into the window's staged entries when the tile has no second half)
-      const int s0 = __builtin_amdgcn_readfirstlane(s_pid[(tb_c >> lgS) - e0]);
-      const int s1 = __builtin_amdgcn_readfirstlane(s_pid[min(((tb_c + 16) >> lgS) - e0, ne - 1)]);
-      const int pid0 = s0;
-      const int pid1 = ct.nv > 16 ? s1 : pid0;
-      ct.base0 = pool + (pid0 >= 0 ? (((int64_t)pid0 << lgS) + (tb_c & (S - 1))) * C::ROWB : 0);
-      ct.base1 = ct.nv > 16 ? pool + (pid1 >= 0 ? (((int64_t)pid1 << lgS) + ((tb_c + 16) & (S - 1))) * C::ROWB : 0)
-                            : ct.base0;
-      ct.dst = (uint32_t)(uintptr_t)((lds_u8*)(s_tile + bi * C::BUF) + 1024 * wave * C::NPW);
-      return ct;
-    };
-    auto copy_one = [&](const CopyTile& ct, int k) {
-      const uint32_t tc = cp_tc[k];
-      const int tok = (int)(tc >> 16);
-      const uint32_t off = tok < ct.nv ? (tc & 0xFFFFu) : 0u;  // past the end: the tile's first row
-      const uint8_t* src = (tok < ct.nv && tok >= 16 ? ct.base1 : ct.base0) + off;
-      lds_copy16(src, ct.dst + 1024 * k);
-    };
-    auto copy_tile = [&](int t, int bi) {
-      const CopyTile ct = copy_prep(t, bi);
+  // Copy tile t of the window into buffer bi: NPW 16-byte global->LDS loads per lane.  Every
+  // lane of every copy loads from inside the pool: tokens past the window end re-read the tile's
+  // first row (finite data, weight 0), padding slots and tiles past the end read the first
+  // row too, and a page id outside the pool reads the pool's first page (the request is zeroed).
+  struct CopyTile {
+    const uint8_t* base0;
+    const uint8_t* base1;
+    uint32_t dst;
+    int nv;
+  };
+  auto copy_prep = [&](int t, int bi) {
+    CopyTile ct;
+    const int tb = w0 + t * kLT;
+    const bool live = t < ntile;
+    ct.nv = live ? w1 - tb : 0;
+    const int tb_c = live ? tb : w0;
+    // the two 16-token halves of a tile each lie inside one page (tile starts are 32-aligned, S % 16 == 0)
+    // wave-uniform: kept in SGPRs, so the copy state costs no VGPRs across QK and PV
+    // (S a power of two: page and slot by shift and mask; both page ids read from LDS together, the
+    // second clamped into the window's staged entries when the tile has no second half)
+    const int s0 = __builtin_amdgcn_readfirstlane(s_pid[(tb_c >> lgS) - e0]);
+    const int s1 = __builtin_amdgcn_readfirstlane(s_pid[min(((tb_c + 16) >> lgS) - e0, ne - 1)]);
+    const int pid0 = s0;
+    const int pid1 = ct.nv > 16 ? s1 : pid0;
+    ct.base0 = pool + (pid0 >= 0 ? (((int64_t)pid0 << lgS) + (tb_c & (S - 1))) * C::ROWB : 0);
+    ct.base1 = ct.nv > 16 ? pool + (pid1 >= 0 ? (((int64_t)pid1 << lgS) + ((tb_c + 16) & (S - 1))) * C::ROWB : 0)
+                          : ct.base0;
+    ct.dst = (uint32_t)(uintptr_t)((lds_u8*)(s_tile + bi * C::BUF) + 1024 * wave * C::NPW);
+    return ct;
+  };
+  auto copy_one = [&](const CopyTile& ct, int k) {
+    const uint32_t tc = cp_tc[k];
+    const int tok = (int)(tc >> 16);
+    const uint32_t off = tok < ct.nv ? (tc & 0xFFFFu) : 0u;  // past the end: the tile's first row
+    const uint8_t* src = (tok < ct.nv && tok >= 16 ? ct.base1 : ct.base0) + off;
+    lds_copy16(src, ct.dst + 1024 * k);
+  };
+  auto copy_tile = [&](int t, int bi) {
+    const CopyTile ct = copy_prep(t, bi);
 #pragma unroll
-      for (int k = 0; k < C::NPW; ++k) copy_one(ct, k);
-    };
+    for (int k = 0; k < C::NPW; ++k) copy_one(ct, k);
+  };
 
-    // Tiles are software-pipelined by one: iteration t publishes tile t+1 and computes its scores
-    // (QK MFMAs) while tile t's exponentials run between them, then accumulates tile t (PV).  The
-    // ring holds tile t (PV), tile t+1 (QK) and NBUF-2 tiles whose copies are in flight.
-    constexpr int QD = FP8 ? 1 : 1, PD = FP8 ? 4 : 2;  // operand reads ahead of the math
-    auto qk_read = [&](const uint8_t* tile, int p, u32x4_t(&dst)[2]) {  // 32 bytes of this lane's row
-      dst[0] = *reinterpret_cast<const u32x4_t*>(tile + qk_off + 64 * p);
-      dst[1] = *reinterpret_cast<const u32x4_t*>(tile + qk_off + 64 * p + 16);
-    };
-    auto pv_read = [&](const lds_u8* lt, int i, u32x4_t& dst) {  // PV step i = 16*ks + db
-      const int db = i & 15, ks = i >> 4;
-      const lds_u8* src = lt + pv_off + ks * 16 * C::RS + 32 * ELT * db;
-      if (FP8) {
-        const i32x2_t t8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)src);
-        dst[0] = (uint32_t)t8[0];
-        dst[1] = (uint32_t)t8[1];
-      } else {
-        const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)src);
-        const i16x4_t t1 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(src + C::RS));
-        const u32x2_t u0 = __builtin_bit_cast(u32x2_t, t0), u1 = __builtin_bit_cast(u32x2_t, t1);
-        dst = u32x4_t{u0[0], u0[1], u1[0], u1[1]};
-      }
-    };
-    auto pv_cvt = [&](const u32x4_t& raw) {
-      if (FP8) {
-        const u32x2_t lo = e4m3x4_to_bf16x4(raw[0]), hi = e4m3x4_to_bf16x4(raw[1]);
-        return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-      }
-      return raw;
-    };
+  // Tiles are software-pipelined by one: iteration t publishes tile t+1 and computes its scores
+  // (QK MFMAs) while tile t's exponentials run between them, then accumulates tile t (PV).  The
+  // ring holds tile t (PV), tile t+1 (QK) and NBUF-2 tiles whose copies are in flight.
+  constexpr int QD = FP8 ? 1 : 1, PD = FP8 ? 4 : 2;  // operand reads ahead of the math
+  auto qk_read = [&](const uint8_t* tile, int p, u32x4_t(&dst)[2]) {  // 32 bytes of this lane's row
+    dst[0] = *reinterpret_cast<const u32x4_t*>(tile + qk_off + 64 * p);
+    dst[1] = *reinterpret_cast<const u32x4_t*>(tile + qk_off + 64 * p + 16);
+  };
+  auto pv_read = [&](const lds_u8* lt, int i, u32x4_t& dst) {  // PV step i = 16*ks + db
+    const int db = i & 15, ks = i >> 4;
+    const lds_u8* src = lt + pv_off + ks * 16 * C::RS + 32 * ELT * db;
+    if (FP8) {
+      const i32x2_t t8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)src);
+      dst[0] = (uint32_t)t8[0];
+      dst[1] = (uint32_t)t8[1];
+    } else {
+      const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)src);
+      const i16x4_t t1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(src + C::RS));
+      const u32x2_t u0 = __builtin_bit_cast(u32x2_t, t0), u1 = __builtin_bit_cast(u32x2_t, t1);
+      dst = u32x4_t{u0[0], u0[1], u1[0], u1[1]};
+    }
+  };
+  auto pv_cvt = [&](const u32x4_t& raw) {
+    if (FP8) {
+      const u32x2_t lo = e4m3x4_to_bf16x4(raw[0]), hi = e4m3x4_to_bf16x4(raw[1]);
+      return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    }
+    return raw;
+  };
 
+  window_setup();
 #pragma unroll
-    for (int t = 0; t < C::NBUF - 2; ++t) copy_tile(t, t);
+  for (int t = 0; t < C::NBUF - 2; ++t) copy_tile(t, t);
+  if constexpr (FP8) {  // q's e4m3 terms, while the first tiles land
+    q_to_fp8();
+    c_qk = a.qk_scale_log2 * q_unscale;
+  }
+  while (true) {
     for (int t = -1; t < ntile; ++t) {
       vm_wait<C::NPW * (C::NBUF - 3)>();  // this wave's copies of tile t+1 have landed
       __syncthreads();                    // everyone's have; everyone is done with tile t-1
@@ -508,6 +557,11 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
       }
     }
     vm_wait<0>();  // copies issued past the window's last tile have landed before the buffers are reused
+    w0 += win;
+    if (w0 >= c1) break;
+    window_setup();
+#pragma unroll
+    for (int t = 0; t < C::NBUF - 2; ++t) copy_tile(t, t);
   }
 
   // ---- write this wave's heads (a page id outside the pool zeroes the request)
