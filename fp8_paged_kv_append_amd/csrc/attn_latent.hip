@@ -68,7 +68,7 @@ struct LCfg {
   static constexpr int NINST = (kLT * SLOTS + 63) / 64;           // 1 KiB copies per tile
   static constexpr int NPW = (NINST + kLWaves - 1) / kLWaves;     // copies per wave per tile
   static constexpr int BUF = NPW * kLWaves * 1024;                // bytes per tile buffer
-  static constexpr int NBUF = FP8 ? 5 : 3;                        // tile buffers
+  static constexpr int NBUF = FP8 ? 4 : 3;                        // tile buffers
 };
 
 // LDS row of tile token t.  FP8: the 8 tokens a PV transpose read of one half-wave
