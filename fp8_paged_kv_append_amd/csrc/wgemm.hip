@@ -24,8 +24,8 @@
 // 256-wide K chunks are staged in LDS (double buffered, the next chunk's global loads issued a chunk
 // ahead).  Either way the four waves share them; each
 // wave streams its own weight tiles with an 8-group register ring (8 KB of INT4 / 16 KB of FP8 in
-// flight per wave).  With several splits, fp32 partials go to the workspace and a second kernel adds
-// them in split order.
+// flight per wave).  With several splits, fp32 partials go to the workspace and the last block of each
+// column group to finish adds them in split order, inside the same launch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
