@@ -119,3 +119,22 @@ def test_latent_query_dynamic_range(kv_dtype):
     for r in range(w.batch):
         ref = c.oracle_request(r)[7]
         assert np.max(attention.row_rel_error(codec.f64_from_bf16(got[r, 7])[None], ref[None])) <= ATTN_TOL
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_latent_128_head_kernel_many_splits(kv_dtype):
+    """6 and 12 splits of more than 1,024 tokens each, so the 128-head kernel runs (not the wave-pair one)
+    and the merge takes groups of 8 and 16 splits: fp16 partials for the FP8 cache, fp32 for BF16.  The
+    second request is shorter, so its last splits are empty.  Rows within tolerance of the oracle, and the
+    split counts agree with each other."""
+    w = wl.WORKLOADS["latent"].with_(batch=2, num_pages=400, ctx_lo=9000, ctx_hi=14000)
+    lens = np.array([14000, 9000], dtype=np.int32)
+    note(f"latent 128-head kernel, 6 and 12 splits {kv_dtype}")
+    c = Case(w, kv_dtype, lens=lens)
+    c.fill_device()
+    outs = []
+    for splits in (6, 12):
+        got = _latent_attend(c, num_splits=splits)
+        _check(c, got)
+        outs.append(codec.f64_from_bf16(got))
+    assert np.max(attention.row_rel_error(outs[1], outs[0])) <= 2.0 ** -7
