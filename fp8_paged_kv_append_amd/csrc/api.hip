@@ -586,7 +586,8 @@ int kv_decode_step_bf16(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* la
 size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t v_dim, int32_t num_splits) {
   if (batch <= 0 || num_q_heads <= 0 || v_dim <= 0 || num_splits <= 1) return 0;
   const size_t rows = (size_t)batch * num_q_heads * num_splits;
-  // the split counters, then the fp32 partials and lse of every (request, head, split)
+  // the split counters, then the partials (fp32; the FP8 latent 128-head kernel stores fp16 in the first
+  // half of the same region) and lse of every (request, head, split)
   return attn_count_bytes(batch, num_q_heads) + rows * (size_t)v_dim * sizeof(float) + rows * sizeof(float);
 }
 
