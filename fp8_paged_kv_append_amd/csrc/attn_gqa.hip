@@ -723,7 +723,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(MergeArgs a) 
   const u32x4_t* part = F16 ? reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.o_part) + e0)
                             : reinterpret_cast<const u32x4_t*>(a.o_part + e0);
   const int stride = a.v_dim / VEC;  // 16-byte vectors per split row
-  // Splits in groups of kGroup (4, 8 or 16: the split count rounded up, at most 16) whose lse values
+  // Splits in groups of kGroup (4, 8, 16 or 32: the split count rounded up, at most 32) whose lse values
   // and partials are all loaded before any is used: one memory round trip per group (with few rows,
   // one request and many splits, the loads each thread has in flight are all the memory-level
   // parallelism there is; with few splits a small group keeps registers and ALU work down).  Groups
@@ -816,11 +816,13 @@ hipError_t launch_merge(const MergeArgs& m_in, int batch, hipStream_t stream) {
   if (m.part_f16) {
     if (m.num_splits <= 4) hipLaunchKernelGGL((attn_merge_kernel<4, true>), g, t, 0, stream, m);
     else if (m.num_splits <= 8) hipLaunchKernelGGL((attn_merge_kernel<8, true>), g, t, 0, stream, m);
-    else hipLaunchKernelGGL((attn_merge_kernel<16, true>), g, t, 0, stream, m);
+    else if (m.num_splits <= 16) hipLaunchKernelGGL((attn_merge_kernel<16, true>), g, t, 0, stream, m);
+    else hipLaunchKernelGGL((attn_merge_kernel<32, true>), g, t, 0, stream, m);
   } else {
     if (m.num_splits <= 4) hipLaunchKernelGGL((attn_merge_kernel<4, false>), g, t, 0, stream, m);
     else if (m.num_splits <= 8) hipLaunchKernelGGL((attn_merge_kernel<8, false>), g, t, 0, stream, m);
-    else hipLaunchKernelGGL((attn_merge_kernel<16, false>), g, t, 0, stream, m);
+    else if (m.num_splits <= 16) hipLaunchKernelGGL((attn_merge_kernel<16, false>), g, t, 0, stream, m);
+    else hipLaunchKernelGGL((attn_merge_kernel<32, false>), g, t, 0, stream, m);
   }
   return hipGetLastError();
 }

@@ -648,10 +648,9 @@ hipError_t launch_attn_latent(const LatentArgs& a, bool fp8, bool pairs, hipStre
   m.flags = a.page_tags != nullptr ? a.flags_out : a.flags;
   m.num_q_heads = a.num_q_heads;
   m.v_dim = kLV;
-  // The FP8 kernel over all 128 heads stores fp16 partials of acc / l (the merge applies the tensor
-  // scale); the head-pair kernel keeps fp32 partials, which merged faster at one request x 32 splits.
-  m.part_f16 = fp8 && !pairs ? 1 : 0;
-  m.out_scale = fp8 && !pairs ? a.v_scale : 1.f;
+  // both FP8 kernels store fp16 partials of acc / l; the merge applies the tensor scale
+  m.part_f16 = fp8 ? 1 : 0;
+  m.out_scale = fp8 ? a.v_scale : 1.f;
   m.num_splits = a.num_splits;
   m.chunk_tokens = a.chunk_tiles * kLT;
   m.max_ctx = a.max_ctx;

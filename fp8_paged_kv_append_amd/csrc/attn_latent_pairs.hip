@@ -411,11 +411,16 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_latent_pair_kernel(LatentAr
       *reinterpret_cast<u32x2_t*>(&a.out[row * kPV + d0]) = u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
     }
   } else {
+    // fp16 partials of acc / l (convex combinations of e4m3 values, |x| <= 448: no overflow, an 11-bit
+    // significand); the merge applies the tensor scale
     const int64_t slot = row * a.num_splits + split;
+    const float il = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* oh = reinterpret_cast<uint16_t*>(a.o_part);
 #pragma unroll
     for (int db = 0; db < 16; ++db) {
       const int d0 = 256 * x + 16 * db + 4 * q4;
-      *reinterpret_cast<f32x4_t*>(&a.o_part[slot * kPV + d0]) = acc[db] * inv;
+      const f32x4_t v = acc[db] * il;
+      *reinterpret_cast<u32x2_t*>(&oh[slot * kPV + d0]) = u32x2_t{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
     }
     if (x == 0 && q4 == 0)
       a.lse_part[slot] = any_bad ? NAN : (l_run == 0.f ? -INFINITY : m_run + __log2f(l_run));
