@@ -138,3 +138,22 @@ def test_latent_128_head_kernel_many_splits(kv_dtype):
         _check(c, got)
         outs.append(codec.f64_from_bf16(got))
     assert np.max(attention.row_rel_error(outs[1], outs[0])) <= 2.0 ** -7
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_latent_one_request_many_splits(kv_dtype):
+    """One request of 4096 tokens over 128 heads at the library's split count (32: the wave-pair kernel with
+    fp16 partials for the FP8 cache, the 128-head kernel with fp32 partials for BF16) and at 20: the merge
+    takes all of a row's splits in one group of 32.  Rows within tolerance of the oracle, and the two split
+    counts agree."""
+    w = wl.WORKLOADS["latent"].with_(batch=1, num_pages=80, ctx_lo=4096, ctx_hi=4096)
+    note(f"latent one request, 32 and 20 splits {kv_dtype}")
+    c = Case(w, kv_dtype)
+    c.fill_device()
+    assert kv.paged_decode_attn_latent_auto_splits(1, w.num_q_heads, c.max_ctx) == 32
+    outs = []
+    for splits in (0, 20):
+        got = _latent_attend(c, num_splits=splits)
+        _check(c, got)
+        outs.append(codec.f64_from_bf16(got))
+    assert np.max(attention.row_rel_error(outs[1], outs[0])) <= 2.0 ** -7
