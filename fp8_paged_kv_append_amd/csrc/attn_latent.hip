@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   constexpr int ELT = C::ELT;
   __shared__ __align__(1024) uint8_t s_tile[C::NBUF * C::BUF];
   __shared__ int s_pid[kLPidWin];
-  __shared__ f32x4_t s_sc[kLWaves][4][kWave];  // each wave's next-tile scores, parked across PV
+  __shared__ f32x4_t s_sc[FP8 ? 1 : kLWaves][4][kWave];  // BF16: each wave's next-tile scores, parked across PV
   __shared__ int s_bad;
   __shared__ uint32_t s_flag[kLWaves];
 
@@ -404,6 +404,7 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
     return raw;
   };
 
+  f32x16_t sc_next = f32x16_t{};  // scores of the next tile, from one iteration's QK to the next one's softmax
   window_setup();
 #pragma unroll
   for (int t = 0; t < C::NBUF - 2; ++t) copy_tile(t, t);
@@ -428,15 +429,18 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
 
       // ---- softmax of tile t, first part: masked scores (log2 domain), tile max, lazy rescale;
       // the scores of head n are those of tokens 8(j/4) + 4hh + j%4 (computed in iteration t-1)
-      f32x16_t sc = f32x16_t{};
-      if (has_cur) {
+      // the scores of tile t (unused, every token masked, while there is no tile t)
+      f32x16_t sc = sc_next;
+      if constexpr (!FP8) {
+        if (has_cur) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const f32x4_t v = s_sc[wave][k][lane];
-          sc[4 * k] = v[0];
-          sc[4 * k + 1] = v[1];
-          sc[4 * k + 2] = v[2];
-          sc[4 * k + 3] = v[3];
+          for (int k = 0; k < 4; ++k) {
+            const f32x4_t v = s_sc[wave][k][lane];
+            sc[4 * k] = v[0];
+            sc[4 * k + 1] = v[1];
+            sc[4 * k + 2] = v[2];
+            sc[4 * k + 3] = v[3];
+          }
         }
       }
       float x[16];
@@ -523,11 +527,16 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // the scores are read by VALU: keep them in VGPRs, leaving the AGPRs to the 256 accumulators;
-      // they wait in LDS while PV runs (the registers are needed there)
+      // the scores are read by VALU: VGPRs (the AGPRs hold the 256 accumulators).  FP8: kept in registers
+      // until the next iteration (in those tile t's exponentials leave free once PV has packed them);
+      // BF16, whose PV holds more registers, parks them in LDS
       asm volatile("" : "+v"(sn));
+      if constexpr (FP8) {
+        sc_next = sn;
+      } else {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) s_sc[wave][k][lane] = f32x4_t{sn[4 * k], sn[4 * k + 1], sn[4 * k + 2], sn[4 * k + 3]};
+        for (int k = 0; k < 4; ++k) s_sc[wave][k][lane] = f32x4_t{sn[4 * k], sn[4 * k + 1], sn[4 * k + 2], sn[4 * k + 3]};
+      }
 
       if (has_cur) {
         // ---- O^T += V^T P^T of tile t: 2 k-steps of 16 tokens x 16 blocks of 32 value dims (the
