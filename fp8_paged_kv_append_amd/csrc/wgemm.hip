@@ -23,8 +23,9 @@
 // output tile 4*blockIdx.x + w.  For M <= 16 the split's activation rows stay resident in LDS; above,
 // 256-wide K chunks are staged in LDS (double buffered, the next chunk's global loads issued a chunk
 // ahead).  Either way the four waves share them; each
-// wave streams its own weight tiles with an 8-group register ring (8 KB of INT4 / 16 KB of FP8 in
-// flight per wave).  With several splits, fp32 partials go to the workspace and the last block of each
+// wave streams its own weight tiles with a register ring of 8 groups (8 KB of INT4 / 16 KB of FP8 in
+// flight per wave; 4 INT4 / 8 FP8 groups when the waves split one tile's K range; M > 16: 8 groups up to
+// 32 rows, 4 above), whose last pass issues no refills.  With several splits, fp32 partials go to the workspace and the last block of each
 // column group to finish adds them in split order, inside the same launch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -87,9 +88,18 @@ __device__ __forceinline__ float sum8_bf16(const u32x4_t& v) {
   return s;
 }
 
-// bf16 pair of two INT4 codes (plus the bias 136) from the nibbles at bits 4i and 16 + 4i.
-__device__ __forceinline__ uint32_t w4_pair(uint32_t w, int i) {
-  return ((w >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
+// bf16 pair of two INT4 codes (plus the bias 136) from the nibbles at bits 4i and 16 + 4i: a shift and one
+// v_and_or_b32.  The bias passes through an empty asm so that the compiler sees a register, not a
+// constant: with two 32-bit constants it splits the AND-OR into two instructions (a three-operand ALU
+// instruction of this ISA takes no literal).  The AND-OR itself stays compiler-generated, so the wait
+// states the compiler inserts between an ALU write and a matrix-core read of the same register apply to it.
+__device__ __forceinline__ uint32_t w4_pair(uint32_t w, int i, uint32_t bias) {
+  return ((w >> (4 * i)) & 0x000F000Fu) | bias;
+}
+__device__ __forceinline__ uint32_t w4_bias() {
+  uint32_t b = 0x43004300u;
+  asm("" : "+v"(b));
+  return b;
 }
 
 // One wave's stream of weight groups: the codes of output tile `tile`, groups g0 + g.  Every load is
@@ -133,16 +143,39 @@ __device__ __forceinline__ void load_scales(const WgemmArgs& a, int tile0, int n
   }
 }
 
+// The same scales in two steps, so that their load latency overlaps the weight ring's instead of coming
+// before it: passes before the last (only when the block's scales exceed one pass of its threads) are
+// staged at once; the last pass is loaded into `last` and the LDS element offset it belongs at returned
+// (-1: none), for the caller to store after the wait that retires it.
+__device__ __forceinline__ int load_scales_split(const WgemmArgs& a, int tile0, int ntiles, int g0, int ng, int gcap,
+                                                 uint16_t* s_sc, int nthreads, u32x4_t& last) {
+  const int KG = a.K / kGroup;
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.s, (uint32_t)((int64_t)a.N * KG * 2));
+  const int total = ntiles * gcap * 2;
+  const int last0 = (total - 1) / nthreads * nthreads;
+  auto off = [&](int i) {
+    const int t = i / (gcap * 2), g = (i / 2) % gcap;
+    const bool ok = i < total && (tile0 + t) * 16 < a.N && g < ng;
+    return ok ? (uint32_t)(((int64_t)(tile0 + t) * KG + g0 + g) * 32 + 16 * (i & 1)) : kOOB;
+  };
+  auto slot = [&](int i) { return ((i / (gcap * 2)) * gcap + (i / 2) % gcap) * 16 + 8 * (i & 1); };
+  for (int i = threadIdx.x; i < last0; i += nthreads)
+    *reinterpret_cast<u32x4_t*>(s_sc + slot(i)) = __builtin_amdgcn_raw_buffer_load_b128(sr, off(i), 0, 0);
+  const int i = last0 + threadIdx.x;
+  last = __builtin_amdgcn_raw_buffer_load_b128(sr, off(i), 0, 0);
+  return i < total ? slot(i) : -1;
+}
+
 // The B operand of k-step j (eight bf16 values e = 0..7) from one group's codes.
 template <bool W4>
 __device__ __forceinline__ u32x4_t expand(const u32x4_t (&w)[W4 ? 1 : 2], int j) {
   u32x4_t b;
   if constexpr (W4) {
-    const uint32_t wd = w[0][j];
-    b[0] = w4_pair(wd, 0);
-    b[1] = w4_pair(wd, 1);
-    b[2] = w4_pair(wd, 2);
-    b[3] = w4_pair(wd, 3);
+    const uint32_t wd = w[0][j], bias = w4_bias();
+    b[0] = w4_pair(wd, 0, bias);
+    b[1] = w4_pair(wd, 1, bias);
+    b[2] = w4_pair(wd, 2, bias);
+    b[3] = w4_pair(wd, 3, bias);
   } else {
     const u32x2_t lo = e4m3x4_to_bf16x4(w[j >> 1][2 * (j & 1)]);
     const u32x2_t hi = e4m3x4_to_bf16x4(w[j >> 1][2 * (j & 1) + 1]);
@@ -247,18 +280,23 @@ __device__ __forceinline__ void store_out(const WgemmArgs& a, const f32x4_t (&ac
 // group sums [group][16]); after one load the waves only stream weights, with no barrier.
 // WK = false: the block covers WB output tiles, one per wave, each over the whole split (the staging is
 // shared by WB tiles).
-// WK = true: the block is one output tile and the four waves split its K range (wave w takes the w-th
-// quarter of the groups); they add their results through LDS in wave order -- a K split with neither
-// a workspace nor a second launch.
-template <bool W4, bool WK, int WB = 4>
-__global__ __launch_bounds__(WK ? 256 : 64 * WB) void wgemm_small_kernel(WgemmArgs a) {
+// WK = true: the block is one output tile and its WB (kWkWaves = 4) waves split its K range (wave w takes
+// the w-th part of the groups); they add their results through LDS in wave order -- a K split with
+// neither a workspace nor a second launch.  Eight or sixteen waves per tile measured slower at M=1
+// (INT4 11.0 / 11.8 against 9.1 us on 8192 x 8192).
+template <bool W4, bool WK, int WB>
+__global__ __launch_bounds__(64 * WB) void wgemm_small_kernel(WgemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int kTiles = WK ? 1 : WB;
-  constexpr int kThr = WK ? 256 : 64 * WB;
-  // groups in flight per wave, measured on 8192 x 8192: with the K range cut among the waves (M <= 4) 4
-  // beats 8 (INT4 M=1 11.7 against 12.4 us, FP8 14.9 against 15.2) and 16 is slower (14.5, 17.0); split over
+  constexpr int kThr = 64 * WB;
+  // groups in flight per wave, measured on 8192 x 8192: with the K range cut among the waves (M <= 4),
+  // INT4 4 (M=1 9.1 us; 6 / 8 / 16: 9.5 / 9.8 / 11.9), FP8 8 (M=1 14.5 against 14.9 with 4); split over
   // blocks, 4 and 8 are alike and 12 and 16 slower
-  constexpr int kRingS = WK ? 4 : kRing;
+  constexpr int kRingS = WK ? (W4 ? 4 : 8) : kRing;
+  // Activation passes wholly past the data are skipped (a load past the buffer still costs an issue slot and a
+  // return: at M=1 the 12 of 16 that are empty cost ~2 us per launch) -- in the K-split form only: the branches
+  // raise the eight-wave kernel from 87 to 239 VGPRs (one block per CU instead of two, INT4 M=16 13.7 -> 16.1 us)
+  constexpr bool kXLim = WK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nn = lane & 15, qq = lane >> 4;
   const int KG = a.K / kGroup;
@@ -272,14 +310,15 @@ __global__ __launch_bounds__(WK ? 256 : 64 * WB) void wgemm_small_kernel(WgemmAr
 
   // the wave's tile and groups
   const int tile = WK ? blockIdx.x : blockIdx.x * WB + wave;
-  const int gq = WK ? (ng + 3) / 4 : ng;
+  const int gq = WK ? (ng + WB - 1) / WB : ng;
   const int gw0 = WK ? wave * gq : 0;                    // first group of the wave inside the split
   const int ngw = WK ? max(0, min(gq, ng - gw0)) : ng;
   const int st = WK ? 0 : wave;                          // the wave's tile inside s_sc
 
   const WStream<W4> ws(a, tile, g0 + gw0, ngw, lane);
   constexpr int kB = WStream<W4>::kB;
-  load_scales(a, WK ? blockIdx.x : blockIdx.x * WB, kTiles, g0, ng, gcap, s_sc, kThr);
+  u32x4_t sc_last;
+  const int sc_slot = load_scales_split(a, WK ? blockIdx.x : blockIdx.x * WB, kTiles, g0, ng, gcap, s_sc, kThr, sc_last);
 
   // Activations, then the weight ring, then one wait that leaves exactly the ring outstanding: the
   // loads retire in issue order, so the activations go first (their latency overlaps the ring's), and
@@ -313,7 +352,10 @@ __global__ __launch_bounds__(WK ? 256 : 64 * WB) void wgemm_small_kernel(WgemmAr
   }
   u32x4_t v[kXB];
 #pragma unroll
-  for (int t = 0; t < kXB; ++t) v[t] = __builtin_amdgcn_raw_buffer_load_b128(xr, x_off(xbase + kThr * t + tid), 0, 0);
+  for (int t = 0; t < kXB; ++t) {
+    if (!kXLim || xbase + kThr * t < total) v[t] = __builtin_amdgcn_raw_buffer_load_b128(xr, x_off(xbase + kThr * t + tid), 0, 0);
+    else v[t] = u32x4_t{0u, 0u, 0u, 0u};
+  }
   __builtin_amdgcn_sched_barrier(0);
   u32x4_t wr[kRingS][kB / 16];
 #pragma unroll
@@ -323,31 +365,40 @@ __global__ __launch_bounds__(WK ? 256 : 64 * WB) void wgemm_small_kernel(WgemmAr
   }
   __builtin_amdgcn_s_waitcnt(vm_wait_enc(kRingS * (kB / 16)));
 #pragma unroll
-  for (int t = 0; t < kXB; ++t) x_put(xbase + kThr * t + tid, v[t]);
+  for (int t = 0; t < kXB; ++t)
+    if (!kXLim || xbase + kThr * t < total) x_put(xbase + kThr * t + tid, v[t]);
+  if (sc_slot >= 0) *reinterpret_cast<u32x4_t*>(s_sc + sc_slot) = sc_last;
   __syncthreads();
 
   // rows >= M read row M-1: their results are never stored
   const uint8_t* xa = smem + min(nn, a.M - 1) * row_bytes + 16 * qq;
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int base = 0; base < ngw; base += kRingS) {
+  auto group = [&](int base, int u, bool refill) {
+    const int gc = gw0 + min(base + u, ngw - 1);   // a group past the wave's range has zero codes and scale
+    u32x4_t av[4];
 #pragma unroll
-    for (int u = 0; u < kRingS; ++u) {
-      const int gc = gw0 + min(base + u, ngw - 1);   // a group past the wave's range has zero codes and scale
-      u32x4_t av[4];
+    for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const u32x4_t*>(xa + (gc * kGroup + 32 * j) * 2);
+    const float sc = bf16_bits_to_f32(s_sc[(st * gcap + gc) * 16 + nn]);
+    // rows >= M start from whatever their unused entries hold: their results are never stored
+    f32x4_t accg = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (W4) accg = *reinterpret_cast<const f32x4_t*>(&xs[gc * 16 + 4 * qq]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const u32x4_t*>(xa + (gc * kGroup + 32 * j) * 2);
-      const float sc = bf16_bits_to_f32(s_sc[(st * gcap + gc) * 16 + nn]);
-      // rows >= M start from whatever their unused entries hold: their results are never stored
-      f32x4_t accg = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if constexpr (W4) accg = *reinterpret_cast<const f32x4_t*>(&xs[gc * 16 + 4 * qq]);
+    for (int j = 0; j < 4; ++j) accg = mfma_bf16(av[j], expand<W4>(wr[u], j), accg);
+    add_group(acc, accg, base + u < ngw ? sc : 0.f);
+    // refill this slot now: without the fence the scheduler sinks all refills of the unrolled loop
+    // to its end, and every pass then waits a full memory latency for loads it has just issued
+    if (refill) ws.load(wr[u], base + u + kRingS);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // the last pass refills nothing (refills past the wave's groups would be out-of-range loads)
+  int base = 0;
+  for (; base + kRingS < ngw; base += kRingS) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) accg = mfma_bf16(av[j], expand<W4>(wr[u], j), accg);
-      add_group(acc, accg, base + u < ngw ? sc : 0.f);
-      // refill this slot now: without the fence the scheduler sinks all refills of the unrolled loop
-      // to its end, and every pass then waits a full memory latency for loads it has just issued
-      ws.load(wr[u], base + u + kRingS);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int u = 0; u < kRingS; ++u) group(base, u, true);
+  }
+  if (base < ngw) {
+#pragma unroll
+    for (int u = 0; u < kRingS; ++u) group(base, u, false);
   }
   if constexpr (WK) {
     s_red[wave * 64 + lane] = acc;
@@ -355,7 +406,7 @@ __global__ __launch_bounds__(WK ? 256 : 64 * WB) void wgemm_small_kernel(WgemmAr
     if (wave != 0) return;
     acc = s_red[lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) acc += s_red[w * 64 + lane];
+    for (int w = 1; w < WB; ++w) acc += s_red[w * 64 + lane];
   }
   f32x4_t out[1] = {acc};
   store_out<1>(a, out, tile, nn, qq);
@@ -432,7 +483,8 @@ __global__ __launch_bounds__(64 * WB, 8 / WB) void wgemm_kernel(WgemmArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int base = 0; base < ng; base += kR) {
+  // the last pass refills nothing (refills past the split would be out-of-range loads)
+  auto pass = [&](int base, bool refill) {
 #pragma unroll
     for (int u = 0; u < kR; ++u) {
       const int buf = (u >> 1) & 1;           // chunk parity (base is a multiple of 4 groups)
@@ -454,14 +506,17 @@ __global__ __launch_bounds__(64 * WB, 8 / WB) void wgemm_kernel(WgemmArgs a) {
       const float sc = bf16_bits_to_f32(s_sc[(wave * kMaxGroupsChunked + min(base + u, kMaxGroupsChunked - 1)) * 16 + nn]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) add_group(acc[mt], accg[mt], base + u < ng ? sc : 0.f);
-      ws.load(wr[u], base + u + kR);
+      if (refill) ws.load(wr[u], base + u + kR);
       __builtin_amdgcn_sched_barrier(0);
       if (gl == 1) {
         x_store(buf ^ 1, buf ^ 1);
         __syncthreads();
       }
     }
-  }
+  };
+  int base = 0;
+  for (; base + kR < ng; base += kR) pass(base, true);
+  pass(base, false);
   store_out<MT>(a, acc, tile, nn, qq);
 }
 
@@ -540,16 +595,17 @@ constexpr int64_t kTargetBlocks = 512;      // two blocks of four waves per CU
 constexpr size_t kSmallLdsMax = 80 * 1024;  // dynamic LDS of the M <= 16 kernel (two 4-wave blocks fit a CU)
 
 // activations [M][gps*128 + 8] bf16, group sums [gps][16] fp32, scales [tiles][gps][16] bf16, and for
-// the in-block K split the four waves' results [4][64] f32x4
+// the in-block K split the waves' results [kWkWaves][64] f32x4
 // Tiles (waves) per block of the split M <= 16 kernel: INT4 gains from sharing the staging and group
 // sums among eight (M=16 17.7 -> 15.2 us on 8192 x 8192), FP8, streaming twice the bytes, keeps two
 // blocks of four per CU (19.7 us against 22.6 with eight).  The LDS size allows for eight either way.
 constexpr int kSmallWaves = 8;
+constexpr int kWkWaves = 4;
 constexpr int small_waves(bool w4) { return w4 ? 8 : 4; }
 
 size_t small_lds_bytes(int32_t m, int32_t gps, bool wk = false) {
   return (size_t)m * (gps * kGroup * 2 + 16) + (size_t)gps * 16 * 4 + (size_t)(wk ? 1 : kSmallWaves) * gps * 16 * 2 +
-         (wk ? 4 * 64 * 16 : 0);
+         (wk ? kWkWaves * 64 * 16 : 0);
 }
 
 // M <= 16 with enough output tiles to fill the chip: one split, K cut among a block's waves
@@ -629,9 +685,9 @@ int gemm_common(const uint16_t* x, int32_t m, const uint8_t* w, const uint16_t* 
   if (wk) {
     const size_t lw = small_lds_bytes(m, a.groups_per_split, true);
     if (w4)
-      hipLaunchKernelGGL((wgemm_small_kernel<true, true>), dim3(n / 16, 1), dim3(256), lw, stream, a);
+      hipLaunchKernelGGL((wgemm_small_kernel<true, true, kWkWaves>), dim3(n / 16, 1), dim3(64 * kWkWaves), lw, stream, a);
     else
-      hipLaunchKernelGGL((wgemm_small_kernel<false, true>), dim3(n / 16, 1), dim3(256), lw, stream, a);
+      hipLaunchKernelGGL((wgemm_small_kernel<false, true, kWkWaves>), dim3(n / 16, 1), dim3(64 * kWkWaves), lw, stream, a);
   } else if (small) {
     constexpr int W8 = small_waves(true), W4 = small_waves(false);
     if (w4)
