@@ -563,9 +563,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
 #define KVFP8_ISSUE(T_, t_) \
   issue_tile<FP8>(T_, w0 + (t_) * kTile, w1, e0, ne, s_pid, kpool, vpool, blk, S, lgS, a.num_kv_heads, g, q4, n)
     if (FP8) {
-      // Two tiles in flight per wave.  Tiles past the end issue loads of the pool's first
-      // line (masked), so the body is straight-line and both loop edges leave the same
-      // 2 x 16 loads outstanding (A older than B).
+      // Two tiles in flight per wave (A older than B).  The first two are issued whatever the wave's
+      // count (a tile past the end reads masked copies of the pool's first line); after them no refill
+      // goes past the wave's last tile -- such loads still cost their issue and return, and the block's
+      // final wait waits for them.  The loop runs while both refills lie inside; the last two or three
+      // tiles form a tail after it, the third issued only if it exists (a branch after the loop, so the
+      // loop's load counts stay exact).
       const int nt = wave < ntile ? (ntile - wave + kWaves - 1) / kWaves : 0;  // this wave's tiles
       TileRegs<FP8> A, B;
       KVFP8_ISSUE(A, t);
@@ -573,13 +576,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gqa_split_kernel(AttnArgs a)
       KVFP8_ISSUE(B, t + kWaves);
       __builtin_amdgcn_sched_barrier(0);
       int i = 0;
-      for (; i + 2 <= nt; i += 2) {
+      for (; i + 4 <= nt; i += 2) {
         compute_tile<FP8>(A, qv, c_log2, st);
         KVFP8_ISSUE(A, t + (i + 2) * kWaves);
         __builtin_amdgcn_sched_barrier(0);
         compute_tile<FP8>(B, qv, c_log2, st);
         KVFP8_ISSUE(B, t + (i + 3) * kWaves);
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i + 2 <= nt) {
+        compute_tile<FP8>(A, qv, c_log2, st);
+        if (i + 3 == nt) KVFP8_ISSUE(A, t + (i + 2) * kWaves);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_tile<FP8>(B, qv, c_log2, st);
+        i += 2;
       }
       if (i < nt) compute_tile<FP8>(A, qv, c_log2, st);
     } else {
