@@ -108,6 +108,20 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// wait until at most the copies of n tiles (NPW loads each; n clamped to 0 .. MAXT) are outstanding
+template <int NPW, int MAXT>
+__device__ __forceinline__ void vm_wait_tiles(int n) {
+  if constexpr (MAXT > 0) {
+    if (n >= MAXT) {
+      vm_wait<NPW * MAXT>();
+      return;
+    }
+    vm_wait_tiles<NPW, MAXT - 1>(n);
+  } else {
+    vm_wait<0>();
+  }
+}
+
 // CHECK: the launch also runs the tag check (a.page_tags non-null).  A variant of its own, so that the
 // launches without it keep the register allocation of the kernel without the check code (the
 // 128-head kernel uses the whole register file).
@@ -330,10 +344,12 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
     ntile = (w1 - w0 + kLT - 1) / kLT;
   };
 
-  // Copy tile t of the window into buffer bi: NPW 16-byte global->LDS loads per lane.  Every
-  // lane of every copy loads from inside the pool: tokens past the window end re-read the tile's
-  // first row (finite data, weight 0), padding slots and tiles past the end read the first
-  // row too, and a page id outside the pool reads the pool's first page (the request is zeroed).
+  // Copy tile t of the window into buffer bi: NPW 16-byte global->LDS loads per lane.  FP8 copies no
+  // tile past the window's end (such loads would still cost their issue and return); BF16 does, since
+  // the branch costs it a spill.  Every lane of every copy loads from inside the pool: tokens past the
+  // window end re-read the tile's first row (finite data, weight 0), padding slots and tiles past the
+  // end read the first row too, and a page id outside the pool reads the pool's first page (the
+  // request is zeroed).
   struct CopyTile {
     const uint8_t* base0;
     const uint8_t* base1;
@@ -368,6 +384,9 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
     lds_copy16(src, ct.dst + 1024 * k);
   };
   auto copy_tile = [&](int t, int bi) {
+    if constexpr (FP8) {
+      if (t >= ntile) return;
+    }
     const CopyTile ct = copy_prep(t, bi);
 #pragma unroll
     for (int k = 0; k < C::NPW; ++k) copy_one(ct, k);
@@ -414,7 +433,9 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
   }
   while (true) {
     for (int t = -1; t < ntile; ++t) {
-      vm_wait<C::NPW * (C::NBUF - 3)>();  // this wave's copies of tile t+1 have landed
+      // this wave's copies of tile t+1 have landed: those issued after them are the copies of the next
+      // NBUF-3 tiles (FP8: of those that exist)
+      vm_wait_tiles<C::NPW, C::NBUF - 3>(FP8 ? ntile - (t + 2) : C::NBUF - 3);
       __syncthreads();                    // everyone's have; everyone is done with tile t-1
       copy_tile(t + C::NBUF - 1, (t + C::NBUF - 1) % C::NBUF);
       if (!active) continue;
@@ -479,8 +500,8 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_split_kernel(LatentArgs
       }
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
-      // ---- S^T of tile t+1 = C q^T over all 576 dims (past the last tile the reads hit a buffer with
-      // finite data and the result is unused).  Step p issues the read QD steps ahead and one or two
+      // ---- S^T of tile t+1 = C q^T over all 576 dims (past the last tile the reads hit a buffer whose
+      // contents are stale and the result is unused).  Step p issues the read QD steps ahead and one or two
       // of tile t's exponentials while the MFMAs of step p-1 run, then issues step p's MFMAs.
       float psum = 0.f;
       u32x4_t qb[QD + 1][2];

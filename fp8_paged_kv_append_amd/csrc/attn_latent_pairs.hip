@@ -77,6 +77,20 @@ __device__ __forceinline__ void pair_vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// wait until at most the copies of n tiles (NPW loads each; n clamped to 0 .. MAXT) are outstanding
+template <int NPW, int MAXT>
+__device__ __forceinline__ void pair_vm_wait_tiles(int n) {
+  if constexpr (MAXT > 0) {
+    if (n >= MAXT) {
+      pair_vm_wait<NPW * MAXT>();
+      return;
+    }
+    pair_vm_wait_tiles<NPW, MAXT - 1>(n);
+  } else {
+    pair_vm_wait<0>();
+  }
+}
+
 // token of PV slot 8 q4 + j
 __device__ __forceinline__ int pv_token(int q4, int j) { return j < 4 ? 4 * q4 + j : 16 + 4 * q4 + (j - 4); }
 
@@ -245,13 +259,13 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_latent_pair_kernel(LatentAr
     __syncthreads();
     const int ntile = (w1 - w0 + kPT - 1) / kPT;
 
-    // Copy tile t into buffer bi; every load stays inside the pool (tokens past the end, padding
-    // slots and tiles past the window re-read the tile's first row; a bad page id reads page 0).
+    // Copy tile t into buffer bi; a tile past the window is not copied (such loads would still cost
+    // their issue and return).  Every load stays inside the pool (tokens past the end and padding
+    // slots re-read the tile's first row; a bad page id reads page 0).
     auto copy_tile = [&](int t, int bi) {
-      const int tb = w0 + t * kPT;
-      const bool live = t < ntile;
-      const int nv = live ? w1 - tb : 0;
-      const int tb_c = live ? tb : w0;
+      if (t >= ntile) return;
+      const int tb_c = w0 + t * kPT;  // t < ntile
+      const int nv = w1 - tb_c;
       // (S a power of two: page and slot by shift and mask; both page ids read from LDS together)
       const int s0 = __builtin_amdgcn_readfirstlane(s_pid[(tb_c >> lgS) - e0]);
       const int s1 = __builtin_amdgcn_readfirstlane(s_pid[min(((tb_c + 16) >> lgS) - e0, ne - 1)]);
@@ -273,7 +287,9 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_latent_pair_kernel(LatentAr
 #pragma unroll
     for (int t = 0; t < kNBuf - 2; ++t) copy_tile(t, t);
     for (int t = -1; t < ntile; ++t) {
-      pair_vm_wait<kNPW * (kNBuf - 3)>();  // this wave's copies of tile t+1 have landed
+      // this wave's copies of tile t+1 have landed: those issued after them are the copies of the next
+      // kNBuf-3 tiles that exist
+      pair_vm_wait_tiles<kNPW, kNBuf - 3>(ntile - (t + 2));
       __syncthreads();                     // everyone's have; everyone is done with tile t-1
       copy_tile(t + kNBuf - 1, (t + kNBuf - 1) % kNBuf);
       if (!active) continue;
@@ -318,7 +334,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_latent_pair_kernel(LatentAr
       }
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
-      // ---- partial S^T of tile t+1 over this wave's dims (reads past the last tile hit finite data);
+      // ---- partial S^T of tile t+1 over this wave's dims (past the last tile the reads hit stale data);
       // the two token blocks' MFMA chains alternate
       f32x4_t sn[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
