@@ -284,7 +284,9 @@ __device__ __forceinline__ void store_out(const WgemmArgs& a, const f32x4_t (&ac
 // the w-th part of the groups); they add their results through LDS in wave order -- a K split with
 // neither a workspace nor a second launch.  Eight or sixteen waves per tile measured slower at M=1
 // (INT4 11.0 / 11.8 against 9.1 us on 8192 x 8192).
-template <bool W4, bool WK, int WB>
+// XB: activation loads per thread and batch (0: 4096 / threads); the launch sizes it to the split's rows so
+// that no pass of the last batch lies wholly past them in the split form.
+template <bool W4, bool WK, int WB, int XB = 0>
 __global__ __launch_bounds__(64 * WB) void wgemm_small_kernel(WgemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int kTiles = WK ? 1 : WB;
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(64 * WB) void wgemm_small_kernel(WgemmArgs a) {
       if (i < total && (threadIdx.x & 15) == 0) xs[((i % per_row) >> 4) * 16 + i / per_row] = -kW4Bias * sum;
     }
   };
-  constexpr int kXB = 4096 / kThr;                       // activation loads per thread and batch
+  constexpr int kXB = XB ? XB : 4096 / kThr;             // activation loads per thread and batch
   int xbase = 0;
   for (; xbase + kThr * kXB < total; xbase += kThr * kXB) {
     u32x4_t v[kXB];
@@ -690,12 +692,20 @@ int gemm_common(const uint16_t* x, int32_t m, const uint8_t* w, const uint16_t* 
       hipLaunchKernelGGL((wgemm_small_kernel<false, true, kWkWaves>), dim3(n / 16, 1), dim3(64 * kWkWaves), lw, stream, a);
   } else if (small) {
     constexpr int W8 = small_waves(true), W4 = small_waves(false);
-    if (w4)
-      hipLaunchKernelGGL((wgemm_small_kernel<true, false, W8>), dim3((n / 16 + W8 - 1) / W8, splits), dim3(64 * W8),
-                         lds, stream, a);
-    else
-      hipLaunchKernelGGL((wgemm_small_kernel<false, false, W4>), dim3((n / 16 + W4 - 1) / W4, splits),
-                         dim3(64 * W4), lds, stream, a);
+    // loads per thread that cover a full split's rows: half the default where that suffices
+    const int64_t rows16 = (int64_t)m * a.groups_per_split * (kGroup / 8);   // 16-byte activation loads
+    const dim3 g8((n / 16 + W8 - 1) / W8, splits), g4((n / 16 + W4 - 1) / W4, splits);
+    if (w4) {
+      if (rows16 <= 64 * W8 * (2048 / (64 * W8)))
+        hipLaunchKernelGGL((wgemm_small_kernel<true, false, W8, 2048 / (64 * W8)>), g8, dim3(64 * W8), lds, stream, a);
+      else
+        hipLaunchKernelGGL((wgemm_small_kernel<true, false, W8>), g8, dim3(64 * W8), lds, stream, a);
+    } else {
+      if (rows16 <= 64 * W4 * (2048 / (64 * W4)))
+        hipLaunchKernelGGL((wgemm_small_kernel<false, false, W4, 2048 / (64 * W4)>), g4, dim3(64 * W4), lds, stream, a);
+      else
+        hipLaunchKernelGGL((wgemm_small_kernel<false, false, W4>), g4, dim3(64 * W4), lds, stream, a);
+    }
   } else {
     const int mt = (m + 15) / 16;
     if (w4) {
