@@ -22,11 +22,11 @@
 // Work decomposition.  Block = 4 waves = 64 output channels x one split of the K range; wave w owns
 // output tile 4*blockIdx.x + w.  For M <= 16 the split's activation rows stay resident in LDS; above,
 // 256-wide K chunks are staged in LDS (double buffered, the next chunk's global loads issued a chunk
-// ahead).  Either way the four waves share them; each
-// wave streams its own weight tiles with a register ring of 8 groups (8 KB of INT4 / 16 KB of FP8 in
-// flight per wave; 4 INT4 / 8 FP8 groups when the waves split one tile's K range; M > 16: 8 groups up to
-// 32 rows, 4 above), whose last pass issues no refills.  With several splits, fp32 partials go to the workspace and the last block of each
-// column group to finish adds them in split order, inside the same launch.
+// ahead).  Either way the four waves share them; each wave streams its own weight tiles with a register
+// ring of 8 groups (8 KB of INT4 / 16 KB of FP8 in flight per wave; 4 INT4 / 8 FP8 groups when the waves
+// split one tile's K range; M > 16: 8 groups up to 32 rows, 4 above), whose last pass issues no refills.
+// With several splits, fp32 partials go to the workspace and the last block of each column group to
+// finish adds them in split order, inside the same launch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
