@@ -56,6 +56,20 @@ def test_gqa_ragged_lengths(kv_dtype):
 
 
 @pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_wave_tile_counts(kv_dtype):
+    """Every count of 64-token tiles per wave from 0 to 7, odd and even (each wave of a block takes every
+    fourth tile: its two-tile ring has a tail of two or three and issues nothing past its last tile), in one
+    split and in two (a short last chunk)."""
+    lens = np.array([64, 128, 320, 512, 576, 768, 1088, 1280, 1344, 1536, 1600, 1283], dtype=np.int32)
+    w = wl.WORKLOADS["gqa_batch"].with_(batch=len(lens), num_pages=1000, ctx_lo=64, ctx_hi=1600)
+    note(f"wave tile counts {kv_dtype}")
+    c = Case(w, kv_dtype, lens=lens)
+    c.fill_device()
+    for splits in (1, 2):
+        _check(c, c.attend(num_splits=splits))
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
 def test_long_context_outliers_page64(kv_dtype):
     """Page size 64, 32 splits with log-sum-exp merge, K outliers x20 past the calibrated range (saturating)."""
     w = wl.WORKLOADS["long"].with_(batch=2, num_pages=300, ctx_lo=8000, ctx_hi=8192)

@@ -60,6 +60,25 @@ def test_latent_ragged(kv_dtype, hq):
 
 
 @pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_latent_short_last_splits(kv_dtype):
+    """Two splits of 35 tiles (1,120 tokens: the 128-head kernel, not the wave-pair one), the requests' second
+    split holding 1 to 6 tiles and the first a whole one: the tile-copy ring copies nothing past a split's
+    last tile and waits only for copies it issued.  Then the library's split count (the wave-pair kernel for
+    FP8, splits of at most 1,024 tokens) over the same requests."""
+    lens = np.array([1121, 1152, 1184, 1216, 1248, 1280, 1312, 2240], dtype=np.int32)
+    w = wl.WORKLOADS["latent"].with_(batch=len(lens), num_pages=250, ctx_lo=1121, ctx_hi=2240)
+    note(f"latent short last splits {kv_dtype}")
+    c = Case(w, kv_dtype, lens=lens)
+    c.fill_device()
+    outs = []
+    for splits in (2, 0):
+        got = _latent_attend(c, num_splits=splits)
+        _check(c, got)
+        outs.append(codec.f64_from_bf16(got))
+    assert np.max(attention.row_rel_error(outs[1], outs[0])) <= 2.0 ** -7
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
 def test_latent_page16_and_abort(kv_dtype):
     w = wl.WORKLOADS["latent"].with_(batch=4, num_q_heads=64, page_size=16, num_pages=200, ctx_lo=100, ctx_hi=800)
     note(f"latent page16/abort {kv_dtype}")
