@@ -1,5 +1,5 @@
 """The oracle's multi-layer step (CPU): layers that share one page table and one set of tags take one
-tag check, and its verdict holds in every layer (agentlenshq summary, section "KV Cache 完整性检查": a
+tag check, and its outcome holds in every layer (agentlenshq summary, section "KV Cache 完整性检查": a
 stale request is aborted before anything reads the cache).  Pins: a stale request is zero and its
 new token is written in no layer; permuting the layers permutes the results; with nothing stale each
 layer equals the single-layer step (itself pinned by closed forms and brute force)."""
