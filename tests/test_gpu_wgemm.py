@@ -129,10 +129,12 @@ def test_gemm_tiny_and_zero_rows(bits):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("m", [1, 3, 64])
+@pytest.mark.parametrize("m", [1, 3, 8, 16, 64])
 def test_gemm_full_size_sampled(bits, m):
-    """8192 x 8192 weights (one matrix of the benchmark's stack), the library's split choice: the codes of
-    sampled 16-row tiles bit-exact to the oracle's, and y on those tiles' columns within tolerance."""
+    """8192 x 8192 weights (one matrix of the benchmark's stack), the library's split choice at the
+    benchmark's row counts and M=3 (the in-block K split at M <= 4, the split form with its staging sized to
+    8 rows and to 16, the chunked form at 64): the codes of sampled 16-row tiles bit-exact to the oracle's,
+    and y on those tiles' columns within tolerance."""
     sh = wsyn.SHAPES["stack_8k"]
     note(f"gemm w{bits} 8192x8192 m={m}")
     w = wsyn.weights(sh, layer=0)
