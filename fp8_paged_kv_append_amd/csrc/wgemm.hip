@@ -108,22 +108,29 @@ __device__ __forceinline__ uint32_t w4_bias() {
 // loop (scales and activations come from LDS), which keeps the compiler's waits exact: a conditional
 // load, or a second load kind issued in another order before the loop, makes it wait for the whole ring.
 // POL: the loads' cache policy (non-temporal by default; see the M <= 16 kernel for the exception).
+// rot: the stream starts at group rot (mod ng) and wraps around, so that waves whose ranges start a
+// multiple of 16 KB apart do not read the same offset of them at the same time.
 template <bool W4, int POL = kNT>
 struct WStream {
   static constexpr int kB = W4 ? 16 : 32;   // code bytes per lane per group
   __amdgpu_buffer_rsrc_t codes;
   uint32_t cbase;
-  int ng;
+  int ng, rot;
   bool active;
-  __device__ WStream(const WgemmArgs& a, int tile, int g0, int ng_, int lane) {
+  __device__ WStream(const WgemmArgs& a, int tile, int g0, int ng_, int lane, int rot_ = 0) {
     const int KG = a.K / kGroup;
     active = tile * 16 < a.N;
     ng = ng_;
+    rot = ng_ > 0 ? rot_ % ng_ : 0;
     codes = make_rsrc(a.w, (uint32_t)((int64_t)a.N * a.K / (W4 ? 2 : 1)));
     cbase = (uint32_t)((((int64_t)tile * KG + g0) * 64 + lane) * kB);
   }
+  __device__ __forceinline__ int idx(int g) const {   // the group read in place g of the stream
+    const int gg = g + rot;
+    return gg >= ng ? gg - ng : gg;
+  }
   __device__ __forceinline__ void load(u32x4_t (&w)[kB / 16], int g) const {
-    const uint32_t co = (active && g < ng) ? cbase + (uint32_t)g * 64 * kB : kOOB;
+    const uint32_t co = (active && g < ng) ? cbase + (uint32_t)idx(g) * 64 * kB : kOOB;
 #pragma unroll
     for (int d = 0; d < kB / 16; ++d) w[d] = __builtin_amdgcn_raw_buffer_load_b128(codes, co + 16 * d, 0, POL);
   }
@@ -319,8 +326,10 @@ __global__ __launch_bounds__(64 * WB) void wgemm_small_kernel(WgemmArgs a) {
   const int st = WK ? 0 : wave;                          // the wave's tile inside s_sc
 
   // FP8 codes over split blocks stream faster with the default cache policy than non-temporal (M = 8 / 16:
-  // 18.35 -> 17.6 / 19.4 -> 18.3 us on 8192 x 8192); every other form measured level or slower with it
-  const WStream<W4, (!W4 && !WK) ? 0 : kNT> ws(a, tile, g0 + gw0, ngw, lane);
+  // 18.35 -> 17.6 / 19.4 -> 18.3 us on 8192 x 8192); every other form measured level or slower with it.
+  // Over split blocks each wave also starts its groups at a rotation of its own (tiles are 64 KB apart in
+  // memory): M = 8 INT4 12.5 -> 12.0, FP8 17.6 -> 16.8 us; the K-split form measured slower with it.
+  const WStream<W4, (!W4 && !WK) ? 0 : kNT> ws(a, tile, g0 + gw0, ngw, lane, WK ? 0 : tile * 7 + wave * 5);
   constexpr int kB = WStream<W4>::kB;
   u32x4_t sc_last;
   const int sc_slot = load_scales_split(a, WK ? blockIdx.x : blockIdx.x * WB, kTiles, g0, ng, gcap, s_sc, kThr, sc_last);
@@ -379,7 +388,7 @@ __global__ __launch_bounds__(64 * WB) void wgemm_small_kernel(WgemmArgs a) {
   const uint8_t* xa = smem + min(nn, a.M - 1) * row_bytes + 16 * qq;
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
   auto group = [&](int base, int u, bool refill) {
-    const int gc = gw0 + min(base + u, ngw - 1);   // a group past the wave's range has zero codes and scale
+    const int gc = gw0 + ws.idx(min(base + u, ngw - 1));   // past the wave's range: zero codes and scale
     u32x4_t av[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const u32x4_t*>(xa + (gc * kGroup + 32 * j) * 2);
