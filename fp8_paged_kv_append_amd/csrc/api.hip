@@ -28,8 +28,10 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // 30.7; 4 x 131072 tokens at 32 splits 167.0 us with the separate merge, 182.5 with the merge inside.
 constexpr int32_t kMergeInLaunchMaxSplits = 16;
 
+// The split counts at the head of an attention workspace: a 128-byte line per (request, query head), so
+// that the GQA counts (one per (request, KV head), a line apart) never share one.
 inline size_t attn_count_bytes(int32_t batch, int32_t num_q_heads) {
-  return ((size_t)batch * num_q_heads * 4 + 255) / 256 * 256;
+  return ((size_t)batch * num_q_heads * 128 + 255) / 256 * 256;
 }
 inline bool good_scale(float s) { return isfinite(s) && s > 0.f; }
 // The softmax scale a caller passes, with 0 standing for the usual 1/sqrt(score dim).
@@ -586,8 +588,8 @@ int kv_decode_step_bf16(const kvfp8_pool_desc* desc, const kvfp8_layer_stack* la
 size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t v_dim, int32_t num_splits) {
   if (batch <= 0 || num_q_heads <= 0 || v_dim <= 0 || num_splits <= 1) return 0;
   const size_t rows = (size_t)batch * num_q_heads * num_splits;
-  // the split counters, then the partials (fp32; the FP8 latent 128-head kernel stores fp16 in the first
-  // half of the same region) and lse of every (request, head, split)
+  // the split counters, then the partials (fp32; the FP8 kernels store fp16 in the first half of the same
+  // region) and lse of every (request, head, split)
   return attn_count_bytes(batch, num_q_heads) + rows * (size_t)v_dim * sizeof(float) + rows * sizeof(float);
 }
 

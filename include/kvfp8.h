@@ -175,9 +175,10 @@ int kv_tag_check_append_bf16(const kvfp8_pool_desc* desc, uint16_t* k_pool, uint
  *   num_splits: 0 = chosen by the library; otherwise at most
  *   ceil(max_ctx_len/64).  workspace (device, 16-byte aligned): at least
  *   paged_decode_attn_workspace_bytes(...) bytes for the split count used
- *   (0 when it is 1; then workspace may be NULL).  It opens with
- *   B*Hq uint32 counters (padded to 256 bytes) that must be zero before the
- *   first call that uses the workspace (allocate it zeroed once); every call
+ *   (0 when it is 1; then workspace may be NULL).  It opens with B*Hq
+ *   128-byte lines of uint32 counters (padded to 256 bytes; counters that
+ *   shared a line would make the split blocks queue on it) that must be zero
+ *   before the first call that uses the workspace (allocate it zeroed once); every call
  *   leaves them zero, so a workspace serves any sequence of ordered calls,
  *   GQA or latent, of any shape it is large enough for.  With 2..16 splits
  *   the GQA launch merges them itself (the last split block of each

@@ -171,5 +171,5 @@ def test_host_validation_codes(lib):
     assert lib.kv_read_blocks(A + 8, 16, 2048, A, 4, A, None) == -5
     assert lib.paged_decode_attn_workspace_bytes(64, 64, 128, 1) == 0
     # split counters (one per request and query head, padded to 256 B), then partials and lse
-    assert lib.paged_decode_attn_workspace_bytes(64, 64, 128, 2) == 64 * 64 * 4 + 64 * 64 * 2 * 129 * 4
-    assert lib.paged_decode_attn_workspace_bytes(1, 8, 512, 4) == 256 + 8 * 4 * 513 * 4
+    assert lib.paged_decode_attn_workspace_bytes(64, 64, 128, 2) == 64 * 64 * 128 + 64 * 64 * 2 * 129 * 4
+    assert lib.paged_decode_attn_workspace_bytes(1, 8, 512, 4) == 1024 + 8 * 4 * 513 * 4
