@@ -73,8 +73,9 @@ int w8_quantize_bf16(const uint16_t* w, int32_t n, int32_t k, uint8_t* packed, u
  * go to `workspace` (device, 16-byte aligned, at least
  * wgemm_workspace_bytes(M, N, K, splits) bytes; 0 and NULL allowed for one
  * split), and the last block of each column group to finish adds them in
- * split order.  The workspace opens with ceil(N/16) uint32 counters (padded
- * to 256 bytes) that must be zero before the first call that uses it (e.g.
+ * split order.  The workspace opens with ceil(N/16) uint32 counters, one
+ * per 128-byte line (padded to 256 bytes), that must be zero before the
+ * first call that uses it (e.g.
  * allocate it zeroed once); every call leaves them zero, so one workspace
  * serves any sequence of calls on one stream.  Calls that overlap in time
  * must not share a workspace. */

@@ -156,9 +156,9 @@ def test_host_validation_codes(lib):
     assert lib.wgemm_workspace_bytes(4, 64, 512, 1) == 0
     # counters (padded to 256 B), then 1 KiB of partials per split, 16-channel tile (N rounded up to 128) and
     # 16-row tile
-    assert lib.wgemm_workspace_bytes(4, 64, 512, 2) == 256 + 2 * 8 * 1024
-    assert lib.wgemm_workspace_bytes(1, 8192, 8192, 4) == 2048 + 4 * 512 * 1024
-    assert lib.wgemm_workspace_bytes(33, 8192, 8192, 4) == 2048 + 4 * 512 * 3 * 1024
+    assert lib.wgemm_workspace_bytes(4, 64, 512, 2) == 512 + 2 * 8 * 1024
+    assert lib.wgemm_workspace_bytes(1, 8192, 8192, 4) == 65536 + 4 * 512 * 1024
+    assert lib.wgemm_workspace_bytes(33, 8192, 8192, 4) == 65536 + 4 * 512 * 3 * 1024
     assert 1 <= lib.wgemm_auto_splits(1, 8192, 8192) <= 32
     # read-rate calibration
     assert lib.kv_read_stream(A, 0, A, None) == 0
