@@ -56,6 +56,30 @@ def test_gqa_ragged_lengths(kv_dtype):
 
 
 @pytest.mark.parametrize("kv_dtype", DTYPES)
+def test_values_beyond_fp16_range_with_splits(kv_dtype, monkeypatch):
+    """Values up to ~2e7 in magnitude, far beyond fp16's largest finite 65504 (each drawn value times 2^22,
+    exact in bf16): the split partials and their merge, inside the launch up to 16 splits and by a merge launch
+    beyond, keep every row within the bar.  The FP8 cache's partials are fp16 in units of the e4m3 codes,
+    which stay within 448 whatever the scale; partials of the scaled values themselves would overflow."""
+    draw_v = wl.request_v
+
+    def big_v(w, r, length):
+        f = (draw_v(w, r, length).astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** 22)
+        return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+    monkeypatch.setattr(wl, "request_v", big_v)
+    w = wl.WORKLOADS["gqa_batch"].with_(batch=3, num_pages=400, ctx_lo=1, ctx_hi=2000)
+    note(f"values beyond fp16 range {kv_dtype}")
+    c = Case(w, kv_dtype, lens=np.array([2000, 1100, 333], dtype=np.int32))
+    assert np.abs(codec.f64_from_bf16(c.v)).max() > 65504.0
+    c.fill_device()
+    for splits in (1, 4, 16, 20):
+        got = c.attend(num_splits=splits)
+        assert np.abs(codec.f64_from_bf16(got)).max() > 65504.0
+        _check(c, got)
+
+
+@pytest.mark.parametrize("kv_dtype", DTYPES)
 def test_wave_tile_counts(kv_dtype):
     """Every count of 64-token tiles per wave from 0 to 7, odd and even (each wave of a block takes every
     fourth tile: its two-tile ring has a tail of two or three and issues nothing past its last tile), in one
