@@ -277,7 +277,7 @@ __device__ __forceinline__ void compute_tile(TileRegs<FP8>& T, const u32x4_t (&q
 // zero after it.  Counts that shared a line made the blocks of different KV heads queue on it (one
 // request, 61 layers: 16 splits 12.84 -> 12.68 us per layer; 24 / 32 splits merged here 14.5 / 15.7 ->
 // 13.7 / 14.2 us).  FP8 partials are fp16 in units of the e4m3 codes: o / l is a convex combination of
-// decoded codes (|x| <= 448, no overflow, rounding 2^-12 relative) and the merge applies v_scale; half
+// decoded codes (|x| <= 448, no overflow, rounding at most 2^-11 relative) and the merge applies v_scale; half
 // the bytes of fp32 partials to store and to merge (12.74 -> 12.64 us per layer).  BF16 partials are fp32.
 constexpr int kCohAux = 16;       // cache-policy operand of a buffer access: sc1
 constexpr int kMergeGroup = 16;   // splits whose lse and partials are loaded together
